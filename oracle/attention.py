@@ -1,0 +1,117 @@
+"""Mixed-mask canvas attention over a paged KV prefix.
+
+Follows:
+  * DiffusionGemma/vLLM page, section "Two modes, one set of weights": the
+    encoder mode (prompt prefill and the commit pass) is causal and writes
+    K/V to the cache; the decoder (denoise) mode is bidirectional over the
+    canvas and only reads the cache;
+  * same page, section "Dynamic per-sequence causal attention": requests at
+    different phases share one batch, causality is a per-request property,
+    and in the three-request figure a canvas of 4 sees its whole context and
+    every canvas key while prefill/commit rows see keys up to themselves;
+  * single-pass-reads page ("DiffusionGemma's execution path merged",
+    portfolio.ywsung.com), section on keeping each row's visibility: a merged
+    launch splits a request into input (causal) rows and canvas rows that
+    share the request's KV block table; in the p0 p1 c0 c1 example p0 sees
+    p0, p1 sees p0 p1, and c0, c1 see p0 p1 c0 c1.
+
+Visibility rule for one request with ``cached`` prefix tokens, ``n_causal``
+causal rows and ``n_canvas`` canvas rows (key index space: cache positions
+0 .. cached + n_causal - 1, then the canvas rows):
+  causal row j  -> keys 0 .. cached + j
+  canvas row    -> every key of the request
+Causal rows' K/V are appended to the paged cache at positions cached + j
+before any row reads; canvas K/V are never written.  Scores use
+scale * q . k, softmax over visible keys only, output = sum p v.  GQA: query
+head h reads KV head h // (Hq / Hkv).  No position encoding is applied (the
+inputs are synthetic Q/K/V).
+
+Pinned by tests/test_oracle_attention.py: the p0/p1/c0/c1 and the
+three-request visibility fixtures in tests/golden/, brute-force dense-mask
+attention on random shapes, one-visible-key and equal-score special cases,
+and permutation / page-relabelling invariances.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def visibility_mask(cached: int, n_causal: int, n_canvas: int) -> np.ndarray:
+    """Boolean [n_causal + n_canvas, cached + n_causal + n_canvas] mask of one request."""
+    nk = cached + n_causal + n_canvas
+    rows = n_causal + n_canvas
+    mask = np.zeros((rows, nk), dtype=bool)
+    for j in range(n_causal):
+        mask[j, :cached + j + 1] = True
+    mask[n_causal:, :] = True
+    return mask
+
+
+def dense_mask_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float) -> np.ndarray:
+    """Brute force: q [R, D], k/v [K, D], mask [R, K] -> out [R, D] (fp64).  Rows with no visible key give 0."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for r in range(q.shape[0]):
+        idx = np.nonzero(mask[r])[0]
+        if idx.size == 0:
+            continue
+        s = scale * (k[idx] @ q[r])
+        w = np.exp(s - np.max(s))
+        out[r] = (w / np.sum(w)) @ v[idx]
+    return out
+
+
+def append_causal_kv(k_cache, v_cache, k_new, v_new, page_table, row0, cached, n_causal, page0, page_size):
+    """Write one request's causal-row K/V ([rows, Hkv, D]) into its pages at positions cached + j."""
+    for j in range(n_causal):
+        pos = cached + j
+        page = int(page_table[page0 + pos // page_size])
+        k_cache[page, :, pos % page_size, :] = k_new[row0 + j]
+        v_cache[page, :, pos % page_size, :] = v_new[row0 + j]
+
+
+def gather_request_kv(k_cache, v_cache, k_new, v_new, page_table, row0, cached, n_causal, n_canvas, page0, page_size):
+    """Keys/values of one request in key-index order: cache positions, then canvas rows. [nk, Hkv, D]."""
+    n_cache = cached + n_causal
+    Hkv, D = k_cache.shape[1], k_cache.shape[3]
+    K = np.zeros((n_cache + n_canvas, Hkv, D), dtype=np.float64)
+    Vv = np.zeros_like(K)
+    for pos in range(n_cache):
+        page = int(page_table[page0 + pos // page_size])
+        K[pos] = k_cache[page, :, pos % page_size, :]
+        Vv[pos] = v_cache[page, :, pos % page_size, :]
+    c0 = row0 + n_causal
+    K[n_cache:] = k_new[c0:c0 + n_canvas]
+    Vv[n_cache:] = v_new[c0:c0 + n_canvas]
+    return K, Vv
+
+
+def canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, page_size: int, scale: float):
+    """Oracle for one launch.
+
+    q [rows, Hq, D]; k, v [rows, Hkv, D]; caches [pages, Hkv, page_size, D] (float arrays);
+    splits: iterable of (row0, cached, n_causal, n_canvas, page0).
+    Returns (out [rows, Hq, D] fp64, k_cache', v_cache' with causal K/V appended).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    rows, Hq, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((rows, Hq, D))
+    splits = [tuple(int(t) for t in s) for s in splits]
+    for (row0, cached, n_causal, n_canvas, page0) in splits:
+        append_causal_kv(kc, vc, k, v, page_table, row0, cached, n_causal, page0, page_size)
+    for (row0, cached, n_causal, n_canvas, page0) in splits:
+        K, Vv = gather_request_kv(kc, vc, k, v, page_table, row0, cached, n_causal, n_canvas, page0, page_size)
+        mask = visibility_mask(cached, n_causal, n_canvas)
+        nr = n_causal + n_canvas
+        for h in range(Hq):
+            hk = h // group
+            out[row0:row0 + nr, h] = dense_mask_attention(q[row0:row0 + nr, h], K[:, hk], Vv[:, hk], mask, scale)
+    return out, kc, vc

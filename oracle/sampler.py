@@ -1,0 +1,112 @@
+"""Per-position denoise sampler: softmax statistics, entropy, argmax, Gumbel-max candidate.
+
+Follows the DiffusionGemma/vLLM page (discuss.pytorch.kr, "DiffusionGemma: the
+first dLLM natively supported by vLLM"):
+  * section "Entropy-based denoising": every position is resampled each step
+    and its confidence is the entropy H(p) = -sum_i p_i log p_i of its
+    predicted distribution;
+  * section "DiffusionGemmaModelState and DiffusionSampler", denoise case:
+    logits are divided by the temperature T and a candidate is drawn with the
+    Gumbel-max trick, argmax(logits / T + g); the argmax canvas is recorded.
+
+Readings (the pages are silent): natural log (nats); H clamped at 0; argmax
+and sample ties go to the lowest vocabulary index; the Gumbel noise is the
+Philox stream of ``oracle.philox``.  Also returned: m = max_i x_i and
+ln Z = ln sum_i exp(x_i - m), which define p_i = exp(x_i - m - ln Z) for the
+self-conditioning step.
+
+Pinned by tests/test_oracle_sampler.py: entropy closed forms (uniform row ->
+ln V, one-hot -> 0, two-point, k equal maxima -> ln k), shift invariance,
+sum p = 1, argmax == numpy.argmax, and a chi-square test that Gumbel-max
+samples follow softmax(x).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import philox
+
+
+@dataclass
+class SampleOut:
+    entropy: np.ndarray     # float64 [rows]
+    argmax: np.ndarray      # int64 [rows]
+    sample: np.ndarray      # int64 [rows]  (-1 when argmax-only)
+    row_max: np.ndarray     # float64 [rows]  m = max x
+    row_lnz: np.ndarray     # float64 [rows]  ln sum exp(x - m)
+    argmax_gap: np.ndarray  # float64 [rows]  top value minus best value at any other index
+    key_gap: np.ndarray     # float64 [rows]  same for the Gumbel keys (inf when argmax-only)
+
+
+def softmax_stats(x: np.ndarray):
+    """m, Z, S and H for one row of scaled logits x (fp64).
+
+    m = max x;  Z = sum exp(x - m);  S = sum exp(x - m) (x - m);
+    H = -sum p log p with p = exp(x - m) / Z, which expands to ln Z - S / Z.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x)
+    e = np.exp(x - m)
+    Z = np.sum(e)
+    S = np.sum(e * (x - m))
+    H = max(0.0, float(np.log(Z) - S / Z))
+    return float(m), float(Z), float(S), H
+
+
+def entropy_direct(p: np.ndarray) -> float:
+    """-sum p log p with 0 log 0 = 0 (the definition, used by the pins)."""
+    p = np.asarray(p, dtype=np.float64)
+    nz = p > 0
+    return float(-np.sum(p[nz] * np.log(p[nz])))
+
+
+def _top2_gap(v: np.ndarray) -> float:
+    if v.size < 2:
+        return np.inf
+    i = int(np.argmax(v))
+    rest = np.delete(v, i)
+    return float(v[i] - np.max(rest))
+
+
+def denoise_sample(logits: np.ndarray, temperature: float, seeds, steps, rows_per_req: int,
+                   argmax_only: bool = False, active=None) -> SampleOut:
+    """Sampler over logit rows.
+
+    logits: [rows, V] (already decoded to float; bf16 inputs are exact in fp64).
+    Row r belongs to request r // rows_per_req at canvas position r % rows_per_req;
+    seeds[req] (uint64) and steps[req] key its Gumbel noise.
+    active: optional per-request flags; rows of inactive requests are left as NaN / -1.
+    """
+    logits = np.asarray(logits)
+    rows, V = logits.shape
+    out = SampleOut(*(np.full(rows, np.nan) for _ in range(1)),
+                    argmax=np.full(rows, -1, np.int64), sample=np.full(rows, -1, np.int64),
+                    row_max=np.full(rows, np.nan), row_lnz=np.full(rows, np.nan),
+                    argmax_gap=np.full(rows, np.inf), key_gap=np.full(rows, np.inf))
+    for r in range(rows):
+        req, pos = divmod(r, rows_per_req)
+        if active is not None and not active[req]:
+            continue
+        l = logits[r].astype(np.float64)
+        out.argmax[r] = int(np.argmax(l))          # first occurrence = lowest index
+        out.argmax_gap[r] = _top2_gap(l)
+        if argmax_only:
+            continue
+        x = l / float(temperature)
+        m, Z, _S, H = softmax_stats(x)
+        out.entropy[r] = H
+        out.row_max[r] = m
+        out.row_lnz[r] = np.log(Z)
+        g = philox.gumbel_row(int(seeds[req]), pos, int(steps[req]), V)
+        key = x + g
+        out.sample[r] = int(np.argmax(key))
+        out.key_gap[r] = _top2_gap(key)
+    return out
+
+
+def probabilities(logits_row: np.ndarray, temperature: float) -> np.ndarray:
+    x = np.asarray(logits_row, dtype=np.float64) / float(temperature)
+    e = np.exp(x - np.max(x))
+    return e / np.sum(e)

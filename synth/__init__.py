@@ -1,0 +1,205 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU-side tests.
+
+This module only *generates* inputs (numpy PCG64 streams, fixed recipes); it
+holds none of the denoise step's arithmetic.  Both the CPU oracle (through the
+tests) and the HIP path (through the binding) consume exactly the bytes made
+here, so a parity test compares the two on identical inputs.
+
+Storage conventions
+  * bf16 tensors are returned as ``uint16`` arrays holding the bf16 bit pattern
+    (the top half of an IEEE fp32, rounded to nearest even).
+  * fp32 tensors are ``float32`` arrays.
+
+Recipes (all values drawn from ``numpy.random.Generator(PCG64(seed))`` with a
+per-tensor sub-seed, so changing one tensor never shifts another):
+  * logits: ``sqrt(3) * z - alpha_r * 1.1 * ln(1 + rank_r(i))`` with
+    ``z ~ N(0, 1)``, ``alpha_r ~ U(0, 3)`` per row and ``rank_r`` a random
+    permutation of ``0..V-1`` per row: a N(0, 3) body plus a per-row Zipf(1.1)
+    bias of random strength, so row entropies spread from near 0 to ~11 nats.
+  * embedding table E: ``N(0, 1) / 8``.
+  * MLP / projection weights: ``N(0, 0.02^2)``.
+  * attention Q/K/V: ``N(0, 1)``.
+  * page tables: a shuffled free list of physical pages.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bf16", "normal_f32",
+    "zipf_logits_bf16", "zipf_logits_f32", "page_table", "SplitSpec", "attention_problem",
+    "PagedAttentionProblem",
+]
+
+
+def rng_for(seed: int, *tags) -> np.random.Generator:
+    """Independent PCG64 stream for (seed, tags...)."""
+    h = hashlib.sha256(repr((int(seed),) + tuple(tags)).encode()).digest()
+    return np.random.Generator(np.random.PCG64(int.from_bytes(h[:16], "little")))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_f32(seed: int, tag: str, shape, std: float = 1.0) -> np.ndarray:
+    rng = rng_for(seed, tag)
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat.size, step):
+        n = min(step, flat.size - s)
+        flat[s:s + n] = rng.standard_normal(n, dtype=np.float32) * np.float32(std)
+    return out
+
+
+def normal_bf16(seed: int, tag: str, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) rounded to bf16; generated in chunks so large tables stay cheap."""
+    rng = rng_for(seed, tag)
+    out = np.empty(shape, dtype=np.uint16)
+    flat = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat.size, step):
+        n = min(step, flat.size - s)
+        flat[s:s + n] = f32_to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * np.float32(std))
+    return out
+
+
+def _zipf_rows(seed: int, tag: str, rows: int, V: int, alpha_max: float) -> np.ndarray:
+    rng = rng_for(seed, tag)
+    alpha = rng.uniform(0.0, alpha_max, size=rows)
+    base = (-1.1 * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+    out = np.empty((rows, V), dtype=np.float32)
+    for r in range(rows):
+        z = rng.standard_normal(V, dtype=np.float32)
+        perm = rng.permutation(V)
+        out[r] = np.float32(np.sqrt(3.0)) * z + np.float32(alpha[r]) * base[perm]
+    return out
+
+
+def zipf_logits_f32(seed: int, tag: str, rows: int, V: int, alpha_max: float = 3.0) -> np.ndarray:
+    return _zipf_rows(seed, tag, rows, V, alpha_max)
+
+
+def zipf_logits_bf16(seed: int, tag: str, rows: int, V: int, alpha_max: float = 3.0) -> np.ndarray:
+    """bf16 logit rows (uint16 bits), N(0, 3) body + per-row Zipf(1.1) bias of strength U(0, alpha_max)."""
+    out = np.empty((rows, V), dtype=np.uint16)
+    chunk = max(1, (1 << 23) // max(V, 1))
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        out[r0:r1] = f32_to_bf16_bits(_zipf_rows(seed, (tag, r0), r1 - r0, V, alpha_max))
+    return out
+
+
+def page_table(seed: int, tag: str, n_pages_total: int) -> np.ndarray:
+    """A shuffled free list of physical page ids (int32)."""
+    return rng_for(seed, tag).permutation(n_pages_total).astype(np.int32)
+
+
+@dataclass
+class SplitSpec:
+    """One request's row split for one attention launch.
+
+    cached   : tokens already resident in the request's pages
+    n_causal : causal rows (prompt chunk / commit pass) in this launch
+    n_canvas : bidirectional canvas rows in this launch
+    """
+    cached: int
+    n_causal: int
+    n_canvas: int
+
+
+@dataclass
+class PagedAttentionProblem:
+    Hq: int
+    Hkv: int
+    D: int
+    page_size: int
+    splits: list            # list[SplitSpec]
+    row0: np.ndarray        # int32 [n_req]
+    page0: np.ndarray       # int32 [n_req]
+    page_table: np.ndarray  # int32 [sum pages]
+    q: np.ndarray           # [rows, Hq, D]   (uint16 bf16 bits or float32)
+    k: np.ndarray           # [rows, Hkv, D]
+    v: np.ndarray           # [rows, Hkv, D]
+    k_cache: np.ndarray     # [n_pages, Hkv, page_size, D]
+    v_cache: np.ndarray
+    dtype: str = "bf16"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return int(self.q.shape[0])
+
+
+def attention_problem(seed: int, splits, Hq: int, Hkv: int, D: int, page_size: int = 16,
+                      dtype: str = "bf16", spare_pages: int = 3, tag: str = "attn") -> PagedAttentionProblem:
+    """Random Q/K/V, a paged cache filled for each request's cached prefix, and shuffled page tables.
+
+    Each request owns ceil((cached + n_causal) / page_size) pages (room for the causal rows'
+    K/V to be appended), drawn from one global shuffled pool with ``spare_pages`` extra pages
+    that no request owns (they stay as random junk so reading a wrong page shows up).
+    """
+    splits = [s if isinstance(s, SplitSpec) else SplitSpec(*s) for s in splits]
+    need = [max(1, -(-(s.cached + s.n_causal) // page_size)) for s in splits]
+    n_pages = int(sum(need)) + spare_pages
+    pool = page_table(seed, (tag, "pool"), n_pages)
+    page0 = np.zeros(len(splits), np.int32)
+    row0 = np.zeros(len(splits), np.int32)
+    tbl = []
+    r = 0
+    p = 0
+    for i, (s, n) in enumerate(zip(splits, need)):
+        page0[i] = p
+        row0[i] = r
+        tbl.extend(pool[p:p + n].tolist())
+        p += n
+        r += s.n_causal + s.n_canvas
+    rows = r
+    gen = normal_bf16 if dtype == "bf16" else normal_f32
+    q = gen(seed, (tag, "q"), (rows, Hq, D))
+    k = gen(seed, (tag, "k"), (rows, Hkv, D))
+    v = gen(seed, (tag, "v"), (rows, Hkv, D))
+    kc = gen(seed, (tag, "kc"), (n_pages, Hkv, page_size, D))
+    vc = gen(seed, (tag, "vc"), (n_pages, Hkv, page_size, D))
+    return PagedAttentionProblem(Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, splits=splits,
+                                 row0=row0, page0=page0, page_table=np.asarray(tbl, np.int32),
+                                 q=q, k=k, v=v, k_cache=kc, v_cache=vc, dtype=dtype)
+
+
+def tiny_loop_inputs(cfg: dict, variant_scale: float | None = None) -> dict:
+    """Weights, embedding table, prefix tokens and page table of the one-layer fp32 tiny loop.
+
+    ``variant_scale`` only relabels the logit scale (test-only variants that exercise
+    acceptance and convergence); the arrays are the same for every variant.
+    """
+    s, d, V = cfg["seed"], cfg["d"], cfg["V"]
+    HqD, HkvD, h = cfg["Hq"] * cfg["D"], cfg["Hkv"] * cfg["D"], cfg["hidden"]
+    n_tok = cfg["prefix"] + cfg["C"]
+    n_pages = -(-n_tok // cfg["page_size"])
+    return dict(
+        E=normal_f32(s, "tiny.E", (V, d), cfg["e_std"]),
+        wq=normal_f32(s, "tiny.wq", (d, HqD), cfg["w_std"]),
+        wk=normal_f32(s, "tiny.wk", (d, HkvD), cfg["w_std"]),
+        wv=normal_f32(s, "tiny.wv", (d, HkvD), cfg["w_std"]),
+        wo=normal_f32(s, "tiny.wo", (HqD, d), cfg["w_std"]),
+        w_gate=normal_f32(s, "tiny.wg", (d, h), cfg["w_std"]),
+        w_up=normal_f32(s, "tiny.wu", (d, h), cfg["w_std"]),
+        w_down=normal_f32(s, "tiny.wd", (h, d), cfg["w_std"]),
+        prefix=rng_for(s, "tiny.prefix").integers(0, V, cfg["prefix"]).astype(np.int32),
+        page_table=page_table(s, "tiny.pages", n_pages + 2)[:n_pages].copy(),
+        n_pages_total=n_pages + 2,
+        logit_scale=float(cfg["logit_scale"] if variant_scale is None else variant_scale),
+        seed64=np.uint64(s),
+    )

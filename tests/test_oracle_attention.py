@@ -1,0 +1,163 @@
+"""Pins for oracle.attention.
+
+* the page's visibility examples (tests/golden/) fix the mask rule;
+* an independent brute force: every key of every request laid out in one
+  global list by inverting the page tables, visibility decided by a position
+  predicate (same request and (canvas query or key position <= query
+  position)), softmax written with -inf masking over the full score matrix;
+* special cases with known outputs and invariances.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention
+from tests.golden.fixtures import read_blocks
+
+
+def test_p0p1c0c1_fixture():
+    blocks = read_blocks("visibility_p0p1c0c1.txt")
+    _, rows = blocks[("mask", "p0p1c0c1")]
+    assert attention.visibility_mask(0, 2, 2).astype(int).tolist() == rows
+
+
+def test_three_request_fixture_masks_and_tiles():
+    blocks = read_blocks("visibility_three_requests.txt")
+    for name in ("request0", "request1", "request2"):
+        hdr, rows = blocks[("mask", name)]
+        cached, nc, nv = (int(t) for t in hdr[0].split("=")[1].split(","))
+        m = attention.visibility_mask(cached, nc, nv)
+        assert m.astype(int).tolist() == rows
+        if ("skipped_tiles", name) in blocks:
+            _, tiles = blocks[("skipped_tiles", name)]
+            tr, tc = -(-m.shape[0] // 2), -(-m.shape[1] // 2)
+            skip = [[int(not m[2 * i:2 * i + 2, 2 * j:2 * j + 2].any()) for j in range(tc)] for i in range(tr)]
+            assert skip == tiles
+
+
+def _as_float(p, a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if p.dtype == "bf16" else a.astype(np.float64)
+
+
+def brute_force(p, scale):
+    """Global dense-mask attention over all requests (independent of the oracle's gather)."""
+    q, k, v = _as_float(p, p.q), _as_float(p, p.k), _as_float(p, p.v)
+    kc, vc = _as_float(p, p.k_cache), _as_float(p, p.v_cache)
+    ps = p.page_size
+    owner = {}                                    # physical page -> (request, logical page)
+    for r, s in enumerate(p.splits):
+        n = max(1, -(-(s.cached + s.n_causal) // ps))
+        for lp in range(n):
+            owner[int(p.page_table[p.page0[r] + lp])] = (r, lp)
+    keys, vals, kreq, kpos, kcanvas = [], [], [], [], []
+    for phys in range(kc.shape[0]):              # prefix keys straight from the physical pages
+        if phys not in owner:
+            continue
+        r, lp = owner[phys]
+        for slot in range(ps):
+            pos = lp * ps + slot
+            if pos < p.splits[r].cached:
+                keys.append(kc[phys, :, slot]); vals.append(vc[phys, :, slot])
+                kreq.append(r); kpos.append(pos); kcanvas.append(False)
+    qreq, qpos, qcanvas = [], [], []
+    for r, s in enumerate(p.splits):             # new rows: causal rows then canvas rows
+        for j in range(s.n_causal + s.n_canvas):
+            row = p.row0[r] + j
+            is_canvas = j >= s.n_causal
+            pos = s.cached + j
+            keys.append(k[row]); vals.append(v[row]); kreq.append(r); kpos.append(pos); kcanvas.append(is_canvas)
+            qreq.append(r); qpos.append(pos); qcanvas.append(is_canvas)
+    K, Vv = np.stack(keys), np.stack(vals)        # [nk, Hkv, D]
+    kreq, kpos = np.array(kreq), np.array(kpos)
+    qreq, qpos, qcanvas = np.array(qreq), np.array(qpos), np.array(qcanvas)
+    vis = (qreq[:, None] == kreq[None, :]) & (qcanvas[:, None] | (kpos[None, :] <= qpos[:, None]))
+    group = p.Hq // p.Hkv
+    out = np.zeros(q.shape)
+    for h in range(p.Hq):
+        sc = scale * q[:, h] @ K[:, h // group].T
+        sc = np.where(vis, sc, -np.inf)
+        w = np.exp(sc - sc.max(axis=1, keepdims=True))
+        out[:, h] = (w / w.sum(axis=1, keepdims=True)) @ Vv[:, h // group]
+    return out
+
+
+def run_oracle(p, scale):
+    f = lambda a: _as_float(p, a)
+    splits = [(p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i]) for i, s in enumerate(p.splits)]
+    return attention.canvas_attention(f(p.q), f(p.k), f(p.v), f(p.k_cache), f(p.v_cache), p.page_table,
+                                      splits, p.page_size, scale)
+
+
+CASES = [
+    ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 8),                 # the three-request batch
+    ([(0, 2, 2)], 2, 2, 4),                                      # p0 p1 c0 c1
+    ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 16),
+    ([(100, 0, 33)], 8, 2, 32),
+]
+
+
+@pytest.mark.parametrize("splits,Hq,Hkv,D", CASES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_oracle_matches_brute_force(splits, Hq, Hkv, D, dtype):
+    p = synth.attention_problem(11, splits, Hq, Hkv, D, dtype=dtype)
+    scale = 1.0 / np.sqrt(D)
+    out, kc, _vc = run_oracle(p, scale)
+    np.testing.assert_allclose(out, brute_force(p, scale), rtol=1e-12, atol=1e-12)
+    # causal rows' K/V appended at cached + j, nothing else touched
+    base = _as_float(p, p.k_cache)
+    knew = _as_float(p, p.k)
+    touched = np.zeros(base.shape[:1] + base.shape[2:3], bool)
+    for r, s in enumerate(p.splits):
+        for j in range(s.n_causal):
+            pos = s.cached + j
+            phys = p.page_table[p.page0[r] + pos // p.page_size]
+            np.testing.assert_array_equal(kc[phys, :, pos % p.page_size], knew[p.row0[r] + j])
+            touched[phys, pos % p.page_size] = True
+    for phys in range(base.shape[0]):
+        for slot in range(p.page_size):
+            if not touched[phys, slot]:
+                np.testing.assert_array_equal(kc[phys, :, slot], base[phys, :, slot])
+
+
+def test_single_visible_key_returns_its_value():
+    p = synth.attention_problem(3, [(0, 3, 0)], 2, 2, 8, dtype="f32")
+    out, _, _ = run_oracle(p, 0.3)
+    v = p.v.astype(np.float64)
+    np.testing.assert_allclose(out[0], v[0], rtol=0, atol=1e-15)     # first causal row sees only itself
+
+
+def test_equal_scores_average_visible_values():
+    p = synth.attention_problem(4, [(5, 2, 3)], 2, 1, 8, dtype="f32")
+    p.q[:] = 0.0                                                     # all scores equal
+    out, kc, vc = run_oracle(p, 1.0)
+    K, Vv = attention.gather_request_kv(kc, vc, p.k.astype(np.float64), p.v.astype(np.float64),
+                                        p.page_table, 0, 5, 2, 3, 0, p.page_size)
+    np.testing.assert_allclose(out[0, 0], Vv[:6, 0].mean(0), atol=1e-14)   # causal row 0 sees 5 + 1 keys
+    np.testing.assert_allclose(out[4, 1], Vv[:, 0].mean(0), atol=1e-14)    # canvas row sees all 10
+
+
+def test_canvas_row_permutation_and_prompt_isolation():
+    p = synth.attention_problem(5, [(8, 4, 6)], 4, 2, 16, dtype="f32")
+    out, _, _ = run_oracle(p, 0.25)
+    perm = np.array([0, 1, 2, 3, 9, 7, 4, 8, 5, 6])
+    p2 = synth.attention_problem(5, [(8, 4, 6)], 4, 2, 16, dtype="f32")
+    p2.q, p2.k, p2.v = p.q[perm], p.k[perm], p.v[perm]
+    out2, _, _ = run_oracle(p2, 0.25)
+    np.testing.assert_allclose(out2, out[perm], atol=1e-13)
+    p3 = synth.attention_problem(5, [(8, 4, 6)], 4, 2, 16, dtype="f32")
+    p3.k[4:] = np.random.default_rng(0).normal(size=p3.k[4:].shape)   # change canvas K/V only
+    p3.v[4:] = 7.0
+    out3, _, _ = run_oracle(p3, 0.25)
+    np.testing.assert_array_equal(out3[:4], out[:4])                 # prompt rows never see the canvas
+    assert not np.allclose(out3[4:], out[4:])
+
+
+def test_page_relabelling_invariance():
+    p = synth.attention_problem(6, [(40, 3, 5), (17, 0, 2)], 4, 2, 8, dtype="f32")
+    out, _, _ = run_oracle(p, 0.3)
+    relabel = np.random.default_rng(1).permutation(p.k_cache.shape[0])
+    p.k_cache = p.k_cache[np.argsort(relabel)]
+    p.v_cache = p.v_cache[np.argsort(relabel)]
+    p.page_table = relabel[p.page_table].astype(np.int32)
+    out2, _, _ = run_oracle(p, 0.3)
+    np.testing.assert_array_equal(out2, out)

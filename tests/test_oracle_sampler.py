@@ -1,0 +1,102 @@
+"""Pins for oracle.sampler: entropy closed forms, softmax/argmax identities, Gumbel-max law."""
+import math
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import sampler
+
+NEG = -1.0e4  # exp(NEG - max) underflows to exactly 0 in fp64
+
+
+def _one(row, T=1.0):
+    return sampler.denoise_sample(np.asarray(row, np.float64)[None, :], T, [3], [0], 1)
+
+
+@pytest.mark.parametrize("V,expect", [(1024, 6.931471805599453), (262144, 12.476649250079015),
+                                      (151936, 11.931214658529285)])
+def test_uniform_row_entropy_is_log_v(V, expect):
+    o = _one(np.full(V, 0.37))
+    assert o.entropy[0] == pytest.approx(expect, abs=1e-12)
+    assert expect == pytest.approx(math.log(V), abs=1e-12)
+    assert o.argmax[0] == 0            # all tied -> lowest index
+
+
+def test_one_hot_entropy_zero():
+    row = np.full(1000, NEG)
+    row[417] = 2.5
+    o = _one(row)
+    assert o.entropy[0] == 0.0
+    assert o.argmax[0] == 417 and o.sample[0] == 417
+
+
+@pytest.mark.parametrize("a,b", [(0.0, 0.0), (1.3, -0.2), (5.0, 0.0), (-3.0, 4.0)])
+def test_two_point_entropy(a, b):
+    row = np.full(64, NEG)
+    row[5], row[40] = a, b
+    p = 1.0 / (1.0 + math.exp(b - a))
+    expect = -(p * math.log(p) + (1 - p) * math.log(1 - p))
+    assert _one(row).entropy[0] == pytest.approx(expect, abs=1e-12)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 256])
+def test_k_equal_maxima_entropy_log_k(k):
+    row = np.full(4096, NEG)
+    idx = np.random.default_rng(k).choice(4096, k, replace=False)
+    row[idx] = 1.25
+    o = _one(row)
+    assert o.entropy[0] == pytest.approx(math.log(k), abs=1e-12)
+    assert o.argmax[0] == idx.min()
+
+
+def test_entropy_matches_definition_and_shift_invariance():
+    rng = np.random.default_rng(0)
+    for T in (1.0, 0.7, 2.0):
+        row = rng.normal(0, 3, 5000)
+        p = sampler.probabilities(row, T)
+        assert np.sum(p) == pytest.approx(1.0, abs=1e-12)
+        o1 = _one(row, T)
+        o2 = _one(row + 123.0, T)
+        assert o1.entropy[0] == pytest.approx(sampler.entropy_direct(p), abs=1e-10)
+        assert o2.entropy[0] == pytest.approx(o1.entropy[0], abs=1e-9)
+        assert o1.row_lnz[0] == pytest.approx(np.log(np.sum(np.exp(row / T - np.max(row / T)))), abs=1e-12)
+        assert o1.row_max[0] == np.max(row) / T
+
+
+def test_argmax_is_first_occurrence_like_numpy():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        row = rng.integers(-3, 3, 300).astype(np.float64)   # many exact ties
+        assert _one(row).argmax[0] == int(np.argmax(row))
+
+
+def test_gumbel_max_follows_softmax():
+    V, n = 8, 20000
+    logits = np.array([0.0, 1.0, -1.0, 2.0, 0.5, -2.0, 1.5, 0.0])
+    rows = np.tile(logits, (n, 1))
+    o = sampler.denoise_sample(rows, 1.0, [2024], [11], n)      # one request, n positions
+    counts = np.bincount(o.sample, minlength=V)
+    p = sampler.probabilities(logits, 1.0)
+    assert stats.chisquare(counts, p * n).pvalue > 1e-4
+    # temperature sharpens
+    o2 = sampler.denoise_sample(rows, 0.25, [2024], [11], n)
+    assert np.bincount(o2.sample, minlength=V)[3] > counts[3]
+
+
+def test_samples_depend_on_seed_step_position_only():
+    rng = np.random.default_rng(2)
+    rows = rng.normal(0, 1, (6, 500))
+    a = sampler.denoise_sample(rows, 1.0, [5, 6], [10, 10], 3)
+    b = sampler.denoise_sample(rows, 1.0, [5, 6], [10, 10], 3)
+    c = sampler.denoise_sample(rows, 1.0, [5, 6], [11, 10], 3)
+    assert np.array_equal(a.sample, b.sample)
+    assert not np.array_equal(a.sample[:3], c.sample[:3])      # diffuse rows: a new step redraws
+    assert np.array_equal(a.sample[3:], c.sample[3:])
+
+
+def test_argmax_only_and_inactive():
+    rows = np.random.default_rng(3).normal(0, 1, (4, 100))
+    o = sampler.denoise_sample(rows, 1.0, [1, 2], [0, 0], 2, argmax_only=True, active=[1, 0])
+    assert np.array_equal(o.argmax[:2], np.argmax(rows[:2], axis=1))
+    assert np.all(o.argmax[2:] == -1) and np.all(o.sample == -1)
