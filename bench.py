@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Denoise-step throughput on one MI355X: canvas positions denoised per second.
+
+One step = one pass of the whole hot path over one 256-token canvas
+(16 query / 8 KV heads, head_dim 256, 2048-token paged bf16 prefix,
+V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096):
+    dg_canvas_attention -> dg_denoise_sample -> dg_entropy_accept -> dg_converged -> dg_selfcond_embed
+Every input is synthetic and already resident in HBM when timing starts; the
+logits of successive steps rotate through a pool of distinct sets (768 MiB,
+three times the 256 MB Infinity Cache) so that no step reads them from cache.
+The logits stand in for the LM head output of a real backbone.
+
+Prints ONE JSON line (see --help).  The P.E contraction kernel, the step's
+dominant launch, is timed with HIP events recorded around it on the launch
+stream over the whole timed region; its roofline fraction uses the algorithmic
+bytes E (V x d, 16-bit) + P (C x V, 16-bit) per launch.  The CPU oracle is
+timed on a bounded sample of the same step (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
+           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0)
+PE_KERNEL = "gemm_f16_splitk_kernel"
+PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp", "denoise_step_amd/csrc/selfcond.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in PE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pe_algorithmic_bytes(c=CFG) -> int:
+    """E read once (V x d) + P read once (C x V), both 16-bit, per launch (one canvas)."""
+    return 2 * c["V"] * c["d"] + 2 * c["B"] * c["C"] * c["V"]
+
+
+def traffic_from_counters(per_launch_alg: int):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they match the current kernel."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha():
+        return None                      # the kernel changed since the counters were taken
+    return int(rec["hbm_bytes_per_dispatch"])
+
+
+class Workload:
+    """All device buffers of the single-canvas step, allocated once."""
+
+    def __init__(self, c=CFG):
+        import numpy as np
+        import torch
+
+        import denoise_step_amd as dg
+        import synth
+        self.c = c
+        self.dg = dg
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+        C, V, d, h = c["C"], c["V"], c["d"], c["hidden"]
+        Hq, Hkv, D, ps, L = c["Hq"], c["Hkv"], c["D"], c["page_size"], c["L"]
+        s = c["seed"]
+        log("generating inputs on the GPU")
+        self.q = synth.normal_torch(s, "bench.q", (C, Hq, D), 1.0, bf, dev)
+        self.k = synth.normal_torch(s, "bench.k", (C, Hkv, D), 1.0, bf, dev)
+        self.v = synth.normal_torch(s, "bench.v", (C, Hkv, D), 1.0, bf, dev)
+        n_pages = L // ps + 2
+        self.k_cache = synth.normal_torch(s, "bench.kc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
+        self.v_cache = synth.normal_torch(s, "bench.vc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
+        self.page_table = torch.as_tensor(synth.page_table(s, "bench.pages", n_pages)[: L // ps].copy(), device=dev)
+        self.splits = torch.tensor([[0, L, 0, C, 0, 0]], dtype=torch.int32, device=dev)
+        self.pool = [synth.zipf_logits_torch(s, ("bench.logits", i), C, V, dev) for i in range(c["pool"])]
+        self.E = synth.normal_torch(s, "bench.E", (V, d), 1 / 8, bf, dev)
+        self.wg = synth.normal_torch(s, "bench.wg", (d, h), 0.02, bf, dev)
+        self.wu = synth.normal_torch(s, "bench.wu", (d, h), 0.02, bf, dev)
+        self.wd = synth.normal_torch(s, "bench.wd", (h, d), 0.02, bf, dev)
+        log("preparing the fp16 operand copies")
+        self.prepared = dg.dg_selfcond_prepare(self.E, self.wg, self.wu, self.wd)
+        self.seed = torch.tensor([s], dtype=torch.int64, device=dev)
+        z = lambda n, dt=torch.int32: torch.zeros(n, dtype=dt, device=dev)
+        self.state = dict(prev_argmax=z((1, C)), unchanged=z(1), step_in_block=torch.full((1,), -1, dtype=torch.int32,
+                                                                                            device=dev),
+                          step_global=z(1), canvas=z((1, C)), sc_on=z(1, torch.uint8), committed=z(1, torch.uint8),
+                          out_tokens=z((1, C)), steps_used=z(1), num_sampled=z(1))
+        dummy_i, dummy_f = z((1, C)), torch.zeros((1, C), dtype=torch.float32, device=dev)
+        dg.dg_converged(dummy_i, dummy_f, V, c["k"], c["tau"], c["max_steps"], self.seed, self.state)  # prefill
+        self.att_out = torch.empty_like(self.q)
+        self.so = dict(entropy=torch.empty(C, dtype=torch.float32, device=dev), argmax=z(C), sample=z(C),
+                       row_max=torch.empty(C, dtype=torch.float32, device=dev),
+                       row_lnz=torch.empty(C, dtype=torch.float32, device=dev))
+        self.ws_s = torch.empty(dg.dg_denoise_sample_ws_bytes(C, V), dtype=torch.uint8, device=dev)
+        self.ws_sc = torch.empty(dg.dg_selfcond_ws_bytes(C, V, d, h, dg.DG_BF16), dtype=torch.uint8, device=dev)
+        self.accept = torch.zeros((1, C), dtype=torch.uint8, device=dev)
+        self.n_accept = z(1)
+        self.x = torch.empty((C, d), dtype=bf, device=dev)
+        self.scale = 1.0 / math.sqrt(D)
+        torch.cuda.synchronize()
+
+    def step(self, t: int, ev=None, pe_ev=None):
+        """One denoise step.  ev: optional list of 6 events recorded between the calls."""
+        c, dg, s = self.c, self.dg, self.state
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
+                               c["C"], c["L"] + c["C"], self.scale, out=self.att_out)
+        rec(1)
+        logits = self.pool[t % len(self.pool)]
+        dg.dg_denoise_sample(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"], out=self.so,
+                             ws=self.ws_s)
+        rec(2)
+        dg.dg_entropy_accept(self.so["entropy"], self.so["sample"], s["canvas"], c["V"], c["budget"], self.seed,
+                             s["step_global"], accept=self.accept, n_accept=self.n_accept)
+        rec(3)
+        dg.dg_converged(self.so["argmax"], self.so["entropy"], c["V"], c["k"], c["tau"], c["max_steps"], self.seed, s)
+        rec(4)
+        dg.dg_selfcond_embed(logits, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"], s["canvas"], self.E,
+                             self.wg, self.wu, self.wd, self.prepared, c["temperature"], x_out=self.x, ws=self.ws_sc,
+                             pe_events=pe_ev)
+        rec(5)
+
+
+def cpu_baseline(w: Workload, rows: int):
+    """Time the oracle, as it stands, on `rows` canvas positions of the same step (host cores)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import accept, attention, converged, sampler, selfcond
+    c = w.c
+    C, V, D = c["C"], c["V"], c["D"]
+    log(f"cpu baseline: copying inputs for {rows} positions to the host")
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    q = f64(w.q[:rows])
+    k_new, v_new = f64(w.k), f64(w.v)
+    kc, vc = f64(w.k_cache), f64(w.v_cache)
+    pt = w.page_table.cpu().numpy()
+    logits = f64(w.pool[0][:rows])
+    E = w.E.float().cpu().numpy()
+    wg, wu, wd = f64(w.wg), f64(w.wu), f64(w.wd)
+    ent_canvas = np.random.default_rng(0).gamma(1.0, 2.0, (1, C)).astype(np.float32)
+    threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    log("cpu baseline: timing the oracle")
+    t0 = time.perf_counter()
+    K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
+    group = c["Hq"] // c["Hkv"]
+    mask = np.ones((rows, K.shape[0]), bool)
+    for h in range(c["Hq"]):
+        attention.dense_mask_attention(q[:, h], K[:, h // group], Vv[:, h // group], mask, 1.0 / math.sqrt(D))
+    so = sampler.denoise_sample(logits, 1.0, [0], [1], rows)
+    st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
+                             unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
+                             step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
+    samp = np.zeros((1, C), np.int64)
+    accept.entropy_accept(ent_canvas, samp, st.canvas, c["budget"], [0], [1], V)
+    converged.converged(np.zeros((1, C), np.int64), ent_canvas, st, c["k"], c["tau"], c["max_steps"], [0], V)
+    P = selfcond.probs_from_stats(logits, 1.0, so.row_max, so.row_lnz)
+    selfcond.selfcond_embed(P, np.zeros((1, rows), np.int64), np.ones(1, np.uint8), E, wg, wu, wd, rows,
+                            to_bf16=True)
+    dt = time.perf_counter() - t0
+    cores = min(len(os.sched_getaffinity(0)), max(threads, 1))
+    return dict(value=rows / dt, unit="positions/s", cores=cores, kind="oracle",
+                sample=(f"{rows} canvas positions of the single-canvas step on the host in fp64 numpy: attention for "
+                        f"{rows} rows x 16 heads over 2304 keys, sampler over {rows} rows of V=262144 (Philox "
+                        f"Gumbel), accept + converged over the 256-position canvas, P.E + MLP for {rows} rows "
+                        f"against the full 262144 x 4096 table; {dt:.1f} s"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=8, help="canvas positions in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (no sharding, no collectives); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import denoise_step_amd as dg
+    dg.lib()
+    w = Workload()
+    c = w.c
+    log(f"warmup {args.warmup} steps")
+    for t in range(args.warmup):
+        w.step(t)
+    torch.cuda.synchronize()
+    K = args.steps
+    pe_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for t in range(K):
+        w.step(args.warmup + t, pe_ev=pe_ev[t])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    pe_ms = sum(a.elapsed_time(b) for a, b in pe_ev) / K
+    # per-call breakdown over a few extra steps (not part of the timed region)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    names = ["canvas_attention", "denoise_sample", "entropy_accept", "converged", "selfcond_embed"]
+    brk = {n: 0.0 for n in names}
+    nb = 5
+    for t in range(nb):
+        w.step(10_000 + t, ev=ev)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            brk[n] += ev[i].elapsed_time(ev[i + 1]) * 1000.0 / nb
+    alg = pe_algorithmic_bytes()
+    achieved = alg / (pe_ms * 1e-3) / 1e9
+    positions = c["B"] * c["C"]
+    result = {
+        "metric": METRIC,
+        "value": positions * K / (ms_total * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single_canvas", "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],
+                   "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["D"], "page_size": c["page_size"],
+                   "d_embed": c["d"], "mlp_hidden": c["hidden"], "logit_pool": c["pool"]},
+        "steps_per_s": 1000.0 / ms_step,
+        "wall_s_timed_region": wall,
+        "roofline": {"kernel": PE_KERNEL, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(alg),
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_us": pe_ms * 1000.0,
+                     "source_sha": source_sha()},
+        "breakdown_us": brk,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""Python binding of libdg (the denoise step's C ABI): argument marshalling only.
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU (torch provides device memory and
+streams), passes their raw pointers through ctypes and raises ``DGError`` on a
+non-zero status.  No arithmetic of the step happens in Python.  If the
+shared library has not been built the import of any entry point fails loudly:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DGError", "lib", "DG_F32", "DG_BF16", "DG_SAMPLE_ARGMAX_ONLY", "SPLIT_FIELDS",
+    "dg_version", "dg_philox4x32_10", "dg_canvas_attention", "dg_canvas_attention_ws_bytes",
+    "dg_denoise_sample", "dg_denoise_sample_ws_bytes", "dg_entropy_accept", "dg_converged",
+    "dg_selfcond_prepared_bytes", "dg_selfcond_prepare", "dg_selfcond_ws_bytes", "dg_selfcond_embed",
+    "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
+]
+
+DG_F32, DG_BF16 = 0, 1
+DG_SAMPLE_ARGMAX_ONLY = 1
+SPLIT_FIELDS = ("row0", "cached", "n_causal", "n_canvas", "page0", "window")
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+
+_p, _i32, _i64, _u32, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                          ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+
+# name -> (restype, argtypes): mirrors include/dg.h
+_SIGS = {
+    "dg_version": (_i32, []),
+    "dg_status_str": (ctypes.c_char_p, [_i32]),
+    "dg_philox4x32_10": (_i32, [_p, _p, _i64, _p, _p]),
+    "dg_canvas_attention_ws_bytes": (_sz, [_i32] * 6 + [_i32]),
+    "dg_canvas_attention": (_i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _i32, _f32, _i32, _p, _p, _sz, _p]),
+    "dg_denoise_sample_ws_bytes": (_sz, [_i32, _i32]),
+    "dg_denoise_sample": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _u32, _p, _p, _p, _p, _p, _p,
+                                 _sz, _p]),
+    "dg_entropy_accept": (_i32, [_p, _p, _i32, _i32, _i32, _f64, _p, _p, _p, _p, _p, _p, _p]),
+    "dg_converged": (_i32, [_p, _p, _i32, _i32, _i32, _i32, _f64, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                            _p, _p]),
+    "dg_selfcond_prepared_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "dg_selfcond_prepare": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _sz, _p]),
+    "dg_selfcond_ws_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "dg_selfcond_embed": (_i32, [_p, _i64, _i32, _f32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i32, _i32,
+                                 _i32, _p, _p, _p, _sz, _p]),
+    "dg_selfcond_embed_traced": (_i32, [_p, _i64, _i32, _f32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i32,
+                                        _i32, _i32, _p, _p, _p, _sz, _p, _p, _p]),
+    "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
+    "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
+    "dg_linear": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p]),
+    "dg_gather_rows": (_i32, [_p, _i32, _i32, _i32, _p, _i32, _p, _p]),
+}
+EXPORTED = tuple(_SIGS)
+
+
+class DGError(RuntimeError):
+    pass
+
+
+_LIB = None
+
+
+def lib():
+    """Load libdg.so (built in-tree by ``python -m denoise_step_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise DGError(f"{LIB_PATH} is missing; build it with `python -m denoise_step_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = lib().dg_status_str(status).decode()
+        raise DGError(f"{name} failed with status {status} ({msg})")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise DGError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise DGError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return DG_BF16
+    if t.dtype == torch.float32:
+        return DG_F32
+    raise DGError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ws(nbytes: int, ws, device):
+    if nbytes == 0:
+        return ws
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def dg_version() -> int:
+    return int(lib().dg_version())
+
+
+def dg_philox4x32_10(ctr: torch.Tensor, key: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """ctr [n,4] int32/uint32 bits, key [n,2] -> out [n,4] (int32 storage of uint32 bits)."""
+    n = ctr.shape[0]
+    out = torch.empty((n, 4), dtype=torch.int32, device=ctr.device) if out is None else out
+    _check(lib().dg_philox4x32_10(_ptr(ctr), _ptr(key), n, _ptr(out), _stream(stream)), "dg_philox4x32_10")
+    return out
+
+
+def dg_canvas_attention_ws_bytes(n_req, max_rows, max_keys, Hq, Hkv, D, dtype) -> int:
+    return int(lib().dg_canvas_attention_ws_bytes(n_req, max_rows, max_keys, Hq, Hkv, D, dtype))
+
+
+def dg_canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, max_rows_per_req, max_keys_per_req,
+                        scale, out=None, ws=None, stream=None):
+    """q [rows,Hq,D], k/v [rows,Hkv,D], caches [pages,Hkv,page,D], page_table int32, splits int32 [n_req,6]."""
+    rows, Hq, D = q.shape
+    Hkv = k.shape[1]
+    n_pages, _, page_size, _ = k_cache.shape
+    n_req = splits.shape[0]
+    dt = _dtype_code(q)
+    out = torch.empty_like(q) if out is None else out
+    nb = dg_canvas_attention_ws_bytes(n_req, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dt)
+    ws = _ws(nb, ws, q.device)
+    _check(lib().dg_canvas_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), n_pages,
+                                     _ptr(page_table), page_table.numel(), _ptr(splits), n_req, rows,
+                                     max_rows_per_req, max_keys_per_req, Hq, Hkv, D, page_size, float(scale), dt,
+                                     _ptr(out), _ptr(ws) if nb else None, nb, _stream(stream)),
+           "dg_canvas_attention")
+    return out
+
+
+def dg_denoise_sample_ws_bytes(rows, V) -> int:
+    return int(lib().dg_denoise_sample_ws_bytes(rows, V))
+
+
+def dg_denoise_sample(logits, V, rows_per_req, seed, step, temperature=1.0, active=None, argmax_only=False,
+                      out=None, ws=None, stream=None):
+    """logits [rows, ld] -> dict(entropy, argmax, sample, row_max, row_lnz) device tensors."""
+    rows, ld = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(argmax=torch.empty(rows, dtype=torch.int32, device=dev))
+        if not argmax_only:
+            out.update(entropy=torch.empty(rows, dtype=torch.float32, device=dev),
+                       sample=torch.empty(rows, dtype=torch.int32, device=dev),
+                       row_max=torch.empty(rows, dtype=torch.float32, device=dev),
+                       row_lnz=torch.empty(rows, dtype=torch.float32, device=dev))
+    nb = dg_denoise_sample_ws_bytes(rows, V)
+    ws = _ws(nb, ws, dev)
+    g = out.get
+    _check(lib().dg_denoise_sample(_ptr(logits), ld, _dtype_code(logits), rows, V, rows_per_req, _ptr(seed),
+                                   _ptr(step), _ptr(active), float(temperature),
+                                   DG_SAMPLE_ARGMAX_ONLY if argmax_only else 0, _ptr(g("entropy")),
+                                   _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")), _ptr(g("row_lnz")),
+                                   _ptr(ws), nb, _stream(stream)), "dg_denoise_sample")
+    return out
+
+
+def dg_entropy_accept(entropy, sample, canvas, V, budget, seed, step, active=None, accept=None, n_accept=None,
+                      stream=None):
+    B, C = canvas.shape
+    _check(lib().dg_entropy_accept(_ptr(entropy), _ptr(sample), B, C, V, float(budget), _ptr(seed), _ptr(step),
+                                   _ptr(active), _ptr(canvas), _ptr(accept), _ptr(n_accept), _stream(stream)),
+           "dg_entropy_accept")
+
+
+def dg_converged(argmax, entropy, V, k, tau, max_steps, seed, state: dict, active=None, stream=None):
+    """state: dict of device tensors prev_argmax, unchanged, step_in_block, step_global, canvas, sc_on,
+    committed, out_tokens, steps_used, num_sampled (updated in place)."""
+    B, C = state["canvas"].shape
+    s = state
+    _check(lib().dg_converged(_ptr(argmax), _ptr(entropy), B, C, V, int(k), float(tau), int(max_steps), _ptr(seed),
+                              _ptr(active), _ptr(s["prev_argmax"]), _ptr(s["unchanged"]), _ptr(s["step_in_block"]),
+                              _ptr(s["step_global"]), _ptr(s["canvas"]), _ptr(s["sc_on"]), _ptr(s["committed"]),
+                              _ptr(s["out_tokens"]), _ptr(s["steps_used"]), _ptr(s["num_sampled"]),
+                              _stream(stream)), "dg_converged")
+
+
+def dg_selfcond_prepared_bytes(V, d, hidden, dtype) -> int:
+    return int(lib().dg_selfcond_prepared_bytes(V, d, hidden, dtype))
+
+
+def dg_selfcond_prepare(E, w_gate, w_up, w_down, stream=None):
+    """Build the fp16 operand copies used by the bf16 path (E^T, [W_gate|W_up]^T, W_down^T)."""
+    V, d = E.shape
+    hidden = w_gate.shape[1]
+    dt = _dtype_code(E)
+    nb = dg_selfcond_prepared_bytes(V, d, hidden, dt)
+    prepared = torch.empty(max(nb, 1), dtype=torch.uint8, device=E.device)
+    _check(lib().dg_selfcond_prepare(_ptr(E), _ptr(w_gate), _ptr(w_up), _ptr(w_down), V, d, hidden, dt,
+                                     _ptr(prepared), nb, _stream(stream)), "dg_selfcond_prepare")
+    return prepared
+
+
+def dg_selfcond_ws_bytes(rows, V, d, hidden, dtype) -> int:
+    return int(lib().dg_selfcond_ws_bytes(rows, V, d, hidden, dtype))
+
+
+def dg_selfcond_embed(logits, V, row_max, row_lnz, sc_on, canvas, E, w_gate, w_up, w_down, prepared,
+                      temperature=1.0, x_out=None, s_out=None, ws=None, stream=None, pe_events=None):
+    """pe_events: optional (start, stop) torch.cuda.Event pair recorded around the P.E kernel."""
+    B, C = canvas.shape
+    rows, ld = logits.shape
+    d = E.shape[1]
+    hidden = w_gate.shape[1]
+    dt = _dtype_code(logits)
+    x_out = torch.empty((rows, d), dtype=E.dtype, device=E.device) if x_out is None else x_out
+    nb = dg_selfcond_ws_bytes(rows, V, d, hidden, dt)
+    ws = _ws(nb, ws, logits.device)
+    ev0, ev1 = (None, None) if pe_events is None else (pe_events[0].cuda_event, pe_events[1].cuda_event)
+    _check(lib().dg_selfcond_embed_traced(_ptr(logits), ld, dt, float(temperature), _ptr(row_max), _ptr(row_lnz),
+                                          _ptr(sc_on), _ptr(canvas), B, C, _ptr(E), _ptr(w_gate), _ptr(w_up),
+                                          _ptr(w_down), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
+                                          _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_traced")
+    return x_out
+
+
+def dg_allowed_probs(logits, V, slot_row, offsets, ids, temperature=1.0, q=None, answer=None, stream=None):
+    n_rows, ld = logits.shape
+    n_slots = slot_row.numel()
+    q = torch.empty(ids.numel(), dtype=torch.float32, device=logits.device) if q is None else q
+    answer = torch.empty(n_slots, dtype=torch.int32, device=logits.device) if answer is None else answer
+    _check(lib().dg_allowed_probs(_ptr(logits), ld, _dtype_code(logits), n_rows, n_slots, V, _ptr(slot_row),
+                                  _ptr(offsets), _ptr(ids), float(temperature), _ptr(q), _ptr(answer),
+                                  _stream(stream)), "dg_allowed_probs")
+    return q, answer
+
+
+def dg_verify_prefix(draft, target, accepted=None, stream=None):
+    B, L = draft.shape
+    accepted = torch.empty(B, dtype=torch.int32, device=draft.device) if accepted is None else accepted
+    _check(lib().dg_verify_prefix(_ptr(draft), _ptr(target), B, L, _ptr(accepted), _stream(stream)),
+           "dg_verify_prefix")
+    return accepted
+
+
+def dg_linear(A, B, residual=None, trans_b=False, alpha=1.0, out=None, stream=None):
+    M, K = A.shape
+    N = B.shape[0] if trans_b else B.shape[1]
+    out = torch.empty((M, N), dtype=torch.float32, device=A.device) if out is None else out
+    _check(lib().dg_linear(_ptr(A), _ptr(B), _ptr(residual), _ptr(out), M, N, K, int(bool(trans_b)), float(alpha),
+                           _stream(stream)), "dg_linear")
+    return out
+
+
+def dg_gather_rows(table, idx, out=None, stream=None):
+    n_table, d = table.shape
+    n = idx.numel()
+    out = torch.empty((n, d), dtype=table.dtype, device=table.device) if out is None else out
+    _check(lib().dg_gather_rows(_ptr(table), n_table, d, _dtype_code(table), _ptr(idx), n, _ptr(out),
+                                _stream(stream)), "dg_gather_rows")
+    return out

@@ -1,0 +1,222 @@
+// dg_canvas_attention: mixed-mask attention over a paged KV prefix.
+//
+// Method: DiffusionGemma/vLLM page, section "Two modes, one set of weights"
+// (encoder rows are causal and write K/V; decoder/canvas rows are
+// bidirectional and only read K/V) and section "Dynamic per-sequence causal
+// attention" (causality per request inside one batch; tiles holding only
+// masked entries are skipped); single-pass-reads page, section on keeping
+// each row's visibility (a request split into causal input rows and canvas
+// rows that share its KV block table; the p0 p1 c0 c1 example).
+//
+// Launch order on the stream: (1) the causal rows' K/V are appended to the
+// request's pages at positions cached + j; (2) the attention kernel reads
+// every prefix and causal key from the pages and the canvas keys from the
+// k/v inputs.
+#include "dg_device.hpp"
+#include "dg_host.hpp"
+
+namespace dg {
+namespace {
+
+template <bool BF16>
+DG_DEV float ld_elem(const void* p, int64_t i) {
+  if constexpr (BF16)
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else
+    return reinterpret_cast<const float*>(p)[i];
+}
+
+DG_DEV int32_t clamp_page(int32_t p, int32_t n_pages) { return min(max(p, 0), n_pages - 1); }
+
+DG_DEV int32_t page_of(const int32_t* page_table, int32_t page_table_len, int32_t n_pages, const dg_split& sp,
+                       int32_t pos, int32_t page_size) {
+  const int32_t idx = min(max(sp.page0 + pos / page_size, 0), page_table_len - 1);
+  return clamp_page(page_table[idx], n_pages);
+}
+
+// (1) append: one workgroup per (request, causal row); element-wise copy of Hkv * D values.
+template <bool BF16>
+__global__ void append_kv_kernel(const void* __restrict__ k, const void* __restrict__ v, void* __restrict__ k_cache,
+                                 void* __restrict__ v_cache, int32_t n_pages, const int32_t* __restrict__ page_table,
+                                 int32_t page_table_len, const dg_split* __restrict__ splits, int32_t rows,
+                                 int32_t Hkv, int32_t D, int32_t page_size) {
+  const dg_split sp = splits[blockIdx.y];
+  const int j = blockIdx.x;
+  if (j >= sp.n_causal) return;
+  const int32_t row = sp.row0 + j;
+  if (row < 0 || row >= rows) return;
+  const int32_t pos = sp.cached + j;
+  const int64_t page = page_of(page_table, page_table_len, n_pages, sp, pos, page_size);
+  const int32_t slot = pos % page_size;
+  const int n = Hkv * D;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int h = e / D, d = e - h * D;
+    const int64_t src = (static_cast<int64_t>(row) * Hkv + h) * D + d;
+    const int64_t dst = ((page * Hkv + h) * page_size + slot) * D + d;
+    if constexpr (BF16) {
+      reinterpret_cast<uint16_t*>(k_cache)[dst] = reinterpret_cast<const uint16_t*>(k)[src];
+      reinterpret_cast<uint16_t*>(v_cache)[dst] = reinterpret_cast<const uint16_t*>(v)[src];
+    } else {
+      reinterpret_cast<float*>(k_cache)[dst] = reinterpret_cast<const float*>(k)[src];
+      reinterpret_cast<float*>(v_cache)[dst] = reinterpret_cast<const float*>(v)[src];
+    }
+  }
+}
+
+// (2) one wave per (query row, query head): keys in blocks of 64, one key per lane for the
+// score, online softmax across blocks, each lane owning D / 64 output columns.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kWave) void attend_wave_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache, int32_t n_pages,
+    const int32_t* __restrict__ page_table, int32_t page_table_len, const dg_split* __restrict__ splits,
+    int32_t rows, int32_t Hq, int32_t Hkv, int32_t page_size, float scale, void* __restrict__ out) {
+  constexpr int kCols = (D + kWave - 1) / kWave;
+  __shared__ float qs[D];
+  const dg_split sp = splits[blockIdx.z];
+  const int j = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  if (j >= sp.n_causal + sp.n_canvas) return;
+  const int32_t row = sp.row0 + j;
+  if (row < 0 || row >= rows) return;
+  const int hk = h / (Hq / Hkv);
+  const int32_t n_cache = sp.cached + sp.n_causal;
+  const int32_t n_vis = (j < sp.n_causal) ? sp.cached + j + 1 : n_cache + sp.n_canvas;
+  for (int d = lane; d < D; d += kWave) qs[d] = ld_elem<BF16>(q, (static_cast<int64_t>(row) * Hq + h) * D + d) * scale;
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f;
+  float acc[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) acc[c] = 0.f;
+
+  for (int kb = 0; kb < n_vis; kb += kWave) {
+    const int kk = kb + lane;
+    int64_t kbase = -1;  // element offset of this lane's key row (K and V share the layout)
+    const void* ksrc = nullptr;
+    const void* vsrc = nullptr;
+    float s = -INFINITY;
+    if (kk < n_vis) {
+      if (kk < n_cache) {
+        const int64_t page = page_of(page_table, page_table_len, n_pages, sp, kk, page_size);
+        kbase = ((page * Hkv + hk) * page_size + kk % page_size) * D;
+        ksrc = k_cache;
+        vsrc = v_cache;
+      } else {
+        const int64_t crow = sp.row0 + sp.n_causal + (kk - n_cache);
+        kbase = (crow * Hkv + hk) * D;
+        ksrc = k;
+        vsrc = v;
+      }
+      float dot = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) dot = fmaf(qs[d], ld_elem<BF16>(ksrc, kbase + d), dot);
+      s = dot;
+    }
+    const float bm = wave_max(s);
+    const float mn = fmaxf(m, bm);
+    const float f = (m == -INFINITY) ? 0.f : __expf(m - mn);
+    const float p = (kk < n_vis) ? __expf(s - mn) : 0.f;
+    l = l * f + wave_sum(p);
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[c] *= f;
+    m = mn;
+    const int nb = min(kWave, n_vis - kb);
+    for (int i = 0; i < nb; ++i) {
+      const float pi = __shfl(p, i, kWave);
+      const int64_t vb = __shfl(kbase, i, kWave);
+      const bool from_cache = (kb + i) < n_cache;
+      const void* vs = from_cache ? v_cache : v;
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        const int d = lane + c * kWave;
+        if (d < D) acc[c] = fmaf(pi, ld_elem<BF16>(vs, vb + d), acc[c]);
+      }
+    }
+    (void)vsrc;
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) {
+    const int d = lane + c * kWave;
+    if (d < D) {
+      const int64_t o = (static_cast<int64_t>(row) * Hq + h) * D + d;
+      if constexpr (BF16)
+        reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(acc[c] * inv);
+      else
+        reinterpret_cast<float*>(out)[o] = acc[c] * inv;
+    }
+  }
+}
+
+template <bool BF16, int D>
+void launch_attend_wave(const void* q, const void* k, const void* v, const void* kc, const void* vc, int32_t n_pages,
+                        const int32_t* pt, int32_t ptl, const dg_split* splits, int32_t n_req, int32_t rows,
+                        int32_t max_rows, int32_t Hq, int32_t Hkv, int32_t ps, float scale, void* out, hipStream_t s) {
+  const dim3 grid(max_rows, Hq, n_req);
+  attend_wave_kernel<BF16, D><<<grid, kWave, 0, s>>>(q, k, v, kc, vc, n_pages, pt, ptl, splits, rows, Hq, Hkv, ps,
+                                                     scale, out);
+}
+
+}  // namespace
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t max_rows_per_req, int32_t max_keys_per_req,
+                                               int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype) {
+  (void)n_req; (void)max_rows_per_req; (void)max_keys_per_req; (void)Hq; (void)Hkv; (void)D; (void)dtype;
+  return 0;
+}
+
+extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                                         int32_t n_pages, const int32_t* page_table, int32_t page_table_len,
+                                         const dg_split* splits, int32_t n_req, int32_t rows,
+                                         int32_t max_rows_per_req, int32_t max_keys_per_req, int32_t Hq,
+                                         int32_t Hkv, int32_t D, int32_t page_size, float scale, int32_t dtype,
+                                         void* out, void* ws, size_t ws_bytes, dg_stream_t stream) {
+  DG_ARG(q && k && v && k_cache && v_cache && page_table && splits && out);
+  DG_ARG(n_pages > 0 && page_table_len > 0 && n_req > 0 && rows > 0 && max_rows_per_req > 0 &&
+         max_keys_per_req > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0);
+  DG_ARG(n_req <= 65535 && max_rows_per_req <= (1 << 20) && Hq <= 65535);
+  DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
+  DG_UNSUP(page_size == 16);
+  DG_UNSUP(D == 32 || D == 64 || D == 128 || D == 256);
+  const size_t need = dg_canvas_attention_ws_bytes(n_req, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
+  DG_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), DG_E_WORKSPACE);
+  hipStream_t s = as_stream(stream);
+  const bool bf = dtype == DG_BF16;
+  {
+    const dim3 grid(max_rows_per_req, n_req);
+    if (bf)
+      append_kv_kernel<true><<<grid, 256, 0, s>>>(k, v, k_cache, v_cache, n_pages, page_table, page_table_len,
+                                                  splits, rows, Hkv, D, page_size);
+    else
+      append_kv_kernel<false><<<grid, 256, 0, s>>>(k, v, k_cache, v_cache, n_pages, page_table, page_table_len,
+                                                   splits, rows, Hkv, D, page_size);
+    DG_LAUNCHED();
+  }
+#define DG_ATT(BF, DD)                                                                                        \
+  launch_attend_wave<BF, DD>(q, k, v, k_cache, v_cache, n_pages, page_table, page_table_len, splits, n_req, rows, \
+                             max_rows_per_req, Hq, Hkv, page_size, scale, out, s)
+  if (bf) {
+    switch (D) {
+      case 32: DG_ATT(true, 32); break;
+      case 64: DG_ATT(true, 64); break;
+      case 128: DG_ATT(true, 128); break;
+      default: DG_ATT(true, 256); break;
+    }
+  } else {
+    switch (D) {
+      case 32: DG_ATT(false, 32); break;
+      case 64: DG_ATT(false, 64); break;
+      case 128: DG_ATT(false, 128); break;
+      default: DG_ATT(false, 256); break;
+    }
+  }
+#undef DG_ATT
+  DG_LAUNCHED();
+  (void)max_keys_per_req;
+  return DG_OK;
+}

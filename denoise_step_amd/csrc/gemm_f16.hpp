@@ -1,0 +1,145 @@
+// Split-K fp16 MFMA GEMM for gfx950 with fp32 partial outputs:
+//   part[split][m][n] = sum_{k in split} A[m][k] * Bt[n][k]
+// A [M][lda] and Bt [N][ldb] are fp16 row-major with K contiguous (Bt is the
+// transposed right operand, prepared once for the constant tables).
+//
+// Workgroup tile 128 x 128, four wave64s in a 2 x 2 arrangement, each wave
+// computing 64 x 64 with four v_mfma_f32_32x32x16_f16 accumulators.  K is
+// staged through LDS 32 at a time, double buffered: the next stage's global
+// loads (16 bytes per lane, consecutive lanes on consecutive addresses) are
+// issued before the current stage's MFMAs.  Rows are padded by 8 halves in
+// LDS so the 16-byte operand reads of the 32 lanes of a half-wave fall in
+// different banks.
+#pragma once
+#include "dg_device.hpp"
+
+namespace dg {
+
+constexpr int kGemmTM = 128;
+constexpr int kGemmTN = 128;
+constexpr int kGemmTK = 32;
+constexpr int kGemmThreads = 256;
+constexpr int kGemmLdsRow = kGemmTK + 8;  // halves per LDS row
+
+struct GemmArgs {
+  const _Float16* A;
+  int64_t lda;
+  const _Float16* Bt;
+  int64_t ldb;
+  float* part;  // [splits][M][N]
+  int32_t M, N, K;
+  int32_t kchunk;  // K per split (multiple of kGemmTK)
+};
+
+// One 16-byte global chunk per (row, 8-half column group): a 128 x 32 tile is 512 chunks,
+// two per lane.  Rows beyond M are clamped (their results are never stored).
+DG_DEV void gemm_load_tile(const _Float16* __restrict__ src, int64_t ld, int32_t row0, int32_t nrows, int32_t k0,
+                           uint4 (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * kGemmThreads;
+    const int row = c >> 2, col = (c & 3) * 8;
+    const int64_t gr = min(row0 + row, nrows - 1);
+    r[i] = *reinterpret_cast<const uint4*>(src + gr * ld + k0 + col);
+  }
+}
+
+DG_DEV void gemm_store_tile(_Float16* __restrict__ lds, const uint4 (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * kGemmThreads;
+    const int row = c >> 2, col = (c & 3) * 8;
+    *reinterpret_cast<uint4*>(lds + row * kGemmLdsRow + col) = r[i];
+  }
+}
+
+__global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kGemmTM * kGemmLdsRow];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kGemmTN * kGemmLdsRow];
+  const int n0 = blockIdx.x * kGemmTN;
+  const int m0 = blockIdx.y * kGemmTM;
+  const int split = blockIdx.z;
+  const int k_begin = split * g.kchunk;
+  const int k_end = min(g.K, k_begin + g.kchunk);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  uint4 ra[2], rb[2];
+  int buf = 0;
+  if (k_begin < k_end) {
+    gemm_load_tile(g.A, g.lda, m0, g.M, k_begin, ra);
+    gemm_load_tile(g.Bt, g.ldb, n0, g.N, k_begin, rb);
+    gemm_store_tile(As[0], ra);
+    gemm_store_tile(Bs[0], rb);
+  }
+  __syncthreads();
+  for (int k0 = k_begin; k0 < k_end; k0 += kGemmTK) {
+    const bool more = k0 + kGemmTK < k_end;
+    if (more) {
+      gemm_load_tile(g.A, g.lda, m0, g.M, k0 + kGemmTK, ra);
+      gemm_load_tile(g.Bt, g.ldb, n0, g.N, k0 + kGemmTK, rb);
+    }
+    const _Float16* as = As[buf];
+    const _Float16* bs = Bs[buf];
+#pragma unroll
+    for (int kk = 0; kk < kGemmTK; kk += 16) {
+      half8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const half8*>(as + (wm + i * 32 + (lane & 31)) * kGemmLdsRow + kk + 8 * (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const half8*>(bs + (wn + j * 32 + (lane & 31)) * kGemmLdsRow + kk + 8 * (lane >> 5));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      gemm_store_tile(As[buf ^ 1], ra);
+      gemm_store_tile(Bs[buf ^ 1], rb);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
+  float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int n = n0 + wn + j * 32 + (lane & 31);
+        if (m < g.M) out[static_cast<int64_t>(m) * g.N + n] = acc[i][j][e];
+      }
+}
+
+struct GemmPlan {
+  int32_t splits, kchunk;
+  dim3 grid;
+};
+
+// N % 128 == 0 and K % 32 == 0 are required; M may be ragged.
+inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 512) {
+  const int32_t tiles = static_cast<int32_t>(((M + kGemmTM - 1) / kGemmTM) * (N / kGemmTN));
+  int32_t splits = (target_wgs + tiles - 1) / tiles;
+  const int32_t max_splits = (K + 1023) / 1024;
+  splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+  int32_t kchunk = (K + splits - 1) / splits;
+  kchunk = (kchunk + kGemmTK - 1) / kGemmTK * kGemmTK;
+  splits = (K + kchunk - 1) / kchunk;
+  return {splits, kchunk, dim3(N / kGemmTN, (M + kGemmTM - 1) / kGemmTM, splits)};
+}
+
+}  // namespace dg

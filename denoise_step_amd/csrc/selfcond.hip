@@ -1,0 +1,382 @@
+// dg_selfcond_prepare / dg_selfcond_embed: self-conditioning of the next
+// denoise pass.
+//
+// Method: DiffusionGemma/vLLM page, section "Self-conditioning" (the previous
+// step's full softmax becomes a probability-weighted mean of the token
+// embeddings, goes through a small gated MLP and is added to the canvas
+// embedding; zero for encoder passes) and section "DiffusionGemmaModelState
+// and DiffusionSampler" (prepare_inputs embeds the canvas and applies it).
+//
+// bf16 path (gfx950):
+//   1. probs:   w[r][i] = fp16(exp(x_i - m_r) * 2^15), zero-padded to Kp = roundup(V, 64).
+//               The 2^15 scale keeps every weight above exp(-20) in fp16's normal range
+//               (a plain fp16 or bf16 probability would lose 11+ bits on diffuse rows).
+//   2. P.E:     split-K fp16 MFMA GEMM against E^T (fp16, prepared once; bf16 values
+//               convert exactly except below 2^-14, where the absolute error is < 2^-25).
+//   3. reduce:  s = sum(partials) * 2^-15 * exp(-ln Z) -> s (fp32, optional output) and fp16.
+//   4. MLP:     [gate | up] = s [W_gate | W_up] (one GEMM), h = gelu_tanh(gate) * up (fp16),
+//               y = h W_down (second GEMM).
+//   5. embed:   x_out = bf16(E[canvas] + (sc_on ? y : 0)).
+// fp32 path: the same steps with fp32 kernels (used by the tiny closed loop).
+#include "dg_device.hpp"
+#include "dg_host.hpp"
+#include "gemm_f16.hpp"
+
+#include <algorithm>
+
+namespace dg {
+namespace {
+
+constexpr float kProbScale = 32768.0f;  // 2^15
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+
+// ---------------------------------------------------------------- prepare
+// dst[n][k] = fp16(src[k][n]) for k < K (rows of src), zero for K <= k < Kp.
+__global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16_t* __restrict__ src, int32_t K,
+                                                                    int32_t N, int64_t Kp,
+                                                                    _Float16* __restrict__ dst) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int k = k0 + i, n = n0 + tx;
+    tile[i][tx] = (k < K && n < N) ? bf16_to_f32(src[static_cast<int64_t>(k) * N + n]) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int n = n0 + i, k = k0 + tx;
+    if (n < N && k < Kp) dst[static_cast<int64_t>(n) * Kp + k] = static_cast<_Float16>(tile[tx][i]);
+  }
+}
+
+// ---------------------------------------------------------------- bf16 path kernels
+template <bool BF16>
+__global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__ logits, int64_t ld, int32_t V,
+                                                        int64_t Kp, float inv_t, const float* __restrict__ row_max,
+                                                        _Float16* __restrict__ w) {
+  const int r = blockIdx.y;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i0 >= Kp) return;
+  const float m = row_max[r];
+  float l[8];
+  if constexpr (BF16) {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(logits) + r * ld;
+    if (i0 + 8 <= V) {
+      const uint4 q = *reinterpret_cast<const uint4*>(row + i0);
+      l[0] = bf16_lo(q.x); l[1] = bf16_hi(q.x); l[2] = bf16_lo(q.y); l[3] = bf16_hi(q.y);
+      l[4] = bf16_lo(q.z); l[5] = bf16_hi(q.z); l[6] = bf16_lo(q.w); l[7] = bf16_hi(q.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l[j] = (i0 + j < V) ? bf16_to_f32(row[i0 + j]) : -INFINITY;
+    }
+  } else {
+    const float* row = reinterpret_cast<const float*>(logits) + r * ld;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l[j] = (i0 + j < V) ? row[i0 + j] : -INFINITY;
+  }
+  half8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(__expf(l[j] * inv_t - m) * kProbScale);
+  *reinterpret_cast<half8*>(w + r * Kp + i0) = o;
+}
+
+// s = sum_split part * 2^-15 / Z ; writes fp32 s (optional) and fp16 s
+__global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
+                                                        int32_t N, const float* __restrict__ row_lnz,
+                                                        float* __restrict__ s_out, _Float16* __restrict__ s16) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * N) return;
+  const int r = static_cast<int>(idx / N);
+  float acc = 0.f;
+  for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + idx];
+  const float v = acc * (1.0f / kProbScale) * __expf(-row_lnz[r]);
+  if (s_out != nullptr) s_out[idx] = v;
+  s16[idx] = static_cast<_Float16>(v);
+}
+
+DG_DEV float gelu_tanh(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * z * (1.f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+// h[r][j] = gelu_tanh(gate) * up from the partials of the [gate | up] GEMM
+__global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
+                                                         int32_t H, _Float16* __restrict__ h16) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * H) return;
+  const int r = static_cast<int>(idx / H), j = static_cast<int>(idx - static_cast<int64_t>(r) * H);
+  const int64_t N2 = 2 * static_cast<int64_t>(H);
+  float gsum = 0.f, usum = 0.f;
+  for (int k = 0; k < splits; ++k) {
+    const float* p = part + static_cast<int64_t>(k) * M * N2 + r * N2;
+    gsum += p[j];
+    usum += p[H + j];
+  }
+  h16[idx] = static_cast<_Float16>(gelu_tanh(gsum) * usum);
+}
+
+// x_out = bf16(E[canvas] + (sc_on ? y : 0)), y from the partials of the down GEMM
+__global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
+                                                           int32_t d, int32_t V, int32_t C,
+                                                           const uint16_t* __restrict__ E,
+                                                           const int32_t* __restrict__ canvas,
+                                                           const uint8_t* __restrict__ sc_on,
+                                                           uint16_t* __restrict__ x_out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * d) return;
+  const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
+  const int64_t tok = min(max(canvas[r], 0), V - 1);
+  float x = bf16_to_f32(E[tok * d + c]);
+  if (sc_on[r / C]) {
+    float y = 0.f;
+    for (int k = 0; k < splits; ++k) y += part[static_cast<int64_t>(k) * M * d + idx];
+    x += y;
+  }
+  x_out[idx] = f32_to_bf16(x);
+}
+
+// ---------------------------------------------------------------- fp32 path kernels
+__global__ __launch_bounds__(256) void probs_f32_kernel(const float* __restrict__ logits, int64_t ld, int32_t V,
+                                                        float inv_t, const float* __restrict__ row_max,
+                                                        const float* __restrict__ row_lnz, float* __restrict__ P) {
+  const int r = blockIdx.y;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= V) return;
+  P[r * static_cast<int64_t>(V) + i] = expf(logits[r * ld + i] * inv_t - row_max[r] - row_lnz[r]);
+}
+
+__global__ __launch_bounds__(256) void glu_f32_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                      int64_t n, float* __restrict__ h) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) h[i] = gelu_tanh(g[i]) * u[i];
+}
+
+__global__ __launch_bounds__(256) void embed_f32_kernel(const float* __restrict__ y, int32_t M, int32_t d, int32_t V,
+                                                        int32_t C, const float* __restrict__ E,
+                                                        const int32_t* __restrict__ canvas,
+                                                        const uint8_t* __restrict__ sc_on, float* __restrict__ x_out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(M) * d) return;
+  const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
+  const int64_t tok = min(max(canvas[r], 0), V - 1);
+  x_out[idx] = E[tok * d + c] + (sc_on[r / C] ? y[idx] : 0.f);
+}
+
+// ---------------------------------------------------------------- workspace plans
+struct PreparedLayout {
+  int64_t Kp;
+  size_t off_et, off_wgu, off_wd, bytes;
+};
+
+PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
+  PreparedLayout p{};
+  p.Kp = pad64(V);
+  p.off_et = 0;
+  p.off_wgu = round_up(p.off_et + static_cast<size_t>(d) * p.Kp * 2, 256);
+  p.off_wd = round_up(p.off_wgu + static_cast<size_t>(2) * hidden * d * 2, 256);
+  p.bytes = round_up(p.off_wd + static_cast<size_t>(d) * hidden * 2, 256);
+  return p;
+}
+
+struct Bf16Plan {
+  int64_t Kp;
+  GemmPlan pe, g1, g2;
+  size_t off_w, off_part, off_s16, off_h16, bytes;
+};
+
+Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
+  Bf16Plan p{};
+  p.Kp = pad64(V);
+  p.pe = plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
+  p.g1 = plan_gemm(rows, 2 * hidden, d);
+  p.g2 = plan_gemm(rows, d, hidden);
+  size_t part = 0;
+  part = std::max(part, static_cast<size_t>(p.pe.splits) * rows * d * 4);
+  part = std::max(part, static_cast<size_t>(p.g1.splits) * rows * 2 * hidden * 4);
+  part = std::max(part, static_cast<size_t>(p.g2.splits) * rows * d * 4);
+  p.off_w = 0;
+  p.off_part = round_up(p.off_w + static_cast<size_t>(rows) * p.Kp * 2, 256);
+  p.off_s16 = round_up(p.off_part + part, 256);
+  p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows) * d * 2, 256);
+  p.bytes = round_up(p.off_h16 + static_cast<size_t>(rows) * hidden * 2, 256);
+  return p;
+}
+
+struct F32Plan {
+  size_t off_P, off_s, off_g, off_u, off_h, off_y, bytes;
+};
+
+F32Plan f32_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
+  F32Plan p{};
+  p.off_P = 0;
+  p.off_s = round_up(p.off_P + static_cast<size_t>(rows) * V * 4, 256);
+  p.off_g = round_up(p.off_s + static_cast<size_t>(rows) * d * 4, 256);
+  p.off_u = round_up(p.off_g + static_cast<size_t>(rows) * hidden * 4, 256);
+  p.off_h = round_up(p.off_u + static_cast<size_t>(rows) * hidden * 4, 256);
+  p.off_y = round_up(p.off_h + static_cast<size_t>(rows) * hidden * 4, 256);
+  p.bytes = round_up(p.off_y + static_cast<size_t>(rows) * d * 4, 256);
+  return p;
+}
+
+unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+}  // namespace
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" size_t dg_selfcond_prepared_bytes(int32_t V, int32_t d, int32_t hidden, int32_t dtype) {
+  if (dtype != DG_BF16 || V <= 0 || d <= 0 || hidden <= 0) return 0;
+  return prepared_layout(V, d, hidden).bytes;
+}
+
+extern "C" dg_status dg_selfcond_prepare(const void* E, const void* w_gate, const void* w_up, const void* w_down,
+                                         int32_t V, int32_t d, int32_t hidden, int32_t dtype, void* prepared,
+                                         size_t prepared_bytes, dg_stream_t stream) {
+  DG_ARG(V > 0 && d > 0 && hidden > 0);
+  DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
+  if (dtype == DG_F32) return DG_OK;  // the fp32 path reads the tables as given
+  DG_ARG(E && w_gate && w_up && w_down && prepared);
+  DG_UNSUP(d % kGemmTN == 0 && hidden % kGemmTN == 0);
+  const PreparedLayout L = prepared_layout(V, d, hidden);
+  DG_REQUIRE(prepared_bytes >= L.bytes, DG_E_WORKSPACE);
+  hipStream_t s = as_stream(stream);
+  char* base = reinterpret_cast<char*>(prepared);
+  auto* et = reinterpret_cast<_Float16*>(base + L.off_et);
+  auto* wgu = reinterpret_cast<_Float16*>(base + L.off_wgu);
+  auto* wd = reinterpret_cast<_Float16*>(base + L.off_wd);
+  const auto* Eb = reinterpret_cast<const uint16_t*>(E);
+  // E [V][d] -> E^T [d][Kp]
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(L.Kp, 64)), static_cast<unsigned>(cdiv(d, 64))), 256,
+                                 0, s>>>(Eb, V, d, L.Kp, et);
+  DG_LAUNCHED();
+  // W_gate, W_up [d][hidden] -> rows [0, hidden) and [hidden, 2 hidden) of [2 hidden][d]
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_gate), d, hidden, d, wgu);
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_up), d, hidden, d,
+                                              wgu + static_cast<int64_t>(hidden) * d);
+  // W_down [hidden][d] -> [d][hidden]
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(hidden, 64)), static_cast<unsigned>(cdiv(d, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_down), hidden, d, hidden, wd);
+  DG_LAUNCHED();
+  return DG_OK;
+}
+
+extern "C" size_t dg_selfcond_ws_bytes(int32_t rows, int32_t V, int32_t d, int32_t hidden, int32_t dtype) {
+  if (rows <= 0 || V <= 0 || d <= 0 || hidden <= 0) return 0;
+  if (dtype == DG_BF16) {
+    if (d % kGemmTN != 0 || hidden % kGemmTN != 0) return 0;
+    return bf16_plan(rows, V, d, hidden).bytes;
+  }
+  return f32_plan(rows, V, d, hidden).bytes;
+}
+
+extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, int32_t dtype, float temperature,
+                                              const float* row_max, const float* row_lnz, const uint8_t* sc_on,
+                                              const int32_t* canvas, int32_t B, int32_t C, const void* E,
+                                              const void* w_gate, const void* w_up, const void* w_down,
+                                              const void* prepared, int32_t V, int32_t d, int32_t hidden, void* x_out,
+                                              float* s_out, void* ws, size_t ws_bytes, void* pe_start, void* pe_stop,
+                                              dg_stream_t stream) {
+  DG_ARG(logits && row_max && row_lnz && sc_on && canvas && E && x_out);
+  DG_ARG(B > 0 && C > 0 && V > 0 && d > 0 && hidden > 0 && ld >= V);
+  DG_ARG(temperature > 0.f && temperature < INFINITY);
+  DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
+  const int64_t rows64 = static_cast<int64_t>(B) * C;
+  DG_ARG(rows64 <= 65535);
+  const int32_t rows = static_cast<int32_t>(rows64);
+  hipStream_t s = as_stream(stream);
+  const float inv_t = 1.0f / temperature;
+  char* wsb = reinterpret_cast<char*>(ws);
+
+  if (dtype == DG_F32) {
+    DG_ARG(w_gate && w_up && w_down);
+    const F32Plan p = f32_plan(rows, V, d, hidden);
+    DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
+    float* P = reinterpret_cast<float*>(wsb + p.off_P);
+    float* sv = reinterpret_cast<float*>(wsb + p.off_s);
+    float* g = reinterpret_cast<float*>(wsb + p.off_g);
+    float* u = reinterpret_cast<float*>(wsb + p.off_u);
+    float* h = reinterpret_cast<float*>(wsb + p.off_h);
+    float* y = reinterpret_cast<float*>(wsb + p.off_y);
+    const float* Ef = reinterpret_cast<const float*>(E);
+    probs_f32_kernel<<<dim3(blocks_for(V), rows), 256, 0, s>>>(reinterpret_cast<const float*>(logits), ld, V, inv_t,
+                                                               row_max, row_lnz, P);
+    DG_LAUNCHED();
+    dg_status st;
+    if ((st = dg_linear(P, Ef, nullptr, sv, rows, d, V, 0, 1.f, stream)) != DG_OK) return st;
+    if ((st = dg_linear(sv, reinterpret_cast<const float*>(w_gate), nullptr, g, rows, hidden, d, 0, 1.f, stream)) !=
+        DG_OK)
+      return st;
+    if ((st = dg_linear(sv, reinterpret_cast<const float*>(w_up), nullptr, u, rows, hidden, d, 0, 1.f, stream)) !=
+        DG_OK)
+      return st;
+    glu_f32_kernel<<<blocks_for(rows64 * hidden), 256, 0, s>>>(g, u, rows64 * hidden, h);
+    DG_LAUNCHED();
+    if ((st = dg_linear(h, reinterpret_cast<const float*>(w_down), nullptr, y, rows, d, hidden, 0, 1.f, stream)) !=
+        DG_OK)
+      return st;
+    embed_f32_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(y, rows, d, V, C, Ef, canvas, sc_on,
+                                                            reinterpret_cast<float*>(x_out));
+    DG_LAUNCHED();
+    if (s_out != nullptr) {
+      DG_REQUIRE(hipMemcpyAsync(s_out, sv, static_cast<size_t>(rows) * d * 4, hipMemcpyDeviceToDevice, s) ==
+                     hipSuccess,
+                 DG_E_HIP);
+    }
+    return DG_OK;
+  }
+
+  // bf16 path
+  DG_ARG(prepared != nullptr);
+  DG_UNSUP(d % kGemmTN == 0 && hidden % kGemmTN == 0);
+  DG_UNSUP(ld % 8 == 0 && aligned16(logits));
+  const Bf16Plan p = bf16_plan(rows, V, d, hidden);
+  DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
+  const PreparedLayout L = prepared_layout(V, d, hidden);
+  const char* pb = reinterpret_cast<const char*>(prepared);
+  const auto* et = reinterpret_cast<const _Float16*>(pb + L.off_et);
+  const auto* wgu = reinterpret_cast<const _Float16*>(pb + L.off_wgu);
+  const auto* wd = reinterpret_cast<const _Float16*>(pb + L.off_wd);
+  auto* w = reinterpret_cast<_Float16*>(wsb + p.off_w);
+  auto* part = reinterpret_cast<float*>(wsb + p.off_part);
+  auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
+  auto* h16 = reinterpret_cast<_Float16*>(wsb + p.off_h16);
+
+  probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 2048)), rows), 256, 0, s>>>(logits, ld, V, p.Kp,
+                                                                                            inv_t, row_max, w);
+  DG_LAUNCHED();
+  if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
+  gemm_f16_splitk_kernel<<<p.pe.grid, kGemmThreads, 0, s>>>(
+      GemmArgs{w, p.Kp, et, p.Kp, part, rows, d, static_cast<int32_t>(p.Kp), p.pe.kchunk});
+  DG_LAUNCHED();
+  if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
+  pe_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s_out, s16);
+  DG_LAUNCHED();
+  gemm_f16_splitk_kernel<<<p.g1.grid, kGemmThreads, 0, s>>>(
+      GemmArgs{s16, d, wgu, d, part, rows, 2 * hidden, d, p.g1.kchunk});
+  DG_LAUNCHED();
+  glu_reduce_kernel<<<blocks_for(rows64 * hidden), 256, 0, s>>>(part, p.g1.splits, rows, hidden, h16);
+  DG_LAUNCHED();
+  gemm_f16_splitk_kernel<<<p.g2.grid, kGemmThreads, 0, s>>>(
+      GemmArgs{h16, hidden, wd, hidden, part, rows, d, hidden, p.g2.kchunk});
+  DG_LAUNCHED();
+  embed_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
+                                                             reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
+                                                             reinterpret_cast<uint16_t*>(x_out));
+  DG_LAUNCHED();
+  return DG_OK;
+}
+
+extern "C" dg_status dg_selfcond_embed(const void* logits, int64_t ld, int32_t dtype, float temperature,
+                                       const float* row_max, const float* row_lnz, const uint8_t* sc_on,
+                                       const int32_t* canvas, int32_t B, int32_t C, const void* E,
+                                       const void* w_gate, const void* w_up, const void* w_down, const void* prepared,
+                                       int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out, void* ws,
+                                       size_t ws_bytes, dg_stream_t stream) {
+  return dg_selfcond_embed_traced(logits, ld, dtype, temperature, row_max, row_lnz, sc_on, canvas, B, C, E, w_gate,
+                                  w_up, w_down, prepared, V, d, hidden, x_out, s_out, ws, ws_bytes, nullptr, nullptr,
+                                  stream);
+}

@@ -203,3 +203,46 @@ def tiny_loop_inputs(cfg: dict, variant_scale: float | None = None) -> dict:
         logit_scale=float(cfg["logit_scale"] if variant_scale is None else variant_scale),
         seed64=np.uint64(s),
     )
+
+
+# ---------------------------------------------------------------- large inputs generated on the GPU
+# Full-size tables (a 262144 x 4096 embedding table, thousands of 262144-wide logit rows) are
+# drawn with torch's seeded device generator instead of numpy, then copied to the host where
+# the oracle needs them.  Same recipes as above; values are deterministic for a given seed,
+# shape and device type.
+
+def _torch_gen(seed: int, tag, device):
+    import torch
+    h = hashlib.sha256(repr((int(seed), "torch") + (tag if isinstance(tag, tuple) else (tag,))).encode()).digest()
+    g = torch.Generator(device=device)
+    g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
+    return g
+
+
+def normal_torch(seed: int, tag, shape, std: float, dtype, device, chunk_rows: int = 1 << 14):
+    """N(0, std^2) of `shape`, rounded to `dtype` (torch.bfloat16 or float32), generated on `device`."""
+    import torch
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(shape[0], -1)
+    g = _torch_gen(seed, tag, device)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        flat[r0:r1] = (torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device) * std).to(dtype)
+    return out
+
+
+def zipf_logits_torch(seed: int, tag, rows: int, V: int, device, alpha_max: float = 3.0, dtype=None,
+                      chunk_rows: int = 64):
+    """Same recipe as zipf_logits_bf16: sqrt(3) z - alpha_r * 1.1 * ln(1 + rank_r(i)), bf16."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = _torch_gen(seed, tag, device)
+    alpha = torch.rand(rows, generator=g, device=device) * alpha_max
+    base = -1.1 * torch.log1p(torch.arange(V, device=device, dtype=torch.float32))
+    out = torch.empty((rows, V), dtype=dtype, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        z = torch.randn((r1 - r0, V), generator=g, device=device)
+        perm = torch.argsort(torch.rand((r1 - r0, V), generator=g, device=device), dim=1)
+        out[r0:r1] = (np.sqrt(3.0) * z + alpha[r0:r1, None] * base[perm]).to(dtype)
+    return out

@@ -1,0 +1,73 @@
+"""CPU checks of the boundary: libdg loads, exports every entry point of include/dg.h, and rejects bad
+arguments on the host before launching anything (no GPU needed for these calls)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "dg.h")).read()
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import denoise_step_amd as dg
+    if not os.path.exists(dg.LIB_PATH):
+        from denoise_step_amd import build
+        build.build()
+    return dg.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+    import denoise_step_amd as dg
+    assert set(names) == set(dg.EXPORTED)
+
+
+def test_version_and_status_strings(L):
+    assert L.dg_version() >= 100
+    assert L.dg_status_str(0) == b"ok"
+    assert L.dg_status_str(-3).startswith(b"workspace")
+
+
+def test_host_validation_rejects_before_launch(L):
+    # null logits / bad sizes / unsupported dtype / misaligned ld / missing workspace
+    args = dict(logits=None, ld=1024, dtype=1, rows=16, V=1024, rpr=16)
+    f = lambda **kw: L.dg_denoise_sample(kw.get("logits", 16), kw.get("ld", 1024), kw.get("dtype", 1),
+                                         kw.get("rows", 16), kw.get("V", 1024), kw.get("rpr", 16), 64, 64, None,
+                                         kw.get("T", 1.0), 0, 64, 64, 64, 64, 64, kw.get("ws", 64),
+                                         kw.get("wsb", 1 << 20), None)
+    assert f(logits=None) == -1
+    assert f(rows=0) == -1
+    assert f(rows=15) == -1                    # rows not a multiple of rows_per_req
+    assert f(ld=1000) == -1                    # ld < V
+    assert f(dtype=7) == -2
+    assert f(ld=1028) == -2                    # ld % 8 != 0
+    assert f(logits=17) == -2                  # not 16-byte aligned
+    assert f(T=0.0) == -1
+    assert f(ws=None) == -3
+    assert f(wsb=1) == -3
+    assert L.dg_entropy_accept(64, 64, 1, 1025, 10, 1.0, 64, 64, None, 64, None, None, None) == -1
+    assert L.dg_converged(64, 64, 1, 0, 10, 2, 0.5, 32, 64, None, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, None) == -1
+    # attention: unsupported head_dim / page size, Hq % Hkv
+    att = lambda D=128, ps=16, Hq=16, Hkv=8: L.dg_canvas_attention(64, 64, 64, 64, 64, 4, 64, 4, 64, 1, 16, 16, 32,
+                                                                     Hq, Hkv, D, ps, 0.1, 1, 64, None, 0, None)
+    assert att(D=96) == -2 and att(ps=32) == -2 and att(Hq=12, Hkv=8) == -1
+    # self-conditioning: bf16 requires d, hidden multiples of 128 and a prepared table
+    assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, None, 1024, 128, 128, 64,
+                               None, 64, 1 << 30, None) == -1
+    assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, 64, 1024, 96, 128, 64,
+                               None, 64, 1 << 30, None) == -2
+
+
+def test_workspace_sizes(L):
+    assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 8 * 32
+    assert L.dg_selfcond_ws_bytes(256, 262144, 4096, 1024, 1) >= 256 * 262144 * 2
+    assert L.dg_selfcond_prepared_bytes(262144, 4096, 1024, 1) >= 262144 * 4096 * 2 + 3 * 4096 * 1024 * 2

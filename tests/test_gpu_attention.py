@@ -1,0 +1,67 @@
+"""GPU parity of dg_canvas_attention against oracle.attention (through the C ABI)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as oatt
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _f(p, a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if p.dtype == "bf16" else a.astype(np.float64)
+
+
+def run_case(splits, Hq, Hkv, D, dtype, seed=0, check_cache=True):
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    p = synth.attention_problem(seed, splits, Hq, Hkv, D, dtype=dtype)
+    up = (lambda a: P.dev_bf16(a)) if dtype == "bf16" else (lambda a: P.dev(a))
+    q, k, v, kc, vc = (up(a) for a in (p.q, p.k, p.v, p.k_cache, p.v_cache))
+    sp = np.array([[p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i], 0] for i, s in enumerate(p.splits)],
+                  np.int32)
+    max_rows = max(s.n_causal + s.n_canvas for s in p.splits)
+    max_keys = max(s.cached + s.n_causal + s.n_canvas for s in p.splits)
+    scale = 1.0 / np.sqrt(D)
+    out = dg.dg_canvas_attention(q, k, v, kc, vc, P.dev(p.page_table), P.dev(sp), max_rows, max_keys, scale)
+    torch.cuda.synchronize()
+    ref, rkc, rvc = oatt.canvas_attention(_f(p, p.q), _f(p, p.k), _f(p, p.v), _f(p, p.k_cache), _f(p, p.v_cache),
+                                          p.page_table, [tuple(r[:5]) for r in sp], p.page_size, scale)
+    got = P.host_f64(out)
+    tol = P.TOL_ATT_BF16 if dtype == "bf16" else P.TOL_ATT_F32
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"max |delta| {err}"
+    if check_cache:
+        assert np.array_equal(P.host_f64(kc), rkc) and np.array_equal(P.host_f64(vc), rvc)
+    return err
+
+
+SMALL = [
+    ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 32),                # the three-request batch
+    ([(0, 2, 2)], 2, 2, 32),                                     # p0 p1 c0 c1
+    ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 64),
+    ([(100, 0, 33)], 8, 2, 128),
+    ([(300, 40, 70), (1, 0, 129)], 16, 8, 256),
+    ([(0, 200, 56)], 32, 8, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_attention_small(case, dtype):
+    splits, Hq, Hkv, D = SMALL[case]
+    print(f"attention case={case} dtype={dtype}", flush=True)
+    run_case(splits, Hq, Hkv, D, dtype, seed=case)
+
+
+def test_attention_single_canvas_full_size():
+    """One 256-row canvas over a 2048-token paged prefix, 16 query / 8 KV heads, head_dim 256, bf16."""
+    print("attention full size single canvas", flush=True)
+    run_case([(2048, 0, 256)], 16, 8, 256, "bf16", seed=7)
+
+
+def test_attention_tiny_loop_shapes_f32():
+    """The tiny loop's launches: 32-row causal prefill, 16-row canvas over 32, 16-row commit pass."""
+    for sp in ([(0, 32, 0)], [(32, 0, 16)], [(32, 16, 0)]):
+        run_case(sp, 2, 2, 32, "f32", seed=11)

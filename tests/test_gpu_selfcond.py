@@ -1,0 +1,113 @@
+"""GPU parity of dg_selfcond_embed against oracle.selfcond (through the C ABI)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import sampler as osamp
+from oracle import selfcond as osc
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _sampler_stats(logits_t, V, rows_per_req):
+    import denoise_step_amd as dg
+    n_req = logits_t.shape[0] // rows_per_req
+    seeds = P.dev(np.arange(n_req, dtype=np.int64))
+    steps = P.dev(np.zeros(n_req, np.int32))
+    return dg.dg_denoise_sample(logits_t, V, rows_per_req, seeds, steps)
+
+
+@pytest.mark.parametrize("V,d,hidden,w_std", [(1000, 128, 128, 0.02), (4096, 256, 384, 0.02), (2500, 128, 256, 0.5),
+                                               (1000, 128, 128, 0.5)])
+def test_selfcond_bf16_small(V, d, hidden, w_std):
+    """w_std 0.5 makes the MLP output dominate x_out, so the normwise check exercises the MLP GEMMs."""
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    print(f"selfcond bf16 V={V} d={d} h={hidden}", flush=True)
+    B, C = 3, 16
+    rows = B * C
+    ld = (V + 7) // 8 * 8
+    L = synth.zipf_logits_f32(5, ("sc", V), rows, ld)
+    bits = synth.f32_to_bf16_bits(L)
+    E = synth.normal_bf16(5, ("sc.E", V), (V, d), 1 / 8)
+    wg = synth.normal_bf16(5, ("sc.wg", V), (d, hidden), w_std)
+    wu = synth.normal_bf16(5, ("sc.wu", V), (d, hidden), w_std)
+    wd = synth.normal_bf16(5, ("sc.wd", V), (hidden, d), w_std)
+    canvas = synth.rng_for(5, "sc.canvas").integers(0, V, (B, C)).astype(np.int32)
+    sc_on = np.array([1, 0, 1], np.uint8)
+    lt = P.dev_bf16(bits)
+    Et, wgt, wut, wdt = (P.dev_bf16(a) for a in (E, wg, wu, wd))
+    st = _sampler_stats(lt, V, C)
+    prepared = dg.dg_selfcond_prepare(Et, wgt, wut, wdt)
+    s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(sc_on), P.dev(canvas), Et, wgt, wut, wdt,
+                             prepared, s_out=s_out)
+    torch.cuda.synchronize()
+    host_l = synth.bf16_bits_to_f32(bits).astype(np.float64)[:, :V]
+    ref = osamp.denoise_sample(host_l, 1.0, np.arange(B), np.zeros(B), C)
+    Pm = osc.probs_from_stats(host_l, 1.0, ref.row_max, ref.row_lnz)
+    f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)
+    rx, rs, ry = osc.selfcond_embed(Pm, canvas, sc_on, f(E), f(wg), f(wu), f(wd), C, to_bf16=False)
+    es = P.rel_norm_err(s_out.cpu().numpy(), rs)
+    assert es.max() <= P.TOL_NORM_REL, es.max()
+    gx = P.host_f64(x)
+    P.check_bf16_output(gx, rx)
+    on = np.repeat(sc_on.astype(bool), C)
+    assert np.array_equal(gx[~on], f(E)[canvas.reshape(-1)][~on])       # self-conditioning off: plain lookup
+
+
+@pytest.mark.parametrize("w_std", [0.02, 0.5])
+def test_selfcond_f32_tiny_sizes(w_std):
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    B, C, V, d, hidden = 1, 16, 1024, 64, 128
+    rows = B * C
+    L = synth.zipf_logits_f32(6, "sc32", rows, V)
+    E = synth.normal_f32(6, "sc32.E", (V, d), 1 / 8)
+    w = [synth.normal_f32(6, t, sh, w_std) for t, sh in (("g", (d, hidden)), ("u", (d, hidden)), ("d", (hidden, d)))]
+    canvas = synth.rng_for(6, "c").integers(0, V, (B, C)).astype(np.int32)
+    lt = P.dev(L)
+    st = _sampler_stats(lt, V, C)
+    s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(np.array([1], np.uint8)), P.dev(canvas),
+                             P.dev(E), *(P.dev(a) for a in w), None, s_out=s_out)
+    torch.cuda.synchronize()
+    ref = osamp.denoise_sample(L.astype(np.float64), 1.0, [0], [0], C)
+    Pm = osc.probs_from_stats(L.astype(np.float64), 1.0, ref.row_max, ref.row_lnz)
+    rx, rs, ry = osc.selfcond_embed(Pm, canvas, np.array([1]), E, *w, C, to_bf16=False)
+    assert P.rel_norm_err(s_out.cpu().numpy(), rs).max() <= 1e-5
+    assert P.rel_norm_err(x.cpu().numpy(), rx).max() <= 1e-5
+
+
+def test_selfcond_single_canvas_full_size_sampled_rows():
+    """256 canvas rows, V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096, in the bench's launch configuration."""
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    print("selfcond full size", flush=True)
+    V, d, hidden, C = 262144, 4096, 1024, 256
+    E = synth.normal_torch(0, "single_canvas.E", (V, d), 1 / 8, torch.bfloat16, "cuda")
+    wg = synth.normal_torch(0, "single_canvas.wg", (d, hidden), 0.02, torch.bfloat16, "cuda")
+    wu = synth.normal_torch(0, "single_canvas.wu", (d, hidden), 0.02, torch.bfloat16, "cuda")
+    wd = synth.normal_torch(0, "single_canvas.wd", (hidden, d), 0.02, torch.bfloat16, "cuda")
+    lt = synth.zipf_logits_torch(0, "single_canvas.logits_t", C, V, "cuda")
+    canvas = synth.rng_for(0, "single_canvas.canvas").integers(0, V, (1, C)).astype(np.int32)
+    st = _sampler_stats(lt, V, C)
+    prepared = dg.dg_selfcond_prepare(E, wg, wu, wd)
+    s_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
+    x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(np.array([1], np.uint8)), P.dev(canvas), E,
+                             wg, wu, wd, prepared, s_out=s_out)
+    torch.cuda.synchronize()
+    rows = [0, 77, 128, 255]
+    host_l = lt[rows].float().cpu().numpy().astype(np.float64)
+    Pm = np.stack([osamp.probabilities(host_l[i], 1.0) for i in range(len(rows))])
+    Eh = E.float().cpu().numpy()
+    s_ref = np.zeros((len(rows), d))
+    for v0 in range(0, V, 16384):                      # fp64 P.E in chunks of the table
+        s_ref += Pm[:, v0:v0 + 16384] @ Eh[v0:v0 + 16384].astype(np.float64)
+    es = P.rel_norm_err(s_out.cpu().numpy()[rows], s_ref)
+    assert es.max() <= P.TOL_NORM_REL, es
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    y_ref = osc.gated_mlp(s_ref, f(wg), f(wu), f(wd))
+    x_ref = Eh[canvas[0, rows]].astype(np.float64) + y_ref
+    P.check_bf16_output(P.host_f64(x)[rows], x_ref)
