@@ -33,9 +33,31 @@ METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
            tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0)
-PE_KERNEL = "gemm_f16_splitk_kernel"
+PE_KERNEL = "gemm_f16_splitk_kernel<0>"
 PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp", "denoise_step_amd/csrc/selfcond.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same soname, same instance)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        assert self.hip.hipEventCreate(self.ct.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
+        return ms.value
 
 
 def log(msg):
@@ -212,7 +234,8 @@ def main():
         w.step(t)
     torch.cuda.synchronize()
     K = args.steps
-    pe_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    hev = HipEvents()
+    pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {K} steps")
     torch.cuda.synchronize()
@@ -225,7 +248,7 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
-    pe_ms = sum(a.elapsed_time(b) for a, b in pe_ev) / K
+    pe_ms = sum(hev.elapsed_ms(a, b) for a, b in pe_ev) / K
     # per-call breakdown over a few extra steps (not part of the timed region)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     names = ["canvas_attention", "denoise_sample", "entropy_accept", "converged", "selfcond_embed"]

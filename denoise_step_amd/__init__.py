@@ -49,9 +49,9 @@ _SIGS = {
     "dg_selfcond_prepare": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _sz, _p]),
     "dg_selfcond_ws_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "dg_selfcond_embed": (_i32, [_p, _i64, _i32, _f32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i32, _i32,
-                                 _i32, _p, _p, _p, _sz, _p]),
+                                 _i32, _p, _p, _p, _p, _sz, _p]),
     "dg_selfcond_embed_traced": (_i32, [_p, _i64, _i32, _f32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i32,
-                                        _i32, _i32, _p, _p, _p, _sz, _p, _p, _p]),
+                                        _i32, _i32, _p, _p, _p, _p, _sz, _p, _p, _p]),
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
     "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
     "dg_linear": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p]),
@@ -229,8 +229,8 @@ def dg_selfcond_ws_bytes(rows, V, d, hidden, dtype) -> int:
 
 
 def dg_selfcond_embed(logits, V, row_max, row_lnz, sc_on, canvas, E, w_gate, w_up, w_down, prepared,
-                      temperature=1.0, x_out=None, s_out=None, ws=None, stream=None, pe_events=None):
-    """pe_events: optional (start, stop) torch.cuda.Event pair recorded around the P.E kernel."""
+                      temperature=1.0, x_out=None, s_out=None, y_out=None, ws=None, stream=None, pe_events=None):
+    """pe_events: optional (start, stop) pair of raw hipEvent_t handles (ints) recorded around the P.E kernel."""
     B, C = canvas.shape
     rows, ld = logits.shape
     d = E.shape[1]
@@ -239,11 +239,12 @@ def dg_selfcond_embed(logits, V, row_max, row_lnz, sc_on, canvas, E, w_gate, w_u
     x_out = torch.empty((rows, d), dtype=E.dtype, device=E.device) if x_out is None else x_out
     nb = dg_selfcond_ws_bytes(rows, V, d, hidden, dt)
     ws = _ws(nb, ws, logits.device)
-    ev0, ev1 = (None, None) if pe_events is None else (pe_events[0].cuda_event, pe_events[1].cuda_event)
+    ev0, ev1 = (None, None) if pe_events is None else (int(pe_events[0]), int(pe_events[1]))
     _check(lib().dg_selfcond_embed_traced(_ptr(logits), ld, dt, float(temperature), _ptr(row_max), _ptr(row_lnz),
                                           _ptr(sc_on), _ptr(canvas), B, C, _ptr(E), _ptr(w_gate), _ptr(w_up),
                                           _ptr(w_down), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
-                                          _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_traced")
+                                          _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)),
+           "dg_selfcond_embed_traced")
     return x_out
 
 

@@ -13,9 +13,11 @@
 //               (a plain fp16 or bf16 probability would lose 11+ bits on diffuse rows).
 //   2. P.E:     split-K fp16 MFMA GEMM against E^T (fp16, prepared once; bf16 values
 //               convert exactly except below 2^-14, where the absolute error is < 2^-25).
-//   3. reduce:  s = sum(partials) * 2^-15 * exp(-ln Z) -> s (fp32, optional output) and fp16.
-//   4. MLP:     [gate | up] = s [W_gate | W_up] (one GEMM), h = gelu_tanh(gate) * up (fp16),
-//               y = h W_down (second GEMM).
+//   3. reduce:  s = sum(partials) * 2^-15 * exp(-ln Z) -> s (fp32, optional output) and an
+//               fp16 copy scaled per row by a power of two (largest |s| in (2^13, 2^14]).
+//   4. MLP:     [gate | up] = s [W_gate | W_up] (one GEMM), h = gelu_tanh(gate) * up, stored in
+//               fp16 with its own per-row power-of-two scale (at the weights' N(0, 0.02^2) scale
+//               h is ~1e-5, below fp16's normal range unscaled), y = h W_down (second GEMM).
 //   5. embed:   x_out = bf16(E[canvas] + (sc_on ? y : 0)).
 // fp32 path: the same steps with fp32 kernels (used by the tiny closed loop).
 #include "dg_device.hpp"
@@ -81,18 +83,47 @@ __global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__
   *reinterpret_cast<half8*>(w + r * Kp + i0) = o;
 }
 
-// s = sum_split part * 2^-15 / Z ; writes fp32 s (optional) and fp16 s
+// Power-of-two scale that brings a row's largest magnitude to (2^13, 2^14]: applied before a
+// row is stored in fp16 so that small activations stay in fp16's normal range (exact, undone
+// by multiplying the GEMM result by the reciprocal).
+DG_DEV float row_pow2_scale(float amax) {
+  if (!(amax > 0.f) || !(amax < INFINITY)) return 1.f;
+  int e;
+  frexpf(amax, &e);  // amax in [2^(e-1), 2^e)
+  return ldexpf(1.f, 14 - e);
+}
+
+DG_DEV float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+// One workgroup per row: s = sum_split part * 2^-15 / Z -> s32 (and s_out), then s16 = fp16(s * scale_r)
+// with scale_r a power of two; inv_scale[r] = 1 / scale_r.
 __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                         int32_t N, const float* __restrict__ row_lnz,
-                                                        float* __restrict__ s_out, _Float16* __restrict__ s16) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(M) * N) return;
-  const int r = static_cast<int>(idx / N);
-  float acc = 0.f;
-  for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + idx];
-  const float v = acc * (1.0f / kProbScale) * __expf(-row_lnz[r]);
-  if (s_out != nullptr) s_out[idx] = v;
-  s16[idx] = static_cast<_Float16>(v);
+                                                        float* __restrict__ s32, float* __restrict__ s_out,
+                                                        _Float16* __restrict__ s16, float* __restrict__ inv_scale) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
+  const int64_t base = static_cast<int64_t>(r) * N;
+  float amax = 0.f;
+  for (int n = threadIdx.x; n < N; n += 256) {
+    float acc = 0.f;
+    for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + base + n];
+    const float v = acc * f;
+    s32[base + n] = v;
+    if (s_out != nullptr) s_out[base + n] = v;
+    amax = fmaxf(amax, fabsf(v));
+  }
+  const float sc = row_pow2_scale(block_max_256(amax, red));
+  for (int n = threadIdx.x; n < N; n += 256) s16[base + n] = static_cast<_Float16>(s32[base + n] * sc);
+  if (threadIdx.x == 0) inv_scale[r] = 1.f / sc;
 }
 
 DG_DEV float gelu_tanh(float z) {
@@ -100,20 +131,32 @@ DG_DEV float gelu_tanh(float z) {
   return 0.5f * z * (1.f + tanhf(c * (z + 0.044715f * z * z * z)));
 }
 
-// h[r][j] = gelu_tanh(gate) * up from the partials of the [gate | up] GEMM
+// One workgroup per row: h = gelu_tanh(gate) * up from the partials of the [gate | up] GEMM (whose
+// input row was scaled by 1 / s_inv[r]), then h16 = fp16(h * scale_r), h_inv[r] = 1 / scale_r.
 __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                         int32_t H, _Float16* __restrict__ h16) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(M) * H) return;
-  const int r = static_cast<int>(idx / H), j = static_cast<int>(idx - static_cast<int64_t>(r) * H);
+                                                         int32_t H, const float* __restrict__ s_inv,
+                                                         float* __restrict__ h32, _Float16* __restrict__ h16,
+                                                         float* __restrict__ h_inv) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
   const int64_t N2 = 2 * static_cast<int64_t>(H);
-  float gsum = 0.f, usum = 0.f;
-  for (int k = 0; k < splits; ++k) {
-    const float* p = part + static_cast<int64_t>(k) * M * N2 + r * N2;
-    gsum += p[j];
-    usum += p[H + j];
+  const float si = s_inv[r];
+  const int64_t base = static_cast<int64_t>(r) * H;
+  float amax = 0.f;
+  for (int j = threadIdx.x; j < H; j += 256) {
+    float gsum = 0.f, usum = 0.f;
+    for (int k = 0; k < splits; ++k) {
+      const float* p = part + static_cast<int64_t>(k) * M * N2 + r * N2;
+      gsum += p[j];
+      usum += p[H + j];
+    }
+    const float h = gelu_tanh(gsum * si) * (usum * si);
+    h32[base + j] = h;
+    amax = fmaxf(amax, fabsf(h));
   }
-  h16[idx] = static_cast<_Float16>(gelu_tanh(gsum) * usum);
+  const float sc = row_pow2_scale(block_max_256(amax, red));
+  for (int j = threadIdx.x; j < H; j += 256) h16[base + j] = static_cast<_Float16>(h32[base + j] * sc);
+  if (threadIdx.x == 0) h_inv[r] = 1.f / sc;
 }
 
 // x_out = bf16(E[canvas] + (sc_on ? y : 0)), y from the partials of the down GEMM
@@ -122,16 +165,20 @@ __global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restri
                                                            const uint16_t* __restrict__ E,
                                                            const int32_t* __restrict__ canvas,
                                                            const uint8_t* __restrict__ sc_on,
-                                                           uint16_t* __restrict__ x_out) {
+                                                           const float* __restrict__ h_inv,
+                                                           uint16_t* __restrict__ x_out, float* __restrict__ y_out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(M) * d) return;
   const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
   const int64_t tok = min(max(canvas[r], 0), V - 1);
   float x = bf16_to_f32(E[tok * d + c]);
-  if (sc_on[r / C]) {
+  const bool on = sc_on[r / C] != 0;
+  if (on || y_out != nullptr) {
     float y = 0.f;
     for (int k = 0; k < splits; ++k) y += part[static_cast<int64_t>(k) * M * d + idx];
-    x += y;
+    y *= h_inv[r];
+    if (on) x += y;
+    if (y_out != nullptr) y_out[idx] = y;
   }
   x_out[idx] = f32_to_bf16(x);
 }
@@ -155,12 +202,14 @@ __global__ __launch_bounds__(256) void glu_f32_kernel(const float* __restrict__ 
 __global__ __launch_bounds__(256) void embed_f32_kernel(const float* __restrict__ y, int32_t M, int32_t d, int32_t V,
                                                         int32_t C, const float* __restrict__ E,
                                                         const int32_t* __restrict__ canvas,
-                                                        const uint8_t* __restrict__ sc_on, float* __restrict__ x_out) {
+                                                        const uint8_t* __restrict__ sc_on, float* __restrict__ x_out,
+                                                        float* __restrict__ y_out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(M) * d) return;
   const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
   const int64_t tok = min(max(canvas[r], 0), V - 1);
   x_out[idx] = E[tok * d + c] + (sc_on[r / C] ? y[idx] : 0.f);
+  if (y_out != nullptr) y_out[idx] = y[idx];
 }
 
 // ---------------------------------------------------------------- workspace plans
@@ -182,7 +231,7 @@ PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
 struct Bf16Plan {
   int64_t Kp;
   GemmPlan pe, g1, g2;
-  size_t off_w, off_part, off_s16, off_h16, bytes;
+  size_t off_w, off_part, off_s16, off_h16, off_s32, off_h32, off_sinv, off_hinv, bytes;
 };
 
 Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
@@ -199,7 +248,11 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   p.off_part = round_up(p.off_w + static_cast<size_t>(rows) * p.Kp * 2, 256);
   p.off_s16 = round_up(p.off_part + part, 256);
   p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows) * d * 2, 256);
-  p.bytes = round_up(p.off_h16 + static_cast<size_t>(rows) * hidden * 2, 256);
+  p.off_s32 = round_up(p.off_h16 + static_cast<size_t>(rows) * hidden * 2, 256);
+  p.off_h32 = round_up(p.off_s32 + static_cast<size_t>(rows) * d * 4, 256);
+  p.off_sinv = round_up(p.off_h32 + static_cast<size_t>(rows) * hidden * 4, 256);
+  p.off_hinv = round_up(p.off_sinv + static_cast<size_t>(rows) * 4, 256);
+  p.bytes = round_up(p.off_hinv + static_cast<size_t>(rows) * 4, 256);
   return p;
 }
 
@@ -278,8 +331,8 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
                                               const int32_t* canvas, int32_t B, int32_t C, const void* E,
                                               const void* w_gate, const void* w_up, const void* w_down,
                                               const void* prepared, int32_t V, int32_t d, int32_t hidden, void* x_out,
-                                              float* s_out, void* ws, size_t ws_bytes, void* pe_start, void* pe_stop,
-                                              dg_stream_t stream) {
+                                              float* s_out, float* y_out, void* ws, size_t ws_bytes, void* pe_start,
+                                              void* pe_stop, dg_stream_t stream) {
   DG_ARG(logits && row_max && row_lnz && sc_on && canvas && E && x_out);
   DG_ARG(B > 0 && C > 0 && V > 0 && d > 0 && hidden > 0 && ld >= V);
   DG_ARG(temperature > 0.f && temperature < INFINITY);
@@ -319,7 +372,7 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
         DG_OK)
       return st;
     embed_f32_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(y, rows, d, V, C, Ef, canvas, sc_on,
-                                                            reinterpret_cast<float*>(x_out));
+                                                            reinterpret_cast<float*>(x_out), y_out);
     DG_LAUNCHED();
     if (s_out != nullptr) {
       DG_REQUIRE(hipMemcpyAsync(s_out, sv, static_cast<size_t>(rows) * d * 4, hipMemcpyDeviceToDevice, s) ==
@@ -344,28 +397,32 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   auto* part = reinterpret_cast<float*>(wsb + p.off_part);
   auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
   auto* h16 = reinterpret_cast<_Float16*>(wsb + p.off_h16);
+  auto* s32 = reinterpret_cast<float*>(wsb + p.off_s32);
+  auto* h32 = reinterpret_cast<float*>(wsb + p.off_h32);
+  auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
+  auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
 
   probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 2048)), rows), 256, 0, s>>>(logits, ld, V, p.Kp,
                                                                                             inv_t, row_max, w);
   DG_LAUNCHED();
   if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
-  gemm_f16_splitk_kernel<<<p.pe.grid, kGemmThreads, 0, s>>>(
+  gemm_f16_splitk_kernel<0><<<p.pe.grid, kGemmThreads, 0, s>>>(
       GemmArgs{w, p.Kp, et, p.Kp, part, rows, d, static_cast<int32_t>(p.Kp), p.pe.kchunk});
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  pe_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s_out, s16);
+  pe_reduce_kernel<<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s32, s_out, s16, s_inv);
   DG_LAUNCHED();
-  gemm_f16_splitk_kernel<<<p.g1.grid, kGemmThreads, 0, s>>>(
+  gemm_f16_splitk_kernel<1><<<p.g1.grid, kGemmThreads, 0, s>>>(
       GemmArgs{s16, d, wgu, d, part, rows, 2 * hidden, d, p.g1.kchunk});
   DG_LAUNCHED();
-  glu_reduce_kernel<<<blocks_for(rows64 * hidden), 256, 0, s>>>(part, p.g1.splits, rows, hidden, h16);
+  glu_reduce_kernel<<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, s_inv, h32, h16, h_inv);
   DG_LAUNCHED();
-  gemm_f16_splitk_kernel<<<p.g2.grid, kGemmThreads, 0, s>>>(
+  gemm_f16_splitk_kernel<1><<<p.g2.grid, kGemmThreads, 0, s>>>(
       GemmArgs{h16, hidden, wd, hidden, part, rows, d, hidden, p.g2.kchunk});
   DG_LAUNCHED();
   embed_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
                                                              reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
-                                                             reinterpret_cast<uint16_t*>(x_out));
+                                                             h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
   DG_LAUNCHED();
   return DG_OK;
 }
@@ -374,9 +431,9 @@ extern "C" dg_status dg_selfcond_embed(const void* logits, int64_t ld, int32_t d
                                        const float* row_max, const float* row_lnz, const uint8_t* sc_on,
                                        const int32_t* canvas, int32_t B, int32_t C, const void* E,
                                        const void* w_gate, const void* w_up, const void* w_down, const void* prepared,
-                                       int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out, void* ws,
-                                       size_t ws_bytes, dg_stream_t stream) {
+                                       int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out, float* y_out,
+                                       void* ws, size_t ws_bytes, dg_stream_t stream) {
   return dg_selfcond_embed_traced(logits, ld, dtype, temperature, row_max, row_lnz, sc_on, canvas, B, C, E, w_gate,
-                                  w_up, w_down, prepared, V, d, hidden, x_out, s_out, ws, ws_bytes, nullptr, nullptr,
-                                  stream);
+                                  w_up, w_down, prepared, V, d, hidden, x_out, s_out, y_out, ws, ws_bytes, nullptr,
+                                  nullptr, stream);
 }

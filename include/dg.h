@@ -202,7 +202,8 @@ dg_status dg_converged(const int32_t* argmax, const float* entropy, int32_t B, i
  *   MFMA against the prepared fp16 copy (dg_selfcond_prepare) with fp32 accumulation.
  * dtype DG_F32: everything fp32 (prepared may be NULL).
  *   logits [rows][ld], ld % 8 == 0; row_max/row_lnz [rows] f32; canvas [rows] i32;
- *   sc_on [B] u8; x_out [rows][d]; s_out [rows][d] f32 or NULL (the P.E result).
+ *   sc_on [B] u8; x_out [rows][d]; s_out [rows][d] f32 or NULL (the P.E result);
+ *   y_out [rows][d] f32 or NULL (the gated-MLP output y, for every row whatever sc_on).
  *   d % 64 == 0 and hidden % 64 == 0 for DG_BF16.
  * Workspace: dg_selfcond_ws_bytes(rows, V, d, hidden, dtype) bytes.
  * ------------------------------------------------------------------------ */
@@ -215,7 +216,7 @@ dg_status dg_selfcond_embed(const void* logits, int64_t ld, int32_t dtype, float
                             const float* row_lnz, const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C,
                             const void* E, const void* w_gate, const void* w_up, const void* w_down,
                             const void* prepared, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,
-                            void* ws, size_t ws_bytes, dg_stream_t stream);
+                            float* y_out, void* ws, size_t ws_bytes, dg_stream_t stream);
 
 /* Same as dg_selfcond_embed; when pe_start / pe_stop (hipEvent_t) are non-NULL they are
  * recorded on `stream` immediately before and after the P.E contraction kernel, so a caller
@@ -224,8 +225,8 @@ dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, int32_t dtype
                                    const float* row_max, const float* row_lnz, const uint8_t* sc_on,
                                    const int32_t* canvas, int32_t B, int32_t C, const void* E, const void* w_gate,
                                    const void* w_up, const void* w_down, const void* prepared, int32_t V, int32_t d,
-                                   int32_t hidden, void* x_out, float* s_out, void* ws, size_t ws_bytes,
-                                   void* pe_start, void* pe_stop, dg_stream_t stream);
+                                   int32_t hidden, void* x_out, float* s_out, float* y_out, void* ws,
+                                   size_t ws_bytes, void* pe_start, void* pe_stop, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * dg_allowed_probs -- structured-read readout (single-pass-reads page,

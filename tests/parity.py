@@ -90,13 +90,14 @@ def check_sampler_rows(got: dict, ref, rows, argmax_only=False):
     assert not bad, bad[:10]
 
 
-def check_bf16_output(got: np.ndarray, exact: np.ndarray, pre_rel: float = TOL_NORM_REL):
+def check_bf16_output(got: np.ndarray, exact: np.ndarray, pre_rel: float = 3 * TOL_NORM_REL):
     """A bf16 output against the oracle's unrounded fp64 value.
 
     A stored bf16 value cannot be closer than half a bf16 step (2^(e-7) in [2^e, 2^(e+1)));
     the check is that every element lies within one step of the exact value, widened by
-    `pre_rel` times the row's rms for cancellation near zero, and that the row's normwise
-    error stays within bf16's unit roundoff 2^-8.
+    `pre_rel` times the row's rms (the fp16/fp32 path's own error before the final rounding,
+    whose normwise size is checked separately at 1e-3 on the fp32 outputs), and that the
+    row's normwise error stays within bf16's unit roundoff 2^-8.
     """
     got = np.asarray(got, np.float64)
     exact = np.asarray(exact, np.float64)

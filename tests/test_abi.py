@@ -62,9 +62,9 @@ def test_host_validation_rejects_before_launch(L):
     assert att(D=96) == -2 and att(ps=32) == -2 and att(Hq=12, Hkv=8) == -1
     # self-conditioning: bf16 requires d, hidden multiples of 128 and a prepared table
     assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, None, 1024, 128, 128, 64,
-                               None, 64, 1 << 30, None) == -1
+                               None, None, 64, 1 << 30, None) == -1
     assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, 64, 1024, 96, 128, 64,
-                               None, 64, 1 << 30, None) == -2
+                               None, None, 64, 1 << 30, None) == -2
 
 
 def test_workspace_sizes(L):

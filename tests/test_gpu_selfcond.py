@@ -41,8 +41,9 @@ def test_selfcond_bf16_small(V, d, hidden, w_std):
     st = _sampler_stats(lt, V, C)
     prepared = dg.dg_selfcond_prepare(Et, wgt, wut, wdt)
     s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    y_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
     x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(sc_on), P.dev(canvas), Et, wgt, wut, wdt,
-                             prepared, s_out=s_out)
+                             prepared, s_out=s_out, y_out=y_out)
     torch.cuda.synchronize()
     host_l = synth.bf16_bits_to_f32(bits).astype(np.float64)[:, :V]
     ref = osamp.denoise_sample(host_l, 1.0, np.arange(B), np.zeros(B), C)
@@ -50,7 +51,10 @@ def test_selfcond_bf16_small(V, d, hidden, w_std):
     f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)
     rx, rs, ry = osc.selfcond_embed(Pm, canvas, sc_on, f(E), f(wg), f(wu), f(wd), C, to_bf16=False)
     es = P.rel_norm_err(s_out.cpu().numpy(), rs)
+    ey = P.rel_norm_err(y_out.cpu().numpy(), ry)
+    print(f"P.E max normwise rel err {es.max():.2e}, MLP {ey.max():.2e}")
     assert es.max() <= P.TOL_NORM_REL, es.max()
+    assert ey.max() <= P.TOL_NORM_REL, ey.max()
     gx = P.host_f64(x)
     P.check_bf16_output(gx, rx)
     on = np.repeat(sc_on.astype(bool), C)
@@ -95,8 +99,9 @@ def test_selfcond_single_canvas_full_size_sampled_rows():
     st = _sampler_stats(lt, V, C)
     prepared = dg.dg_selfcond_prepare(E, wg, wu, wd)
     s_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
+    y_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
     x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(np.array([1], np.uint8)), P.dev(canvas), E,
-                             wg, wu, wd, prepared, s_out=s_out)
+                             wg, wu, wd, prepared, s_out=s_out, y_out=y_out)
     torch.cuda.synchronize()
     rows = [0, 77, 128, 255]
     host_l = lt[rows].float().cpu().numpy().astype(np.float64)
@@ -109,5 +114,8 @@ def test_selfcond_single_canvas_full_size_sampled_rows():
     assert es.max() <= P.TOL_NORM_REL, es
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     y_ref = osc.gated_mlp(s_ref, f(wg), f(wu), f(wd))
+    ey = P.rel_norm_err(y_out.cpu().numpy()[rows], y_ref)
+    print(f"full size: P.E max normwise rel err {es.max():.2e}, MLP {ey.max():.2e}")
+    assert ey.max() <= P.TOL_NORM_REL, ey
     x_ref = Eh[canvas[0, rows]].astype(np.float64) + y_ref
     P.check_bf16_output(P.host_f64(x)[rows], x_ref)
