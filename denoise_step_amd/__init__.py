@@ -36,7 +36,7 @@ _SIGS = {
     "dg_version": (_i32, []),
     "dg_status_str": (ctypes.c_char_p, [_i32]),
     "dg_philox4x32_10": (_i32, [_p, _p, _i64, _p, _p]),
-    "dg_canvas_attention_ws_bytes": (_sz, [_i32] * 6 + [_i32]),
+    "dg_canvas_attention_ws_bytes": (_sz, [_i32] * 8),
     "dg_canvas_attention": (_i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _i32, _f32, _i32, _p, _p, _sz, _p]),
     "dg_denoise_sample_ws_bytes": (_sz, [_i32, _i32]),
@@ -138,8 +138,8 @@ def dg_philox4x32_10(ctr: torch.Tensor, key: torch.Tensor, out: torch.Tensor | N
     return out
 
 
-def dg_canvas_attention_ws_bytes(n_req, max_rows, max_keys, Hq, Hkv, D, dtype) -> int:
-    return int(lib().dg_canvas_attention_ws_bytes(n_req, max_rows, max_keys, Hq, Hkv, D, dtype))
+def dg_canvas_attention_ws_bytes(n_req, rows, max_rows, max_keys, Hq, Hkv, D, dtype) -> int:
+    return int(lib().dg_canvas_attention_ws_bytes(n_req, rows, max_rows, max_keys, Hq, Hkv, D, dtype))
 
 
 def dg_canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, max_rows_per_req, max_keys_per_req,
@@ -151,7 +151,7 @@ def dg_canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, max_rows_
     n_req = splits.shape[0]
     dt = _dtype_code(q)
     out = torch.empty_like(q) if out is None else out
-    nb = dg_canvas_attention_ws_bytes(n_req, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dt)
+    nb = dg_canvas_attention_ws_bytes(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dt)
     ws = _ws(nb, ws, q.device)
     _check(lib().dg_canvas_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), n_pages,
                                      _ptr(page_table), page_table.numel(), _ptr(splits), n_req, rows,

@@ -12,8 +12,11 @@
 // request's pages at positions cached + j; (2) the attention kernel reads
 // every prefix and causal key from the pages and the canvas keys from the
 // k/v inputs.
+#include "attention_mfma.hpp"
 #include "dg_device.hpp"
 #include "dg_host.hpp"
+
+#include <algorithm>
 
 namespace dg {
 namespace {
@@ -159,15 +162,45 @@ void launch_attend_wave(const void* q, const void* k, const void* v, const void*
                                                      scale, out);
 }
 
+struct AttPlan {
+  bool mfma;
+  int32_t qtiles, nsplit, split_keys;
+  size_t off_ml, bytes;
+};
+
+AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t max_keys, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t dtype) {
+  AttPlan p{};
+  p.mfma = dtype == DG_BF16 && (D == 128 || D == 256);
+  if (!p.mfma) return p;
+  const int32_t G = Hq / Hkv;
+  p.qtiles = static_cast<int32_t>(cdiv(static_cast<int64_t>(max_rows) * G, kAttRows));
+  const int32_t nblocks = static_cast<int32_t>(cdiv(max_keys, kAttKeys));
+  const int64_t base = static_cast<int64_t>(n_req) * Hkv * p.qtiles;
+  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(512, base), std::max(1, nblocks / 4)));
+  nsplit = std::max(1, std::min(nsplit, 65535 / Hkv));
+  p.split_keys = static_cast<int32_t>(cdiv(nblocks, nsplit)) * kAttKeys;
+  p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));
+  if (p.nsplit > 1) {
+    const size_t n = static_cast<size_t>(p.nsplit) * rows * Hq;
+    p.off_ml = round_up(n * D * sizeof(float), 256);
+    p.bytes = round_up(p.off_ml + n * sizeof(float2), 256);
+  }
+  return p;
+}
+
 }  // namespace
 }  // namespace dg
 
 using namespace dg;
 
-extern "C" size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t max_rows_per_req, int32_t max_keys_per_req,
-                                               int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype) {
-  (void)n_req; (void)max_rows_per_req; (void)max_keys_per_req; (void)Hq; (void)Hkv; (void)D; (void)dtype;
-  return 0;
+extern "C" size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t rows, int32_t max_rows_per_req,
+                                               int32_t max_keys_per_req, int32_t Hq, int32_t Hkv, int32_t D,
+                                               int32_t dtype) {
+  if (n_req <= 0 || rows <= 0 || max_rows_per_req <= 0 || max_keys_per_req <= 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0)
+    return 0;
+  return plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype).bytes;
 }
 
 extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
@@ -183,8 +216,8 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
   DG_UNSUP(page_size == 16);
   DG_UNSUP(D == 32 || D == 64 || D == 128 || D == 256);
-  const size_t need = dg_canvas_attention_ws_bytes(n_req, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
-  DG_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), DG_E_WORKSPACE);
+  const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
+  DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
   const bool bf = dtype == DG_BF16;
   {
@@ -196,6 +229,46 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
       append_kv_kernel<false><<<grid, 256, 0, s>>>(k, v, k_cache, v_cache, n_pages, page_table, page_table_len,
                                                    splits, rows, Hkv, D, page_size);
     DG_LAUNCHED();
+  }
+  if (plan.mfma) {
+    AttArgs a{};
+    a.q = reinterpret_cast<const uint16_t*>(q);
+    a.k = reinterpret_cast<const uint16_t*>(k);
+    a.v = reinterpret_cast<const uint16_t*>(v);
+    a.k_cache = reinterpret_cast<const uint16_t*>(k_cache);
+    a.v_cache = reinterpret_cast<const uint16_t*>(v_cache);
+    a.n_pages = n_pages;
+    a.page_table = page_table;
+    a.page_table_len = page_table_len;
+    a.splits = splits;
+    a.rows = rows;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.page_size = page_size;
+    a.scale_log2 = scale * kLog2e;
+    a.nsplit = plan.nsplit;
+    a.split_keys = plan.split_keys;
+    a.out = reinterpret_cast<uint16_t*>(out);
+    a.o_part = reinterpret_cast<float*>(ws);
+    a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
+    const dim3 grid(plan.qtiles, Hkv * plan.nsplit, n_req);
+    if (D == 256)
+      attend_mfma_kernel<256><<<grid, kAttThreads, 0, s>>>(a);
+    else
+      attend_mfma_kernel<128><<<grid, kAttThreads, 0, s>>>(a);
+    DG_LAUNCHED();
+    if (plan.nsplit > 1) {
+      const unsigned nrh = static_cast<unsigned>(static_cast<int64_t>(rows) * Hq);
+      if (D == 256)
+        attend_merge_kernel<256><<<nrh, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                     a.out);
+      else
+        attend_merge_kernel<128><<<nrh, 128, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                     a.out);
+      DG_LAUNCHED();
+    }
+    return DG_OK;
   }
 #define DG_ATT(BF, DD)                                                                                        \
   launch_attend_wave<BF, DD>(q, k, v, k_cache, v_cache, n_pages, page_table, page_table_len, splits, n_req, rows, \

@@ -113,8 +113,8 @@ typedef struct dg_split {
   int32_t window;    /* must be 0 (symmetric sliding windows are not implemented)     */
 } dg_split;
 
-size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t max_rows_per_req, int32_t max_keys_per_req,
-                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype);
+size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t rows, int32_t max_rows_per_req,
+                                    int32_t max_keys_per_req, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype);
 dg_status dg_canvas_attention(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
                               int32_t n_pages, const int32_t* page_table, int32_t page_table_len,
                               const dg_split* splits, int32_t n_req, int32_t rows,
