@@ -1,125 +1,210 @@
 // Split-K fp16 MFMA GEMM for gfx950 with fp32 partial outputs:
 //   part[split][m][n] = sum_{k in split} A[m][k] * Bt[n][k]
-// A [M][lda] and Bt [N][ldb] are fp16 row-major with K contiguous (Bt is the
-// transposed right operand, prepared once for the constant tables).
+// Both operands are fp16 in the K-blocked layout of kblk_index(): element
+// (row, k) of an R-row operand lives at ((k / 32) R + row) 32 + k % 32, so the
+// 32-wide K slice of any run of rows is one contiguous block of memory.  Bt is
+// the transposed right operand (prepared once for the constant tables); A is
+// written in this layout by the kernel that produces it.
 //
-// Workgroup tile 128 x 128, four wave64s in a 2 x 2 arrangement, each wave
-// computing 64 x 64 with four v_mfma_f32_32x32x16_f16 accumulators.  K is
-// staged through LDS 32 at a time, double buffered: the next stage's global
-// loads (16 bytes per lane, consecutive lanes on consecutive addresses) are
-// issued before the current stage's MFMAs.  Rows are padded by 8 halves in
-// LDS so the 16-byte operand reads of the 32 lanes of a half-wave fall in
-// different banks.
+// Shaped for the self-conditioning contraction P.E, where M (canvas rows) is
+// small, K (the vocabulary) is huge and the right operand E must stream from
+// HBM exactly once:
+//   * workgroup tile 256 x 256 (256 x 128 when N is not a multiple of 256)
+//     with eight wave64s (2 x 4, two per SIMD so one wave's LDS and barrier
+//     waits overlap the other's MFMAs), each wave 128 x 64 as 4 x 2
+//     v_mfma_f32_32x32x16_f16 accumulators; a canvas of 256 rows is one M
+//     tile, so every E element is fetched by exactly one workgroup;
+//   * K advances 32 per stage through four LDS stages filled by direct
+//     global -> LDS copies (no staging registers) issued three stages ahead,
+//     about 96 KB per CU in flight against HBM latency;
+//   * an XOR swizzle of the 16-byte chunks keeps the MFMA operand reads free
+//     of LDS bank conflicts;
+//   * XCD-aware order: hardware deals workgroup L to XCD L % 8; tiles are
+//     numbered so the workgroups on one XCD share their A chunk (the same
+//     probability rows) or their B chunk, which then comes from that XCD's L2.
 #pragma once
 #include "dg_device.hpp"
 
 namespace dg {
 
-constexpr int kGemmTM = 128;
-constexpr int kGemmTN = 128;
-constexpr int kGemmTK = 32;
-constexpr int kGemmThreads = 256;
-constexpr int kGemmLdsRow = kGemmTK + 8;  // halves per LDS row
+constexpr int kGemmTM = 256;
+constexpr int kGemmTK = 32;          // K per LDS stage
+constexpr int kGemmStages = 4;       // LDS stages (loads run kGemmStages - 1 ahead)
+constexpr int kGemmThreads = 512;      // eight wave64s: 2 (M) x 4 (N)
+constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kGemmXcds = 8;
+
+// index of element (row, k) of an operand with R rows in the K-blocked layout
+DG_DEV int64_t kblk_index(int64_t row, int64_t k, int64_t R) { return ((k >> 5) * R + row) * 32 + (k & 31); }
 
 struct GemmArgs {
   const _Float16* A;
-  int64_t lda;
+  int64_t lda;        // rows of the A operand's blocked layout (M rounded up to 256)
   const _Float16* Bt;
-  int64_t ldb;
+  int64_t ldb;        // rows of Bt (N)
   float* part;  // [splits][M][N]
   int32_t M, N, K;
-  int32_t kchunk;  // K per split (multiple of kGemmTK)
+  int32_t kchunk;  // K per split (multiple of kGemmStages * kGemmTK)
+  int32_t mtiles, ntiles, splits;
 };
 
-// One 16-byte global chunk per (row, 8-half column group): a 128 x 32 tile is 512 chunks,
-// two per lane.  Rows beyond M are clamped (their results are never stored).
-DG_DEV void gemm_load_tile(const _Float16* __restrict__ src, int64_t ld, int32_t row0, int32_t nrows, int32_t k0,
-                           uint4 (&r)[2]) {
+// LDS layout of one stage: rows of 32 halves = four 16-byte chunks, chunk c of row r stored at
+// slot 4 r + (c ^ f(r)), f(r) = ((r >> 1) & 7) + ((r >> 3) & 1) (mod 4).  A 16-byte LDS read serves
+// the lanes in groups that ask for one chunk of 8 or 16 consecutive rows; f is a bijection on every
+// set of rows that would share a bank in either grouping (same parity within 8 rows, same residue
+// mod 4 within 16 rows), so the reads are conflict-free.  f depends on r mod 16 only, which the
+// copy below relies on.
+DG_DEV int gemm_swz(int row) { return (((row >> 1) & 7) + ((row >> 3) & 1)) & 3; }
+DG_DEV int gemm_slot(int row, int c) { return row * 4 + (c ^ gemm_swz(row)); }
+
+// Direct global -> LDS copy: one instruction fills 64 consecutive slots (1 KB) starting at `lds`;
+// lane i writes slot i.  For instruction q, slot 64 q + i holds row 16 q + i / 4 and, by the
+// swizzle, chunk (i & 3) ^ f(i / 4) -- independent of q (f only sees the row mod 16).  In the
+// K-blocked layout rows 16 q .. 16 q + 15 of one K slice are 1 KB of contiguous memory, so each
+// lane keeps one byte offset inside that kilobyte and the instruction adds a wave-uniform base.
+DG_DEV uint32_t gemm_lane_offset() {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = (lane & 3) ^ gemm_swz(lane >> 2);
+  return static_cast<uint32_t>(((lane >> 2) * 32 + 8 * c) * 2);
+}
+
+// The copy is issued from inline asm (M0 = LDS destination, scalar base + per-lane 32-bit offset) so
+// that its completion is tracked only by the explicit vmcnt waits of the pipeline below; the main
+// loop issues no other vector-memory instruction, so those counts are exact.
+DG_DEV void gemm_dma(const _Float16* __restrict__ base, int64_t rows, int row0, int k0, uint32_t lane_off,
+                     _Float16* lds, int q) {
+  const char* ub = reinterpret_cast<const char*>(base) + kblk_index(row0 + 16 * q, k0, rows) * 2;
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + q * kWave * 8));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(lane_off), "s"(ub)
+      : "memory", "m0");
+}
+
+// Issue one stage: A (256 rows) and B (TN rows) as 1-KB instructions shared round-robin by the waves.
+// A has mtiles * 256 rows in its layout (rows past M are read but never stored); Bt has N rows.
+template <int TN>
+DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, int wave, _Float16* as,
+                       _Float16* bs) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
-    const int row = c >> 2, col = (c & 3) * 8;
-    const int64_t gr = min(row0 + row, nrows - 1);
-    r[i] = *reinterpret_cast<const uint4*>(src + gr * ld + k0 + col);
+  for (int i = 0; i < kGemmTM / 16 / kGemmWaves; ++i) gemm_dma(g.A, g.lda, m0, k0, off, as, wave + kGemmWaves * i);
+#pragma unroll
+  for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
+}
+
+// Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.
+template <int TN>
+DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __restrict__ bs, int wm, int wn, int lane,
+                         floatx16 (&acc)[4][TN / 128]) {
+  constexpr int NJ = TN / 128;
+#pragma unroll
+  for (int kk = 0; kk < kGemmTK / 8; kk += 2) {  // chunk pair (kk, kk + 1) = 16 K
+    const int c = kk + (lane >> 5);
+    half8 a[4], b[NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      b[j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(wn + j * 32 + (lane & 31), c));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
 }
 
-DG_DEV void gemm_store_tile(_Float16* __restrict__ lds, const uint4 (&r)[2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
-    const int row = c >> 2, col = (c & 3) * 8;
-    *reinterpret_cast<uint4*>(lds + row * kGemmLdsRow + col) = r[i];
-  }
+// vector-memory instructions a wave issues per stage
+template <int TN>
+constexpr int gemm_dma_per_stage() {
+  return (kGemmTM + TN) / 16 / kGemmWaves;
+}
+
+// s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `pending` later stages of this wave's copies are still in flight, then
+// barrier.  A bare s_barrier is used instead of __syncthreads(): the latter's release fence would
+// wait for every outstanding copy, including the prefetched stages.  The empty asm statements keep
+// the compiler from moving LDS accesses across the wait and the barrier.
+template <int TN>
+DG_DEV void gemm_wait_barrier(int pending) {
+  constexpr int n = gemm_dma_per_stage<TN>();
+  asm volatile("" ::: "memory");
+  if (pending >= 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * n));
+  else if (pending == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(n));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ROLE only names the instantiation (0: P.E contraction, 1: MLP GEMMs) so that profilers report the
-// dominant P.E launch under its own symbol.
-template <int ROLE>
+// dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
+// of 256).
+template <int ROLE, int TN>
 __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kGemmTM * kGemmLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kGemmTN * kGemmLdsRow];
-  const int n0 = blockIdx.x * kGemmTN;
-  const int m0 = blockIdx.y * kGemmTM;
-  const int split = blockIdx.z;
+  constexpr int NJ = TN / 128;
+  __shared__ __attribute__((aligned(16))) _Float16 As0[kGemmTM * kGemmTK], As1[kGemmTM * kGemmTK],
+      As2[kGemmTM * kGemmTK], As3[kGemmTM * kGemmTK];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs0[TN * kGemmTK], Bs1[TN * kGemmTK], Bs2[TN * kGemmTK],
+      Bs3[TN * kGemmTK];
+  // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
+  const int total = g.mtiles * g.ntiles * g.splits;
+  const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
+  const int t = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
+  if (t >= total) return;
+  const int mt = t % g.mtiles;
+  const int nt = (t / g.mtiles) % g.ntiles;
+  const int split = t / (g.mtiles * g.ntiles);
+  const int m0 = mt * kGemmTM, n0 = nt * TN;
   const int k_begin = split * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
+  const int nstage = (k_end - k_begin) / kGemmTK;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
+  const uint32_t off = gemm_lane_offset();
 
-  floatx16 acc[2][2];
+  floatx16 acc[4][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[2], rb[2];
-  int buf = 0;
-  if (k_begin < k_end) {
-    gemm_load_tile(g.A, g.lda, m0, g.M, k_begin, ra);
-    gemm_load_tile(g.Bt, g.ldb, n0, g.N, k_begin, rb);
-    gemm_store_tile(As[0], ra);
-    gemm_store_tile(Bs[0], rb);
+  if (nstage > 0) gemm_issue<TN>(g, m0, n0, k_begin, off, wave, As0, Bs0);
+  if (nstage > 1) gemm_issue<TN>(g, m0, n0, k_begin + kGemmTK, off, wave, As1, Bs1);
+  if (nstage > 2) gemm_issue<TN>(g, m0, n0, k_begin + 2 * kGemmTK, off, wave, As2, Bs2);
+  // iteration s: wait for stage s, barrier (stage s visible; every wave is past compute(s - 1), so
+  // that stage's buffer may be refilled), issue stage s + 3, compute stage s
+#define DG_GEMM_STEP(S_OFF, AC, BC, AN, BN)                                                   \
+  {                                                                                           \
+    const int s_ = s + (S_OFF);                                                               \
+    gemm_wait_barrier<TN>(min(2, nstage - 1 - s_));                                           \
+    if (s_ + 3 < nstage)                                                                      \
+      gemm_issue<TN>(g, m0, n0, k_begin + (s_ + 3) * kGemmTK, off, wave, AN, BN);             \
+    gemm_compute<TN>(AC, BC, wm, wn, lane, acc);                                              \
   }
-  __syncthreads();
-  for (int k0 = k_begin; k0 < k_end; k0 += kGemmTK) {
-    const bool more = k0 + kGemmTK < k_end;
-    if (more) {
-      gemm_load_tile(g.A, g.lda, m0, g.M, k0 + kGemmTK, ra);
-      gemm_load_tile(g.Bt, g.ldb, n0, g.N, k0 + kGemmTK, rb);
-    }
-    const _Float16* as = As[buf];
-    const _Float16* bs = Bs[buf];
-#pragma unroll
-    for (int kk = 0; kk < kGemmTK; kk += 16) {
-      half8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const half8*>(as + (wm + i * 32 + (lane & 31)) * kGemmLdsRow + kk + 8 * (lane >> 5));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const half8*>(bs + (wn + j * 32 + (lane & 31)) * kGemmLdsRow + kk + 8 * (lane >> 5));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      gemm_store_tile(As[buf ^ 1], ra);
-      gemm_store_tile(Bs[buf ^ 1], rb);
-    }
-    __syncthreads();
-    buf ^= 1;
+  for (int s = 0; s < nstage; s += 4) {
+    DG_GEMM_STEP(0, As0, Bs0, As3, Bs3)
+    DG_GEMM_STEP(1, As1, Bs1, As0, Bs0)
+    DG_GEMM_STEP(2, As2, Bs2, As1, Bs1)
+    DG_GEMM_STEP(3, As3, Bs3, As2, Bs2)
   }
+#undef DG_GEMM_STEP
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -129,20 +214,32 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
 }
 
 struct GemmPlan {
-  int32_t splits, kchunk;
+  int32_t splits, kchunk, mtiles, ntiles, tn;
   dim3 grid;
 };
 
-// N % 128 == 0 and K % 32 == 0 are required; M may be ragged.
-inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 512) {
-  const int32_t tiles = static_cast<int32_t>(((M + kGemmTM - 1) / kGemmTM) * (N / kGemmTN));
+// N % 128 == 0 and K % 128 == 0 are required (every split runs a whole number of 4-stage rounds);
+// M may be ragged.  The N tile is 256 when N allows it.
+// About one workgroup per CU (each holds up to ~144 KB of LDS); splits are added only to reach that.
+inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 256) {
+  const int32_t tn = (N % 256 == 0) ? 256 : 128;
+  const int32_t mtiles = (M + kGemmTM - 1) / kGemmTM, ntiles = N / tn;
+  const int32_t tiles = mtiles * ntiles;
   int32_t splits = (target_wgs + tiles - 1) / tiles;
   const int32_t max_splits = (K + 1023) / 1024;
   splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
   int32_t kchunk = (K + splits - 1) / splits;
-  kchunk = (kchunk + kGemmTK - 1) / kGemmTK * kGemmTK;
+  constexpr int32_t round = kGemmStages * kGemmTK;
+  kchunk = (kchunk + round - 1) / round * round;
   splits = (K + kchunk - 1) / kchunk;
-  return {splits, kchunk, dim3(N / kGemmTN, (M + kGemmTM - 1) / kGemmTM, splits)};
+  const int32_t total = tiles * splits;
+  const int32_t launched = (total + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
+  return {splits, kchunk, mtiles, ntiles, tn, dim3(launched)};
+}
+
+inline GemmArgs gemm_args(const _Float16* A, int64_t lda, const _Float16* Bt, int64_t ldb, float* part, int32_t M,
+                          int32_t N, int32_t K, const GemmPlan& p) {
+  return GemmArgs{A, lda, Bt, ldb, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
 }
 
 }  // namespace dg

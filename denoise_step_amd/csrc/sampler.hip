@@ -16,11 +16,12 @@
 // merge is associative, with lowest-index tie-breaks at every level).
 //
 // The Gumbel noise of element i is word i & 3 of Philox4x32-10 at counter
-// (i >> 2, pos, step, 0): one Philox call per 4 logits.  The exact key
-// x + g needs two accurate logs; they are evaluated only for elements that
-// could still beat the lane's running best key, using the bound
-// g = -ln(-ln(1 - v)) < -ln(v) <= (24 - floor(log2(2b + 1))) ln 2 with
-// v = (2b + 1) 2^-24, b = (~w) >> 9 (integer ops only).  The pruning is exact.
+// (i >> 2, pos, step, 0): one Philox call per 4 logits.  Everything runs in
+// base 2 (x2 = x log2 e): the softmax sums use the hardware exp2, and the
+// Gumbel key is compared as x2 - log2(-log2 u), which orders elements exactly
+// as x + g does; two hardware log2 per element, no branches.  The sampler is
+// bound by this ALU work (Philox plus two transcendentals per logit), not by
+// the logit bytes.
 #include "dg_device.hpp"
 #include "dg_host.hpp"
 
@@ -39,9 +40,12 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 32, "partial layout");
 
+// Online softmax state in base 2: m = max x2, Z = sum 2^(x2 - m), S = sum 2^(x2 - m) (x2 - m).
 struct SoftState {
   float m, Z, S;
 };
+
+DG_DEV float exp2f_fast(float d) { return __builtin_amdgcn_exp2f(d); }
 
 // merge b into a (both relative to their own max); Z == 0 marks an empty state
 DG_DEV void soft_merge(SoftState& a, SoftState b) {
@@ -52,7 +56,7 @@ DG_DEV void soft_merge(SoftState& a, SoftState b) {
   }
   const float m = fmaxf(a.m, b.m);
   const float da = a.m - m, db = b.m - m;
-  const float fa = __expf(da), fb = __expf(db);
+  const float fa = exp2f_fast(da), fb = exp2f_fast(db);
   a.S = fa * (a.S + da * a.Z) + fb * (b.S + db * b.Z);
   a.Z = fa * a.Z + fb * b.Z;
   a.m = m;
@@ -66,25 +70,15 @@ DG_DEV void wave_soft_merge(SoftState& s) {
   }
 }
 
-// exact Gumbel value from a Philox word: g = -ln(-ln u), u = (2a + 1) 2^-24, a = w >> 9
-DG_DEV float gumbel_exact(uint32_t w) {
-  const uint32_t a = w >> 9;
-  float t;
-  if (a >= (1u << 22)) {  // u > 1/2: -ln(u) = -log1p(-v), v = 1 - u exact
-    const float v = fmaf(static_cast<float>((~w) >> 9), 0x1.0p-23f, 0x1.0p-24f);
-    t = -log1pf(-v);
-  } else {
-    const float u = fmaf(static_cast<float>(a), 0x1.0p-23f, 0x1.0p-24f);
-    t = -logf(u);
-  }
-  return -logf(t);
-}
-
-// upper bound of gumbel_exact(w) from integer ops (plus a margin above fp32 rounding)
-DG_DEV float gumbel_bound(uint32_t w) {
-  const uint32_t odd = (((~w) >> 9) << 1) | 1u;
-  const int e = 31 - __clz(odd);
-  return static_cast<float>(24 - e) * 0.69314718f + 1e-4f;
+// Gumbel-max key in log2 units.  With u = (2a + 1) 2^-24 (a = w >> 9, exact in fp32),
+// g = -ln(-ln u) and x2 = x log2(e):
+//   (x + g) log2(e) = x2 - log2(-log2 u) - log2(ln 2),
+// so argmax_i (x_i + g_i) = argmax_i (x2_i - log2(-log2 u_i)) (a positive rescale and a shift).
+// Both logs are the hardware base-2 logarithm on normal inputs (u >= 2^-24, -log2 u >= 2^-24 / ln 2).
+DG_DEV float gumbel_key2(float x2, uint32_t w) {
+  const float u = fmaf(static_cast<float>(w >> 9), 0x1.0p-23f, 0x1.0p-24f);
+  const float L = -__builtin_amdgcn_logf(u);
+  return x2 - __builtin_amdgcn_logf(L);
 }
 
 template <bool BF16>
@@ -106,8 +100,8 @@ DG_DEV void load8(const void* row, int64_t idx, float (&l)[kGroup]) {
 template <bool BF16, bool ARGMAX_ONLY>
 __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
     const void* __restrict__ logits, int64_t ld, int32_t V, int32_t rows_per_req, const uint64_t* __restrict__ seed,
-    const int32_t* __restrict__ step, const uint8_t* __restrict__ active, float inv_t, int32_t chunk, int32_t nsplit,
-    Partial* __restrict__ part) {
+    const int32_t* __restrict__ step, const uint8_t* __restrict__ active, float inv_t2, int32_t chunk,
+    int32_t nsplit, Partial* __restrict__ part) {
   const int r = blockIdx.y;
   const int split = blockIdx.x;
   const int req = r / rows_per_req;
@@ -148,28 +142,39 @@ __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
       }
     }
     if constexpr (!ARGMAX_ONLY) {
+      // x2 = l * log2(e) / T: softmax statistics and keys in base 2 (S is rescaled by ln 2 at the end)
       float x[kGroup];
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
-        x[j] = l[j] * inv_t;
+        x[j] = l[j] * inv_t2;
         mx = fmaxf(mx, x[j]);
       }
       if (mx > ss.m) {
         if (ss.Z != 0.f) {
           const float d = ss.m - mx;
-          const float f = __expf(d);
+          const float f = exp2f_fast(d);
           ss.S = f * (ss.S + d * ss.Z);
           ss.Z *= f;
         }
         ss.m = mx;
       }
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const float d = x[j] - ss.m;
-        const float e = __expf(d);  // d = -inf -> 0
-        ss.Z += e;
-        ss.S = (e != 0.f) ? fmaf(e, d, ss.S) : ss.S;
+        for (int j = 0; j < kGroup; ++j) {
+          const float d = x[j] - ss.m;
+          const float e = exp2f_fast(d);
+          ss.Z += e;
+          ss.S = fmaf(e, d, ss.S);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const float d = x[j] - ss.m;
+          const float e = exp2f_fast(d);  // d = -inf -> 0
+          ss.Z += e;
+          ss.S = (e != 0.f) ? fmaf(e, d, ss.S) : ss.S;
+        }
       }
       // Gumbel candidates: two Philox calls cover the 8 logits (base is a multiple of 8)
       const uint32_t c = static_cast<uint32_t>(base >> 2);
@@ -178,12 +183,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
       const uint32_t w[kGroup] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
-        if (x[j] + gumbel_bound(w[j]) > kv) {
-          const float key = x[j] + gumbel_exact(w[j]);
-          if (key > kv) {
-            kv = key;
-            ki = static_cast<int32_t>(base + j);
-          }
+        const float key = gumbel_key2(x[j], w[j]);
+        if (key > kv) {
+          kv = key;
+          ki = static_cast<int32_t>(base + j);
         }
       }
     }
@@ -245,10 +248,12 @@ __global__ __launch_bounds__(kWave) void sample_merge_kernel(const Partial* __re
   if (threadIdx.x == 0) {
     argmax[r] = ai;
     if constexpr (!ARGMAX_ONLY) {
+      // back to natural units: x = x2 ln 2, ln Z = log2(Z) ln 2, S_nat = S ln 2
+      constexpr float kLn2 = 0.69314718055994531f;
       const float lnz = logf(ss.Z);
-      entropy[r] = fmaxf(0.f, lnz - ss.S / ss.Z);
+      entropy[r] = fmaxf(0.f, lnz - kLn2 * ss.S / ss.Z);
       sample[r] = ki;
-      row_max[r] = ss.m;
+      row_max[r] = ss.m * kLn2;
       row_lnz[r] = lnz;
     }
   }
@@ -300,7 +305,7 @@ extern "C" dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t d
   hipStream_t s = as_stream(stream);
   Partial* part = reinterpret_cast<Partial*>(ws);
   const dim3 grid(p.nsplit, rows);
-  const float inv_t = 1.0f / temperature;
+  const float inv_t = 1.4426950408889634f / temperature;  // log2(e) / T
   if (dtype == DG_BF16) {
     if (amax_only)
       sample_partial_kernel<true, true><<<grid, kSampleThreads, 0, s>>>(logits, ld, V, rows_per_req, seed, step,

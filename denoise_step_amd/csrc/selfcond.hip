@@ -8,7 +8,7 @@
 // and DiffusionSampler" (prepare_inputs embeds the canvas and applies it).
 //
 // bf16 path (gfx950):
-//   1. probs:   w[r][i] = fp16(exp(x_i - m_r) * 2^15), zero-padded to Kp = roundup(V, 64).
+//   1. probs:   w[r][i] = fp16(exp(x_i - m_r) * 2^15), zero-padded to Kp = roundup(V, 128).
 //               The 2^15 scale keeps every weight above exp(-20) in fp16's normal range
 //               (a plain fp16 or bf16 probability would lose 11+ bits on diffuse rows).
 //   2. P.E:     split-K fp16 MFMA GEMM against E^T (fp16, prepared once; bf16 values
@@ -31,13 +31,14 @@ namespace {
 
 constexpr float kProbScale = 32768.0f;  // 2^15
 
-int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
 
 // ---------------------------------------------------------------- prepare
-// dst[n][k] = fp16(src[k][n]) for k < K (rows of src), zero for K <= k < Kp.
+// dst = fp16(src^T) placed at rows row_off .. row_off + N - 1 of a K-blocked operand with R rows:
+// element (row_off + n, k) = src[k][n] for k < K (rows of src), zero for K <= k < Kp.
 __global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16_t* __restrict__ src, int32_t K,
-                                                                    int32_t N, int64_t Kp,
-                                                                    _Float16* __restrict__ dst) {
+                                                                    int32_t N, int64_t Kp, int32_t row_off,
+                                                                    int32_t R, _Float16* __restrict__ dst) {
   __shared__ float tile[64][65];
   const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -48,15 +49,16 @@ __global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int n = n0 + i, k = k0 + tx;
-    if (n < N && k < Kp) dst[static_cast<int64_t>(n) * Kp + k] = static_cast<_Float16>(tile[tx][i]);
+    if (n < N && k < Kp) dst[kblk_index(row_off + n, k, R)] = static_cast<_Float16>(tile[tx][i]);
   }
 }
 
 // ---------------------------------------------------------------- bf16 path kernels
+// w is written in the K-blocked layout with Mp rows (the GEMM's left operand).
 template <bool BF16>
 __global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__ logits, int64_t ld, int32_t V,
-                                                        int64_t Kp, float inv_t, const float* __restrict__ row_max,
-                                                        _Float16* __restrict__ w) {
+                                                        int64_t Kp, int64_t Mp, float inv_t,
+                                                        const float* __restrict__ row_max, _Float16* __restrict__ w) {
   const int r = blockIdx.y;
   const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
   if (i0 >= Kp) return;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__
   half8 o;
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(__expf(l[j] * inv_t - m) * kProbScale);
-  *reinterpret_cast<half8*>(w + r * Kp + i0) = o;
+  *reinterpret_cast<half8*>(w + kblk_index(r, i0, Mp)) = o;
 }
 
 // Power-of-two scale that brings a row's largest magnitude to (2^13, 2^14]: applied before a
@@ -105,7 +107,7 @@ DG_DEV float block_max_256(float v, float* red) {
 // One workgroup per row: s = sum_split part * 2^-15 / Z -> s32 (and s_out), then s16 = fp16(s * scale_r)
 // with scale_r a power of two; inv_scale[r] = 1 / scale_r.
 __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                        int32_t N, const float* __restrict__ row_lnz,
+                                                        int32_t N, int64_t Mp, const float* __restrict__ row_lnz,
                                                         float* __restrict__ s32, float* __restrict__ s_out,
                                                         _Float16* __restrict__ s16, float* __restrict__ inv_scale) {
   __shared__ float red[4];
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict_
     amax = fmaxf(amax, fabsf(v));
   }
   const float sc = row_pow2_scale(block_max_256(amax, red));
-  for (int n = threadIdx.x; n < N; n += 256) s16[base + n] = static_cast<_Float16>(s32[base + n] * sc);
+  for (int n = threadIdx.x; n < N; n += 256) s16[kblk_index(r, n, Mp)] = static_cast<_Float16>(s32[base + n] * sc);
   if (threadIdx.x == 0) inv_scale[r] = 1.f / sc;
 }
 
@@ -134,7 +136,7 @@ DG_DEV float gelu_tanh(float z) {
 // One workgroup per row: h = gelu_tanh(gate) * up from the partials of the [gate | up] GEMM (whose
 // input row was scaled by 1 / s_inv[r]), then h16 = fp16(h * scale_r), h_inv[r] = 1 / scale_r.
 __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                         int32_t H, const float* __restrict__ s_inv,
+                                                         int32_t H, int64_t Mp, const float* __restrict__ s_inv,
                                                          float* __restrict__ h32, _Float16* __restrict__ h16,
                                                          float* __restrict__ h_inv) {
   __shared__ float red[4];
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict
     amax = fmaxf(amax, fabsf(h));
   }
   const float sc = row_pow2_scale(block_max_256(amax, red));
-  for (int j = threadIdx.x; j < H; j += 256) h16[base + j] = static_cast<_Float16>(h32[base + j] * sc);
+  for (int j = threadIdx.x; j < H; j += 256) h16[kblk_index(r, j, Mp)] = static_cast<_Float16>(h32[base + j] * sc);
   if (threadIdx.x == 0) h_inv[r] = 1.f / sc;
 }
 
@@ -220,7 +222,7 @@ struct PreparedLayout {
 
 PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
   PreparedLayout p{};
-  p.Kp = pad64(V);
+  p.Kp = pad128(V);
   p.off_et = 0;
   p.off_wgu = round_up(p.off_et + static_cast<size_t>(d) * p.Kp * 2, 256);
   p.off_wd = round_up(p.off_wgu + static_cast<size_t>(2) * hidden * d * 2, 256);
@@ -229,14 +231,17 @@ PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
 }
 
 struct Bf16Plan {
-  int64_t Kp;
+  int64_t Kp, Mp;
   GemmPlan pe, g1, g2;
   size_t off_w, off_part, off_s16, off_h16, off_s32, off_h32, off_sinv, off_hinv, bytes;
 };
 
 Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   Bf16Plan p{};
-  p.Kp = pad64(V);
+  // GEMM left operands are allocated with whole 256-row tiles (the tail rows are read, never stored)
+  const int64_t rows_p = (static_cast<int64_t>(rows) + kGemmTM - 1) / kGemmTM * kGemmTM;
+  p.Mp = rows_p;
+  p.Kp = pad128(V);
   p.pe = plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
   p.g1 = plan_gemm(rows, 2 * hidden, d);
   p.g2 = plan_gemm(rows, d, hidden);
@@ -245,10 +250,10 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   part = std::max(part, static_cast<size_t>(p.g1.splits) * rows * 2 * hidden * 4);
   part = std::max(part, static_cast<size_t>(p.g2.splits) * rows * d * 4);
   p.off_w = 0;
-  p.off_part = round_up(p.off_w + static_cast<size_t>(rows) * p.Kp * 2, 256);
+  p.off_part = round_up(p.off_w + static_cast<size_t>(rows_p) * p.Kp * 2, 256);
   p.off_s16 = round_up(p.off_part + part, 256);
-  p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows) * d * 2, 256);
-  p.off_s32 = round_up(p.off_h16 + static_cast<size_t>(rows) * hidden * 2, 256);
+  p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows_p) * d * 2, 256);
+  p.off_s32 = round_up(p.off_h16 + static_cast<size_t>(rows_p) * hidden * 2, 256);
   p.off_h32 = round_up(p.off_s32 + static_cast<size_t>(rows) * d * 4, 256);
   p.off_sinv = round_up(p.off_h32 + static_cast<size_t>(rows) * hidden * 4, 256);
   p.off_hinv = round_up(p.off_sinv + static_cast<size_t>(rows) * 4, 256);
@@ -274,6 +279,14 @@ F32Plan f32_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
 
 unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
 
+template <int ROLE>
+void launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  if (p.tn == 256)
+    gemm_f16_splitk_kernel<ROLE, 256><<<p.grid, kGemmThreads, 0, s>>>(a);
+  else
+    gemm_f16_splitk_kernel<ROLE, 128><<<p.grid, kGemmThreads, 0, s>>>(a);
+}
+
 }  // namespace
 }  // namespace dg
 
@@ -291,7 +304,7 @@ extern "C" dg_status dg_selfcond_prepare(const void* E, const void* w_gate, cons
   DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
   if (dtype == DG_F32) return DG_OK;  // the fp32 path reads the tables as given
   DG_ARG(E && w_gate && w_up && w_down && prepared);
-  DG_UNSUP(d % kGemmTN == 0 && hidden % kGemmTN == 0);
+  DG_UNSUP(d % 128 == 0 && hidden % 128 == 0);
   const PreparedLayout L = prepared_layout(V, d, hidden);
   DG_REQUIRE(prepared_bytes >= L.bytes, DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
@@ -300,19 +313,20 @@ extern "C" dg_status dg_selfcond_prepare(const void* E, const void* w_gate, cons
   auto* wgu = reinterpret_cast<_Float16*>(base + L.off_wgu);
   auto* wd = reinterpret_cast<_Float16*>(base + L.off_wd);
   const auto* Eb = reinterpret_cast<const uint16_t*>(E);
-  // E [V][d] -> E^T [d][Kp]
+  // E [V][d] -> E^T (d rows, Kp columns)
   transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(L.Kp, 64)), static_cast<unsigned>(cdiv(d, 64))), 256,
-                                 0, s>>>(Eb, V, d, L.Kp, et);
+                                 0, s>>>(Eb, V, d, L.Kp, 0, d, et);
   DG_LAUNCHED();
-  // W_gate, W_up [d][hidden] -> rows [0, hidden) and [hidden, 2 hidden) of [2 hidden][d]
+  // W_gate, W_up [d][hidden] -> rows [0, hidden) and [hidden, 2 hidden) of one operand (2 hidden rows, d columns)
   transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
-                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_gate), d, hidden, d, wgu);
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_gate), d, hidden, d, 0, 2 * hidden,
+                                              wgu);
   transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
-                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_up), d, hidden, d,
-                                              wgu + static_cast<int64_t>(hidden) * d);
-  // W_down [hidden][d] -> [d][hidden]
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_up), d, hidden, d, hidden,
+                                              2 * hidden, wgu);
+  // W_down [hidden][d] -> d rows, hidden columns
   transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(hidden, 64)), static_cast<unsigned>(cdiv(d, 64))),
-                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_down), hidden, d, hidden, wd);
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_down), hidden, d, hidden, 0, d, wd);
   DG_LAUNCHED();
   return DG_OK;
 }
@@ -320,7 +334,7 @@ extern "C" dg_status dg_selfcond_prepare(const void* E, const void* w_gate, cons
 extern "C" size_t dg_selfcond_ws_bytes(int32_t rows, int32_t V, int32_t d, int32_t hidden, int32_t dtype) {
   if (rows <= 0 || V <= 0 || d <= 0 || hidden <= 0) return 0;
   if (dtype == DG_BF16) {
-    if (d % kGemmTN != 0 || hidden % kGemmTN != 0) return 0;
+    if (d % 128 != 0 || hidden % 128 != 0) return 0;
     return bf16_plan(rows, V, d, hidden).bytes;
   }
   return f32_plan(rows, V, d, hidden).bytes;
@@ -384,7 +398,7 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
 
   // bf16 path
   DG_ARG(prepared != nullptr);
-  DG_UNSUP(d % kGemmTN == 0 && hidden % kGemmTN == 0);
+  DG_UNSUP(d % 128 == 0 && hidden % 128 == 0);
   DG_UNSUP(ld % 8 == 0 && aligned16(logits));
   const Bf16Plan p = bf16_plan(rows, V, d, hidden);
   DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
@@ -403,22 +417,19 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
 
   probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 2048)), rows), 256, 0, s>>>(logits, ld, V, p.Kp,
-                                                                                            inv_t, row_max, w);
+                                                                                            p.Mp, inv_t, row_max, w);
   DG_LAUNCHED();
   if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
-  gemm_f16_splitk_kernel<0><<<p.pe.grid, kGemmThreads, 0, s>>>(
-      GemmArgs{w, p.Kp, et, p.Kp, part, rows, d, static_cast<int32_t>(p.Kp), p.pe.kchunk});
+  launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  pe_reduce_kernel<<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s32, s_out, s16, s_inv);
+  pe_reduce_kernel<<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s32, s_out, s16, s_inv);
   DG_LAUNCHED();
-  gemm_f16_splitk_kernel<1><<<p.g1.grid, kGemmThreads, 0, s>>>(
-      GemmArgs{s16, d, wgu, d, part, rows, 2 * hidden, d, p.g1.kchunk});
+  launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
-  glu_reduce_kernel<<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, s_inv, h32, h16, h_inv);
+  glu_reduce_kernel<<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h32, h16, h_inv);
   DG_LAUNCHED();
-  gemm_f16_splitk_kernel<1><<<p.g2.grid, kGemmThreads, 0, s>>>(
-      GemmArgs{h16, hidden, wd, hidden, part, rows, d, hidden, p.g2.kchunk});
+  launch_gemm<1>(p.g2, gemm_args(h16, p.Mp, wd, d, part, rows, d, hidden, p.g2), s);
   DG_LAUNCHED();
   embed_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
                                                              reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
