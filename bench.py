@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
            tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0)
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
-PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp", "denoise_step_amd/csrc/selfcond.hip")
+PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp",)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
 
 
@@ -216,6 +216,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=8, help="canvas positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three plain 1 GiB device copies (reference for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (no sharding, no collectives); "
@@ -225,6 +227,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        x = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 2 ** 30, "copy_probe_bytes_written": 2 ** 30, "calls": 3}))
+        return
     import denoise_step_amd as dg
     dg.lib()
     w = Workload()
