@@ -226,7 +226,7 @@ inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 
   const int32_t mtiles = (M + kGemmTM - 1) / kGemmTM, ntiles = N / tn;
   const int32_t tiles = mtiles * ntiles;
   int32_t splits = (target_wgs + tiles - 1) / tiles;
-  const int32_t max_splits = (K + 1023) / 1024;
+  const int32_t max_splits = (K + 255) / 256;
   splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
   int32_t kchunk = (K + splits - 1) / splits;
   constexpr int32_t round = kGemmStages * kGemmTK;

@@ -54,14 +54,18 @@ __global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16
 }
 
 // ---------------------------------------------------------------- bf16 path kernels
-// w is written in the K-blocked layout with Mp rows (the GEMM's left operand).
+// w is written in the K-blocked layout with Mp rows (the GEMM's left operand).  A workgroup covers
+// 8 rows x 256 columns: each row is read as 512 contiguous bytes and, for each of the 8 K slices of
+// 32, the 8 rows are written as 512 contiguous bytes.
 template <bool BF16>
 __global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__ logits, int64_t ld, int32_t V,
-                                                        int64_t Kp, int64_t Mp, float inv_t,
-                                                        const float* __restrict__ row_max, _Float16* __restrict__ w) {
-  const int r = blockIdx.y;
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
-  if (i0 >= Kp) return;
+                                                        int64_t Kp, int64_t Mp, int32_t rows, float inv_t,
+                                                        const float* __restrict__ row_max, _Float16* __restrict__ w,
+                                                        uint32_t* __restrict__ row_amax) {
+  const int r = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + (threadIdx.x & 31) * 8;
+  if (r >= rows || i0 >= Kp) return;
+  if (i0 == 0) row_amax[r] = 0u;  // consumed by the P.E reduce, which runs after the GEMM
   const float m = row_max[r];
   float l[8];
   if constexpr (BF16) {
@@ -104,28 +108,40 @@ DG_DEV float block_max_256(float v, float* red) {
   return v;
 }
 
-// One workgroup per row: s = sum_split part * 2^-15 / Z -> s32 (and s_out), then s16 = fp16(s * scale_r)
-// with scale_r a power of two; inv_scale[r] = 1 / scale_r.
+// Split-K reduce of the P.E partials: one thread per (row, column), 256 columns per workgroup:
+// s = sum_split part * 2^-15 / Z -> s32 (and s_out); the row's largest |s| is folded into
+// row_amax[r] with an atomic max on the (non-negative) fp32 bit pattern.
 __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                        int32_t N, int64_t Mp, const float* __restrict__ row_lnz,
+                                                        int32_t N, const float* __restrict__ row_lnz,
                                                         float* __restrict__ s32, float* __restrict__ s_out,
-                                                        _Float16* __restrict__ s16, float* __restrict__ inv_scale) {
+                                                        uint32_t* __restrict__ row_amax) {
   __shared__ float red[4];
-  const int r = blockIdx.x;
+  const int r = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
   const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
-  const int64_t base = static_cast<int64_t>(r) * N;
-  float amax = 0.f;
-  for (int n = threadIdx.x; n < N; n += 256) {
+  const int64_t idx = static_cast<int64_t>(r) * N + n;
+  float v = 0.f;
+  if (n < N) {
     float acc = 0.f;
-    for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + base + n];
-    const float v = acc * f;
-    s32[base + n] = v;
-    if (s_out != nullptr) s_out[base + n] = v;
-    amax = fmaxf(amax, fabsf(v));
+    for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + idx];
+    v = acc * f;
+    s32[idx] = v;
+    if (s_out != nullptr) s_out[idx] = v;
   }
-  const float sc = row_pow2_scale(block_max_256(amax, red));
-  for (int n = threadIdx.x; n < N; n += 256) s16[kblk_index(r, n, Mp)] = static_cast<_Float16>(s32[base + n] * sc);
-  if (threadIdx.x == 0) inv_scale[r] = 1.f / sc;
+  const float amax = block_max_256(fabsf(v), red);
+  if (threadIdx.x == 0) atomicMax(row_amax + r, __float_as_uint(amax));
+}
+
+// s16 = fp16(s * scale_r) in the K-blocked layout, scale_r the power of two that brings the row's
+// largest |s| into (2^13, 2^14]; inv_scale[r] = 1 / scale_r.
+__global__ __launch_bounds__(256) void pe_to_f16_kernel(const float* __restrict__ s32, int32_t N, int64_t Mp,
+                                                        const uint32_t* __restrict__ row_amax,
+                                                        _Float16* __restrict__ s16, float* __restrict__ inv_scale) {
+  const int r = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const float sc = row_pow2_scale(__uint_as_float(row_amax[r]));
+  if (n < N) s16[kblk_index(r, n, Mp)] = static_cast<_Float16>(s32[static_cast<int64_t>(r) * N + n] * sc);
+  if (n == 0) inv_scale[r] = 1.f / sc;
 }
 
 DG_DEV float gelu_tanh(float z) {
@@ -233,7 +249,7 @@ PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
 struct Bf16Plan {
   int64_t Kp, Mp;
   GemmPlan pe, g1, g2;
-  size_t off_w, off_part, off_s16, off_h16, off_s32, off_h32, off_sinv, off_hinv, bytes;
+  size_t off_w, off_part, off_s16, off_h16, off_s32, off_h32, off_sinv, off_hinv, off_amax, bytes;
 };
 
 Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
@@ -257,7 +273,8 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   p.off_h32 = round_up(p.off_s32 + static_cast<size_t>(rows) * d * 4, 256);
   p.off_sinv = round_up(p.off_h32 + static_cast<size_t>(rows) * hidden * 4, 256);
   p.off_hinv = round_up(p.off_sinv + static_cast<size_t>(rows) * 4, 256);
-  p.bytes = round_up(p.off_hinv + static_cast<size_t>(rows) * 4, 256);
+  p.off_amax = round_up(p.off_hinv + static_cast<size_t>(rows) * 4, 256);
+  p.bytes = round_up(p.off_amax + static_cast<size_t>(rows) * 4, 256);
   return p;
 }
 
@@ -415,15 +432,19 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   auto* h32 = reinterpret_cast<float*>(wsb + p.off_h32);
   auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
   auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
+  auto* row_amax = reinterpret_cast<uint32_t*>(wsb + p.off_amax);
 
-  probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 2048)), rows), 256, 0, s>>>(logits, ld, V, p.Kp,
-                                                                                            p.Mp, inv_t, row_max, w);
+  probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 256)), static_cast<unsigned>(cdiv(rows, 8))), 256, 0,
+                          s>>>(logits, ld, V, p.Kp, p.Mp, rows, inv_t, row_max, w, row_amax);
   DG_LAUNCHED();
   if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
   launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  pe_reduce_kernel<<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s32, s_out, s16, s_inv);
+  const dim3 rgrid(static_cast<unsigned>(cdiv(d, 256)), rows);
+  pe_reduce_kernel<<<rgrid, 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s32, s_out, row_amax);
+  DG_LAUNCHED();
+  pe_to_f16_kernel<<<rgrid, 256, 0, s>>>(s32, d, p.Mp, row_amax, s16, s_inv);
   DG_LAUNCHED();
   launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
