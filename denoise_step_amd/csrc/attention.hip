@@ -177,7 +177,10 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   p.qtiles = static_cast<int32_t>(cdiv(static_cast<int64_t>(max_rows) * G, kAttRows));
   const int32_t nblocks = static_cast<int32_t>(cdiv(max_keys, kAttKeys));
   const int64_t base = static_cast<int64_t>(n_req) * Hkv * p.qtiles;
-  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(512, base), std::max(1, nblocks / 4)));
+  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 8)));
+  // a split's page ids are staged in LDS: at most kAttMaxPages pages (16 keys each) per split
+  nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys,
+                                                               static_cast<int64_t>(kAttMaxPages - 8) * 16)));
   nsplit = std::max(1, std::min(nsplit, 65535 / Hkv));
   p.split_keys = static_cast<int32_t>(cdiv(nblocks, nsplit)) * kAttKeys;
   p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));

@@ -5,7 +5,7 @@
 // hk * G + g of the KV group), so the G query heads that share a KV head share
 // every K/V tile.  Four wave64s own 32 packed rows each.
 //
-// Per 32-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// Per 64-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q preloaded in registers): each lane then holds 16
 // scores of ONE query row, so the online softmax is in-lane plus one xor-32
 // shuffle.  The probabilities stay in registers as the B operand of
@@ -29,8 +29,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttRows = 128;   // packed query rows per workgroup
-constexpr int kAttKeys = 32;    // keys per block
+constexpr int kAttKeys = 64;    // keys per block
 constexpr int kAttThreads = 256;
+constexpr int kAttMaxPages = 1024;  // page ids of one split staged in LDS (16K keys)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttArgs {
@@ -56,25 +57,88 @@ template <int D>
 struct AttSmem {
   static constexpr int kPitch = D + 8;          // bf16 per K row in LDS
   static constexpr int vPitch = kAttKeys + 4;   // bf16 per transposed V row in LDS
-  uint16_t K[kAttKeys * kPitch];
-  uint16_t Vt[D * vPitch];
+  uint16_t K[2][kAttKeys * kPitch];
+  uint16_t Vt[2][D * vPitch];
+  int32_t pages[kAttMaxPages];
 };
 
-DG_DEV const uint16_t* att_key_row(const AttArgs& a, const dg_split& sp, int32_t hk, int32_t kk, int32_t n_cache,
-                                   bool is_v, int D) {
+// Registers holding one key block between its global loads and its LDS stores.
+template <int D>
+struct AttStage {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kK = kAttKeys * kChunks / kAttThreads;        // 16-byte K chunks per lane
+  static constexpr int kV = (kAttKeys / 2) * kChunks / kAttThreads;  // V key-pair chunks per lane
+  uint4 k[kK];
+  uint4 v0[kV], v1[kV];
+};
+
+// Key kk of a request: cache positions come from the staged page ids (index and id clamped, so a
+// stale entry can only give a wrong key, never an out-of-range address), canvas keys from k / v.
+template <int D>
+DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk,
+                               int kk, int n_cache, bool is_v) {
   if (kk < n_cache) {
-    const int32_t ti = min(max(sp.page0 + kk / a.page_size, 0), a.page_table_len - 1);
-    const int64_t page = min(max(a.page_table[ti], 0), a.n_pages - 1);
-    const int64_t off = ((page * a.Hkv + hk) * a.page_size + kk % a.page_size) * D;
-    return (is_v ? a.v_cache : a.k_cache) + off;
+    const int slot = min(max(kk / 16 - page_lo, 0), kAttMaxPages - 1);
+    const int64_t page = min(max(pages[slot], 0), a.n_pages - 1);
+    return (is_v ? a.v_cache : a.k_cache) + ((page * a.Hkv + hk) * 16 + (kk & 15)) * D;
   }
   const int64_t row = sp.row0 + sp.n_causal + (kk - n_cache);
   return (is_v ? a.v : a.k) + (row * a.Hkv + hk) * D;
 }
 
+// Keys at or past k_end (the split's last visible key + 1) are masked for every row of the tile;
+// they are filled with zeros and never loaded (their pages are not staged).
+template <int D>
+DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
+                     int n_cache, int k_end, AttStage<D>& st) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int i = 0; i < AttStage<D>::kK; ++i) {
+    const int u = threadIdx.x + i * kAttThreads;
+    const int kk = kb + u / kChunks, c = u % kChunks;
+    st.k[i] = (kk < k_end) ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk, n_cache, false) + 8 * c)
+                             : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AttStage<D>::kV; ++i) {
+    const int u = threadIdx.x + i * kAttThreads;
+    const int pair = u % (kAttKeys / 2), c = u / (kAttKeys / 2);
+    const int kk = kb + 2 * pair;
+    st.v0[i] = (kk < k_end) ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk, n_cache, true) + 8 * c)
+                              : make_uint4(0, 0, 0, 0);
+    st.v1[i] = (kk + 1 < k_end)
+                   ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk + 1, n_cache, true) + 8 * c)
+                   : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+DG_DEV void att_store(AttSmem<D>& sm, int buf, const AttStage<D>& st) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int i = 0; i < AttStage<D>::kK; ++i) {
+    const int u = threadIdx.x + i * kAttThreads;
+    *reinterpret_cast<uint4*>(&sm.K[buf][(u / kChunks) * AttSmem<D>::kPitch + 8 * (u % kChunks)]) = st.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < AttStage<D>::kV; ++i) {
+    const int u = threadIdx.x + i * kAttThreads;
+    const int pair = u % (kAttKeys / 2), c = u / (kAttKeys / 2);
+    const uint32_t w0[4] = {st.v0[i].x, st.v0[i].y, st.v0[i].z, st.v0[i].w};
+    const uint32_t w1[4] = {st.v1[i].x, st.v1[i].y, st.v1[i].z, st.v1[i].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // d = 8c + 2t (low halves) and 8c + 2t + 1 (high halves); keys 2 pair, 2 pair + 1
+      const uint32_t lo = (w0[t] & 0xFFFFu) | (w1[t] << 16);
+      const uint32_t hi = (w0[t] >> 16) | (w1[t] & 0xFFFF0000u);
+      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(8 * c + 2 * t) * AttSmem<D>::vPitch + 2 * pair]) = lo;
+      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(8 * c + 2 * t + 1) * AttSmem<D>::vPitch + 2 * pair]) = hi;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
-  constexpr int kChunks = D / 8;                 // 16-byte chunks per key row
   constexpr int kDSteps = D / 16;                // MFMA k-steps over D
   constexpr int kDTiles = D / 32;                // 32-wide output tiles over D
   __shared__ __attribute__((aligned(16))) AttSmem<D> sm;
@@ -104,6 +168,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int row = sp.row0 + j;
   const int lim = !row_ok ? 0 : (j < sp.n_causal ? sp.cached + j + 1 : n_total);
 
+  // stage the physical page ids of the split's cache positions (clamped into range)
+  const int page_lo = k_begin / 16;
+  const int page_hi = min((min(k_end, n_cache) + 15) / 16, page_lo + kAttMaxPages);
+  for (int p = page_lo + tid; p < page_hi; p += kAttThreads) {
+    const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
+    sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
+  }
+
   // Q fragment (B operand of S^T = K Q^T): 8 consecutive d per MFMA step
   bf16x8 qf[kDSteps];
   {
@@ -119,84 +191,79 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  AttStage<D> st;
+  __syncthreads();  // page ids visible
+  if (k_begin < k_end) {
+    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, n_cache, k_end, st);
+    att_store<D>(sm, 0, st);
+  }
+  __syncthreads();
+  int buf = 0;
   for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
-    __syncthreads();  // previous block's LDS reads are done
-    // ---- stage K (row-major) and V (transposed) for keys kb .. kb+31
-    for (int u = tid; u < kAttKeys * kChunks; u += kAttThreads) {
-      const int key = u / kChunks, c = u % kChunks;
-      const int kk = kb + key;
-      uint4 kv = make_uint4(0, 0, 0, 0);
-      if (kk < n_total) kv = *reinterpret_cast<const uint4*>(att_key_row(a, sp, hk, kk, n_cache, false, D) + 8 * c);
-      *reinterpret_cast<uint4*>(&sm.K[key * AttSmem<D>::kPitch + 8 * c]) = kv;
-    }
-    for (int u = tid; u < (kAttKeys / 2) * kChunks; u += kAttThreads) {
-      const int pair = u % (kAttKeys / 2), c = u / (kAttKeys / 2);
-      const int kk = kb + 2 * pair;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (kk < n_total) v0 = *reinterpret_cast<const uint4*>(att_key_row(a, sp, hk, kk, n_cache, true, D) + 8 * c);
-      if (kk + 1 < n_total)
-        v1 = *reinterpret_cast<const uint4*>(att_key_row(a, sp, hk, kk + 1, n_cache, true, D) + 8 * c);
-      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-      const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+    const bool more = kb + kAttKeys < k_end;
+    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, n_cache, k_end, st);
+    const uint16_t* Kb = sm.K[buf];
+    const uint16_t* Vb = sm.Vt[buf];
+    // ---- S^T = K Q^T : two 32-key sub-blocks x 32 rows
+    floatx16 sc[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // d = 8c + 2t (low halves) and 8c + 2t + 1 (high halves)
-        const uint32_t lo = (w0[t] & 0xFFFFu) | (w1[t] << 16);
-        const uint32_t hi = (w0[t] >> 16) | (w1[t] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(&sm.Vt[(8 * c + 2 * t) * AttSmem<D>::vPitch + 2 * pair]) = lo;
-        *reinterpret_cast<uint32_t*>(&sm.Vt[(8 * c + 2 * t + 1) * AttSmem<D>::vPitch + 2 * pair]) = hi;
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < kDSteps; ++s) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&Kb[(32 * b + (lane & 31)) * AttSmem<D>::kPitch + 16 * s + 8 * half]);
+        sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
       }
     }
-    __syncthreads();
-
-    // ---- S^T = K Q^T : 32 keys x 32 rows
-    floatx16 st;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kDSteps; ++s) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sm.K[(lane & 31) * AttSmem<D>::kPitch + 16 * s + 8 * half]);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st, 0, 0, 0);
-    }
-    // ---- online softmax; element e holds key 8 * (e / 4) + 4 * half + e % 4 of this lane's row
+    // ---- online softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kb + 8 * (e >> 2) + 4 * half + (e & 3);
-      st[e] = (key < lim) ? st[e] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, st[e]);
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb + 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
+        sc[b][e] = (key < lim) ? sc[b][e] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[b][e]);
+      }
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
-    bf16x8 pf[2];
+    bf16x8 pf[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = (st[e] == -INFINITY) ? 0.f : exp2f(st[e] - m_new);
-      psum += p;
-      pf[e >> 3][e & 7] = static_cast<__bf16>(p);
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = (sc[b][e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[b][e] - m_new);
+        psum += p;
+        pf[2 * b + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+      }
     psum += __shfl_xor(psum, 32, kWave);
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // the running max moved for some row of the wave
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t)
+      for (int t = 0; t < kDTiles; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
-
-    // ---- O^T += V^T P^T over two 16-key chunks; key slots follow the accumulator layout
+        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+    }
+    // ---- O^T += V^T P^T over four 16-key chunks; key slots follow the accumulator layout
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int t = 0; t < kDTiles; ++t) {
-        const uint16_t* vrow = &sm.Vt[(32 * t + (lane & 31)) * AttSmem<D>::vPitch + 16 * c + 4 * half];
+        const uint16_t* vrow = &Vb[(32 * t + (lane & 31)) * AttSmem<D>::vPitch + 16 * c + 4 * half];
         const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
         const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
       }
     }
+    if (more) att_store<D>(sm, buf ^ 1, st);
+    __syncthreads();
+    buf ^= 1;
   }
 
   if (!row_ok) return;
