@@ -71,16 +71,28 @@ DG_DEV uint32_t gemm_lane_offset() {
 // The copy is issued from inline asm (M0 = LDS destination, scalar base + per-lane 32-bit offset) so
 // that its completion is tracked only by the explicit vmcnt waits of the pipeline below; the main
 // loop issues no other vector-memory instruction, so those counts are exact.
+// NT marks the load non-temporal: used for the right operand, which every workgroup streams once
+// (E^T is read by exactly one tile per K range), so it does not evict the left operand that the
+// workgroups of the other N tiles re-read from L2.
+template <bool NT>
 DG_DEV void gemm_dma(const _Float16* __restrict__ base, int64_t rows, int row0, int k0, uint32_t lane_off,
                      _Float16* lds, int q) {
   const char* ub = reinterpret_cast<const char*>(base) + kblk_index(row0 + 16 * q, k0, rows) * 2;
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + q * kWave * 8));
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_addr), "v"(lane_off), "s"(ub)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(lds_addr), "v"(lane_off), "s"(ub)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_addr), "v"(lane_off), "s"(ub)
+        : "memory", "m0");
 }
 
 // Issue one stage: A (256 rows) and B (TN rows) as 1-KB instructions shared round-robin by the waves.
@@ -89,9 +101,9 @@ template <int TN>
 DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, int wave, _Float16* as,
                        _Float16* bs) {
 #pragma unroll
-  for (int i = 0; i < kGemmTM / 16 / kGemmWaves; ++i) gemm_dma(g.A, g.lda, m0, k0, off, as, wave + kGemmWaves * i);
+  for (int i = 0; i < kGemmTM / 16 / kGemmWaves; ++i) gemm_dma<false>(g.A, g.lda, m0, k0, off, as, wave + kGemmWaves * i);
 #pragma unroll
-  for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
+  for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma<true>(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
 }
 
 // Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.

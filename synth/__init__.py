@@ -143,14 +143,33 @@ class PagedAttentionProblem:
         return int(self.q.shape[0])
 
 
-def attention_problem(seed: int, splits, Hq: int, Hkv: int, D: int, page_size: int = 16,
-                      dtype: str = "bf16", spare_pages: int = 3, tag: str = "attn") -> PagedAttentionProblem:
-    """Random Q/K/V, a paged cache filled for each request's cached prefix, and shuffled page tables.
+@dataclass
+class PagedLayout:
+    """Row and page placement of one attention launch (no tensor data)."""
+    splits: list            # list[SplitSpec]
+    row0: np.ndarray        # int32 [n_req]
+    page0: np.ndarray       # int32 [n_req]
+    page_table: np.ndarray  # int32 [sum of the requests' pages]
+    n_pages: int            # physical pages in the pool (owned + spare)
+    rows: int               # packed rows of the launch
+    page_size: int
 
-    Each request owns ceil((cached + n_causal) / page_size) pages (room for the causal rows'
-    K/V to be appended), drawn from one global shuffled pool with ``spare_pages`` extra pages
-    that no request owns (they stay as random junk so reading a wrong page shows up).
-    """
+    def split_array(self) -> np.ndarray:
+        """[n_req, 6] int32 rows of (row0, cached, n_causal, n_canvas, page0, window = 0)."""
+        return np.array([[self.row0[i], s.cached, s.n_causal, s.n_canvas, self.page0[i], 0]
+                         for i, s in enumerate(self.splits)], np.int32).reshape(-1, 6)
+
+    def pages_of(self, i: int) -> np.ndarray:
+        """Physical page ids of request i, in position order."""
+        s = self.splits[i]
+        n = max(1, -(-(s.cached + s.n_causal) // self.page_size))
+        return self.page_table[self.page0[i]:self.page0[i] + n]
+
+
+def paged_layout(seed: int, splits, page_size: int = 16, spare_pages: int = 3, tag: str = "attn") -> PagedLayout:
+    """Each request owns ceil((cached + n_causal) / page_size) pages (room for the causal rows'
+    K/V to be appended), drawn from one global shuffled pool with ``spare_pages`` extra pages that
+    no request owns; rows are packed request after request."""
     splits = [s if isinstance(s, SplitSpec) else SplitSpec(*s) for s in splits]
     need = [max(1, -(-(s.cached + s.n_causal) // page_size)) for s in splits]
     n_pages = int(sum(need)) + spare_pages
@@ -166,16 +185,45 @@ def attention_problem(seed: int, splits, Hq: int, Hkv: int, D: int, page_size: i
         tbl.extend(pool[p:p + n].tolist())
         p += n
         r += s.n_causal + s.n_canvas
-    rows = r
+    return PagedLayout(splits=splits, row0=row0, page0=page0, page_table=np.asarray(tbl, np.int32),
+                       n_pages=n_pages, rows=r, page_size=page_size)
+
+
+def attention_problem(seed: int, splits, Hq: int, Hkv: int, D: int, page_size: int = 16,
+                      dtype: str = "bf16", spare_pages: int = 3, tag: str = "attn") -> PagedAttentionProblem:
+    """Random Q/K/V, a paged cache filled for each request's cached prefix, and shuffled page tables
+    (layout of paged_layout; the spare pages stay as random junk so reading a wrong page shows up)."""
+    lay = paged_layout(seed, splits, page_size, spare_pages, tag)
+    rows, n_pages = lay.rows, lay.n_pages
     gen = normal_bf16 if dtype == "bf16" else normal_f32
     q = gen(seed, (tag, "q"), (rows, Hq, D))
     k = gen(seed, (tag, "k"), (rows, Hkv, D))
     v = gen(seed, (tag, "v"), (rows, Hkv, D))
     kc = gen(seed, (tag, "kc"), (n_pages, Hkv, page_size, D))
     vc = gen(seed, (tag, "vc"), (n_pages, Hkv, page_size, D))
-    return PagedAttentionProblem(Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, splits=splits,
-                                 row0=row0, page0=page0, page_table=np.asarray(tbl, np.int32),
+    return PagedAttentionProblem(Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, splits=lay.splits,
+                                 row0=lay.row0, page0=lay.page0, page_table=lay.page_table,
                                  q=q, k=k, v=v, k_cache=kc, v_cache=vc, dtype=dtype)
+
+
+def batched_splits(cfg: dict, commit_requests=(5, 21)) -> list:
+    """Batched serving snapshot: prefixes U{L_min..L_max}; the listed requests are in the launch
+    right after their commit (256 causal rows appended, no canvas rows), the others denoise a
+    canvas of C rows."""
+    L = rng_for(cfg["seed"], "batched.L").integers(cfg["L_min"], cfg["L_max"] + 1, cfg["B"])
+    return [SplitSpec(int(L[r]), cfg["C"], 0) if r in commit_requests else SplitSpec(int(L[r]), 0, cfg["C"])
+            for r in range(cfg["B"])]
+
+
+def structured_read_splits(cfg: dict) -> list:
+    """Final prompt chunk (causal rows, nothing cached before it) plus the canvas, per request."""
+    return [SplitSpec(0, cfg["n_causal"], cfg["C"]) for _ in range(cfg["B"])]
+
+
+def block_draft_splits(cfg: dict) -> list:
+    """Injected context U{L_min..L_max} per request plus the draft block as canvas rows."""
+    L = rng_for(cfg["seed"], "block_draft.L").integers(cfg["L_min"], cfg["L_max"] + 1, cfg["B"])
+    return [SplitSpec(int(L[r]), 0, cfg["block"]) for r in range(cfg["B"])]
 
 
 def tiny_loop_inputs(cfg: dict, variant_scale: float | None = None) -> dict:

@@ -88,28 +88,13 @@ def test_sampler_single_canvas_full_size_sampled_rows():
     # the oracle takes the chosen rows at their canvas positions
     ref = osamp.SampleOut(*(np.zeros(C) for _ in range(5)), argmax_gap=np.zeros(C), key_gap=np.zeros(C))
     for i, r in enumerate(rows):
-        one = _oracle_row(host[i], seeds[0], r, steps[0])
+        one = P.sampler_oracle_row(host[i], seeds[0], r, steps[0])
         for f in ("entropy", "argmax", "sample", "row_max", "row_lnz", "argmax_gap", "key_gap"):
             getattr(ref, f)[r] = getattr(one, f)[0]
     sub = {k: v[rows] for k, v in got.items()}
     P.check_sampler_rows(sub, ref, rows)
     # entropies spread over the recipe's range
     assert got["entropy"].min() < 1.0 and got["entropy"].max() > 9.0
-
-
-def _oracle_row(row, seed, pos, step):
-    """Oracle for one row at canvas position `pos` (a request of pos + 1 rows whose last row is this one)."""
-    from oracle import philox
-    x = np.asarray(row, np.float64)
-    m, Z, S, H = osamp.softmax_stats(x)
-    g = philox.gumbel_row(seed, pos, step, x.size)
-    key = x + g
-    srt = np.sort(x)
-    ks = np.sort(key)
-    return osamp.SampleOut(entropy=np.array([H]), argmax=np.array([int(np.argmax(x))]),
-                           sample=np.array([int(np.argmax(key))]), row_max=np.array([m]),
-                           row_lnz=np.array([np.log(Z)]), argmax_gap=np.array([srt[-1] - srt[-2]]),
-                           key_gap=np.array([ks[-1] - ks[-2]]))
 
 
 def test_sampler_block_draft_argmax_full_size():
