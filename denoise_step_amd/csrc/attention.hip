@@ -8,10 +8,12 @@
 // each row's visibility (a request split into causal input rows and canvas
 // rows that share its KV block table; the p0 p1 c0 c1 example).
 //
-// Launch order on the stream: (1) the causal rows' K/V are appended to the
-// request's pages at positions cached + j; (2) the attention kernel reads
-// every prefix and causal key from the pages and the canvas keys from the
-// k/v inputs.
+// bf16, head_dim 128 / 256: one MFMA kernel reads prefix keys from the pages
+// and causal / canvas keys from the k/v inputs, and appends the causal rows'
+// K/V to the pages itself (then a merge kernel if the keys were split).
+// Other shapes: (1) the causal rows' K/V are appended to the request's pages
+// at positions cached + j; (2) one wave per (row, head) reads every prefix and
+// causal key from the pages and the canvas keys from the k/v inputs.
 #include "attention_mfma.hpp"
 #include "dg_device.hpp"
 #include "dg_host.hpp"
@@ -177,11 +179,12 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   p.qtiles = static_cast<int32_t>(cdiv(static_cast<int64_t>(max_rows) * G, kAttRows));
   const int32_t nblocks = static_cast<int32_t>(cdiv(max_keys, kAttKeys));
   const int64_t base = static_cast<int64_t>(n_req) * Hkv * p.qtiles;
-  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 8)));
+  // about one workgroup per CU, at least 4 key blocks per split
+  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 4)));
   // a split's page ids are staged in LDS: at most kAttMaxPages pages (16 keys each) per split
   nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys,
                                                                static_cast<int64_t>(kAttMaxPages - 8) * 16)));
-  nsplit = std::max(1, std::min(nsplit, 65535 / Hkv));
+  nsplit = std::max(1, std::min({nsplit, 65535 / Hkv, kMergeSplits}));
   p.split_keys = static_cast<int32_t>(cdiv(nblocks, nsplit)) * kAttKeys;
   p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));
   if (p.nsplit > 1) {
@@ -223,7 +226,7 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
   const bool bf = dtype == DG_BF16;
-  {
+  if (!plan.mfma) {
     const dim3 grid(max_rows_per_req, n_req);
     if (bf)
       append_kv_kernel<true><<<grid, 256, 0, s>>>(k, v, k_cache, v_cache, n_pages, page_table, page_table_len,
@@ -240,6 +243,8 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
     a.v = reinterpret_cast<const uint16_t*>(v);
     a.k_cache = reinterpret_cast<const uint16_t*>(k_cache);
     a.v_cache = reinterpret_cast<const uint16_t*>(v_cache);
+    a.k_cache_w = reinterpret_cast<uint16_t*>(k_cache);
+    a.v_cache_w = reinterpret_cast<uint16_t*>(v_cache);
     a.n_pages = n_pages;
     a.page_table = page_table;
     a.page_table_len = page_table_len;
@@ -262,13 +267,12 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
       attend_mfma_kernel<128><<<grid, kAttThreads, 0, s>>>(a);
     DG_LAUNCHED();
     if (plan.nsplit > 1) {
-      const unsigned nrh = static_cast<unsigned>(static_cast<int64_t>(rows) * Hq);
       if (D == 256)
-        attend_merge_kernel<256><<<nrh, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                     a.out);
+        attend_merge_kernel<256><<<rows, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                      a.out);
       else
-        attend_merge_kernel<128><<<nrh, 128, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                     a.out);
+        attend_merge_kernel<128><<<rows, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                      a.out);
       DG_LAUNCHED();
     }
     return DG_OK;

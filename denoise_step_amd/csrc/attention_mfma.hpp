@@ -5,6 +5,10 @@
 // hk * G + g of the KV group), so the G query heads that share a KV head share
 // every K/V tile.  Four wave64s own 32 packed rows each.
 //
+// K blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per lane,
+// no staging registers) into a chunk-major layout; V blocks go through registers, where each pair
+// of keys is transposed on its way into LDS.  Both are prefetched one block ahead.
+//
 // Per 64-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q preloaded in registers): each lane then holds 16
 // scores of ONE query row, so the online softmax is in-lane plus one xor-32
@@ -12,13 +16,23 @@
 // O^T = V^T P^T (A = V^T read from a transposed LDS copy of the V block); the
 // key order inside each 16-key MFMA step is permuted consistently on both
 // operands to match the accumulator layout.  O^T accumulates in fp32 (each
-// lane again owns one row, so the rescale is in-lane).
+// lane again owns one row, so the rescale is in-lane).  The softmax reference
+// (running max) moves only when a block's maximum exceeds it by more than 2^8,
+// so the rescale of O (and the AGPR round trip it costs) is rare; probabilities
+// are then at most 2^8, which bf16 and the fp32 sums hold as well as values
+// below 1.  The final division uses the same reference, so the result is the
+// same softmax.
 //
-// Visibility (per request): key index kk (cache positions first, then canvas
-// rows) is visible to causal row j iff kk <= cached + j, to a canvas row
-// always.  Blocks past the last visible key of the tile are never loaded
-// (tiles holding only masked entries are skipped).  With several KV splits each
-// split writes unnormalised partials (O, running max, running sum) and a merge
+// Visibility (per request): key index kk (prefix positions first, then causal
+// rows, then canvas rows) is visible to causal row j iff kk <= cached + j, to a
+// canvas row always.  Keys at or past `cached` are read from the k / v inputs
+// (the causal rows' K/V are exactly the values this launch appends to the
+// pages), so the append has no ordering constraint and the same kernel does it:
+// the split-0 workgroup of each row tile writes its causal rows' K/V for its KV
+// head.  Blocks past the last visible key of the tile are never loaded (tiles
+// holding only masked entries are skipped); only blocks that are not fully
+// visible to every row of a wave evaluate the mask.  With several KV splits
+// each split writes unnormalised partials (O, reference max, sum) and a merge
 // kernel combines them with log-sum-exp weights.
 #pragma once
 #include "dg_device.hpp"
@@ -40,6 +54,8 @@ struct AttArgs {
   const uint16_t* v;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
+  uint16_t* k_cache_w;  // the same pages, written by the append of the causal rows
+  uint16_t* v_cache_w;
   int32_t n_pages;
   const int32_t* page_table;
   int32_t page_table_len;
@@ -55,71 +71,89 @@ struct AttArgs {
 
 template <int D>
 struct AttSmem {
-  static constexpr int kPitch = D + 8;          // bf16 per K row in LDS
+  static constexpr int kChunks = D / 8;         // 16-byte chunks per K row
   static constexpr int vPitch = kAttKeys + 4;   // bf16 per transposed V row in LDS
-  uint16_t K[2][kAttKeys * kPitch];
+  uint16_t K[2][kAttKeys * D];
   uint16_t Vt[2][D * vPitch];
   int32_t pages[kAttMaxPages];
 };
 
-// Registers holding one key block between its global loads and its LDS stores.
+// Registers holding one V block between its global loads and its LDS stores.
 template <int D>
 struct AttStage {
   static constexpr int kChunks = D / 8;
-  static constexpr int kK = kAttKeys * kChunks / kAttThreads;        // 16-byte K chunks per lane
   static constexpr int kV = (kAttKeys / 2) * kChunks / kAttThreads;  // V key-pair chunks per lane
-  uint4 k[kK];
   uint4 v0[kV], v1[kV];
 };
 
-// Key kk of a request: cache positions come from the staged page ids (index and id clamped, so a
-// stale entry can only give a wrong key, never an out-of-range address), canvas keys from k / v.
+// K in LDS, chunk-major: chunk c (8 bf16) of key r of the block sits in 16-byte slot c * 64 + r.
+// An MFMA operand read has 16 consecutive keys ask for one chunk per 16-lane group: 16
+// consecutive slots, one 256-byte bank row, so the reads are conflict-free.
+template <int D>
+DG_DEV int att_kslot(int r, int c) {
+  return c * kAttKeys + r;
+}
+
+// Key kk of a request: prefix positions (kk < cached) come from the staged page ids (index and id
+// clamped, so a stale entry can only give a wrong key, never an out-of-range address); the causal
+// and canvas keys from rows row0 + kk - cached of k / v.  Both candidates are formed and one is
+// selected, so the address math has no branches.
 template <int D>
 DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk,
-                               int kk, int n_cache, bool is_v) {
-  if (kk < n_cache) {
-    const int slot = min(max(kk / 16 - page_lo, 0), kAttMaxPages - 1);
-    const int64_t page = min(max(pages[slot], 0), a.n_pages - 1);
-    return (is_v ? a.v_cache : a.k_cache) + ((page * a.Hkv + hk) * 16 + (kk & 15)) * D;
-  }
-  const int64_t row = sp.row0 + sp.n_causal + (kk - n_cache);
-  return (is_v ? a.v : a.k) + (row * a.Hkv + hk) * D;
+                               int kk, bool is_v) {
+  const int slot = min(max(kk / 16 - page_lo, 0), kAttMaxPages - 1);
+  const int64_t page = min(max(pages[slot], 0), a.n_pages - 1);
+  const int64_t cache_off = ((page * a.Hkv + hk) * 16 + (kk & 15)) * D;
+  const int64_t row = sp.row0 + max(kk - sp.cached, 0);
+  const int64_t new_off = (row * a.Hkv + hk) * D;
+  const uint16_t* cache = is_v ? a.v_cache : a.k_cache;
+  const uint16_t* fresh = is_v ? a.v : a.k;
+  return kk < sp.cached ? cache + cache_off : fresh + new_off;
 }
 
-// Keys at or past k_end (the split's last visible key + 1) are masked for every row of the tile;
-// they are filled with zeros and never loaded (their pages are not staged).
+// Keys at or past k_end (the split's last visible key + 1) are masked for every row of the tile:
+// they re-read the last visible key (whose page is staged) and their V chunks are zeroed.
+//
+// K: copy c fills chunk plane c of the block, one key per lane, so each lane forms one address per
+// block and its copies differ only by the chunk offset.
 template <int D>
 DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
-                     int n_cache, int k_end, AttStage<D>& st) {
+                     int k_end, uint16_t* kdst, AttStage<D>& st) {
   constexpr int kChunks = D / 8;
+  constexpr int kPerWave = kChunks / (kAttThreads / kWave);  // chunk planes copied by each wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: M0 is scalar
+  const uint16_t* krow = att_row<D>(a, sp, pages, page_lo, hk, min(kb + lane, k_end - 1), false);
 #pragma unroll
-  for (int i = 0; i < AttStage<D>::kK; ++i) {
-    const int u = threadIdx.x + i * kAttThreads;
-    const int kk = kb + u / kChunks, c = u % kChunks;
-    st.k[i] = (kk < k_end) ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk, n_cache, false) + 8 * c)
-                             : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kPerWave; ++i) {
+    const int c = wave * kPerWave + i;
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kAttKeys * 8 * c));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_addr), "v"(krow + 8 * c)
+        : "memory", "m0");
   }
+  // V: lane pair p = tid % 32 carries keys 2 p and 2 p + 1, chunks tid / 32 + 8 i
+  const int kk0 = kb + 2 * (threadIdx.x % (kAttKeys / 2));
+  const uint16_t* v0row = att_row<D>(a, sp, pages, page_lo, hk, min(kk0, k_end - 1), true);
+  const uint16_t* v1row = att_row<D>(a, sp, pages, page_lo, hk, min(kk0 + 1, k_end - 1), true);
+  const bool ok0 = kk0 < k_end, ok1 = kk0 + 1 < k_end;
 #pragma unroll
   for (int i = 0; i < AttStage<D>::kV; ++i) {
-    const int u = threadIdx.x + i * kAttThreads;
-    const int pair = u % (kAttKeys / 2), c = u / (kAttKeys / 2);
-    const int kk = kb + 2 * pair;
-    st.v0[i] = (kk < k_end) ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk, n_cache, true) + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
-    st.v1[i] = (kk + 1 < k_end)
-                   ? *reinterpret_cast<const uint4*>(att_row<D>(a, sp, pages, page_lo, hk, kk + 1, n_cache, true) + 8 * c)
-                   : make_uint4(0, 0, 0, 0);
+    const int c = threadIdx.x / (kAttKeys / 2) + (kAttThreads / (kAttKeys / 2)) * i;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(v0row + 8 * c);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(v1row + 8 * c);
+    st.v0[i] = ok0 ? x0 : make_uint4(0, 0, 0, 0);
+    st.v1[i] = ok1 ? x1 : make_uint4(0, 0, 0, 0);
   }
 }
 
+// Stores the V block (transposed) and waits for every outstanding copy, so that after the next
+// barrier both K (direct copies) and V of the block are visible.
 template <int D>
 DG_DEV void att_store(AttSmem<D>& sm, int buf, const AttStage<D>& st) {
-  constexpr int kChunks = D / 8;
-#pragma unroll
-  for (int i = 0; i < AttStage<D>::kK; ++i) {
-    const int u = threadIdx.x + i * kAttThreads;
-    *reinterpret_cast<uint4*>(&sm.K[buf][(u / kChunks) * AttSmem<D>::kPitch + 8 * (u % kChunks)]) = st.k[i];
-  }
 #pragma unroll
   for (int i = 0; i < AttStage<D>::kV; ++i) {
     const int u = threadIdx.x + i * kAttThreads;
@@ -135,12 +169,34 @@ DG_DEV void att_store(AttSmem<D>& sm, int buf, const AttStage<D>& st) {
       *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(8 * c + 2 * t + 1) * AttSmem<D>::vPitch + 2 * pair]) = hi;
     }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+}
+
+// Causal rows' K/V of one KV head into the pages at positions cached + j (16-byte chunks).
+template <int D>
+DG_DEV void att_append(const AttArgs& a, const dg_split& sp, int hk, int j0, int j1) {
+  constexpr int kChunks = D / 8;
+  const int n = (j1 - j0) * kChunks;
+  for (int u = threadIdx.x; u < 2 * n; u += kAttThreads) {
+    const bool is_v = u >= n;
+    const int w = is_v ? u - n : u;
+    const int j = j0 + w / kChunks, c = w % kChunks;
+    const int pos = sp.cached + j;
+    const int ti = min(max(sp.page0 + pos / 16, 0), a.page_table_len - 1);
+    const int64_t page = min(max(a.page_table[ti], 0), a.n_pages - 1);
+    const int64_t src = ((static_cast<int64_t>(sp.row0) + j) * a.Hkv + hk) * D + 8 * c;
+    const int64_t dst = ((page * a.Hkv + hk) * 16 + (pos & 15)) * D + 8 * c;
+    const uint16_t* from = is_v ? a.v : a.k;
+    uint16_t* to = is_v ? a.v_cache_w : a.k_cache_w;
+    *reinterpret_cast<uint4*>(to + dst) = *reinterpret_cast<const uint4*>(from + src);
+  }
 }
 
 template <int D>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   constexpr int kDSteps = D / 16;                // MFMA k-steps over D
   constexpr int kDTiles = D / 32;                // 32-wide output tiles over D
+  constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
   __shared__ __attribute__((aligned(16))) AttSmem<D> sm;
 
   const dg_split sp = a.splits[blockIdx.z];
@@ -149,8 +205,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int nr = sp.n_causal + sp.n_canvas;
   const int m_tile0 = blockIdx.x * kAttRows;
   if (m_tile0 >= nr * a.G) return;
-  const int n_cache = sp.cached + sp.n_causal;
-  const int n_total = n_cache + sp.n_canvas;
+  const int n_total = sp.cached + nr;
   // last visible key + 1 over the tile's rows (rows are ordered causal then canvas)
   const int j_last = min(nr - 1, (m_tile0 + kAttRows - 1) / a.G);
   const int tile_lim = (j_last < sp.n_causal) ? sp.cached + j_last + 1 : n_total;
@@ -166,11 +221,15 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int j = row_ok ? m / a.G : 0;
   const int h = hk * a.G + (row_ok ? m % a.G : 0);
   const int row = sp.row0 + j;
-  const int lim = !row_ok ? 0 : (j < sp.n_causal ? sp.cached + j + 1 : n_total);
+  // rows past the tile's end compute an unused copy of row 0 and never force masking
+  const int lim = (row_ok && j < sp.n_causal) ? sp.cached + j + 1 : n_total;
+  int wave_lim = lim;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wave_lim = min(wave_lim, __shfl_xor(wave_lim, o, kWave));
 
-  // stage the physical page ids of the split's cache positions (clamped into range)
+  // stage the physical page ids of the split's prefix positions (clamped into range)
   const int page_lo = k_begin / 16;
-  const int page_hi = min((min(k_end, n_cache) + 15) / 16, page_lo + kAttMaxPages);
+  const int page_hi = min((min(k_end, sp.cached) + 15) / 16, page_lo + kAttMaxPages);
   for (int p = page_lo + tid; p < page_hi; p += kAttThreads) {
     const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
     sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
@@ -189,19 +248,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   for (int t = 0; t < kDTiles; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and sum of 2^(x - m_ref)
 
   AttStage<D> st;
   __syncthreads();  // page ids visible
   if (k_begin < k_end) {
-    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, n_cache, k_end, st);
+    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], st);
     att_store<D>(sm, 0, st);
   }
   __syncthreads();
   int buf = 0;
   for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
     const bool more = kb + kAttKeys < k_end;
-    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, n_cache, k_end, st);
+    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], st);
     const uint16_t* Kb = sm.K[buf];
     const uint16_t* Vb = sm.Vt[buf];
     // ---- S^T = K Q^T : two 32-key sub-blocks x 32 rows
@@ -212,43 +271,51 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
       for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
 #pragma unroll
       for (int s = 0; s < kDSteps; ++s) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Kb[(32 * b + (lane & 31)) * AttSmem<D>::kPitch + 16 * s + 8 * half]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), 2 * s + half)]);
         sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
       }
     }
-    // ---- online softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
+    // ---- softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
+    if (kb + kAttKeys > wave_lim) {  // some key of the block is masked for some row of the wave
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
+          sc[b][e] = (key < lim) ? sc[b][e] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb + 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
-        sc[b][e] = (key < lim) ? sc[b][e] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sc[b][e]);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float mb = mx * a.scale_log2;  // block max in log2 units (-inf if the whole block is masked)
+    const bool grow = mb > m_ref + kRescaleAbove;
+    const bool rescale = grow && m_ref != -INFINITY;  // before the first visible key O and l are zero
+    if (__any(rescale)) {
+      const float alpha = rescale ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+    }
+    if (grow) m_ref = mb;
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // masked scores give 2^-inf = 0 either way
     float psum = 0.f;
     bf16x8 pf[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = (sc[b][e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[b][e] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[b][e], a.scale_log2, -m_use));
         psum += p;
         pf[2 * b + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
     psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {  // the running max moved for some row of the wave
-#pragma unroll
-      for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
-    }
+    l_run += psum;
     // ---- O^T += V^T P^T over four 16-key chunks; key slots follow the accumulator layout
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -264,6 +331,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     if (more) att_store<D>(sm, buf ^ 1, st);
     __syncthreads();
     buf ^= 1;
+  }
+
+  // append: the split-0 workgroup writes the causal rows whose first packed row is in its tile
+  if (split == 0) {
+    const int j0 = (m_tile0 + a.G - 1) / a.G;
+    const int j1 = min(sp.n_causal, (m_tile0 + kAttRows + a.G - 1) / a.G);
+    if (j0 < j1) att_append<D>(a, sp, hk, j0, j1);
   }
 
   if (!row_ok) return;
@@ -294,36 +368,64 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
         *reinterpret_cast<float4*>(orow + d) =
             make_float4(o[t][4 * g4], o[t][4 * g4 + 1], o[t][4 * g4 + 2], o[t][4 * g4 + 3]);
       }
-    if (half == 0) a.ml_part[ridx] = make_float2(m_run, l_run);
+    if (half == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
   }
 }
 
-// Combine KV splits: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  One workgroup per (row, head).
+// Combine KV splits: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  One
+// workgroup per packed row, four consecutive d per thread, every split's loads issued before the
+// sums.  Rows outside every request's range were never written and are skipped.
+constexpr int kMergeSplits = 16;  // the most splits a launch uses
+
 template <int D>
-__global__ __launch_bounds__(D) void attend_merge_kernel(const float* __restrict__ o_part,
-                                                         const float2* __restrict__ ml_part, int32_t nsplit,
-                                                         int32_t rows, int32_t Hq, const dg_split* __restrict__ splits,
-                                                         int32_t n_req, uint16_t* __restrict__ out) {
-  const int64_t rh = blockIdx.x;  // row * Hq + h
-  const int row = static_cast<int>(rh / Hq);
-  // rows outside every request's range were never written: skip them
-  bool owned = false;
-  for (int r = 0; r < n_req && !owned; ++r) {
+__global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restrict__ o_part,
+                                                           const float2* __restrict__ ml_part, int32_t nsplit,
+                                                           int32_t rows, int32_t Hq,
+                                                           const dg_split* __restrict__ splits, int32_t n_req,
+                                                           uint16_t* __restrict__ out) {
+  const int row = blockIdx.x;
+  int owned = 0;
+  for (int r = threadIdx.x; r < n_req; r += 256) {
     const dg_split sp = splits[r];
-    owned = row >= sp.row0 && row < sp.row0 + sp.n_causal + sp.n_canvas;
+    owned |= (row >= sp.row0 && row < sp.row0 + sp.n_causal + sp.n_canvas) ? 1 : 0;
   }
-  if (!owned) return;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_part[s * static_cast<int64_t>(rows) * Hq + rh].x);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = ml_part[s * static_cast<int64_t>(rows) * Hq + rh];
-    if (ml.x == -INFINITY) continue;
-    const float w = exp2f(ml.x - M);
-    L += w * ml.y;
-    acc += w * o_part[(s * static_cast<int64_t>(rows) * Hq + rh) * D + threadIdx.x];
+  if (!__syncthreads_or(owned)) return;
+  const int64_t plane = static_cast<int64_t>(rows) * Hq;  // (row, head) pairs per split
+  for (int e = 4 * threadIdx.x; e < Hq * D; e += 4 * 256) {
+    const int h = e / D, d = e - h * D;
+    const int64_t rh = static_cast<int64_t>(row) * Hq + h;
+    float2 ml[kMergeSplits];
+    float4 ov[kMergeSplits];
+#pragma unroll
+    for (int s = 0; s < kMergeSplits; ++s) {
+      if (s < nsplit) {
+        ml[s] = ml_part[s * plane + rh];
+        ov[s] = *reinterpret_cast<const float4*>(o_part + (s * plane + rh) * D + d);
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMergeSplits; ++s)
+      if (s < nsplit) M = fmaxf(M, ml[s].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < kMergeSplits; ++s) {
+      if (s < nsplit && ml[s].x != -INFINITY) {
+        const float w = exp2f(ml[s].x - M);
+        L += w * ml[s].y;
+        acc.x += w * ov[s].x;
+        acc.y += w * ov[s].y;
+        acc.z += w * ov[s].z;
+        acc.w += w * ov[s].w;
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 wv;
+    wv.x = static_cast<uint32_t>(f32_to_bf16(acc.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+    wv.y = static_cast<uint32_t>(f32_to_bf16(acc.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(out + rh * D + d) = wv;
   }
-  out[rh * D + threadIdx.x] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 }  // namespace dg

@@ -93,4 +93,9 @@ DG_DEV void wave_argmax(float& v, int32_t& i) {
   }
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).  Used where direct global -> LDS copies issued from inline
+// asm must have landed: the compiler does not count those instructions.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 }  // namespace dg

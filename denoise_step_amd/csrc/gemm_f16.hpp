@@ -134,10 +134,6 @@ constexpr int gemm_dma_per_stage() {
   return (kGemmTM + TN) / 16 / kGemmWaves;
 }
 
-// s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
-// lgkmcnt 11:8 left at their maxima).
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // Wait until at most `pending` later stages of this wave's copies are still in flight, then
 // barrier.  A bare s_barrier is used instead of __syncthreads(): the latter's release fence would
 // wait for every outstanding copy, including the prefetched stages.  The empty asm statements keep

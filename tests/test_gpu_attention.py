@@ -65,3 +65,12 @@ def test_attention_tiny_loop_shapes_f32():
     """The tiny loop's launches: 32-row causal prefill, 16-row canvas over 32, 16-row commit pass."""
     for sp in ([(0, 32, 0)], [(32, 0, 16)], [(32, 16, 0)]):
         run_case(sp, 2, 2, 32, "f32", seed=11)
+
+
+@pytest.mark.parametrize("splits,Hq,Hkv,D", [
+    ([(3000, 300, 50)], 16, 8, 256),          # causal rows appended while the keys are split (6 splits)
+    ([(1500, 100, 20), (7, 9, 3)], 32, 8, 128),  # G = 4, 8 splits, a second short request
+])
+def test_attention_causal_rows_with_key_splits(splits, Hq, Hkv, D):
+    print(f"attention causal + splits {splits} {Hq}/{Hkv}/{D}", flush=True)
+    run_case(splits, Hq, Hkv, D, "bf16", seed=21)
