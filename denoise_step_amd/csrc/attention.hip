@@ -184,7 +184,7 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   // a split's page ids are staged in LDS: at most kAttMaxPages pages (16 keys each) per split
   nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys,
                                                                static_cast<int64_t>(kAttMaxPages - 8) * 16)));
-  nsplit = std::max(1, std::min({nsplit, 65535 / Hkv, kMergeSplits}));
+  nsplit = std::max(1, std::min(nsplit, kMergeSplits));
   p.split_keys = static_cast<int32_t>(cdiv(nblocks, nsplit)) * kAttKeys;
   p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));
   if (p.nsplit > 1) {
@@ -260,19 +260,24 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
     a.out = reinterpret_cast<uint16_t*>(out);
     a.o_part = reinterpret_cast<float*>(ws);
     a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
-    const dim3 grid(plan.qtiles, Hkv * plan.nsplit, n_req);
+    a.qtiles = plan.qtiles;
+    const int64_t items = static_cast<int64_t>(n_req) * plan.nsplit * Hkv * plan.qtiles;
+    DG_UNSUP(items <= (int64_t{1} << 30));
+    a.n_items = static_cast<int32_t>(items);
+    const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
     if (D == 256)
       attend_mfma_kernel<256><<<grid, kAttThreads, 0, s>>>(a);
     else
       attend_mfma_kernel<128><<<grid, kAttThreads, 0, s>>>(a);
     DG_LAUNCHED();
     if (plan.nsplit > 1) {
+      const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
       if (D == 256)
-        attend_merge_kernel<256><<<rows, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                      a.out);
+        attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                       a.out);
       else
-        attend_merge_kernel<128><<<rows, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                      a.out);
+        attend_merge_kernel<128><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
+                                                       a.out);
       DG_LAUNCHED();
     }
     return DG_OK;

@@ -6,8 +6,9 @@
 // every K/V tile.  Four wave64s own 32 packed rows each.
 //
 // K blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per lane,
-// no staging registers) into a chunk-major layout; V blocks go through registers, where each pair
-// of keys is transposed on its way into LDS.  Both are prefetched one block ahead.
+// no staging registers; each copy reads whole key rows) into an XOR-swizzled row-major layout; V
+// blocks go through registers (each lane loads 4 d of a key pair), where pairs of keys are
+// transposed on their way into LDS.  Both are prefetched one block ahead.
 //
 // Per 64-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q preloaded in registers): each lane then holds 16
@@ -64,6 +65,8 @@ struct AttArgs {
   float scale_log2;     // scale * log2(e)
   int32_t nsplit;       // KV splits
   int32_t split_keys;   // keys per split (multiple of kAttKeys)
+  int32_t qtiles;       // row tiles of kAttRows packed rows per request
+  int32_t n_items;      // n_req * nsplit * Hkv * qtiles work items
   uint16_t* out;        // [rows][Hq][D] bf16 (nsplit == 1)
   float* o_part;        // [nsplit][rows][Hq][D] (nsplit > 1)
   float2* ml_part;      // [nsplit][rows][Hq]    (nsplit > 1)
@@ -78,32 +81,48 @@ struct AttSmem {
   int32_t pages[kAttMaxPages];
 };
 
-// Registers holding one V block between its global loads and its LDS stores.
+// Registers holding one V block between its global loads and its LDS stores: item i of a lane is
+// 4 consecutive d (8 bytes) of both keys of a pair.
 template <int D>
 struct AttStage {
   static constexpr int kChunks = D / 8;
-  static constexpr int kV = (kAttKeys / 2) * kChunks / kAttThreads;  // V key-pair chunks per lane
-  uint4 v0[kV], v1[kV];
+  static constexpr int kV = (kAttKeys / 2) * kChunks * 2 / kAttThreads;  // items per lane
+  uint2 ev[kV], od[kV];
 };
 
-// K in LDS, chunk-major: chunk c (8 bf16) of key r of the block sits in 16-byte slot c * 64 + r.
-// An MFMA operand read has 16 consecutive keys ask for one chunk per 16-lane group: 16
-// consecutive slots, one 256-byte bank row, so the reads are conflict-free.
+// Item i of a lane: instruction group g = wave * kV + i covers pairs 8 (g % 4) .. + 7 and chunks
+// 4 (g / 4) .. + 3; within it lane l takes pair 8 (g % 4) + l % 8, chunk 4 (g / 4) + (l % 32) / 8
+// and the 4-d half l / 32 of that chunk.  A load instruction then reads 64 contiguous bytes of each
+// of 8 keys, and the transposed stores of the 64 lanes hit 64 distinct banks.
+struct AttVItem {
+  int pair, d0;
+};
 template <int D>
-DG_DEV int att_kslot(int r, int c) {
-  return c * kAttKeys + r;
+DG_DEV AttVItem att_vitem(int i) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = (threadIdx.x / kWave) * AttStage<D>::kV + i;
+  const int l = lane & 31;
+  return {8 * (g % 4) + (l % 8), 8 * (4 * (g / 4) + l / 8) + 4 * (lane >> 5)};
 }
 
-// Key kk of a request: prefix positions (kk < cached) come from the staged page ids (index and id
-// clamped, so a stale entry can only give a wrong key, never an out-of-range address); the causal
-// and canvas keys from rows row0 + kk - cached of k / v.  Both candidates are formed and one is
-// selected, so the address math has no branches.
+// K in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ (r & 15)).
+// An MFMA operand read has 16 consecutive keys ask for one chunk per 16-lane group: the XOR puts
+// them in 16 distinct slots of a 256-byte bank row, so the reads are conflict-free.
 template <int D>
-DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk,
-                               int kk, bool is_v) {
-  const int slot = min(max(kk / 16 - page_lo, 0), kAttMaxPages - 1);
-  const int64_t page = min(max(pages[slot], 0), a.n_pages - 1);
-  const int64_t cache_off = ((page * a.Hkv + hk) * 16 + (kk & 15)) * D;
+DG_DEV int att_kslot(int r, int c) {
+  return r * (D / 8) + (c ^ (r & 15));
+}
+
+// Key kk (kb <= kk < kb + 64) of a request: prefix positions (kk < cached) live in the page of
+// their 16-key group, whose id is one of the block's four staged ids `pq`; the causal and canvas
+// keys are rows row0 + kk - cached of k / v.  Both candidates are formed and one is selected, so
+// the address math has no branches and no memory access.
+template <int D>
+DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, int kb, int hk, int kk, bool is_v) {
+  const int g = (kk - kb) >> 4;
+  int page = g == 0 ? pq.x : (g == 1 ? pq.y : (g == 2 ? pq.z : pq.w));
+  page = min(max(page, 0), a.n_pages - 1);
+  const int64_t cache_off = ((static_cast<int64_t>(page) * a.Hkv + hk) * 16 + (kk & 15)) * D;
   const int64_t row = sp.row0 + max(kk - sp.cached, 0);
   const int64_t new_off = (row * a.Hkv + hk) * D;
   const uint16_t* cache = is_v ? a.v_cache : a.k_cache;
@@ -114,40 +133,47 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, const int32
 // Keys at or past k_end (the split's last visible key + 1) are masked for every row of the tile:
 // they re-read the last visible key (whose page is staged) and their V chunks are zeroed.
 //
-// K: copy c fills chunk plane c of the block, one key per lane, so each lane forms one address per
-// block and its copies differ only by the chunk offset.
+// K: copy q fills slots 64 q .. 64 q + 63, i.e. the 64 / (D / 8) keys q * 64 / (D / 8) ...; lane l
+// fetches chunk (l % (D / 8)) ^ (r & 15) of its key r, so each copy reads whole key rows.
 template <int D>
 DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
                      int k_end, uint16_t* kdst, AttStage<D>& st) {
   constexpr int kChunks = D / 8;
-  constexpr int kPerWave = kChunks / (kAttThreads / kWave);  // chunk planes copied by each wave
+  constexpr int kKeysPerCopy = kWave / kChunks;
+  constexpr int kPerWave = kChunks / (kAttThreads / kWave);  // copies issued by each wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: M0 is scalar
-  const uint16_t* krow = att_row<D>(a, sp, pages, page_lo, hk, min(kb + lane, k_end - 1), false);
+  // the page ids of the block's four 16-key groups in one 16-byte read (kb - k_begin is a multiple
+  // of 64, so the slot is 4-aligned; slots past the staged range are only picked by keys >= cached)
+  const int4 pq = *reinterpret_cast<const int4*>(pages + (kb / 16 - page_lo));
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
-    const int c = wave * kPerWave + i;
-    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kAttKeys * 8 * c));
+    const int q = wave * kPerWave + i;
+    const int r = q * kKeysPerCopy + lane / kChunks;
+    const int c = (lane % kChunks) ^ (r & 15);
+    const uint16_t* src = att_row<D>(a, sp, pq, kb, hk, min(kb + r, k_end - 1), false) + 8 * c;
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "global_load_lds_dwordx4 %1, off"
         :
-        : "s"(lds_addr), "v"(krow + 8 * c)
+        : "s"(lds_addr), "v"(src)
         : "memory", "m0");
   }
-  // V: lane pair p = tid % 32 carries keys 2 p and 2 p + 1, chunks tid / 32 + 8 i
-  const int kk0 = kb + 2 * (threadIdx.x % (kAttKeys / 2));
-  const uint16_t* v0row = att_row<D>(a, sp, pages, page_lo, hk, min(kk0, k_end - 1), true);
-  const uint16_t* v1row = att_row<D>(a, sp, pages, page_lo, hk, min(kk0 + 1, k_end - 1), true);
-  const bool ok0 = kk0 < k_end, ok1 = kk0 + 1 < k_end;
 #pragma unroll
   for (int i = 0; i < AttStage<D>::kV; ++i) {
-    const int c = threadIdx.x / (kAttKeys / 2) + (kAttThreads / (kAttKeys / 2)) * i;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(v0row + 8 * c);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(v1row + 8 * c);
-    st.v0[i] = ok0 ? x0 : make_uint4(0, 0, 0, 0);
-    st.v1[i] = ok1 ? x1 : make_uint4(0, 0, 0, 0);
+    const AttVItem it = att_vitem<D>(i);
+    const int kk0 = kb + 2 * it.pair;
+    const uint16_t* e = att_row<D>(a, sp, pq, kb, hk, min(kk0, k_end - 1), true) + it.d0;
+    const uint16_t* o = att_row<D>(a, sp, pq, kb, hk, min(kk0 + 1, k_end - 1), true) + it.d0;
+    const uint2 xe = *reinterpret_cast<const uint2*>(e);
+    const uint2 xo = *reinterpret_cast<const uint2*>(o);
+    st.ev[i] = kk0 < k_end ? xe : make_uint2(0, 0);
+    st.od[i] = kk0 + 1 < k_end ? xo : make_uint2(0, 0);
   }
+  // keep the V loads here, ahead of the block's MFMA work: without this the compiler sinks them
+  // to their use in att_store and the load latency is no longer hidden behind the compute
+  asm volatile("" ::: "memory");
 }
 
 // Stores the V block (transposed) and waits for every outstanding copy, so that after the next
@@ -156,17 +182,16 @@ template <int D>
 DG_DEV void att_store(AttSmem<D>& sm, int buf, const AttStage<D>& st) {
 #pragma unroll
   for (int i = 0; i < AttStage<D>::kV; ++i) {
-    const int u = threadIdx.x + i * kAttThreads;
-    const int pair = u % (kAttKeys / 2), c = u / (kAttKeys / 2);
-    const uint32_t w0[4] = {st.v0[i].x, st.v0[i].y, st.v0[i].z, st.v0[i].w};
-    const uint32_t w1[4] = {st.v1[i].x, st.v1[i].y, st.v1[i].z, st.v1[i].w};
+    const AttVItem it = att_vitem<D>(i);
+    const uint32_t e[2] = {st.ev[i].x, st.ev[i].y};
+    const uint32_t o[2] = {st.od[i].x, st.od[i].y};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // d = 8c + 2t (low halves) and 8c + 2t + 1 (high halves); keys 2 pair, 2 pair + 1
-      const uint32_t lo = (w0[t] & 0xFFFFu) | (w1[t] << 16);
-      const uint32_t hi = (w0[t] >> 16) | (w1[t] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(8 * c + 2 * t) * AttSmem<D>::vPitch + 2 * pair]) = lo;
-      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(8 * c + 2 * t + 1) * AttSmem<D>::vPitch + 2 * pair]) = hi;
+    for (int t = 0; t < 2; ++t) {
+      // d = d0 + 2t (low halves) and d0 + 2t + 1 (high halves); keys 2 pair (low), 2 pair + 1 (high)
+      const uint32_t lo = (e[t] & 0xFFFFu) | (o[t] << 16);
+      const uint32_t hi = (e[t] >> 16) | (o[t] & 0xFFFF0000u);
+      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(it.d0 + 2 * t) * AttSmem<D>::vPitch + 2 * it.pair]) = lo;
+      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(it.d0 + 2 * t + 1) * AttSmem<D>::vPitch + 2 * it.pair]) = hi;
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
@@ -199,11 +224,18 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
   __shared__ __attribute__((aligned(16))) AttSmem<D> sm;
 
-  const dg_split sp = a.splits[blockIdx.z];
-  const int hk = blockIdx.y % a.Hkv;
-  const int split = blockIdx.y / a.Hkv;
+  // XCD-aware order: the hardware deals workgroup L to XCD L % 8; work item t = (L % 8) * per_xcd +
+  // L / 8, t = ((req * nsplit + split) * Hkv + hk) * qtiles + qtile, so the row tiles that read the
+  // same K/V (same request, KV head and split) run on one XCD and share its L2.
+  const int per_xcd = (a.n_items + 7) / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= a.n_items) return;
+  const int qtile = t % a.qtiles;
+  const int hk = (t / a.qtiles) % a.Hkv;
+  const int split = (t / (a.qtiles * a.Hkv)) % a.nsplit;
+  const dg_split sp = a.splits[t / (a.qtiles * a.Hkv * a.nsplit)];
   const int nr = sp.n_causal + sp.n_canvas;
-  const int m_tile0 = blockIdx.x * kAttRows;
+  const int m_tile0 = qtile * kAttRows;
   if (m_tile0 >= nr * a.G) return;
   const int n_total = sp.cached + nr;
   // last visible key + 1 over the tile's rows (rows are ordered causal then canvas)
@@ -372,9 +404,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   }
 }
 
-// Combine KV splits: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  One
-// workgroup per packed row, four consecutive d per thread, every split's loads issued before the
-// sums.  Rows outside every request's range were never written and are skipped.
+// Combine KV splits: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  Grid
+// (packed row, 1024-value slice of the row's Hq x D outputs); four consecutive d per thread, every
+// split's loads issued before the sums.  Rows outside every request's range were never written and
+// are skipped.
 constexpr int kMergeSplits = 16;  // the most splits a launch uses
 
 template <int D>
@@ -391,7 +424,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restri
   }
   if (!__syncthreads_or(owned)) return;
   const int64_t plane = static_cast<int64_t>(rows) * Hq;  // (row, head) pairs per split
-  for (int e = 4 * threadIdx.x; e < Hq * D; e += 4 * 256) {
+  const int e = blockIdx.y * 1024 + 4 * threadIdx.x;
+  if (e < Hq * D) {
     const int h = e / D, d = e - h * D;
     const int64_t rh = static_cast<int64_t>(row) * Hq + h;
     float2 ml[kMergeSplits];
