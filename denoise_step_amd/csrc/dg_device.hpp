@@ -93,6 +93,70 @@ DG_DEV void wave_argmax(float& v, int32_t& i) {
   }
 }
 
+// ---------------------------------------------------------------- DPP wave reductions
+// Reductions over the 64 lanes by DPP moves (no LDS traffic): inside each row of 16 lanes by
+// quad permutations and mirrors, then across rows by row broadcasts into lane 63, whose value is
+// returned to every lane.  The order of the operations is fixed, so sums are deterministic.
+namespace dpp {
+constexpr int kXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7 - i inside each 8
+constexpr int kMirror = 0x140;      // lane i <-> 15 - i inside each 16
+constexpr int kBcast15 = 0x142;     // lane 15 of row r -> row r + 1 (applied to rows 1 and 3)
+constexpr int kBcast31 = 0x143;     // lane 31 -> rows 2 and 3 (applied to rows 2 and 3)
+}  // namespace dpp
+
+// value of the DPP source lane; lanes the move does not write get `fill`
+template <int CTRL, int ROW_MASK>
+DG_DEV float dpp_f(float v, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+DG_DEV int32_t dpp_i(int32_t v, int32_t fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROW_MASK, 0xF, false);
+}
+DG_DEV float lane63_f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+
+DG_DEV float dpp_wave_max(float v) {
+  v = fmaxf(v, dpp_f<dpp::kXor1, 0xF>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<dpp::kXor2, 0xF>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<dpp::kHalfMirror, 0xF>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<dpp::kMirror, 0xF>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<dpp::kBcast15, 0xA>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<dpp::kBcast31, 0xC>(v, -INFINITY));
+  return lane63_f(v);
+}
+
+DG_DEV float dpp_wave_sum(float v) {
+  v += dpp_f<dpp::kXor1, 0xF>(v, 0.f);
+  v += dpp_f<dpp::kXor2, 0xF>(v, 0.f);
+  v += dpp_f<dpp::kHalfMirror, 0xF>(v, 0.f);
+  v += dpp_f<dpp::kMirror, 0xF>(v, 0.f);
+  v += dpp_f<dpp::kBcast15, 0xA>(v, 0.f);
+  v += dpp_f<dpp::kBcast31, 0xC>(v, 0.f);
+  return lane63_f(v);
+}
+
+// (value, index) maximum with lowest-index tie-break; the result is returned to every lane
+template <int CTRL, int ROW_MASK>
+DG_DEV void dpp_argmax_step(float& v, int32_t& i) {
+  const float v2 = dpp_f<CTRL, ROW_MASK>(v, -INFINITY);
+  const int32_t i2 = dpp_i<CTRL, ROW_MASK>(i, 0x7FFFFFFF);
+  const bool better = v2 > v || (v2 == v && i2 < i);
+  v = better ? v2 : v;
+  i = better ? i2 : i;
+}
+DG_DEV void dpp_wave_argmax(float& v, int32_t& i) {
+  dpp_argmax_step<dpp::kXor1, 0xF>(v, i);
+  dpp_argmax_step<dpp::kXor2, 0xF>(v, i);
+  dpp_argmax_step<dpp::kHalfMirror, 0xF>(v, i);
+  dpp_argmax_step<dpp::kMirror, 0xF>(v, i);
+  dpp_argmax_step<dpp::kBcast15, 0xA>(v, i);
+  dpp_argmax_step<dpp::kBcast31, 0xC>(v, i);
+  v = lane63_f(v);
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
 // s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
 // lgkmcnt 11:8 left at their maxima).  Used where direct global -> LDS copies issued from inline
 // asm must have landed: the compiler does not count those instructions.

@@ -11,10 +11,17 @@ design notes).
 Keying
   key     = (seed & 0xffffffff, seed >> 32)           -- one 64-bit seed per request
   counter = (c0, pos, step, stream)
-      stream GUMBEL  = 0 : c0 = i >> 2, vocabulary element i uses word i & 3
-      stream RENOISE = 1 : c0 = 0, word 0
-      stream INIT    = 2 : c0 = 0, word 0
+      stream GUMBEL       = 0 : one word per block of 16 vocabulary ids (the block level of the
+                                 two-level Gumbel-max draw): block b uses word (b >> 7) & 3 of
+                                 counter c0 = 128 * (b >> 9) + (b & 127)
+      stream RENOISE      = 1 : c0 = 0, word 0
+      stream INIT         = 2 : c0 = 0, word 0
+      stream GUMBEL_INNER = 3 : element level, inside the winning block: vocabulary element i
+                                 uses word i & 3 of counter c0 = i >> 2
   step is the request's global step counter, never reset between blocks.
+  The block map (b -> c0, word) is a bijection: the four blocks p, p + 128, p + 256, p + 384 of
+  each run of 512 blocks share one counter, so one Philox call serves four blocks that lie 128
+  blocks apart (the GPU pass gives them to one lane).
 
 Mappings
   uniform(w) = (2 * (w >> 9) + 1) * 2**-24         in (0, 1); exact in fp32
@@ -38,6 +45,8 @@ MASK32 = np.uint64(0xFFFFFFFF)
 GUMBEL = 0
 RENOISE = 1
 INIT = 2
+GUMBEL_INNER = 3
+GUMBEL_BLOCK = 16   # vocabulary ids per block of the two-level Gumbel-max draw
 
 
 def philox4x32_10(ctr, key):
@@ -90,16 +99,33 @@ def token_from_word(w, V: int) -> np.ndarray:
     return ((np.asarray(w, dtype=np.uint64) * np.uint64(V)) >> np.uint64(32)).astype(np.int64)
 
 
-def gumbel_row(seed: int, pos: int, step: int, V: int) -> np.ndarray:
-    """Gumbel noise g_i, i = 0..V-1, for one canvas position (stream GUMBEL)."""
-    n = (V + 3) // 4
-    ctr = np.zeros((n, 4), np.uint32)
-    ctr[:, 0] = np.arange(n, dtype=np.uint32)
-    ctr[:, 1] = np.uint32(pos)
-    ctr[:, 2] = np.uint32(step & 0xFFFFFFFF)
-    ctr[:, 3] = np.uint32(GUMBEL)
-    words = philox4x32_10(ctr, seed_key(seed)).reshape(-1)[:V]
-    return gumbel_from_word(words)
+def _words(seed: int, pos: int, step: int, c0, word, stream: int) -> np.ndarray:
+    c0 = np.asarray(c0, dtype=np.int64)
+    ctr = np.zeros(c0.shape + (4,), np.uint32)
+    ctr[..., 0] = c0.astype(np.uint32)
+    ctr[..., 1] = np.uint32(pos)
+    ctr[..., 2] = np.uint32(step & 0xFFFFFFFF)
+    ctr[..., 3] = np.uint32(stream)
+    out = philox4x32_10(ctr, seed_key(seed))
+    return np.take_along_axis(out, np.asarray(word, np.int64)[..., None], axis=-1)[..., 0]
+
+
+def block_counter_word(b):
+    """(c0, word) of block b in stream GUMBEL."""
+    b = np.asarray(b, dtype=np.int64)
+    return 128 * (b >> 9) + (b & 127), (b >> 7) & 3
+
+
+def block_gumbels(seed: int, pos: int, step: int, nblocks: int) -> np.ndarray:
+    """Gumbel noise G_b, b = 0..nblocks-1, of the blocks of one canvas position (stream GUMBEL)."""
+    c0, w = block_counter_word(np.arange(nblocks))
+    return gumbel_from_word(_words(seed, pos, step, c0, w, GUMBEL))
+
+
+def inner_gumbels(seed: int, pos: int, step: int, lo: int, hi: int) -> np.ndarray:
+    """Gumbel noise g_i, i = lo..hi-1, of vocabulary elements (stream GUMBEL_INNER)."""
+    i = np.arange(lo, hi, dtype=np.int64)
+    return gumbel_from_word(_words(seed, pos, step, i >> 2, i & 3, GUMBEL_INNER))
 
 
 def random_tokens(seed: int, step: int, positions, V: int, stream: int) -> np.ndarray:

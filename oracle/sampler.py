@@ -7,13 +7,25 @@ first dLLM natively supported by vLLM"):
     predicted distribution;
   * section "DiffusionGemmaModelState and DiffusionSampler", denoise case:
     logits are divided by the temperature T and a candidate is drawn with the
-    Gumbel-max trick, argmax(logits / T + g); the argmax canvas is recorded.
+    Gumbel-max trick; the argmax canvas is recorded.
 
 Readings (the pages are silent): natural log (nats); H clamped at 0; argmax
 and sample ties go to the lowest vocabulary index; the Gumbel noise is the
-Philox stream of ``oracle.philox``.  Also returned: m = max_i x_i and
+Philox streams of ``oracle.philox``.  Also returned: m = max_i x_i and
 ln Z = ln sum_i exp(x_i - m), which define p_i = exp(x_i - m - ln Z) for the
 self-conditioning step.
+
+The Gumbel-max candidate is drawn in two levels over blocks of 16 consecutive
+vocabulary ids (the last block of a row may be shorter):
+  1. block b has log-mass L_b = ln sum_{i in b} exp(x_i) and noise G_b; the
+     winning block is b* = argmax_b (L_b + G_b);
+  2. inside b*, the candidate is argmax_{i in b*} (x_i + g_i) with fresh noise g.
+The maximum of Gumbel-perturbed values over a set is itself Gumbel-distributed
+with location the set's log-mass, and its argmax is independent of that
+maximum, so b* is drawn with probability Z_b / Z and the candidate with
+probability exp(x_i) / Z overall: the same law as the flat argmax_i (x_i + g_i)
+over the row, with one noise value per 16 ids at the first level.  A row of at
+most 16 ids is a single block, where the draw is the flat Gumbel-max.
 
 Pinned by tests/test_oracle_sampler.py: entropy closed forms (uniform row ->
 ln V, one-hot -> 0, two-point, k equal maxima -> ln k), shift invariance,
@@ -70,6 +82,27 @@ def _top2_gap(v: np.ndarray) -> float:
     return float(v[i] - np.max(rest))
 
 
+def gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int):
+    """Two-level Gumbel-max candidate for one row of scaled logits x (fp64).
+
+    Returns (candidate id, key gap): the gap is the smaller of the top-2 gaps of
+    the block keys and of the keys inside the winning block (near-tie accounting).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    V = x.size
+    nb = (V + philox.GUMBEL_BLOCK - 1) // philox.GUMBEL_BLOCK
+    xb = np.full(nb * philox.GUMBEL_BLOCK, -np.inf)
+    xb[:V] = x
+    xb = xb.reshape(nb, philox.GUMBEL_BLOCK)
+    mb = np.max(xb, axis=1)
+    log_mass = mb + np.log(np.sum(np.exp(xb - mb[:, None]), axis=1))
+    bkey = log_mass + philox.block_gumbels(seed, pos, step, nb)
+    b = int(np.argmax(bkey))
+    lo, hi = b * philox.GUMBEL_BLOCK, min((b + 1) * philox.GUMBEL_BLOCK, V)
+    ikey = x[lo:hi] + philox.inner_gumbels(seed, pos, step, lo, hi)
+    return lo + int(np.argmax(ikey)), min(_top2_gap(bkey), _top2_gap(ikey))
+
+
 def denoise_sample(logits: np.ndarray, temperature: float, seeds, steps, rows_per_req: int,
                    argmax_only: bool = False, active=None) -> SampleOut:
     """Sampler over logit rows.
@@ -99,10 +132,7 @@ def denoise_sample(logits: np.ndarray, temperature: float, seeds, steps, rows_pe
         out.entropy[r] = H
         out.row_max[r] = m
         out.row_lnz[r] = np.log(Z)
-        g = philox.gumbel_row(int(seeds[req]), pos, int(steps[req]), V)
-        key = x + g
-        out.sample[r] = int(np.argmax(key))
-        out.key_gap[r] = _top2_gap(key)
+        out.sample[r], out.key_gap[r] = gumbel_candidate(x, int(seeds[req]), pos, int(steps[req]))
     return out
 
 

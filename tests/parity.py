@@ -115,15 +115,12 @@ def zipf_bf16(seed, tag, rows, V):
 
 def sampler_oracle_row(row, seed, pos, step):
     """Oracle for one row at canvas position `pos` (a request of pos + 1 rows whose last row is this one)."""
-    from oracle import philox
     from oracle import sampler as _osamp
     x = np.asarray(row, np.float64)
     m, Z, S, H = _osamp.softmax_stats(x)
-    g = philox.gumbel_row(seed, pos, step, x.size)
-    key = x + g
+    cand, key_gap = _osamp.gumbel_candidate(x, seed, pos, step)
     srt = np.sort(x)
-    ks = np.sort(key)
     return _osamp.SampleOut(entropy=np.array([H]), argmax=np.array([int(np.argmax(x))]),
-                           sample=np.array([int(np.argmax(key))]), row_max=np.array([m]),
+                           sample=np.array([cand]), row_max=np.array([m]),
                            row_lnz=np.array([np.log(Z)]), argmax_gap=np.array([srt[-1] - srt[-2]]),
-                           key_gap=np.array([ks[-1] - ks[-2]]))
+                           key_gap=np.array([key_gap]))

@@ -72,6 +72,7 @@ def test_argmax_is_first_occurrence_like_numpy():
 
 
 def test_gumbel_max_follows_softmax():
+    """One block (V <= 16): the flat Gumbel-max law."""
     V, n = 8, 20000
     logits = np.array([0.0, 1.0, -1.0, 2.0, 0.5, -2.0, 1.5, 0.0])
     rows = np.tile(logits, (n, 1))
@@ -82,6 +83,58 @@ def test_gumbel_max_follows_softmax():
     # temperature sharpens
     o2 = sampler.denoise_sample(rows, 0.25, [2024], [11], n)
     assert np.bincount(o2.sample, minlength=V)[3] > counts[3]
+
+
+def test_single_block_is_flat_gumbel_max():
+    from oracle import philox
+    rng = np.random.default_rng(7)
+    for V in (1, 5, 12, 16):
+        x = rng.normal(0, 2, V)
+        for pos in range(20):
+            cand, _ = sampler.gumbel_candidate(x, 99, pos, 4)
+            assert cand == int(np.argmax(x + philox.inner_gumbels(99, pos, 4, 0, V)))
+
+
+def test_two_level_draw_follows_softmax_across_blocks():
+    """Three blocks with a short last one (16 + 16 + 8 ids): the candidate law is softmax(x)."""
+    V, n = 40, 20000
+    logits = np.random.default_rng(8).normal(0, 1.0, V)
+    logits[3] += 2.0
+    logits[35] += 2.5                                   # mass in the short block too
+    rows = np.tile(logits, (n, 1))
+    o = sampler.denoise_sample(rows, 1.0, [77], [5], n)
+    counts = np.bincount(o.sample, minlength=V)
+    p = sampler.probabilities(logits, 1.0)
+    keep = p * n >= 5                                   # chi-square cells with enough expectation
+    obs, exp = counts[keep], p[keep] * n
+    if not keep.all():
+        obs, exp = np.append(obs, counts[~keep].sum()), np.append(exp, p[~keep].sum() * n)
+    assert stats.chisquare(obs, exp).pvalue > 1e-4
+
+
+def test_winning_block_law_is_block_mass():
+    """64 blocks of a ramp: the block of the candidate is drawn with probability Z_b / Z."""
+    V, n = 1024, 6000
+    logits = np.linspace(-1.5, 1.5, V)
+    rows = np.tile(logits, (n, 1))
+    o = sampler.denoise_sample(rows, 1.0, [3], [9], n)
+    blocks = np.bincount(o.sample // 16, minlength=64)
+    pb = sampler.probabilities(logits, 1.0).reshape(64, 16).sum(axis=1)
+    assert stats.chisquare(blocks, pb * n).pvalue > 1e-4
+
+
+def test_block_noise_map_is_a_bijection():
+    from oracle import philox
+    b = np.arange(1 << 14)
+    c0, w = philox.block_counter_word(b)
+    assert len(set(zip(c0.tolist(), w.tolist()))) == b.size
+    assert np.all((w >= 0) & (w < 4))
+    # blocks p, p + 128, p + 256, p + 384 of each run of 512 share one counter, words 0..3
+    for S in (0, 3):
+        for p in (0, 77, 127):
+            bb = 512 * S + p + 128 * np.arange(4)
+            cc, ww = philox.block_counter_word(bb)
+            assert np.all(cc == cc[0]) and np.array_equal(ww, np.arange(4))
 
 
 def test_samples_depend_on_seed_step_position_only():
