@@ -60,12 +60,10 @@ __global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16
 template <bool BF16>
 __global__ __launch_bounds__(256) void probs_f16_kernel(const void* __restrict__ logits, int64_t ld, int32_t V,
                                                         int64_t Kp, int64_t Mp, int32_t rows, float inv_t,
-                                                        const float* __restrict__ row_max, _Float16* __restrict__ w,
-                                                        uint32_t* __restrict__ row_amax) {
+                                                        const float* __restrict__ row_max, _Float16* __restrict__ w) {
   const int r = blockIdx.y * 8 + (threadIdx.x >> 5);
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + (threadIdx.x & 31) * 8;
   if (r >= rows || i0 >= Kp) return;
-  if (i0 == 0) row_amax[r] = 0u;  // consumed by the P.E reduce, which runs after the GEMM
   const float m = row_max[r];
   float l[8];
   if constexpr (BF16) {
@@ -99,49 +97,70 @@ DG_DEV float row_pow2_scale(float amax) {
   return ldexpf(1.f, 14 - e);
 }
 
+// Largest value over the 256 threads of the workgroup (DPP inside each wave, 4 waves via LDS).
 DG_DEV float block_max_256(float v, float* red) {
-  v = wave_max(v);
+  v = dpp_wave_max(v);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return v;
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Split-K reduce of the P.E partials: one thread per (row, column), 256 columns per workgroup:
-// s = sum_split part * 2^-15 / Z -> s32 (and s_out); the row's largest |s| is folded into
-// row_amax[r] with an atomic max on the (non-negative) fp32 bit pattern.
+DG_DEV float4 f4_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+DG_DEV float f4_amax(float4 a) { return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))); }
+
+// four consecutive columns n .. n + 3 (n % 4 == 0) of row r stored as fp16 in the K-blocked layout
+// (they are contiguous there: one 8-byte store)
+DG_DEV void store4_f16(_Float16* dst, int r, int n, int64_t Mp, float4 v, float sc) {
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  half4 h;
+  h[0] = static_cast<_Float16>(v.x * sc);
+  h[1] = static_cast<_Float16>(v.y * sc);
+  h[2] = static_cast<_Float16>(v.z * sc);
+  h[3] = static_cast<_Float16>(v.w * sc);
+  *reinterpret_cast<half4*>(dst + kblk_index(r, n, Mp)) = h;
+}
+
+// Split-K reduce of the P.E partials, one workgroup per row, each thread C groups of 4 columns:
+// s = sum_split part * 2^-15 / Z (-> s_out when requested), then s16 = fp16(s * scale_r) in the
+// K-blocked layout with scale_r the power of two that brings the row's largest |s| into
+// (2^13, 2^14], and s_inv[r] = 1 / scale_r.  The split loads are issued four splits at a time.
+template <int C>
 __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                        int32_t N, const float* __restrict__ row_lnz,
-                                                        float* __restrict__ s32, float* __restrict__ s_out,
-                                                        uint32_t* __restrict__ row_amax) {
+                                                        int32_t N, int64_t Mp, const float* __restrict__ row_lnz,
+                                                        float* __restrict__ s_out, _Float16* __restrict__ s16,
+                                                        float* __restrict__ s_inv) {
   __shared__ float red[4];
-  const int r = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int r = blockIdx.x;
   const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
-  const int64_t idx = static_cast<int64_t>(r) * N + n;
-  float v = 0.f;
-  if (n < N) {
-    float acc = 0.f;
-    for (int k = 0; k < splits; ++k) acc += part[static_cast<int64_t>(k) * M * N + idx];
-    v = acc * f;
-    s32[idx] = v;
-    if (s_out != nullptr) s_out[idx] = v;
+  float4 acc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < splits; ++k) {
+    const float* p = part + (static_cast<int64_t>(k) * M + r) * N;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int n = 4 * (threadIdx.x + 256 * c);
+      if (n < N) acc[c] = f4_add(acc[c], *reinterpret_cast<const float4*>(p + n));
+    }
   }
-  const float amax = block_max_256(fabsf(v), red);
-  if (threadIdx.x == 0) atomicMax(row_amax + r, __float_as_uint(amax));
-}
-
-// s16 = fp16(s * scale_r) in the K-blocked layout, scale_r the power of two that brings the row's
-// largest |s| into (2^13, 2^14]; inv_scale[r] = 1 / scale_r.
-__global__ __launch_bounds__(256) void pe_to_f16_kernel(const float* __restrict__ s32, int32_t N, int64_t Mp,
-                                                        const uint32_t* __restrict__ row_amax,
-                                                        _Float16* __restrict__ s16, float* __restrict__ inv_scale) {
-  const int r = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const float sc = row_pow2_scale(__uint_as_float(row_amax[r]));
-  if (n < N) s16[kblk_index(r, n, Mp)] = static_cast<_Float16>(s32[static_cast<int64_t>(r) * N + n] * sc);
-  if (n == 0) inv_scale[r] = 1.f / sc;
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    acc[c] = make_float4(acc[c].x * f, acc[c].y * f, acc[c].z * f, acc[c].w * f);
+    const int n = 4 * (threadIdx.x + 256 * c);
+    if (n < N) {
+      amax = fmaxf(amax, f4_amax(acc[c]));
+      if (s_out != nullptr) *reinterpret_cast<float4*>(s_out + static_cast<int64_t>(r) * N + n) = acc[c];
+    }
+  }
+  const float sc = row_pow2_scale(block_max_256(amax, red));
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int n = 4 * (threadIdx.x + 256 * c);
+    if (n < N) store4_f16(s16, r, n, Mp, acc[c], sc);
+  }
+  if (threadIdx.x == 0) s_inv[r] = 1.f / sc;
 }
 
 DG_DEV float gelu_tanh(float z) {
@@ -150,34 +169,49 @@ DG_DEV float gelu_tanh(float z) {
 }
 
 // One workgroup per row: h = gelu_tanh(gate) * up from the partials of the [gate | up] GEMM (whose
-// input row was scaled by 1 / s_inv[r]), then h16 = fp16(h * scale_r), h_inv[r] = 1 / scale_r.
+// input row was scaled by 1 / s_inv[r]), then h16 = fp16(h * scale_r) in the K-blocked layout,
+// h_inv[r] = 1 / scale_r.  Each thread owns C groups of 4 hidden units.
+template <int C>
 __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                          int32_t H, int64_t Mp, const float* __restrict__ s_inv,
-                                                         float* __restrict__ h32, _Float16* __restrict__ h16,
-                                                         float* __restrict__ h_inv) {
+                                                         _Float16* __restrict__ h16, float* __restrict__ h_inv) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   const int64_t N2 = 2 * static_cast<int64_t>(H);
-  const float si = s_inv[r];
-  const int64_t base = static_cast<int64_t>(r) * H;
-  float amax = 0.f;
-  for (int j = threadIdx.x; j < H; j += 256) {
-    float gsum = 0.f, usum = 0.f;
-    for (int k = 0; k < splits; ++k) {
-      const float* p = part + static_cast<int64_t>(k) * M * N2 + r * N2;
-      gsum += p[j];
-      usum += p[H + j];
+  float4 g[C], u[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) g[c] = u[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < splits; ++k) {
+    const float* p = part + (static_cast<int64_t>(k) * M + r) * N2;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = 4 * (threadIdx.x + 256 * c);
+      if (j < H) {
+        g[c] = f4_add(g[c], *reinterpret_cast<const float4*>(p + j));
+        u[c] = f4_add(u[c], *reinterpret_cast<const float4*>(p + H + j));
+      }
     }
-    const float h = gelu_tanh(gsum * si) * (usum * si);
-    h32[base + j] = h;
-    amax = fmaxf(amax, fabsf(h));
+  }
+  const float si = s_inv[r];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    g[c] = make_float4(gelu_tanh(g[c].x * si) * (u[c].x * si), gelu_tanh(g[c].y * si) * (u[c].y * si),
+                       gelu_tanh(g[c].z * si) * (u[c].z * si), gelu_tanh(g[c].w * si) * (u[c].w * si));
+    if (4 * (threadIdx.x + 256 * c) < H) amax = fmaxf(amax, f4_amax(g[c]));
   }
   const float sc = row_pow2_scale(block_max_256(amax, red));
-  for (int j = threadIdx.x; j < H; j += 256) h16[kblk_index(r, j, Mp)] = static_cast<_Float16>(h32[base + j] * sc);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = 4 * (threadIdx.x + 256 * c);
+    if (j < H) store4_f16(h16, r, j, Mp, g[c], sc);
+  }
   if (threadIdx.x == 0) h_inv[r] = 1.f / sc;
 }
 
-// x_out = bf16(E[canvas] + (sc_on ? y : 0)), y from the partials of the down GEMM
+// x_out = bf16(E[canvas] + (sc_on ? y : 0)), y from the partials of the down GEMM; one thread per
+// 4 consecutive values of a row
 __global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                            int32_t d, int32_t V, int32_t C,
                                                            const uint16_t* __restrict__ E,
@@ -185,20 +219,25 @@ __global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restri
                                                            const uint8_t* __restrict__ sc_on,
                                                            const float* __restrict__ h_inv,
                                                            uint16_t* __restrict__ x_out, float* __restrict__ y_out) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t idx = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
   if (idx >= static_cast<int64_t>(M) * d) return;
   const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
   const int64_t tok = min(max(canvas[r], 0), V - 1);
-  float x = bf16_to_f32(E[tok * d + c]);
+  const uint2 e = *reinterpret_cast<const uint2*>(E + tok * d + c);
+  float4 x = make_float4(bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y));
   const bool on = sc_on[r / C] != 0;
   if (on || y_out != nullptr) {
-    float y = 0.f;
-    for (int k = 0; k < splits; ++k) y += part[static_cast<int64_t>(k) * M * d + idx];
-    y *= h_inv[r];
-    if (on) x += y;
-    if (y_out != nullptr) y_out[idx] = y;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int k = 0; k < splits; ++k) y = f4_add(y, *reinterpret_cast<const float4*>(part + static_cast<int64_t>(k) * M * d + idx));
+    const float hi = h_inv[r];
+    y = make_float4(y.x * hi, y.y * hi, y.z * hi, y.w * hi);
+    if (on) x = f4_add(x, y);
+    if (y_out != nullptr) *reinterpret_cast<float4*>(y_out + idx) = y;
   }
-  x_out[idx] = f32_to_bf16(x);
+  const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(x.x)) | (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
+  const uint32_t hi2 = static_cast<uint32_t>(f32_to_bf16(x.z)) | (static_cast<uint32_t>(f32_to_bf16(x.w)) << 16);
+  *reinterpret_cast<uint2*>(x_out + idx) = make_uint2(lo, hi2);
 }
 
 // ---------------------------------------------------------------- fp32 path kernels
@@ -249,7 +288,7 @@ PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
 struct Bf16Plan {
   int64_t Kp, Mp;
   GemmPlan pe, g1, g2;
-  size_t off_w, off_part, off_s16, off_h16, off_s32, off_h32, off_sinv, off_hinv, off_amax, bytes;
+  size_t off_w, off_part, off_s16, off_h16, off_sinv, off_hinv, bytes;
 };
 
 Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
@@ -269,12 +308,9 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   p.off_part = round_up(p.off_w + static_cast<size_t>(rows_p) * p.Kp * 2, 256);
   p.off_s16 = round_up(p.off_part + part, 256);
   p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows_p) * d * 2, 256);
-  p.off_s32 = round_up(p.off_h16 + static_cast<size_t>(rows_p) * hidden * 2, 256);
-  p.off_h32 = round_up(p.off_s32 + static_cast<size_t>(rows) * d * 4, 256);
-  p.off_sinv = round_up(p.off_h32 + static_cast<size_t>(rows) * hidden * 4, 256);
+  p.off_sinv = round_up(p.off_h16 + static_cast<size_t>(rows_p) * hidden * 2, 256);
   p.off_hinv = round_up(p.off_sinv + static_cast<size_t>(rows) * 4, 256);
-  p.off_amax = round_up(p.off_hinv + static_cast<size_t>(rows) * 4, 256);
-  p.bytes = round_up(p.off_amax + static_cast<size_t>(rows) * 4, 256);
+  p.bytes = round_up(p.off_hinv + static_cast<size_t>(rows) * 4, 256);
   return p;
 }
 
@@ -415,7 +451,7 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
 
   // bf16 path
   DG_ARG(prepared != nullptr);
-  DG_UNSUP(d % 128 == 0 && hidden % 128 == 0);
+  DG_UNSUP(d % 128 == 0 && hidden % 128 == 0 && d <= 8192 && hidden <= 8192);
   DG_UNSUP(ld % 8 == 0 && aligned16(logits));
   const Bf16Plan p = bf16_plan(rows, V, d, hidden);
   DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
@@ -428,33 +464,42 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   auto* part = reinterpret_cast<float*>(wsb + p.off_part);
   auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
   auto* h16 = reinterpret_cast<_Float16*>(wsb + p.off_h16);
-  auto* s32 = reinterpret_cast<float*>(wsb + p.off_s32);
-  auto* h32 = reinterpret_cast<float*>(wsb + p.off_h32);
   auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
   auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
-  auto* row_amax = reinterpret_cast<uint32_t*>(wsb + p.off_amax);
 
   probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 256)), static_cast<unsigned>(cdiv(rows, 8))), 256, 0,
-                          s>>>(logits, ld, V, p.Kp, p.Mp, rows, inv_t, row_max, w, row_amax);
+                          s>>>(logits, ld, V, p.Kp, p.Mp, rows, inv_t, row_max, w);
   DG_LAUNCHED();
   if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
   launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  const dim3 rgrid(static_cast<unsigned>(cdiv(d, 256)), rows);
-  pe_reduce_kernel<<<rgrid, 256, 0, s>>>(part, p.pe.splits, rows, d, row_lnz, s32, s_out, row_amax);
-  DG_LAUNCHED();
-  pe_to_f16_kernel<<<rgrid, 256, 0, s>>>(s32, d, p.Mp, row_amax, s16, s_inv);
+  const int rc = static_cast<int>(cdiv(d, 1024)), hc = static_cast<int>(cdiv(hidden, 1024));
+  if (rc == 1)
+    pe_reduce_kernel<1><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
+  else if (rc == 2)
+    pe_reduce_kernel<2><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
+  else if (rc <= 4)
+    pe_reduce_kernel<4><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
+  else
+    pe_reduce_kernel<8><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
   DG_LAUNCHED();
   launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
-  glu_reduce_kernel<<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h32, h16, h_inv);
+  if (hc == 1)
+    glu_reduce_kernel<1><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else if (hc == 2)
+    glu_reduce_kernel<2><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else if (hc <= 4)
+    glu_reduce_kernel<4><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else
+    glu_reduce_kernel<8><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
   DG_LAUNCHED();
   launch_gemm<1>(p.g2, gemm_args(h16, p.Mp, wd, d, part, rows, d, hidden, p.g2), s);
   DG_LAUNCHED();
-  embed_reduce_kernel<<<blocks_for(rows64 * d), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
-                                                             reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
-                                                             h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
+  embed_reduce_kernel<<<blocks_for(rows64 * d / 4), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
+                                                                 reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
+                                                                 h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
   DG_LAUNCHED();
   return DG_OK;
 }

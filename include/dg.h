@@ -204,7 +204,7 @@ dg_status dg_converged(const int32_t* argmax, const float* entropy, int32_t B, i
  *   logits [rows][ld], ld % 8 == 0; row_max/row_lnz [rows] f32; canvas [rows] i32;
  *   sc_on [B] u8; x_out [rows][d]; s_out [rows][d] f32 or NULL (the P.E result);
  *   y_out [rows][d] f32 or NULL (the gated-MLP output y, for every row whatever sc_on).
- *   d % 64 == 0 and hidden % 64 == 0 for DG_BF16.
+ *   DG_BF16: d and hidden multiples of 128, at most 8192 (else DG_E_UNSUPPORTED).
  * Workspace: dg_selfcond_ws_bytes(rows, V, d, hidden, dtype) bytes.
  * ------------------------------------------------------------------------ */
 size_t dg_selfcond_prepared_bytes(int32_t V, int32_t d, int32_t hidden, int32_t dtype);

@@ -65,9 +65,11 @@ def test_host_validation_rejects_before_launch(L):
                                None, None, 64, 1 << 30, None) == -1
     assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, 64, 1024, 96, 128, 64,
                                None, None, 64, 1 << 30, None) == -2
+    assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, 64, 1024, 8320, 128, 64,
+                               None, None, 64, 1 << 30, None) == -2      # d above 8192
 
 
 def test_workspace_sizes(L):
-    assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 8 * 32
+    assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 4 * 32      # 4 chunks of 65536 logits per row
     assert L.dg_selfcond_ws_bytes(256, 262144, 4096, 1024, 1) >= 256 * 262144 * 2
     assert L.dg_selfcond_prepared_bytes(262144, 4096, 1024, 1) >= 262144 * 4096 * 2 + 3 * 4096 * 1024 * 2
