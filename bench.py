@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
            tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0)
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
@@ -163,6 +164,35 @@ class Workload:
         rec(5)
 
 
+def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
+    """Per-call GPU time (events around each call in the timed region) against its own bound.
+
+    attention: MFMA work 4 D Hq per visible (query row, key) pair: every one of the C canvas rows sees
+    the L cached keys and all C canvas keys; sampler: the logit bytes (2 V per row, read once);
+    P.E: 2 C V d FLOP on fp16 MFMA and its algorithmic bytes (E + P, 16-bit)."""
+    C, V, d, L = c["B"] * c["C"], c["V"], c["d"], c["L"]
+    att_flop = 4.0 * c["D"] * c["Hq"] * C * (L + C)
+    samp_bytes = 2.0 * C * V
+    pe_flop = 2.0 * C * V * d
+    out = {
+        "canvas_attention": {"us": brk["canvas_attention"], "bound": "mfma",
+                             "tflops": att_flop / (brk["canvas_attention"] * 1e-6) / 1e12},
+        "denoise_sample": {"us": brk["denoise_sample"], "bound": "hbm",
+                           "gbs": samp_bytes / (brk["denoise_sample"] * 1e-6) / 1e9},
+        "pe_contraction": {"us": pe_ms * 1000.0, "bound": "hbm",
+                           "gbs": pe_algorithmic_bytes(c) / (pe_ms * 1e-3) / 1e9,
+                           "tflops": pe_flop / (pe_ms * 1e-3) / 1e12},
+        "entropy_accept": {"us": brk["entropy_accept"], "bound": "latency"},
+        "converged": {"us": brk["converged"], "bound": "latency"},
+    }
+    for k in out.values():
+        if "tflops" in k:
+            k["mfma_frac"] = k["tflops"] / MFMA_PEAK_TFLOPS
+        if "gbs" in k:
+            k["hbm_frac"] = k["gbs"] / HBM_PEAK_GBS
+    return out
+
+
 def cpu_baseline(w: Workload, rows: int):
     """Time the oracle, as it stands, on `rows` canvas positions of the same step (host cores)."""
     import numpy as np
@@ -214,7 +244,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=8, help="canvas positions in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="canvas positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 1 GiB device copies (reference for HBM counter calibration)")
@@ -246,32 +276,27 @@ def main():
     K = args.steps
     hev = HipEvents()
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
+    # events between the calls of every timed step (on the launch stream): per-call GPU time
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for t in range(K):
-        w.step(args.warmup + t, pe_ev=pe_ev[t])
+        w.step(args.warmup + t, ev=call_ev[t], pe_ev=pe_ev[t])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
     pe_ms = sum(hev.elapsed_ms(a, b) for a, b in pe_ev) / K
-    # per-call breakdown over a few extra steps (not part of the timed region)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     names = ["canvas_attention", "denoise_sample", "entropy_accept", "converged", "selfcond_embed"]
-    brk = {n: 0.0 for n in names}
-    nb = 5
-    for t in range(nb):
-        w.step(10_000 + t, ev=ev)
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            brk[n] += ev[i].elapsed_time(ev[i + 1]) * 1000.0 / nb
+    brk = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in call_ev) * 1000.0 / K for i, n in enumerate(names)}
     alg = pe_algorithmic_bytes()
     achieved = alg / (pe_ms * 1e-3) / 1e9
     positions = c["B"] * c["C"]
+    kernels = call_rooflines(brk, pe_ms)
     result = {
         "metric": METRIC,
         "value": positions * K / (ms_total * 1e-3),
@@ -295,6 +320,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg, "avg_launch_us": pe_ms * 1000.0,
                      "source_sha": source_sha()},
         "breakdown_us": brk,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
