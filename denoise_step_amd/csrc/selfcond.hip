@@ -97,12 +97,16 @@ DG_DEV float row_pow2_scale(float amax) {
   return ldexpf(1.f, 14 - e);
 }
 
-// Largest value over the 256 threads of the workgroup (DPP inside each wave, 4 waves via LDS).
-DG_DEV float block_max_256(float v, float* red) {
+// Largest value over the NT threads of the workgroup (DPP inside each wave, the waves via LDS).
+template <int NT>
+DG_DEV float block_max(float v, float* red) {
   v = dpp_wave_max(v);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) m = fmaxf(m, red[w]);
+  return m;
 }
 
 DG_DEV float4 f4_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
@@ -120,27 +124,29 @@ DG_DEV void store4_f16(_Float16* dst, int r, int n, int64_t Mp, float4 v, float 
   *reinterpret_cast<half4*>(dst + kblk_index(r, n, Mp)) = h;
 }
 
-// Split-K reduce of the P.E partials, one workgroup per row, each thread C groups of 4 columns:
-// s = sum_split part * 2^-15 / Z (-> s_out when requested), then s16 = fp16(s * scale_r) in the
-// K-blocked layout with scale_r the power of two that brings the row's largest |s| into
-// (2^13, 2^14], and s_inv[r] = 1 / scale_r.  The split loads are issued four splits at a time.
+// Split-K reduce of the P.E partials, one workgroup of 1024 threads per row, each thread C groups of
+// 4 columns: s = sum_split part * 2^-15 / Z (-> s_out when requested), then s16 = fp16(s * scale_r)
+// in the K-blocked layout with scale_r the power of two that brings the row's largest |s| into
+// (2^13, 2^14], and s_inv[r] = 1 / scale_r.  The split loads are issued eight splits at a time, so
+// a workgroup has up to 128 KB of the row in flight.
+constexpr int kReduceThreads = 1024;
 template <int C>
-__global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
+__global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                         int32_t N, int64_t Mp, const float* __restrict__ row_lnz,
                                                         float* __restrict__ s_out, _Float16* __restrict__ s16,
                                                         float* __restrict__ s_inv) {
-  __shared__ float red[4];
+  __shared__ float red[kReduceThreads / kWave];
   const int r = blockIdx.x;
   const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
   float4 acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
   for (int k = 0; k < splits; ++k) {
     const float* p = part + (static_cast<int64_t>(k) * M + r) * N;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int n = 4 * (threadIdx.x + 256 * c);
+      const int n = 4 * (threadIdx.x + kReduceThreads * c);
       if (n < N) acc[c] = f4_add(acc[c], *reinterpret_cast<const float4*>(p + n));
     }
   }
@@ -148,16 +154,16 @@ __global__ __launch_bounds__(256) void pe_reduce_kernel(const float* __restrict_
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     acc[c] = make_float4(acc[c].x * f, acc[c].y * f, acc[c].z * f, acc[c].w * f);
-    const int n = 4 * (threadIdx.x + 256 * c);
+    const int n = 4 * (threadIdx.x + kReduceThreads * c);
     if (n < N) {
       amax = fmaxf(amax, f4_amax(acc[c]));
       if (s_out != nullptr) *reinterpret_cast<float4*>(s_out + static_cast<int64_t>(r) * N + n) = acc[c];
     }
   }
-  const float sc = row_pow2_scale(block_max_256(amax, red));
+  const float sc = row_pow2_scale(block_max<kReduceThreads>(amax, red));
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    const int n = 4 * (threadIdx.x + 256 * c);
+    const int n = 4 * (threadIdx.x + kReduceThreads * c);
     if (n < N) store4_f16(s16, r, n, Mp, acc[c], sc);
   }
   if (threadIdx.x == 0) s_inv[r] = 1.f / sc;
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict
   float4 g[C], u[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) g[c] = u[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
   for (int k = 0; k < splits; ++k) {
     const float* p = part + (static_cast<int64_t>(k) * M + r) * N2;
 #pragma unroll
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict
                        gelu_tanh(g[c].z * si) * (u[c].z * si), gelu_tanh(g[c].w * si) * (u[c].w * si));
     if (4 * (threadIdx.x + 256 * c) < H) amax = fmaxf(amax, f4_amax(g[c]));
   }
-  const float sc = row_pow2_scale(block_max_256(amax, red));
+  const float sc = row_pow2_scale(block_max<256>(amax, red));
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int j = 4 * (threadIdx.x + 256 * c);
@@ -474,15 +480,11 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  const int rc = static_cast<int>(cdiv(d, 1024)), hc = static_cast<int>(cdiv(hidden, 1024));
+  const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
   if (rc == 1)
-    pe_reduce_kernel<1><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
-  else if (rc == 2)
-    pe_reduce_kernel<2><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
-  else if (rc <= 4)
-    pe_reduce_kernel<4><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
+    pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
   else
-    pe_reduce_kernel<8><<<rows, 256, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
+    pe_reduce_kernel<2><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
   DG_LAUNCHED();
   launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
