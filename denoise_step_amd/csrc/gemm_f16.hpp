@@ -227,10 +227,11 @@ struct GemmPlan {
 };
 
 // N % 128 == 0 and K % 128 == 0 are required (every split runs a whole number of 4-stage rounds);
-// M may be ragged.  The N tile is 256 when N allows it.
-// About one workgroup per CU (each holds up to ~144 KB of LDS); splits are added only to reach that.
-inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 256) {
-  const int32_t tn = (N % 256 == 0) ? 256 : 128;
+// M may be ragged.  The N tile is 256 when N allows it and `narrow` is false, else 128.
+// About `target_wgs` workgroups (one per CU by default; each holds up to ~144 KB of LDS); splits
+// are added only to reach that.
+inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 256, bool narrow = false) {
+  const int32_t tn = (N % 256 == 0 && !narrow) ? 256 : 128;
   const int32_t mtiles = (M + kGemmTM - 1) / kGemmTM, ntiles = N / tn;
   const int32_t tiles = mtiles * ntiles;
   int32_t splits = (target_wgs + tiles - 1) / tiles;

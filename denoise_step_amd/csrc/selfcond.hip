@@ -304,8 +304,11 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   p.Mp = rows_p;
   p.Kp = pad128(V);
   p.pe = plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
-  p.g1 = plan_gemm(rows, 2 * hidden, d);
-  p.g2 = plan_gemm(rows, d, hidden);
+  // the MLP GEMMs are small (M = rows, K = d or hidden): 128-wide N tiles and about 128 workgroups
+  // halve the split-K partials against one 256-wide tile per CU (measured 30 -> 24 us for
+  // 4096 -> 2 x 1024 -> 4096 at 256 rows)
+  p.g1 = plan_gemm(rows, 2 * hidden, d, 128, true);
+  p.g2 = plan_gemm(rows, d, hidden, 128, true);
   size_t part = 0;
   part = std::max(part, static_cast<size_t>(p.pe.splits) * rows * d * 4);
   part = std::max(part, static_cast<size_t>(p.g1.splits) * rows * 2 * hidden * 4);
