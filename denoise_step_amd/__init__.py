@@ -20,6 +20,7 @@ __all__ = [
     "dg_denoise_sample", "dg_denoise_sample_ws_bytes", "dg_entropy_accept", "dg_converged",
     "dg_selfcond_prepared_bytes", "dg_selfcond_prepare", "dg_selfcond_ws_bytes", "dg_selfcond_embed",
     "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
+    "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -52,6 +53,12 @@ _SIGS = {
                                  _i32, _p, _p, _p, _p, _sz, _p]),
     "dg_selfcond_embed_traced": (_i32, [_p, _i64, _i32, _f32, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _i32,
                                         _i32, _i32, _p, _p, _p, _p, _sz, _p, _p, _p]),
+    "dg_selfcond_operand_bytes": (_sz, [_i32, _i32]),
+    "dg_denoise_sample_sc": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p, _p, _p, _p, _sz,
+                                    _p, _sz, _p]),
+    "dg_selfcond_ws_bytes_sc": (_sz, [_i32, _i32, _i32, _i32]),
+    "dg_selfcond_embed_sc": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz,
+                                    _p, _p, _p]),
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
     "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
     "dg_linear": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p]),
@@ -188,6 +195,33 @@ def dg_denoise_sample(logits, V, rows_per_req, seed, step, temperature=1.0, acti
     return out
 
 
+def dg_selfcond_operand_bytes(rows, V) -> int:
+    return int(lib().dg_selfcond_operand_bytes(rows, V))
+
+
+def dg_denoise_sample_sc(logits, V, rows_per_req, seed, step, temperature=1.0, active=None, out=None, ws=None,
+                         sc_operand=None, stream=None):
+    """dg_denoise_sample that also writes the self-conditioning operand; returns (outputs, operand)."""
+    rows, ld = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(argmax=torch.empty(rows, dtype=torch.int32, device=dev),
+                   entropy=torch.empty(rows, dtype=torch.float32, device=dev),
+                   sample=torch.empty(rows, dtype=torch.int32, device=dev),
+                   row_max=torch.empty(rows, dtype=torch.float32, device=dev),
+                   row_lnz=torch.empty(rows, dtype=torch.float32, device=dev))
+    nb = dg_denoise_sample_ws_bytes(rows, V)
+    ws = _ws(nb, ws, dev)
+    ob = dg_selfcond_operand_bytes(rows, V)
+    sc_operand = _ws(ob, sc_operand, dev)
+    g = out.get
+    _check(lib().dg_denoise_sample_sc(_ptr(logits), ld, _dtype_code(logits), rows, V, rows_per_req, _ptr(seed),
+                                      _ptr(step), _ptr(active), float(temperature), _ptr(g("entropy")),
+                                      _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")), _ptr(g("row_lnz")),
+                                      _ptr(ws), nb, _ptr(sc_operand), ob, _stream(stream)), "dg_denoise_sample_sc")
+    return out, sc_operand
+
+
 def dg_entropy_accept(entropy, sample, canvas, V, budget, seed, step, active=None, accept=None, n_accept=None,
                       stream=None):
     B, C = canvas.shape
@@ -245,6 +279,26 @@ def dg_selfcond_embed(logits, V, row_max, row_lnz, sc_on, canvas, E, w_gate, w_u
                                           _ptr(w_down), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
                                           _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)),
            "dg_selfcond_embed_traced")
+    return x_out
+
+
+def dg_selfcond_ws_bytes_sc(rows, V, d, hidden) -> int:
+    return int(lib().dg_selfcond_ws_bytes_sc(rows, V, d, hidden))
+
+
+def dg_selfcond_embed_sc(sc_operand, V, row_max, row_lnz, sc_on, canvas, E, prepared, hidden, x_out=None,
+                         s_out=None, y_out=None, ws=None, stream=None, pe_events=None):
+    """dg_selfcond_embed on the operand written by dg_denoise_sample_sc."""
+    B, C = canvas.shape
+    rows = B * C
+    d = E.shape[1]
+    x_out = torch.empty((rows, d), dtype=E.dtype, device=E.device) if x_out is None else x_out
+    nb = dg_selfcond_ws_bytes_sc(rows, V, d, hidden)
+    ws = _ws(nb, ws, E.device)
+    ev0, ev1 = (None, None) if pe_events is None else (int(pe_events[0]), int(pe_events[1]))
+    _check(lib().dg_selfcond_embed_sc(_ptr(sc_operand), _ptr(row_max), _ptr(row_lnz), _ptr(sc_on), _ptr(canvas), B,
+                                      C, _ptr(E), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
+                                      _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_sc")
     return x_out
 
 

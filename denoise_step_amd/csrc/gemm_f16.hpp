@@ -246,6 +246,16 @@ inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 
   return {splits, kchunk, mtiles, ntiles, tn, dim3(launched)};
 }
 
+// The same tiling with a given K per split (a multiple of kGemmStages * kGemmTK).
+inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk) {
+  const int32_t tn = (N % 256 == 0) ? 256 : 128;
+  const int32_t mtiles = (M + kGemmTM - 1) / kGemmTM, ntiles = N / tn;
+  const int32_t splits = (K + kchunk - 1) / kchunk;
+  const int32_t total = mtiles * ntiles * splits;
+  const int32_t launched = (total + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
+  return {splits, kchunk, mtiles, ntiles, tn, dim3(launched)};
+}
+
 inline GemmArgs gemm_args(const _Float16* A, int64_t lda, const _Float16* Bt, int64_t ldb, float* part, int32_t M,
                           int32_t N, int32_t K, const GemmPlan& p) {
   return GemmArgs{A, lda, Bt, ldb, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};

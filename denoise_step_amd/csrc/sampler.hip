@@ -39,7 +39,6 @@ constexpr int kGroup = 8;                                        // logits per 1
 constexpr int kRounds = 8;                                       // loads per lane per iteration
 constexpr int kIterElems = kSampleThreads * kRounds * kGroup;    // 16384 logits per workgroup iteration
 constexpr int kBlock = 16;                                       // ids per block of the first level
-constexpr uint32_t kStreamBlock = 0u, kStreamInner = 3u;
 
 struct Partial {
   float m, Z, S, amax_v;
@@ -137,10 +136,24 @@ struct LaneState {
   int32_t kb;   // its block
 };
 
+// Self-conditioning operand written by the pass (dg_denoise_sample_sc): w[r][k] = fp16(2^15 2^(x2_k -
+// ref_{r,j})) in the K-blocked layout with Mp rows, k < Kp (zero past V), where ref_{r,j} is the
+// largest x2 of the row's j-th run of 16384 logits; ref [rows][nchunk].
+struct ScOut {
+  _Float16* w;
+  int64_t Mp, Kp;
+  float* ref;
+  int32_t nchunk;
+  int32_t row;
+};
+
 // One iteration of a workgroup: logits E .. E + 16384 of the row.  FULL: all of them are < V.
-template <bool BF16, bool ARGMAX_ONLY, bool FULL>
+// SC: the exponentials of the iteration use the workgroup's largest logit of the iteration as their
+// reference (one block-wide max through `red`), are written as the self-conditioning operand and are
+// folded into the lane's running softmax state.
+template <bool BF16, bool ARGMAX_ONLY, bool FULL, bool SC>
 DG_DEV void sample_iteration(const char* row, int64_t E, int32_t V, float c, uint32_t pos, uint32_t st, uint32_t k0,
-                             uint32_t k1, LaneState& ls) {
+                             uint32_t k1, LaneState& ls, const ScOut& so, float* red) {
   const int t = threadIdx.x, h = t & 1, pr = t >> 1;
   float l[kRounds][kGroup];
 #pragma unroll
@@ -173,43 +186,70 @@ DG_DEV void sample_iteration(const char* row, int64_t E, int32_t V, float c, uin
     float mx = gm[0];
 #pragma unroll
     for (int q = 1; q < kRounds; ++q) mx = fmaxf(mx, gm[q]);
-    // reference shared by the lane pair: the pair's running max in base 2
-    float mn = fmaxf(ls.ss.m, mx * c);
-    mn = fmaxf(mn, pair_swap(mn));
-    if (mn > ls.ss.m) {
-      if (ls.ss.Z != 0.f) {
-        const float d = ls.ss.m - mn;
-        const float f = exp2f_fast(d);
-        ls.ss.S = f * (ls.ss.S + d * ls.ss.Z);
-        ls.ss.Z *= f;
+    // reference of this iteration's exponentials: shared by the lane pair (the pair's running max in
+    // base 2), or by the whole workgroup (the iteration's max) when the operand is written
+    float m;
+    if constexpr (SC) {
+      const float mw = dpp_wave_max(mx * c);
+      if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = mw;
+      __syncthreads();
+      m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      __syncthreads();  // red is reused by the next iteration
+    } else {
+      float mn = fmaxf(ls.ss.m, mx * c);
+      mn = fmaxf(mn, pair_swap(mn));
+      if (mn > ls.ss.m) {
+        if (ls.ss.Z != 0.f) {
+          const float d = ls.ss.m - mn;
+          const float f = exp2f_fast(d);
+          ls.ss.S = f * (ls.ss.S + d * ls.ss.Z);
+          ls.ss.Z *= f;
+        }
+        ls.ss.m = mn;
       }
-      ls.ss.m = mn;
+      m = ls.ss.m;
     }
-    const float m = ls.ss.m;
     float hs[kRounds];  // this lane's half of each round's block, relative to m
-    float S = ls.ss.S, Z = ls.ss.Z;
+    float S = SC ? 0.f : ls.ss.S, Z = SC ? 0.f : ls.ss.Z;
 #pragma unroll
     for (int q = 0; q < kRounds; ++q) {
       float bs = 0.f;
+      float ev[kGroup];
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
         const float d = fmaf(l[q][j], c, -m);
         if (FULL) {
           const float e = exp2f_fast(d);
+          ev[j] = e;
           bs += e;
           S = fmaf(e, d, S);
         } else {
           const bool ok = l[q][j] != -INFINITY;
           const float e = ok ? exp2f_fast(d) : 0.f;
+          ev[j] = e;
           bs += e;
           S = ok ? fmaf(e, d, S) : S;
         }
       }
       hs[q] = bs;
       Z += bs;
+      if constexpr (SC) {
+        const int64_t e0 = E + q * (kSampleThreads * kGroup) + kGroup * t;
+        if (FULL || e0 < so.Kp) {
+          half8 hw;
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j) hw[j] = static_cast<_Float16>(ev[j] * 32768.f);
+          *reinterpret_cast<half8*>(so.w + ((e0 >> 5) * so.Mp + so.row) * 32 + (e0 & 31)) = hw;
+        }
+      }
     }
-    ls.ss.S = S;
-    ls.ss.Z = Z;
+    if constexpr (SC) {
+      soft_merge(ls.ss, SoftState{m, Z, S});
+      if (threadIdx.x == 0) so.ref[static_cast<int64_t>(so.row) * so.nchunk + E / kIterElems] = m;
+    } else {
+      ls.ss.S = S;
+      ls.ss.Z = Z;
+    }
     // lane h of the pair scores the blocks of rounds 4h .. 4h + 3: blocks
     // b = E / 16 + 128 (4h + j) + pr, which share counter 128 (E / 8192 + h) + pr (word j)
     float own[4];
@@ -220,7 +260,7 @@ DG_DEV void sample_iteration(const char* row, int64_t E, int32_t V, float c, uin
       own[j] = mine + pair_swap(give);
     }
     const uint32_t ctr = 128u * static_cast<uint32_t>(E / 8192 + h) + static_cast<uint32_t>(pr);
-    const u32x4 w = philox4x32_10(u32x4{ctr, pos, st, kStreamBlock}, k0, k1);
+    const u32x4 w = philox4x32_10(u32x4{ctr, pos, st, static_cast<uint32_t>(DG_STREAM_GUMBEL)}, k0, k1);
     const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
     const int32_t b0 = static_cast<int32_t>(E / kBlock) + 128 * 4 * h + pr;
 #pragma unroll
@@ -234,11 +274,12 @@ DG_DEV void sample_iteration(const char* row, int64_t E, int32_t V, float c, uin
 }
 
 // One workgroup per (row, chunk of `iters` iterations).  Logits must be finite.
-template <bool BF16, bool ARGMAX_ONLY>
+template <bool BF16, bool ARGMAX_ONLY, bool SC>
 __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
     const void* __restrict__ logits, int64_t ld, int32_t V, int32_t rows_per_req, const uint64_t* __restrict__ seed,
     const int32_t* __restrict__ step, const uint8_t* __restrict__ active, float c, int32_t iters, int32_t nsplit,
-    Partial* __restrict__ part) {
+    Partial* __restrict__ part, ScOut so) {
+  __shared__ float red_sc[kSampleThreads / kWave];
   const int r = blockIdx.y;
   const int split = blockIdx.x;
   const int req = r / rows_per_req;
@@ -256,10 +297,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
   LaneState ls{-INFINITY, -1, SoftState{-INFINITY, 0.f, 0.f}, -INFINITY, 0x7FFFFFFF};
   const int64_t E0 = static_cast<int64_t>(split) * iters * kIterElems;
   const int64_t full_end = min(static_cast<int64_t>(iters), (V - E0) / kIterElems);  // iterations entirely < V
+  so.row = r;
   int64_t it = 0;
-  for (; it < full_end; ++it) sample_iteration<BF16, ARGMAX_ONLY, true>(row, E0 + it * kIterElems, V, c, pos, st, k0, k1, ls);
+  for (; it < full_end; ++it)
+    sample_iteration<BF16, ARGMAX_ONLY, true, SC>(row, E0 + it * kIterElems, V, c, pos, st, k0, k1, ls, so, red_sc);
   if (it < iters && E0 + it * kIterElems < V)
-    sample_iteration<BF16, ARGMAX_ONLY, false>(row, E0 + it * kIterElems, V, c, pos, st, k0, k1, ls);
+    sample_iteration<BF16, ARGMAX_ONLY, false, SC>(row, E0 + it * kIterElems, V, c, pos, st, k0, k1, ls, so, red_sc);
 
   // the argmax travels as (value, first index of its 8-logit group); the merge resolves the index
   float av = ls.av;
@@ -340,7 +383,7 @@ __global__ __launch_bounds__(kWave) void sample_merge_kernel(const Partial* __re
     if (lane < kBlock && i < V) {
       const uint64_t sd = seed[req];
       const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(i >> 2), static_cast<uint32_t>(r - req * rows_per_req),
-                                          static_cast<uint32_t>(step[req]), kStreamInner},
+                                          static_cast<uint32_t>(step[req]), static_cast<uint32_t>(DG_STREAM_GUMBEL_INNER)},
                                     static_cast<uint32_t>(sd), static_cast<uint32_t>(sd >> 32));
       const uint32_t wi = (i & 3) == 0 ? w.x : ((i & 3) == 1 ? w.y : ((i & 3) == 2 ? w.z : w.w));
       key = gumbel_key2(load1<BF16>(row, i) * c, wi);
@@ -376,22 +419,12 @@ SamplePlan plan_sample(int32_t rows, int32_t V) {
   return {nsplit, iters};
 }
 
-}  // namespace
-}  // namespace dg
-
-using namespace dg;
-
-extern "C" size_t dg_denoise_sample_ws_bytes(int32_t rows, int32_t V) {
-  if (rows <= 0 || V <= 0) return 0;
-  const SamplePlan p = plan_sample(rows, V);
-  return static_cast<size_t>(rows) * p.nsplit * sizeof(Partial);
-}
-
-extern "C" dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
-                                       int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
-                                       const uint8_t* active, float temperature, uint32_t flags, float* entropy,
-                                       int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz, void* ws,
-                                       size_t ws_bytes, dg_stream_t stream) {
+// Shared by dg_denoise_sample and dg_denoise_sample_sc (so.w != nullptr: also writes the operand).
+dg_status denoise_sample_impl(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                              int32_t rows_per_req, const uint64_t* seed, const int32_t* step, const uint8_t* active,
+                              float temperature, uint32_t flags, float* entropy, int32_t* argmax, int32_t* sample,
+                              float* row_max, float* row_lnz, void* ws, size_t ws_bytes, ScOut so,
+                              dg_stream_t stream) {
   const bool amax_only = (flags & DG_SAMPLE_ARGMAX_ONLY) != 0;
   DG_ARG(logits != nullptr && argmax != nullptr);
   DG_ARG(rows > 0 && V > 0 && rows_per_req > 0 && rows % rows_per_req == 0 && rows <= 65535);
@@ -409,26 +442,73 @@ extern "C" dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t d
   Partial* part = reinterpret_cast<Partial*>(ws);
   const dim3 grid(p.nsplit, rows);
   const float c = 1.4426950408889634f / (amax_only ? 1.f : temperature);  // log2(e) / T
-#define DG_SAMPLE_LAUNCH(BF, AO)                                                                                   \
-  sample_partial_kernel<BF, AO><<<grid, kSampleThreads, 0, s>>>(logits, ld, V, rows_per_req, seed, step, active, c, \
-                                                                 p.iters, p.nsplit, part);                        \
-  DG_LAUNCHED();                                                                                                   \
-  sample_merge_kernel<BF, AO><<<rows, kWave, 0, s>>>(part, p.nsplit, logits, ld, V, rows_per_req, seed, step,      \
+#define DG_SAMPLE_LAUNCH(BF, AO, SC)                                                                                  \
+  sample_partial_kernel<BF, AO, SC><<<grid, kSampleThreads, 0, s>>>(logits, ld, V, rows_per_req, seed, step, active,  \
+                                                                     c, p.iters, p.nsplit, part, so);                 \
+  DG_LAUNCHED();                                                                                                      \
+  sample_merge_kernel<BF, AO><<<rows, kWave, 0, s>>>(part, p.nsplit, logits, ld, V, rows_per_req, seed, step,         \
                                                       active, c, entropy, argmax, sample, row_max, row_lnz);
-  if (dtype == DG_BF16) {
+  if (so.w != nullptr) {
+    DG_UNSUP(dtype == DG_BF16 && !amax_only);
+    DG_SAMPLE_LAUNCH(true, false, true)
+  } else if (dtype == DG_BF16) {
     if (amax_only) {
-      DG_SAMPLE_LAUNCH(true, true)
+      DG_SAMPLE_LAUNCH(true, true, false)
     } else {
-      DG_SAMPLE_LAUNCH(true, false)
+      DG_SAMPLE_LAUNCH(true, false, false)
     }
   } else {
     if (amax_only) {
-      DG_SAMPLE_LAUNCH(false, true)
+      DG_SAMPLE_LAUNCH(false, true, false)
     } else {
-      DG_SAMPLE_LAUNCH(false, false)
+      DG_SAMPLE_LAUNCH(false, false, false)
     }
   }
 #undef DG_SAMPLE_LAUNCH
   DG_LAUNCHED();
   return DG_OK;
+}
+
+}  // namespace
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" size_t dg_denoise_sample_ws_bytes(int32_t rows, int32_t V) {
+  if (rows <= 0 || V <= 0) return 0;
+  const SamplePlan p = plan_sample(rows, V);
+  return static_cast<size_t>(rows) * p.nsplit * sizeof(Partial);
+}
+
+extern "C" dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                                       int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
+                                       const uint8_t* active, float temperature, uint32_t flags, float* entropy,
+                                       int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz, void* ws,
+                                       size_t ws_bytes, dg_stream_t stream) {
+  return denoise_sample_impl(logits, ld, dtype, rows, V, rows_per_req, seed, step, active, temperature, flags, entropy,
+                             argmax, sample, row_max, row_lnz, ws, ws_bytes, ScOut{nullptr, 0, 0, nullptr, 0, 0},
+                             stream);
+}
+
+extern "C" size_t dg_selfcond_operand_bytes(int32_t rows, int32_t V) {
+  if (rows <= 0 || V <= 0) return 0;
+  const int64_t Mp = (static_cast<int64_t>(rows) + 255) / 256 * 256, Kp = (static_cast<int64_t>(V) + 127) / 128 * 128;
+  const int64_t nchunk = cdiv(V, kIterElems);
+  return static_cast<size_t>(round_up(Mp * Kp * 2, 256) + rows * nchunk * 4);
+}
+
+extern "C" dg_status dg_denoise_sample_sc(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                                          int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
+                                          const uint8_t* active, float temperature, float* entropy, int32_t* argmax,
+                                          int32_t* sample, float* row_max, float* row_lnz, void* ws, size_t ws_bytes,
+                                          void* sc_operand, size_t sc_operand_bytes, dg_stream_t stream) {
+  DG_ARG(sc_operand != nullptr && rows > 0 && V > 0);
+  DG_UNSUP(dtype == DG_BF16);
+  DG_REQUIRE(sc_operand_bytes >= dg_selfcond_operand_bytes(rows, V), DG_E_WORKSPACE);
+  const int64_t Mp = (static_cast<int64_t>(rows) + 255) / 256 * 256, Kp = (static_cast<int64_t>(V) + 127) / 128 * 128;
+  char* base = reinterpret_cast<char*>(sc_operand);
+  const ScOut so{reinterpret_cast<_Float16*>(base), Mp, Kp, reinterpret_cast<float*>(base + round_up(Mp * Kp * 2, 256)),
+                 static_cast<int32_t>(cdiv(V, kIterElems)), 0};
+  return denoise_sample_impl(logits, ld, dtype, rows, V, rows_per_req, seed, step, active, temperature, 0, entropy,
+                             argmax, sample, row_max, row_lnz, ws, ws_bytes, so, stream);
 }

@@ -130,24 +130,34 @@ DG_DEV void store4_f16(_Float16* dst, int r, int n, int64_t Mp, float4 v, float 
 // (2^13, 2^14], and s_inv[r] = 1 / scale_r.  The split loads are issued eight splits at a time, so
 // a workgroup has up to 128 KB of the row in flight.
 constexpr int kReduceThreads = 1024;
+// With sc_ref (the operand written by the sampling pass), split k's probabilities are relative to
+// 2^ref[r][k] instead of the row max, so its partial is weighted by 2^(ref[r][k] - row_max log2 e).
 template <int C>
 __global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
-                                                        int32_t N, int64_t Mp, const float* __restrict__ row_lnz,
+                                                        int32_t N, int64_t Mp, const float* __restrict__ row_max,
+                                                        const float* __restrict__ row_lnz,
+                                                        const float* __restrict__ sc_ref, int32_t nchunk,
                                                         float* __restrict__ s_out, _Float16* __restrict__ s16,
                                                         float* __restrict__ s_inv) {
   __shared__ float red[kReduceThreads / kWave];
   const int r = blockIdx.x;
   const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
+  const float m2 = sc_ref != nullptr ? row_max[r] * 1.4426950408889634f : 0.f;
   float4 acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
   for (int k = 0; k < splits; ++k) {
     const float* p = part + (static_cast<int64_t>(k) * M + r) * N;
+    const float g = sc_ref != nullptr ? exp2f(sc_ref[static_cast<int64_t>(r) * nchunk + k] - m2) : 1.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int n = 4 * (threadIdx.x + kReduceThreads * c);
-      if (n < N) acc[c] = f4_add(acc[c], *reinterpret_cast<const float4*>(p + n));
+      if (n < N) {
+        const float4 v = *reinterpret_cast<const float4*>(p + n);
+        acc[c] = make_float4(fmaf(v.x, g, acc[c].x), fmaf(v.y, g, acc[c].y), fmaf(v.z, g, acc[c].z),
+                             fmaf(v.w, g, acc[c].w));
+      }
     }
   }
   float amax = 0.f;
@@ -297,13 +307,19 @@ struct Bf16Plan {
   size_t off_w, off_part, off_s16, off_h16, off_sinv, off_hinv, bytes;
 };
 
-Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
+// sc: the probability operand comes from the sampling pass (dg_denoise_sample_sc), in runs of
+// kScChunk vocabulary ids with their own reference, so each P.E split covers exactly one run and the
+// workspace holds no operand of its own.
+constexpr int32_t kScChunk = 16384;
+
+Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden, bool sc = false) {
   Bf16Plan p{};
   // GEMM left operands are allocated with whole 256-row tiles (the tail rows are read, never stored)
   const int64_t rows_p = (static_cast<int64_t>(rows) + kGemmTM - 1) / kGemmTM * kGemmTM;
   p.Mp = rows_p;
   p.Kp = pad128(V);
-  p.pe = plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
+  p.pe = sc ? plan_gemm_kchunk(rows, d, static_cast<int32_t>(p.Kp), kScChunk)
+            : plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
   // the MLP GEMMs are small (M = rows, K = d or hidden): 128-wide N tiles and about 128 workgroups
   // halve the split-K partials against one 256-wide tile per CU (measured 30 -> 24 us for
   // 4096 -> 2 x 1024 -> 4096 at 256 rows)
@@ -314,7 +330,7 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
   part = std::max(part, static_cast<size_t>(p.g1.splits) * rows * 2 * hidden * 4);
   part = std::max(part, static_cast<size_t>(p.g2.splits) * rows * d * 4);
   p.off_w = 0;
-  p.off_part = round_up(p.off_w + static_cast<size_t>(rows_p) * p.Kp * 2, 256);
+  p.off_part = round_up(p.off_w + (sc ? 0 : static_cast<size_t>(rows_p) * p.Kp * 2), 256);
   p.off_s16 = round_up(p.off_part + part, 256);
   p.off_h16 = round_up(p.off_s16 + static_cast<size_t>(rows_p) * d * 2, 256);
   p.off_sinv = round_up(p.off_h16 + static_cast<size_t>(rows_p) * hidden * 2, 256);
@@ -347,6 +363,51 @@ void launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     gemm_f16_splitk_kernel<ROLE, 256><<<p.grid, kGemmThreads, 0, s>>>(a);
   else
     gemm_f16_splitk_kernel<ROLE, 128><<<p.grid, kGemmThreads, 0, s>>>(a);
+}
+
+// P.E (from the operand w), its reduce, the gated MLP and the embedding: the bf16 path after the
+// probability operand exists.  sc_ref != nullptr: w comes from the sampling pass (per-run references).
+dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* sc_ref, int32_t nchunk,
+                             const float* row_max, const float* row_lnz, const uint8_t* sc_on, const int32_t* canvas,
+                             int32_t rows, int32_t C, const void* E, const _Float16* et, const _Float16* wgu,
+                             const _Float16* wd, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,
+                             float* y_out, char* wsb, void* pe_start, void* pe_stop, hipStream_t s) {
+  const int64_t rows64 = rows;
+  auto* part = reinterpret_cast<float*>(wsb + p.off_part);
+  auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
+  auto* h16 = reinterpret_cast<_Float16*>(wsb + p.off_h16);
+  auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
+  auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
+  if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
+  launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
+  DG_LAUNCHED();
+  if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
+  const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
+  if (rc == 1)
+    pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
+                                                        nchunk, s_out, s16, s_inv);
+  else
+    pe_reduce_kernel<2><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
+                                                        nchunk, s_out, s16, s_inv);
+  DG_LAUNCHED();
+  launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
+  DG_LAUNCHED();
+  if (hc == 1)
+    glu_reduce_kernel<1><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else if (hc == 2)
+    glu_reduce_kernel<2><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else if (hc <= 4)
+    glu_reduce_kernel<4><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  else
+    glu_reduce_kernel<8><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
+  DG_LAUNCHED();
+  launch_gemm<1>(p.g2, gemm_args(h16, p.Mp, wd, d, part, rows, d, hidden, p.g2), s);
+  DG_LAUNCHED();
+  embed_reduce_kernel<<<blocks_for(rows64 * d / 4), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
+                                                                 reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
+                                                                 h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
+  DG_LAUNCHED();
+  return DG_OK;
 }
 
 }  // namespace
@@ -470,43 +531,12 @@ extern "C" dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, in
   const auto* wgu = reinterpret_cast<const _Float16*>(pb + L.off_wgu);
   const auto* wd = reinterpret_cast<const _Float16*>(pb + L.off_wd);
   auto* w = reinterpret_cast<_Float16*>(wsb + p.off_w);
-  auto* part = reinterpret_cast<float*>(wsb + p.off_part);
-  auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
-  auto* h16 = reinterpret_cast<_Float16*>(wsb + p.off_h16);
-  auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
-  auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
 
   probs_f16_kernel<true><<<dim3(static_cast<unsigned>(cdiv(p.Kp, 256)), static_cast<unsigned>(cdiv(rows, 8))), 256, 0,
                           s>>>(logits, ld, V, p.Kp, p.Mp, rows, inv_t, row_max, w);
   DG_LAUNCHED();
-  if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
-  launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
-  DG_LAUNCHED();
-  if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
-  const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
-  if (rc == 1)
-    pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
-  else
-    pe_reduce_kernel<2><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_lnz, s_out, s16, s_inv);
-  DG_LAUNCHED();
-  launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
-  DG_LAUNCHED();
-  if (hc == 1)
-    glu_reduce_kernel<1><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
-  else if (hc == 2)
-    glu_reduce_kernel<2><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
-  else if (hc <= 4)
-    glu_reduce_kernel<4><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
-  else
-    glu_reduce_kernel<8><<<rows, 256, 0, s>>>(part, p.g1.splits, rows, hidden, p.Mp, s_inv, h16, h_inv);
-  DG_LAUNCHED();
-  launch_gemm<1>(p.g2, gemm_args(h16, p.Mp, wd, d, part, rows, d, hidden, p.g2), s);
-  DG_LAUNCHED();
-  embed_reduce_kernel<<<blocks_for(rows64 * d / 4), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
-                                                                 reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
-                                                                 h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
-  DG_LAUNCHED();
-  return DG_OK;
+  return selfcond_bf16_tail(p, w, nullptr, 0, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden,
+                            x_out, s_out, y_out, wsb, pe_start, pe_stop, s);
 }
 
 extern "C" dg_status dg_selfcond_embed(const void* logits, int64_t ld, int32_t dtype, float temperature,
@@ -518,4 +548,36 @@ extern "C" dg_status dg_selfcond_embed(const void* logits, int64_t ld, int32_t d
   return dg_selfcond_embed_traced(logits, ld, dtype, temperature, row_max, row_lnz, sc_on, canvas, B, C, E, w_gate,
                                   w_up, w_down, prepared, V, d, hidden, x_out, s_out, y_out, ws, ws_bytes, nullptr,
                                   nullptr, stream);
+}
+
+extern "C" size_t dg_selfcond_ws_bytes_sc(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
+  if (rows <= 0 || V <= 0 || d <= 0 || hidden <= 0 || d % 128 != 0 || hidden % 128 != 0) return 0;
+  return bf16_plan(rows, V, d, hidden, true).bytes;
+}
+
+extern "C" dg_status dg_selfcond_embed_sc(const void* sc_operand, const float* row_max, const float* row_lnz,
+                                          const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C,
+                                          const void* E, const void* prepared, int32_t V, int32_t d, int32_t hidden,
+                                          void* x_out, float* s_out, float* y_out, void* ws, size_t ws_bytes,
+                                          void* pe_start, void* pe_stop, dg_stream_t stream) {
+  DG_ARG(sc_operand && row_max && row_lnz && sc_on && canvas && E && prepared && x_out);
+  DG_ARG(B > 0 && C > 0 && V > 0 && d > 0 && hidden > 0);
+  DG_UNSUP(d % 128 == 0 && hidden % 128 == 0 && d <= 8192 && hidden <= 8192);
+  const int64_t rows64 = static_cast<int64_t>(B) * C;
+  DG_ARG(rows64 <= 65535);
+  const int32_t rows = static_cast<int32_t>(rows64);
+  const Bf16Plan p = bf16_plan(rows, V, d, hidden, true);
+  DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
+  const PreparedLayout L = prepared_layout(V, d, hidden);
+  const char* pb = reinterpret_cast<const char*>(prepared);
+  const auto* et = reinterpret_cast<const _Float16*>(pb + L.off_et);
+  const auto* wgu = reinterpret_cast<const _Float16*>(pb + L.off_wgu);
+  const auto* wd = reinterpret_cast<const _Float16*>(pb + L.off_wd);
+  // operand layout of dg_selfcond_operand_bytes: w [Kp / 32][Mp][32] fp16, then ref [rows][nchunk] f32
+  const char* ob = reinterpret_cast<const char*>(sc_operand);
+  const auto* w = reinterpret_cast<const _Float16*>(ob);
+  const auto* ref = reinterpret_cast<const float*>(ob + round_up(static_cast<size_t>(p.Mp) * p.Kp * 2, 256));
+  const int32_t nchunk = static_cast<int32_t>(cdiv(V, kScChunk));
+  return selfcond_bf16_tail(p, w, ref, nchunk, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden,
+                            x_out, s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop, as_stream(stream));
 }

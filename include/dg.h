@@ -57,7 +57,7 @@ enum { DG_F32 = 0, DG_BF16 = 1 };
 enum { DG_SAMPLE_ARGMAX_ONLY = 1 };
 
 /* Philox streams (counter word 3) */
-enum { DG_STREAM_GUMBEL = 0, DG_STREAM_RENOISE = 1, DG_STREAM_INIT = 2 };
+enum { DG_STREAM_GUMBEL = 0, DG_STREAM_RENOISE = 1, DG_STREAM_INIT = 2, DG_STREAM_GUMBEL_INNER = 3 };
 
 int32_t dg_version(void);
 const char* dg_status_str(dg_status s);
@@ -68,7 +68,10 @@ const char* dg_status_str(dg_status s);
  *   ctr: [n][4] uint32, key: [n][2] uint32, out: [n][4] uint32 (device).
  * Keying used by the step (one 64-bit seed per request):
  *   key = (seed & 0xffffffff, seed >> 32), counter = (c0, position, global step, stream);
- *   Gumbel noise of vocabulary element i: word i & 3 of counter (i >> 2, pos, step, 0);
+ *   Gumbel noise of block b (ids 16 b .. 16 b + 15): word (b >> 7) & 3 of counter
+ *     (128 (b >> 9) + (b & 127), pos, step, 0);
+ *   Gumbel noise of vocabulary element i inside the winning block: word i & 3 of counter
+ *     (i >> 2, pos, step, 3);
  *   renoise / init tokens: word 0 of counter (0, pos, step, 1 or 2), token = (w * V) >> 32;
  *   uniform(w) = (2 * (w >> 9) + 1) * 2^-24, Gumbel = -ln(-ln(uniform)).
  * ------------------------------------------------------------------------ */
@@ -127,12 +130,15 @@ dg_status dg_canvas_attention(const void* q, const void* k, const void* v, void*
  *
  * For every logit row (DiffusionGemma/vLLM page, section "Entropy-based
  * denoising" for H(p) = -sum p log p; section "DiffusionGemmaModelState and
- * DiffusionSampler", denoise case, for the Gumbel-max candidate
- * argmax(logits / T + g)), with x = logits / temperature:
+ * DiffusionSampler", denoise case, for the Gumbel-max candidate), with
+ * x = logits / temperature:
  *   row_max = max x,  row_lnz = ln sum exp(x - row_max),
  *   entropy = max(0, row_lnz - sum exp(x - m)(x - m) / sum exp(x - m)),
  *   argmax  = lowest index of the largest logit,
- *   sample  = lowest index of the largest x_i + g_i, g from Philox (see above).
+ *   sample  = a Gumbel-max draw in two levels over blocks of 16 ids: the block
+ *             b* with the largest ln sum_{i in b} exp(x_i) + G_b, then the lowest
+ *             index of the largest x_i + g_i inside b*; G and g from Philox
+ *             (see above).  Its law is softmax(x).
  * Row r belongs to request r / rows_per_req at canvas position r % rows_per_req,
  * keyed by seed[request] and step[request].
  *   logits: [rows][ld] (DG_BF16 or DG_F32), ld % 8 == 0, ld >= V, 16-byte aligned.
@@ -148,6 +154,25 @@ dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t dtype, int32
                             const uint8_t* active, float temperature, uint32_t flags, float* entropy,
                             int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz, void* ws,
                             size_t ws_bytes, dg_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * dg_denoise_sample_sc
+ *
+ * dg_denoise_sample (DG_BF16 logits, full mode) whose streaming pass also
+ * writes the probability operand of the self-conditioning contraction
+ * (DiffusionGemma/vLLM page, section "Self-conditioning": the full softmax of
+ * this step feeds the next pass), so that dg_selfcond_embed_sc does not read
+ * the logits again.  Operand layout (opaque to callers, sized by
+ * dg_selfcond_operand_bytes(rows, V)): fp16 w[r][k] = 2^15 exp(x_k - ref)
+ * for every run of 16384 vocabulary ids, ref being the run's largest x, plus
+ * the refs.  Rows of inactive requests are not written.
+ * ------------------------------------------------------------------------ */
+size_t dg_selfcond_operand_bytes(int32_t rows, int32_t V);
+dg_status dg_denoise_sample_sc(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                               int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
+                               const uint8_t* active, float temperature, float* entropy, int32_t* argmax,
+                               int32_t* sample, float* row_max, float* row_lnz, void* ws, size_t ws_bytes,
+                               void* sc_operand, size_t sc_operand_bytes, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * dg_entropy_accept
@@ -227,6 +252,17 @@ dg_status dg_selfcond_embed_traced(const void* logits, int64_t ld, int32_t dtype
                                    const void* w_up, const void* w_down, const void* prepared, int32_t V, int32_t d,
                                    int32_t hidden, void* x_out, float* s_out, float* y_out, void* ws,
                                    size_t ws_bytes, void* pe_start, void* pe_stop, dg_stream_t stream);
+
+/* dg_selfcond_embed_sc: dg_selfcond_embed (DG_BF16) taking the probability operand written by
+ * dg_denoise_sample_sc of the same step instead of the logits; row_max / row_lnz are that call's
+ * outputs.  Each P.E split covers one 16384-id run of the operand.  pe_start / pe_stop as in
+ * dg_selfcond_embed_traced (may be NULL).  Workspace: dg_selfcond_ws_bytes_sc(rows, V, d, hidden). */
+size_t dg_selfcond_ws_bytes_sc(int32_t rows, int32_t V, int32_t d, int32_t hidden);
+dg_status dg_selfcond_embed_sc(const void* sc_operand, const float* row_max, const float* row_lnz,
+                               const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C, const void* E,
+                               const void* prepared, int32_t V, int32_t d, int32_t hidden, void* x_out,
+                               float* s_out, float* y_out, void* ws, size_t ws_bytes, void* pe_start,
+                               void* pe_stop, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * dg_allowed_probs -- structured-read readout (single-pass-reads page,

@@ -69,6 +69,21 @@ def test_host_validation_rejects_before_launch(L):
                                None, None, 64, 1 << 30, None) == -2      # d above 8192
 
 
+def test_fused_operand_entry_points_validate(L):
+    sc = lambda dtype=1, op=64, opb=1 << 30: L.dg_denoise_sample_sc(64, 1024, dtype, 16, 1024, 16, 64, 64, None, 1.0,
+                                                                     64, 64, 64, 64, 64, 64, 1 << 20, op, opb, None)
+    assert sc(dtype=0) == -2                     # the operand path reads bf16 logits only
+    assert sc(op=None) == -1
+    assert sc(opb=1) == -3
+    assert L.dg_selfcond_operand_bytes(256, 262144) >= 256 * 262144 * 2 + 256 * 16 * 4
+    emb = lambda op=64, d=128, wsb=1 << 30: L.dg_selfcond_embed_sc(op, 64, 64, 64, 64, 1, 16, 64, 64, 1024, d, 128,
+                                                                   64, None, None, 64, wsb, None, None, None)
+    assert emb(op=None) == -1
+    assert emb(d=96) == -2
+    assert emb(wsb=1) == -3
+    assert L.dg_selfcond_ws_bytes_sc(256, 262144, 4096, 1024) > 0
+
+
 def test_workspace_sizes(L):
     assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 4 * 32      # 4 chunks of 65536 logits per row
     assert L.dg_selfcond_ws_bytes(256, 262144, 4096, 1024, 1) >= 256 * 262144 * 2
