@@ -5,16 +5,17 @@
 // hk * G + g of the KV group), so the G query heads that share a KV head share
 // every K/V tile.  Four wave64s own 32 packed rows each.
 //
-// K blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per lane,
-// no staging registers; each copy reads whole key rows) into an XOR-swizzled row-major layout; V
-// blocks go through registers (each lane loads 4 d of a key pair), where pairs of keys are
-// transposed on their way into LDS.  Both are prefetched one block ahead.
+// K and V blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per
+// lane, no staging registers; each copy reads whole key rows) into the same XOR-swizzled row-major
+// layout, prefetched one block ahead.  The V operand of the PV product needs 8 keys at one d per
+// lane: it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each lane of
+// a 16-lane group one column of the 4 rows x 16 columns its lanes address.
 //
 // Per 64-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q preloaded in registers): each lane then holds 16
 // scores of ONE query row, so the online softmax is in-lane plus one xor-32
 // shuffle.  The probabilities stay in registers as the B operand of
-// O^T = V^T P^T (A = V^T read from a transposed LDS copy of the V block); the
+// O^T = V^T P^T (A = V^T, transposing reads of the row-major V block); the
 // key order inside each 16-key MFMA step is permuted consistently on both
 // operands to match the accumulator layout.  O^T accumulates in fp32 (each
 // lane again owns one row, so the rescale is in-lane).  The softmax reference
@@ -74,40 +75,15 @@ struct AttArgs {
 
 template <int D>
 struct AttSmem {
-  static constexpr int kChunks = D / 8;         // 16-byte chunks per K row
-  static constexpr int vPitch = kAttKeys + 4;   // bf16 per transposed V row in LDS
   uint16_t K[2][kAttKeys * D];
-  uint16_t Vt[2][D * vPitch];
+  uint16_t V[2][kAttKeys * D];
   int32_t pages[kAttMaxPages];
 };
 
-// Registers holding one V block between its global loads and its LDS stores: item i of a lane is
-// 4 consecutive d (8 bytes) of both keys of a pair.
-template <int D>
-struct AttStage {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kV = (kAttKeys / 2) * kChunks * 2 / kAttThreads;  // items per lane
-  uint2 ev[kV], od[kV];
-};
-
-// Item i of a lane: instruction group g = wave * kV + i covers pairs 8 (g % 4) .. + 7 and chunks
-// 4 (g / 4) .. + 3; within it lane l takes pair 8 (g % 4) + l % 8, chunk 4 (g / 4) + (l % 32) / 8
-// and the 4-d half l / 32 of that chunk.  A load instruction then reads 64 contiguous bytes of each
-// of 8 keys, and the transposed stores of the 64 lanes hit 64 distinct banks.
-struct AttVItem {
-  int pair, d0;
-};
-template <int D>
-DG_DEV AttVItem att_vitem(int i) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int g = (threadIdx.x / kWave) * AttStage<D>::kV + i;
-  const int l = lane & 31;
-  return {8 * (g % 4) + (l % 8), 8 * (4 * (g / 4) + l / 8) + 4 * (lane >> 5)};
-}
-
-// K in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ (r & 15)).
-// An MFMA operand read has 16 consecutive keys ask for one chunk per 16-lane group: the XOR puts
-// them in 16 distinct slots of a 256-byte bank row, so the reads are conflict-free.
+// K and V in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ (r & 15)).
+// A K operand read has 16 consecutive keys ask for one chunk per 16-lane group, and a transposing
+// V read has 4 consecutive keys ask for 32 bytes each: the XOR puts them in distinct slots of a
+// 256-byte bank row, so the reads are conflict-free.
 template <int D>
 DG_DEV int att_kslot(int r, int c) {
   return r * (D / 8) + (c ^ (r & 15));
@@ -131,13 +107,14 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, in
 }
 
 // Keys at or past k_end (the split's last visible key + 1) are masked for every row of the tile:
-// they re-read the last visible key (whose page is staged) and their V chunks are zeroed.
+// they re-read the last visible key (whose page is staged), so their K and V are finite and their
+// probability is 0.
 //
-// K: copy q fills slots 64 q .. 64 q + 63, i.e. the 64 / (D / 8) keys q * 64 / (D / 8) ...; lane l
+// Copy q fills slots 64 q .. 64 q + 63, i.e. the 64 / (D / 8) keys q * 64 / (D / 8) ...; lane l
 // fetches chunk (l % (D / 8)) ^ (r & 15) of its key r, so each copy reads whole key rows.
 template <int D>
 DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
-                     int k_end, uint16_t* kdst, AttStage<D>& st) {
+                     int k_end, uint16_t* kdst, uint16_t* vdst) {
   constexpr int kChunks = D / 8;
   constexpr int kKeysPerCopy = kWave / kChunks;
   constexpr int kPerWave = kChunks / (kAttThreads / kWave);  // copies issued by each wave
@@ -151,50 +128,48 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
     const int q = wave * kPerWave + i;
     const int r = q * kKeysPerCopy + lane / kChunks;
     const int c = (lane % kChunks) ^ (r & 15);
-    const uint16_t* src = att_row<D>(a, sp, pq, kb, hk, min(kb + r, k_end - 1), false) + 8 * c;
-    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
+    const int kk = min(kb + r, k_end - 1);
+    const uint16_t* ksrc = att_row<D>(a, sp, pq, kb, hk, kk, false) + 8 * c;
+    const uint16_t* vsrc = att_row<D>(a, sp, pq, kb, hk, kk, true) + 8 * c;
+    const uint32_t klds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
+    const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vdst + kWave * 8 * q));
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "global_load_lds_dwordx4 %1, off"
         :
-        : "s"(lds_addr), "v"(src)
+        : "s"(klds), "v"(ksrc)
+        : "memory", "m0");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(vlds), "v"(vsrc)
         : "memory", "m0");
   }
-#pragma unroll
-  for (int i = 0; i < AttStage<D>::kV; ++i) {
-    const AttVItem it = att_vitem<D>(i);
-    const int kk0 = kb + 2 * it.pair;
-    const uint16_t* e = att_row<D>(a, sp, pq, kb, hk, min(kk0, k_end - 1), true) + it.d0;
-    const uint16_t* o = att_row<D>(a, sp, pq, kb, hk, min(kk0 + 1, k_end - 1), true) + it.d0;
-    const uint2 xe = *reinterpret_cast<const uint2*>(e);
-    const uint2 xo = *reinterpret_cast<const uint2*>(o);
-    st.ev[i] = kk0 < k_end ? xe : make_uint2(0, 0);
-    st.od[i] = kk0 + 1 < k_end ? xo : make_uint2(0, 0);
-  }
-  // keep the V loads here, ahead of the block's MFMA work: without this the compiler sinks them
-  // to their use in att_store and the load latency is no longer hidden behind the compute
-  asm volatile("" ::: "memory");
 }
 
-// Stores the V block (transposed) and waits for every outstanding copy, so that after the next
-// barrier both K (direct copies) and V of the block are visible.
+// Waits for every outstanding copy, so that after the next barrier K and V of the block are visible.
+DG_DEV void att_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_only(0)); }
+
+// A operand of O^T = V^T P^T for 32-d tile t and 16-key chunk ch: lane l (d = 32 t + l % 32, half
+// h = l / 32) gets the keys of MFMA k-slots 8 h .. 8 h + 7, which the P^T operand maps to keys
+// 16 ch + 4 h + 0..3 and 16 ch + 8 + 4 h + 0..3.  Two transposing reads: in 16-lane group G = l / 16
+// lane t16 = l % 16 addresses key 16 ch + 4 (G / 2) + t16 / 4 (+ 8), d 32 t + 16 (G % 2) + 4 (t16 % 4).
+typedef short short4v __attribute__((ext_vector_type(4)));
 template <int D>
-DG_DEV void att_store(AttSmem<D>& sm, int buf, const AttStage<D>& st) {
-#pragma unroll
-  for (int i = 0; i < AttStage<D>::kV; ++i) {
-    const AttVItem it = att_vitem<D>(i);
-    const uint32_t e[2] = {st.ev[i].x, st.ev[i].y};
-    const uint32_t o[2] = {st.od[i].x, st.od[i].y};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // d = d0 + 2t (low halves) and d0 + 2t + 1 (high halves); keys 2 pair (low), 2 pair + 1 (high)
-      const uint32_t lo = (e[t] & 0xFFFFu) | (o[t] << 16);
-      const uint32_t hi = (e[t] >> 16) | (o[t] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(it.d0 + 2 * t) * AttSmem<D>::vPitch + 2 * it.pair]) = lo;
-      *reinterpret_cast<uint32_t*>(&sm.Vt[buf][(it.d0 + 2 * t + 1) * AttSmem<D>::vPitch + 2 * it.pair]) = hi;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+DG_DEV bf16x8 att_vfrag(const uint16_t* Vb, int t, int ch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int G = lane >> 4, t16 = lane & 15;
+  const int r1 = 16 * ch + 4 * (G >> 1) + (t16 >> 2);
+  const int col = 32 * t + 16 * (G & 1) + 4 * (t16 & 3);
+  const uint16_t* p1 = Vb + 8 * att_kslot<D>(r1, col >> 3) + (col & 7);
+  const uint16_t* p2 = Vb + 8 * att_kslot<D>(r1 + 8, col >> 3) + (col & 7);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p2));
+  const short4v lohi[2] = {lo, hi};
+  bf16x8 v;
+  __builtin_memcpy(&v, lohi, sizeof(v));
+  return v;
 }
 
 // Causal rows' K/V of one KV head into the pages at positions cached + j (16-byte chunks).
@@ -273,6 +248,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(row_ok ? row : sp.row0) * a.Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < kDSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
+    // land Q before the first K/V copy: the compiler does not count the copies, so a wait for Q that
+    // it placed at the first use inside the block loop would also wait for the prefetched block
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   }
 
   floatx16 o[kDTiles];
@@ -282,30 +260,45 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and sum of 2^(x - m_ref)
 
-  AttStage<D> st;
   __syncthreads();  // page ids visible
   if (k_begin < k_end) {
-    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], st);
-    att_store<D>(sm, 0, st);
+    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
+    att_wait();
   }
   __syncthreads();
   int buf = 0;
   for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
     const bool more = kb + kAttKeys < k_end;
-    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], st);
+    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
     const uint16_t* Kb = sm.K[buf];
-    const uint16_t* Vb = sm.Vt[buf];
+    const uint16_t* Vb = sm.V[buf];
     // ---- S^T = K Q^T : two 32-key sub-blocks x 32 rows
+    // the two sub-blocks' chains advance together; the K operands of step s + 1 are read while the
+    // MFMAs of step s run (the scheduling groups keep the reads ahead of the MFMAs)
     floatx16 sc[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
+    bf16x8 kf[2][2];
 #pragma unroll
-      for (int s = 0; s < kDSteps; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), 2 * s + half)]);
-        sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
+    for (int b = 0; b < 2; ++b)
+      kf[0][b] = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), half)]);
+#pragma unroll
+    for (int s = 0; s < kDSteps; ++s) {
+      if (s + 1 < kDSteps) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          kf[(s + 1) & 1][b] =
+              *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), 2 * (s + 1) + half)]);
       }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][b], qf[s], sc[b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < kDSteps; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two DS reads (step s + 1)
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs (step s)
     }
     // ---- softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
     if (kb + kAttKeys > wave_lim) {  // some key of the block is masked for some row of the wave
@@ -352,15 +345,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int t = 0; t < kDTiles; ++t) {
-        const uint16_t* vrow = &Vb[(32 * t + (lane & 31)) * AttSmem<D>::vPitch + 16 * c + 4 * half];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[t], 0, 0, 0);
-      }
+      for (int t = 0; t < kDTiles; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(att_vfrag<D>(Vb, t, c), pf[c], o[t], 0, 0, 0);
     }
-    if (more) att_store<D>(sm, buf ^ 1, st);
+    if (more) att_wait();
     __syncthreads();
     buf ^= 1;
   }
