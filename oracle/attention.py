@@ -13,13 +13,26 @@ Follows:
     portfolio.ywsung.com), section on keeping each row's visibility: a merged
     launch splits a request into input (causal) rows and canvas rows that
     share the request's KV block table; in the p0 p1 c0 c1 example p0 sees
-    p0, p1 sees p0 p1, and c0, c1 see p0 p1 c0 c1.
+    p0, p1 sees p0 p1, and c0, c1 see p0 p1 c0 c1;
+  * DiffusionGemma/vLLM page, section on symmetric sliding-window attention:
+    in a sliding-window layer of window W a causal row keeps the one-sided
+    window (itself and the W keys before it) while a canvas row sees W keys on
+    each side of itself (2W + 1 keys), so a canvas only sees the context
+    tokens that fall inside its window; only the right edge differs between
+    the two kinds of request.
 
 Visibility rule for one request with ``cached`` prefix tokens, ``n_causal``
 causal rows and ``n_canvas`` canvas rows (key index space: cache positions
-0 .. cached + n_causal - 1, then the canvas rows):
-  causal row j  -> keys 0 .. cached + j
-  canvas row    -> every key of the request
+0 .. cached + n_causal - 1, then the canvas rows; row and key positions are
+their indices in that space, so causal row j sits at cached + j and canvas row
+j at cached + n_causal + j):
+  causal row at position p -> keys 0 .. p
+  canvas row               -> every key of the request
+With a window W > 0 the visible set is further cut to positions
+[p - W, p] for a causal row and [p - W, p + W] for a canvas row.  W = 0 means
+a full-attention layer (no window).  Reading: the page counts the window in
+tokens of the request's sequence; the positions above are that sequence's
+positions (the cached prefix, the causal rows, then the canvas).
 Causal rows' K/V are appended to the paged cache at positions cached + j
 before any row reads; canvas K/V are never written.  Scores use
 scale * q . k, softmax over visible keys only, output = sum p v.  GQA: query
@@ -27,8 +40,9 @@ head h reads KV head h // (Hq / Hkv).  No position encoding is applied (the
 inputs are synthetic Q/K/V).
 
 Pinned by tests/test_oracle_attention.py: the p0/p1/c0/c1 and the
-three-request visibility fixtures in tests/golden/, brute-force dense-mask
-attention on random shapes, one-visible-key and equal-score special cases,
+three-request visibility fixtures in tests/golden/ (with and without the
+W = 2 window), brute-force dense-mask attention on random shapes (window
+decided by a position predicate there), one-visible-key and equal-score special cases,
 and permutation / page-relabelling invariances.
 """
 from __future__ import annotations
@@ -36,14 +50,21 @@ from __future__ import annotations
 import numpy as np
 
 
-def visibility_mask(cached: int, n_causal: int, n_canvas: int) -> np.ndarray:
+def visibility_mask(cached: int, n_causal: int, n_canvas: int, window: int = 0) -> np.ndarray:
     """Boolean [n_causal + n_canvas, cached + n_causal + n_canvas] mask of one request."""
     nk = cached + n_causal + n_canvas
     rows = n_causal + n_canvas
     mask = np.zeros((rows, nk), dtype=bool)
     for j in range(n_causal):
-        mask[j, :cached + j + 1] = True
-    mask[n_causal:, :] = True
+        p = cached + j
+        lo = max(0, p - window) if window > 0 else 0
+        mask[j, lo:p + 1] = True
+    for j in range(n_canvas):
+        p = cached + n_causal + j
+        if window > 0:
+            mask[n_causal + j, max(0, p - window):min(nk, p + window + 1)] = True
+        else:
+            mask[n_causal + j, :] = True
     return mask
 
 
@@ -92,7 +113,8 @@ def canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, page_size: i
     """Oracle for one launch.
 
     q [rows, Hq, D]; k, v [rows, Hkv, D]; caches [pages, Hkv, page_size, D] (float arrays);
-    splits: iterable of (row0, cached, n_causal, n_canvas, page0).
+    splits: iterable of (row0, cached, n_causal, n_canvas, page0[, window]); window 0 (or absent)
+    is full attention.
     Returns (out [rows, Hq, D] fp64, k_cache', v_cache' with causal K/V appended).
     """
     q = np.asarray(q, np.float64)
@@ -104,12 +126,12 @@ def canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, page_size: i
     Hkv = k.shape[1]
     group = Hq // Hkv
     out = np.zeros((rows, Hq, D))
-    splits = [tuple(int(t) for t in s) for s in splits]
-    for (row0, cached, n_causal, n_canvas, page0) in splits:
+    splits = [tuple(int(t) for t in s) + (0,) * (6 - len(s)) for s in splits]
+    for (row0, cached, n_causal, n_canvas, page0, _w) in splits:
         append_causal_kv(kc, vc, k, v, page_table, row0, cached, n_causal, page0, page_size)
-    for (row0, cached, n_causal, n_canvas, page0) in splits:
+    for (row0, cached, n_causal, n_canvas, page0, window) in splits:
         K, Vv = gather_request_kv(kc, vc, k, v, page_table, row0, cached, n_causal, n_canvas, page0, page_size)
-        mask = visibility_mask(cached, n_causal, n_canvas)
+        mask = visibility_mask(cached, n_causal, n_canvas, window)
         nr = n_causal + n_canvas
         for h in range(Hq):
             hk = h // group

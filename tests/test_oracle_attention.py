@@ -21,12 +21,14 @@ def test_p0p1c0c1_fixture():
     assert attention.visibility_mask(0, 2, 2).astype(int).tolist() == rows
 
 
-def test_three_request_fixture_masks_and_tiles():
-    blocks = read_blocks("visibility_three_requests.txt")
+@pytest.mark.parametrize("fixture", ["visibility_three_requests.txt", "visibility_three_requests_window2.txt"])
+def test_three_request_fixture_masks_and_tiles(fixture):
+    blocks = read_blocks(fixture)
     for name in ("request0", "request1", "request2"):
         hdr, rows = blocks[("mask", name)]
         cached, nc, nv = (int(t) for t in hdr[0].split("=")[1].split(","))
-        m = attention.visibility_mask(cached, nc, nv)
+        window = int(hdr[1].split("=")[1]) if len(hdr) > 1 else 0
+        m = attention.visibility_mask(cached, nc, nv, window)
         assert m.astype(int).tolist() == rows
         if ("skipped_tiles", name) in blocks:
             _, tiles = blocks[("skipped_tiles", name)]
@@ -39,8 +41,11 @@ def _as_float(p, a):
     return synth.bf16_bits_to_f32(a).astype(np.float64) if p.dtype == "bf16" else a.astype(np.float64)
 
 
-def brute_force(p, scale):
-    """Global dense-mask attention over all requests (independent of the oracle's gather)."""
+def brute_force(p, scale, window=0):
+    """Global dense-mask attention over all requests (independent of the oracle's gather).
+
+    With window W > 0 a key is visible only if its position is within W of the query's: at most W
+    before it for a causal query, on either side for a canvas query."""
     q, k, v = _as_float(p, p.q), _as_float(p, p.k), _as_float(p, p.v)
     kc, vc = _as_float(p, p.k_cache), _as_float(p, p.v_cache)
     ps = p.page_size
@@ -71,6 +76,9 @@ def brute_force(p, scale):
     kreq, kpos = np.array(kreq), np.array(kpos)
     qreq, qpos, qcanvas = np.array(qreq), np.array(qpos), np.array(qcanvas)
     vis = (qreq[:, None] == kreq[None, :]) & (qcanvas[:, None] | (kpos[None, :] <= qpos[:, None]))
+    if window > 0:
+        dist = kpos[None, :] - qpos[:, None]
+        vis &= (dist >= -window) & (qcanvas[:, None] | (dist <= 0)) & (dist <= window)
     group = p.Hq // p.Hkv
     out = np.zeros(q.shape)
     for h in range(p.Hq):
@@ -81,9 +89,9 @@ def brute_force(p, scale):
     return out
 
 
-def run_oracle(p, scale):
+def run_oracle(p, scale, window=0):
     f = lambda a: _as_float(p, a)
-    splits = [(p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i]) for i, s in enumerate(p.splits)]
+    splits = [(p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i], window) for i, s in enumerate(p.splits)]
     return attention.canvas_attention(f(p.q), f(p.k), f(p.v), f(p.k_cache), f(p.v_cache), p.page_table,
                                       splits, p.page_size, scale)
 
@@ -161,3 +169,45 @@ def test_page_relabelling_invariance():
     p.page_table = relabel[p.page_table].astype(np.int32)
     out2, _, _ = run_oracle(p, 0.3)
     np.testing.assert_array_equal(out2, out)
+
+
+@pytest.mark.parametrize("window", [1, 3, 17])
+@pytest.mark.parametrize("splits,Hq,Hkv,D", CASES)
+def test_oracle_window_matches_brute_force(splits, Hq, Hkv, D, window):
+    p = synth.attention_problem(12, splits, Hq, Hkv, D, dtype="f32")
+    scale = 1.0 / np.sqrt(D)
+    out, _, _ = run_oracle(p, scale, window)
+    np.testing.assert_allclose(out, brute_force(p, scale, window), rtol=1e-12, atol=1e-12)
+
+
+def test_window_wider_than_request_is_full_attention():
+    p = synth.attention_problem(13, [(9, 4, 5), (0, 3, 0)], 4, 2, 8, dtype="f32")
+    full, _, _ = run_oracle(p, 0.4)
+    wide, _, _ = run_oracle(p, 0.4, window=9 + 4 + 5)
+    np.testing.assert_array_equal(wide, full)
+
+
+def test_window_equal_scores_average_the_band():
+    """q = 0 makes every visible score equal: each row returns the mean of its band's values."""
+    p = synth.attention_problem(14, [(7, 2, 4)], 2, 1, 8, dtype="f32")
+    p.q[:] = 0.0
+    out, kc, vc = run_oracle(p, 1.0, window=2)
+    _, Vv = attention.gather_request_kv(kc, vc, p.k.astype(np.float64), p.v.astype(np.float64),
+                                        p.page_table, 0, 7, 2, 4, 0, p.page_size)
+    np.testing.assert_allclose(out[0, 0], Vv[5:8, 0].mean(0), atol=1e-14)    # causal row at 7: keys 5..7
+    np.testing.assert_allclose(out[1, 1], Vv[6:9, 0].mean(0), atol=1e-14)    # causal row at 8: keys 6..8
+    np.testing.assert_allclose(out[2, 0], Vv[7:12, 0].mean(0), atol=1e-14)   # canvas row at 9: keys 7..11
+    np.testing.assert_allclose(out[5, 0], Vv[10:13, 0].mean(0), atol=1e-14)  # canvas row at 12: keys 10..12
+
+
+def test_window_left_edge_is_shared_by_both_row_kinds():
+    """Only the right edge differs: a canvas row's band minus the keys after it is the causal band."""
+    for cached, nc, nv, w in [(5, 3, 4, 2), (0, 6, 6, 1), (30, 0, 8, 5)]:
+        m = attention.visibility_mask(cached, nc, nv, w)
+        for j in range(nv):
+            pos = cached + nc + j
+            row = m[nc + j].copy()
+            row[pos + 1:] = False
+            ref = np.zeros_like(row)
+            ref[max(0, pos - w):pos + 1] = True
+            np.testing.assert_array_equal(row, ref)
