@@ -35,7 +35,7 @@ METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
-           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0)
+           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0)
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
 PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp",)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
@@ -115,7 +115,9 @@ class Workload:
         self.k_cache = synth.normal_torch(s, "bench.kc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
         self.v_cache = synth.normal_torch(s, "bench.vc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
         self.page_table = torch.as_tensor(synth.page_table(s, "bench.pages", n_pages)[: L // ps].copy(), device=dev)
-        self.splits = torch.tensor([[0, L, 0, C, 0, 0]], dtype=torch.int32, device=dev)
+        self.splits = torch.tensor([[0, L, 0, C, 0, c["window"]]], dtype=torch.int32, device=dev)
+        # keys the canvas rows see together: the whole request, or the band of a sliding window
+        self.key_span = L + C if c["window"] <= 0 else min(L + C, C + 2 * c["window"])
         self.pool = [synth.zipf_logits_torch(s, ("bench.logits", i), C, V, dev) for i in range(c["pool"])]
         self.E = synth.normal_torch(s, "bench.E", (V, d), 1 / 8, bf, dev)
         self.wg = synth.normal_torch(s, "bench.wg", (d, h), 0.02, bf, dev)
@@ -150,7 +152,7 @@ class Workload:
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
-                               c["C"], c["L"] + c["C"], self.scale, out=self.att_out)
+                               c["C"], self.key_span, self.scale, out=self.att_out)
         rec(1)
         logits = self.pool[t % len(self.pool)]
         dg.dg_denoise_sample_sc(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"], out=self.so,
@@ -171,10 +173,15 @@ def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
     """Per-call GPU time (events around each call in the timed region) against its own bound.
 
     attention: MFMA work 4 D Hq per visible (query row, key) pair: every one of the C canvas rows sees
-    the L cached keys and all C canvas keys; sampler: the logit bytes (2 V per row, read once);
-    P.E: 2 C V d FLOP on fp16 MFMA and its algorithmic bytes (E + P, 16-bit)."""
-    C, V, d, L = c["B"] * c["C"], c["V"], c["d"], c["L"]
-    att_flop = 4.0 * c["D"] * c["Hq"] * C * (L + C)
+    the L cached keys and all C canvas keys (in a sliding-window layer of window W, canvas row j at
+    position L + j sees positions L + j - W .. L + j + W inside the request); sampler: the logit
+    bytes (2 V per row, read once); P.E: 2 C V d FLOP on fp16 MFMA and its algorithmic bytes
+    (E + P, 16-bit)."""
+    C, V, d, L, W = c["B"] * c["C"], c["V"], c["d"], c["L"], c["window"]
+    pairs = C * (L + C)
+    if W > 0:
+        pairs = c["B"] * sum(min(L + c["C"], L + j + W + 1) - max(0, L + j - W) for j in range(c["C"]))
+    att_flop = 4.0 * c["D"] * c["Hq"] * pairs
     samp_bytes = 2.0 * C * V
     pe_flop = 2.0 * C * V * d
     out = {
@@ -220,7 +227,7 @@ def cpu_baseline(w: Workload, rows: int):
     t0 = time.perf_counter()
     K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
     group = c["Hq"] // c["Hkv"]
-    mask = np.ones((rows, K.shape[0]), bool)
+    mask = attention.visibility_mask(c["L"], 0, C, c["window"])[:rows]
     for h in range(c["Hq"]):
         attention.dense_mask_attention(q[:, h], K[:, h // group], Vv[:, h // group], mask, 1.0 / math.sqrt(D))
     so = sampler.denoise_sample(logits, 1.0, [0], [1], rows)
@@ -249,6 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=128, help="canvas positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="run the step as a sliding-window layer of this window (0: full attention)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 1 GiB device copies (reference for HBM counter calibration)")
     args = ap.parse_args()
@@ -270,7 +279,7 @@ def main():
         return
     import denoise_step_amd as dg
     dg.lib()
-    w = Workload()
+    w = Workload(dict(CFG, window=args.window))
     c = w.c
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
@@ -299,7 +308,7 @@ def main():
     alg = pe_algorithmic_bytes()
     achieved = alg / (pe_ms * 1e-3) / 1e9
     positions = c["B"] * c["C"]
-    kernels = call_rooflines(brk, pe_ms)
+    kernels = call_rooflines(brk, pe_ms, c)
     result = {
         "metric": METRIC,
         "value": positions * K / (ms_total * 1e-3),
@@ -313,9 +322,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "single_canvas", "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],
+        "config": {"workload": "single_canvas" + (f"_window{c['window']}" if c["window"] > 0 else ""), "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],
                    "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["D"], "page_size": c["page_size"],
-                   "d_embed": c["d"], "mlp_hidden": c["hidden"], "logit_pool": c["pool"]},
+                   "d_embed": c["d"], "mlp_hidden": c["hidden"], "logit_pool": c["pool"], "window": c["window"]},
         "steps_per_s": 1000.0 / ms_step,
         "wall_s_timed_region": wall,
         "roofline": {"kernel": PE_KERNEL, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

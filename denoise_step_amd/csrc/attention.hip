@@ -6,7 +6,9 @@
 // attention" (causality per request inside one batch; tiles holding only
 // masked entries are skipped); single-pass-reads page, section on keeping
 // each row's visibility (a request split into causal input rows and canvas
-// rows that share its KV block table; the p0 p1 c0 c1 example).
+// rows that share its KV block table; the p0 p1 c0 c1 example); section on
+// symmetric sliding-window attention (a window W keeps causal rows' keys
+// within W before the row and canvas rows' within W on both sides).
 //
 // bf16, head_dim 128 / 256: one MFMA kernel reads prefix keys from the pages
 // and causal / canvas keys from the k/v inputs, and appends the causal rows'
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(kWave) void attend_wave_kernel(
   if (row < 0 || row >= rows) return;
   const int hk = h / (Hq / Hkv);
   const int32_t n_cache = sp.cached + sp.n_causal;
-  const int32_t n_vis = (j < sp.n_causal) ? sp.cached + j + 1 : n_cache + sp.n_canvas;
+  const int2 rk = att_row_keys(sp, j);  // visible keys [rk.x, rk.y)
+  const int32_t k_lo = rk.x, n_vis = rk.y;
   for (int d = lane; d < D; d += kWave) qs[d] = ld_elem<BF16>(q, (static_cast<int64_t>(row) * Hq + h) * D + d) * scale;
   __syncthreads();
 
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(kWave) void attend_wave_kernel(
 #pragma unroll
   for (int c = 0; c < kCols; ++c) acc[c] = 0.f;
 
-  for (int kb = 0; kb < n_vis; kb += kWave) {
+  for (int kb = k_lo; kb < n_vis; kb += kWave) {
     const int kk = kb + lane;
     int64_t kbase = -1;  // element offset of this lane's key row (K and V share the layout)
     const void* ksrc = nullptr;
@@ -179,8 +182,8 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   p.qtiles = static_cast<int32_t>(cdiv(static_cast<int64_t>(max_rows) * G, kAttRows));
   const int32_t nblocks = static_cast<int32_t>(cdiv(max_keys, kAttKeys));
   const int64_t base = static_cast<int64_t>(n_req) * Hkv * p.qtiles;
-  // about one workgroup per CU, at least 4 key blocks per split
-  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 4)));
+  // about one workgroup per CU, at least 2 key blocks per split
+  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 2)));
   // a split's page ids are staged in LDS: at most kAttMaxPages pages (16 keys each) per split
   nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys,
                                                                static_cast<int64_t>(kAttMaxPages - 8) * 16)));
@@ -223,6 +226,8 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   DG_UNSUP(page_size == 16);
   DG_UNSUP(D == 32 || D == 64 || D == 128 || D == 256);
   const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
+  // a split's page ids (its keys plus one alignment block) must fit the staged list
+  DG_UNSUP(!plan.mfma || plan.split_keys + kAttKeys <= kAttMaxPages * 16);
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
   const bool bf = dtype == DG_BF16;

@@ -89,6 +89,23 @@ DG_DEV int att_kslot(int r, int c) {
   return r * (D / 8) + (c ^ (r & 15));
 }
 
+// Keys [x, y) visible to row j of a request (key positions: the cache, then the canvas rows; row j
+// sits at position cached + j).  Causal rows see up to themselves, canvas rows every key of the
+// request; a window W > 0 keeps positions within W before the row, and for a canvas row also
+// within W after it (DiffusionGemma/vLLM page, section on symmetric sliding-window attention).
+DG_DEV int2 att_row_keys(const dg_split& sp, int j) {
+  const int n_total = sp.cached + sp.n_causal + sp.n_canvas;
+  const int p = sp.cached + j;
+  const bool causal = j < sp.n_causal;
+  const int w = sp.window;
+  int lo = 0, hi = causal ? p + 1 : n_total;
+  if (w > 0) {
+    lo = max(0, p - w);
+    if (!causal) hi = min(hi, p + w + 1);
+  }
+  return make_int2(lo, hi);
+}
+
 // Key kk (kb <= kk < kb + 64) of a request: prefix positions (kk < cached) live in the page of
 // their 16-key group, whose id is one of the block's four staged ids `pq`; the causal and canvas
 // keys are rows row0 + kk - cached of k / v.  Both candidates are formed and one is selected, so
@@ -212,12 +229,15 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int nr = sp.n_causal + sp.n_canvas;
   const int m_tile0 = qtile * kAttRows;
   if (m_tile0 >= nr * a.G) return;
-  const int n_total = sp.cached + nr;
-  // last visible key + 1 over the tile's rows (rows are ordered causal then canvas)
+  // keys seen by the tile's rows: both edges of a row's range grow with the row (rows are ordered
+  // causal then canvas), so the tile sees [lo of its first row, hi of its last row).  The splits
+  // cut that range from its first 64-aligned block; the last split also takes the one block the
+  // alignment can add beyond nsplit * split_keys.
   const int j_last = min(nr - 1, (m_tile0 + kAttRows - 1) / a.G);
-  const int tile_lim = (j_last < sp.n_causal) ? sp.cached + j_last + 1 : n_total;
-  const int k_begin = split * a.split_keys;
-  const int k_end = min(tile_lim, k_begin + a.split_keys);
+  const int tile_lo = att_row_keys(sp, m_tile0 / a.G).x & ~(kAttKeys - 1);
+  const int tile_hi = att_row_keys(sp, j_last).y;
+  const int k_begin = tile_lo + split * a.split_keys;
+  const int k_end = min(tile_hi, k_begin + a.split_keys + (split == a.nsplit - 1 ? kAttKeys : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -228,11 +248,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int j = row_ok ? m / a.G : 0;
   const int h = hk * a.G + (row_ok ? m % a.G : 0);
   const int row = sp.row0 + j;
-  // rows past the tile's end compute an unused copy of row 0 and never force masking
-  const int lim = (row_ok && j < sp.n_causal) ? sp.cached + j + 1 : n_total;
-  int wave_lim = lim;
+  // visible keys [lo, hi) of this lane's row; rows past the tile's end compute an unused copy of
+  // row 0 and never force masking
+  const int2 rk = row_ok ? att_row_keys(sp, j) : make_int2(0, sp.cached + nr);
+  const int lo = rk.x, hi = rk.y;
+  int wave_hi = hi, wave_lo = lo;  // smallest hi and largest lo of the wave's rows
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wave_lim = min(wave_lim, __shfl_xor(wave_lim, o, kWave));
+  for (int o = 32; o > 0; o >>= 1) {
+    wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, o, kWave));
+  }
 
   // stage the physical page ids of the split's prefix positions (clamped into range)
   const int page_lo = k_begin / 16;
@@ -301,13 +326,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs (step s)
     }
     // ---- softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
-    if (kb + kAttKeys > wave_lim) {  // some key of the block is masked for some row of the wave
+    if (kb + kAttKeys > wave_hi || kb < wave_lo) {  // some key of the block is masked for some row of the wave
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
-          sc[b][e] = (key < lim) ? sc[b][e] : -INFINITY;
+          sc[b][e] = (key >= lo && key < hi) ? sc[b][e] : -INFINITY;
         }
     }
     float mx = -INFINITY;

@@ -93,6 +93,11 @@ dg_status dg_philox4x32_10(const uint32_t* ctr, const uint32_t* key, int64_t n, 
  *   canvas row   : sees all cached + n_causal cache positions and every canvas
  *                  row of the request (bidirectional decoder pass); its K/V is
  *                  never written.
+ * Sliding-window layers (same page, section on symmetric sliding-window
+ * attention): with window W > 0 a row at position p (causal row j at
+ * cached + j, canvas row j at cached + n_causal + j) keeps only keys at
+ * positions p - W .. p if causal, p - W .. p + W if canvas (2W + 1 keys).
+ * W <= 0 is a full-attention layer.
  * out = softmax(scale * q k^T over visible keys) v; query head h reads KV head
  * h / (Hq / Hkv).  No position encoding is applied.
  *
@@ -102,9 +107,11 @@ dg_status dg_philox4x32_10(const uint32_t* ctr, const uint32_t* key, int64_t n, 
  *   physical page page_table[splits[r].page0 + p / page_size], slot p % page_size.
  *   splits: device array of n_req dg_split.
  * Host-side bounds (used to size the grid; the caller guarantees them):
- *   max_rows_per_req >= n_causal + n_canvas and max_keys_per_req >= cached + n_causal + n_canvas
- *   for every request.
- * Supported: D in {32, 64, 128, 256}, page_size 16, Hq % Hkv == 0, window == 0.
+ *   max_rows_per_req >= n_causal + n_canvas and max_keys_per_req >= the span of keys the
+ *   request's rows see together: cached + n_causal + n_canvas, or at most
+ *   n_causal + n_canvas + 2 * window for a request with a window.
+ * Supported: D in {32, 64, 128, 256}, page_size 16, Hq % Hkv == 0; bf16 with D 128 / 256
+ * (the MFMA path) also max_keys_per_req <= 261120.
  * Workspace: dg_canvas_attention_ws_bytes(...) bytes (may be 0 -> NULL allowed).
  * ------------------------------------------------------------------------ */
 typedef struct dg_split {
@@ -113,7 +120,7 @@ typedef struct dg_split {
   int32_t n_causal;  /* causal rows in this launch (K/V appended at cached + j)       */
   int32_t n_canvas;  /* bidirectional canvas rows (K/V not written)                   */
   int32_t page0;     /* offset of the request's page list in page_table                */
-  int32_t window;    /* must be 0 (symmetric sliding windows are not implemented)     */
+  int32_t window;    /* sliding window W (> 0) of the layer, 0 for full attention     */
 } dg_split;
 
 size_t dg_canvas_attention_ws_bytes(int32_t n_req, int32_t rows, int32_t max_rows_per_req,

@@ -13,21 +13,22 @@ def _f(p, a):
     return synth.bf16_bits_to_f32(a).astype(np.float64) if p.dtype == "bf16" else a.astype(np.float64)
 
 
-def run_case(splits, Hq, Hkv, D, dtype, seed=0, check_cache=True):
+def run_case(splits, Hq, Hkv, D, dtype, seed=0, check_cache=True, window=0, max_keys=None):
     import denoise_step_amd as dg
     torch = P.torch_mod()
     p = synth.attention_problem(seed, splits, Hq, Hkv, D, dtype=dtype)
     up = (lambda a: P.dev_bf16(a)) if dtype == "bf16" else (lambda a: P.dev(a))
     q, k, v, kc, vc = (up(a) for a in (p.q, p.k, p.v, p.k_cache, p.v_cache))
-    sp = np.array([[p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i], 0] for i, s in enumerate(p.splits)],
-                  np.int32)
+    sp = np.array([[p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i], window]
+                   for i, s in enumerate(p.splits)], np.int32)
     max_rows = max(s.n_causal + s.n_canvas for s in p.splits)
-    max_keys = max(s.cached + s.n_causal + s.n_canvas for s in p.splits)
+    if max_keys is None:
+        max_keys = max(s.cached + s.n_causal + s.n_canvas for s in p.splits)
     scale = 1.0 / np.sqrt(D)
     out = dg.dg_canvas_attention(q, k, v, kc, vc, P.dev(p.page_table), P.dev(sp), max_rows, max_keys, scale)
     torch.cuda.synchronize()
     ref, rkc, rvc = oatt.canvas_attention(_f(p, p.q), _f(p, p.k), _f(p, p.v), _f(p, p.k_cache), _f(p, p.v_cache),
-                                          p.page_table, [tuple(r[:5]) for r in sp], p.page_size, scale)
+                                          p.page_table, [tuple(r) for r in sp], p.page_size, scale)
     got = P.host_f64(out)
     tol = P.TOL_ATT_BF16 if dtype == "bf16" else P.TOL_ATT_F32
     err = np.abs(got - ref).max()
@@ -74,3 +75,30 @@ def test_attention_tiny_loop_shapes_f32():
 def test_attention_causal_rows_with_key_splits(splits, Hq, Hkv, D):
     print(f"attention causal + splits {splits} {Hq}/{Hkv}/{D}", flush=True)
     run_case(splits, Hq, Hkv, D, "bf16", seed=21)
+
+
+WINDOWED = [
+    ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 32, 2, "f32"),      # the W = 2 three-request figure
+    ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 128, 2, "bf16"),
+    ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 64, 5, "f32"),
+    ([(300, 40, 70), (1, 0, 129)], 16, 8, 256, 33, "bf16"),      # band narrower than a key block
+    ([(2048, 0, 256)], 16, 8, 256, 128, "bf16"),                # single canvas, W = 128
+    ([(1000, 100, 200), (70, 0, 64)], 32, 8, 128, 300, "bf16"),  # G = 4, band wider than a tile's rows
+    ([(100, 0, 33)], 8, 2, 128, 1000, "bf16"),                   # window wider than the request
+]
+
+
+@pytest.mark.parametrize("case", range(len(WINDOWED)))
+def test_attention_sliding_window(case):
+    splits, Hq, Hkv, D, W, dtype = WINDOWED[case]
+    print(f"attention window case={case} W={W}", flush=True)
+    run_case(splits, Hq, Hkv, D, dtype, seed=40 + case, window=W)
+
+
+def test_attention_sliding_window_tight_key_bound():
+    """max_keys_per_req given as the band span (rows + 2W), well under cached + rows: fewer, shorter
+    key splits, and the last split takes the block its 64-alignment adds."""
+    splits, W = [(5000, 0, 256), (3001, 64, 0)], 200
+    span = max(s[1] + s[2] for s in splits) + 2 * W
+    print(f"attention window tight bound span={span}", flush=True)
+    run_case(splits, 16, 8, 256, "bf16", seed=51, window=W, max_keys=span)
