@@ -249,6 +249,64 @@ def cpu_baseline(w: Workload, rows: int):
                         f"against the full 262144 x 4096 table; {dt:.1f} s"))
 
 
+def serving_bench(policies=("deficit", "arrival")) -> dict:
+    """The batched serving loop (32 requests in bursts of 8, prompts U[512, 8192], 256-token
+    canvases, two blocks each, V = 262144, 8192 tokens per iteration) run to completion once per
+    admission policy: deficit admission, and admitting every waiting prefill at once.  A decode
+    iteration's time is what every running request waits for its next step (the decode stall).  Per iteration: one mixed
+    attention launch, then sampler / accept / convergence for the denoising requests; GPU time from
+    events around each iteration's launches (the host reads the commit flags once per iteration)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from denoise_step_amd.serving import ServingLoop
+    from synth.configs import SERVING as cfg
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    sched = synth.serving_schedule_inputs(cfg)
+    s, R, C, V = cfg["seed"], cfg["R"], cfg["C"], cfg["V"]
+    # admitting every waiting prefill at once can pack all prompts plus every canvas into one launch
+    n = int(R * C + sched["prompt"].sum())
+    log("serving: generating the Q/K/V row pools and the logit pools on the GPU")
+    base = dict(q=synth.normal_torch(s, "serving.q", (n, cfg["Hq"], cfg["D"]), 1.0, bf, dev),
+                k=synth.normal_torch(s, "serving.k", (n, cfg["Hkv"], cfg["D"]), 1.0, bf, dev),
+                v=synth.normal_torch(s, "serving.v", (n, cfg["Hkv"], cfg["D"]), 1.0, bf, dev),
+                logits=torch.stack([synth.zipf_logits_torch(s, ("serving.logits", i), R * C, V, dev)
+                                    for i in range(cfg["n_pool"])]))
+    out = {}
+    for pol in policies:
+        t = dict(base, k_cache=torch.zeros((sched["n_pages"], cfg["Hkv"], cfg["page_size"], cfg["D"]), dtype=bf,
+                                           device=dev))
+        t["v_cache"] = torch.zeros_like(t["k_cache"])
+        loop = ServingLoop(cfg, sched, t, device=dev, policy=pol)
+        log(f"serving: running the loop with {pol} admission")
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        recs = loop.run()
+        wall = time.perf_counter() - wall0
+        ms = np.array([r["gpu_ms"] for r in recs])
+        tok = np.array([r["tokens"] for r in recs])
+        den_rows = np.array([r["denoise_rows"] for r in recs])
+        wait = [int(np.nonzero([rid in r["admitted"] for r in recs])[0][0]) - int(sched["arrival"][rid])
+                for rid in range(R)]
+        dec_ms = ms[den_rows > 0]
+        out[pol] = {"iterations": len(recs), "gpu_s": float(ms.sum() / 1e3), "wall_s": wall,
+                    "decode_iter_ms_p50": float(np.median(dec_ms)), "decode_iter_ms_max": float(dec_ms.max()),
+                    "positions_per_s": float(den_rows.sum() / (ms.sum() / 1e3)),
+                    "iter_ms_p50": float(np.median(ms)), "iter_ms_max": float(ms.max()),
+                    "tokens_mean": float(tok.mean()), "tokens_max": int(tok.max()),
+                    "prefill_wait_iters_mean": float(np.mean(wait)), "prefill_wait_iters_max": int(max(wait))}
+    return {"metric": "serving loop: canvas positions denoised/sec with deficit token-budget admission",
+            "value": out["deficit"]["positions_per_s"], "unit": "positions/s", "n_gpus": 1,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "serving", "requests": R, "C": C, "V": V, "prompt": [cfg["P_min"], cfg["P_max"]],
+                       "arrival_every": cfg["arrival_every"], "token_budget": cfg["token_budget"],
+                       "blocks": cfg["blocks"], "max_steps": cfg["max_steps"], "heads_q": cfg["Hq"],
+                       "heads_kv": cfg["Hkv"], "head_dim": cfg["D"]},
+            "policies": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +314,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=128, help="canvas positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serving", action="store_true",
+                    help="run the batched serving loop with deficit admission (and admit-on-arrival for "
+                         "comparison) instead of the single-canvas step; prints its own JSON line")
     ap.add_argument("--window", type=int, default=0,
                     help="run the step as a sliding-window layer of this window (0: full attention)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -279,6 +340,9 @@ def main():
         return
     import denoise_step_amd as dg
     dg.lib()
+    if args.serving:
+        print(json.dumps(serving_bench()), flush=True)
+        return
     w = Workload(dict(CFG, window=args.window))
     c = w.c
     log(f"warmup {args.warmup} steps")

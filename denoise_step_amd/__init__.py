@@ -21,6 +21,7 @@ __all__ = [
     "dg_selfcond_prepared_bytes", "dg_selfcond_prepare", "dg_selfcond_ws_bytes", "dg_selfcond_embed",
     "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
     "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
+    "dg_deficit_admit",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -61,6 +62,7 @@ _SIGS = {
                                     _p, _p, _p]),
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
     "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
+    "dg_deficit_admit": (_i32, [_i64, _i64, _p, _i32, _p, _p, _p]),
     "dg_linear": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p]),
     "dg_gather_rows": (_i32, [_p, _i32, _i32, _i32, _p, _i32, _p, _p]),
 }
@@ -319,6 +321,18 @@ def dg_verify_prefix(draft, target, accepted=None, stream=None):
     _check(lib().dg_verify_prefix(_ptr(draft), _ptr(target), B, L, _ptr(accepted), _stream(stream)),
            "dg_verify_prefix")
     return accepted
+
+
+def dg_deficit_admit(budget, decode_tokens, queue, deficit):
+    """Host call: queue = prefill token counts in arrival order.  Returns (n_admitted, deficit, tokens)."""
+    n_q = len(queue)
+    arr = (ctypes.c_int64 * max(n_q, 1))(*[int(x) for x in queue])
+    d = ctypes.c_int64(int(deficit))
+    n = ctypes.c_int32(0)
+    tok = ctypes.c_int64(0)
+    _check(lib().dg_deficit_admit(int(budget), int(decode_tokens), ctypes.cast(arr, _p), n_q, ctypes.byref(d),
+                                  ctypes.byref(n), ctypes.byref(tok)), "dg_deficit_admit")
+    return n.value, d.value, tok.value
 
 
 def dg_linear(A, B, residual=None, trans_b=False, alpha=1.0, out=None, stream=None):

@@ -2,8 +2,9 @@
 
     python -m denoise_step_amd.build          # compiles every source, links libdg.so
 
-Each .hip source is compiled to an object in parallel, then linked into
-``denoise_step_amd/libdg.so``.  hipcc cross-compiles for gfx950 without a GPU.
+Each .hip source (hipcc) and host-only .cpp source (g++) is compiled to an object in
+parallel, then linked into ``denoise_step_amd/libdg.so``.  hipcc cross-compiles for gfx950
+without a GPU.
 """
 from __future__ import annotations
 
@@ -37,9 +38,16 @@ def hipcc() -> str:
     return exe
 
 
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):  # host-only sources (no device code)
+        obj = os.path.join(BUILD, os.path.basename(src).replace(".cpp", "_host.o"))
+        cmd = [shutil.which("g++") or "g++", *HOST_CFLAGS, "-c", src, "-o", obj]
+    else:
+        obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+        cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -48,7 +56,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(8, len(srcs), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

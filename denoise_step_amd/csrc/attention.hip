@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kWave) void attend_wave_kernel(
         ksrc = k_cache;
         vsrc = v_cache;
       } else {
-        const int64_t crow = sp.row0 + sp.n_causal + (kk - n_cache);
+        const int64_t crow = min(max(sp.row0 + sp.n_causal + (kk - n_cache), 0), rows - 1);  // clamped
         kbase = (crow * Hkv + hk) * D;
         ksrc = k;
         vsrc = v;

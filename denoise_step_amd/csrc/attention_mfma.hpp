@@ -116,7 +116,7 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, in
   int page = g == 0 ? pq.x : (g == 1 ? pq.y : (g == 2 ? pq.z : pq.w));
   page = min(max(page, 0), a.n_pages - 1);
   const int64_t cache_off = ((static_cast<int64_t>(page) * a.Hkv + hk) * 16 + (kk & 15)) * D;
-  const int64_t row = sp.row0 + max(kk - sp.cached, 0);
+  const int64_t row = min(max(sp.row0 + max(kk - sp.cached, 0), 0), a.rows - 1);  // clamped: cannot fault
   const int64_t new_off = (row * a.Hkv + hk) * D;
   const uint16_t* cache = is_v ? a.v_cache : a.k_cache;
   const uint16_t* fresh = is_v ? a.v : a.k;
@@ -198,6 +198,7 @@ DG_DEV void att_append(const AttArgs& a, const dg_split& sp, int hk, int j0, int
     const bool is_v = u >= n;
     const int w = is_v ? u - n : u;
     const int j = j0 + w / kChunks, c = w % kChunks;
+    if (sp.row0 + j < 0 || sp.row0 + j >= a.rows) continue;  // a descriptor outside the packed rows
     const int pos = sp.cached + j;
     const int ti = min(max(sp.page0 + pos / 16, 0), a.page_table_len - 1);
     const int64_t page = min(max(a.page_table[ti], 0), a.n_pages - 1);
@@ -248,6 +249,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int j = row_ok ? m / a.G : 0;
   const int h = hk * a.G + (row_ok ? m % a.G : 0);
   const int row = sp.row0 + j;
+  // a descriptor whose rows fall outside [0, rows) reads clamped rows and writes nothing there
+  const bool row_in = row >= 0 && row < a.rows;
+  const int row_c = min(max(row, 0), a.rows - 1);
   // visible keys [lo, hi) of this lane's row; rows past the tile's end compute an unused copy of
   // row 0 and never force masking
   const int2 rk = row_ok ? att_row_keys(sp, j) : make_int2(0, sp.cached + nr);
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   // Q fragment (B operand of S^T = K Q^T): 8 consecutive d per MFMA step
   bf16x8 qf[kDSteps];
   {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(row_ok ? row : sp.row0) * a.Hq + h) * D;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(row_c) * a.Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < kDSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
     // land Q before the first K/V copy: the compiler does not count the copies, so a wait for Q that
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     if (j0 < j1) att_append<D>(a, sp, hk, j0, j1);
   }
 
-  if (!row_ok) return;
+  if (!row_ok || !row_in) return;
   // O^T element e of tile t: d = 32 t + 8 (e / 4) + 4 half + e % 4, row = this lane's row
   if (a.nsplit == 1) {
     const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;

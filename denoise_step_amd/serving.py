@@ -1,0 +1,155 @@
+"""A batched serving loop around the denoise step, with deficit token-budget admission.
+
+Each iteration (Sangam page, section on the deficit token-budget scheduler, for the admission;
+DiffusionGemma/vLLM page, sections "Two modes, one set of weights" and "Dynamic per-sequence
+causal attention", for the phases that share one launch):
+  * decode work is scheduled first: every request that denoises a canvas (C canvas rows) or runs
+    the commit pass of its last block (C causal rows);
+  * dg_deficit_admit decides whether the prefill at the head of the arrival queue enters, whole;
+  * one dg_canvas_attention launch covers every scheduled request in its own phase (prefill and
+    commit rows causal with K/V appended to the request's pages, canvas rows bidirectional);
+  * the denoising requests run dg_denoise_sample -> dg_entropy_accept -> dg_converged; a request
+    admitted this iteration gets its first random canvas from dg_converged's prefill case;
+  * a committed block is followed by its commit pass in the next iteration; after `blocks` blocks
+    the request leaves.
+Activations and logits come from synthetic pools (no trained backbone): the loop exercises the
+scheduling, the launch composition, the paged cache and the per-request state.  All arithmetic
+runs in libdg; this module keeps the request phases and sequences the calls.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import dg_canvas_attention, dg_converged, dg_deficit_admit, dg_denoise_sample, dg_entropy_accept
+
+WAITING, PREFILL, DENOISE, COMMIT, DONE = range(5)
+
+
+class ServingLoop:
+    def __init__(self, cfg: dict, sched: dict, tensors: dict, device="cuda", policy: str = "deficit"):
+        """tensors: q/k/v row pools, k_cache/v_cache, logits pools [n_pool, R*C, V] (torch on `device`)."""
+        self.cfg, self.sched, self.policy = cfg, sched, policy
+        dev = torch.device(device)
+        self.dev = dev
+        self.t = tensors
+        R, C = cfg["R"], cfg["C"]
+        z = lambda shape, dt=torch.int32: torch.zeros(shape, dtype=dt, device=dev)
+        self.state = dict(prev_argmax=z((R, C)), unchanged=z(R),
+                          step_in_block=torch.full((R,), -1, dtype=torch.int32, device=dev), step_global=z(R),
+                          canvas=z((R, C)), sc_on=z(R, torch.uint8), committed=z(R, torch.uint8),
+                          out_tokens=z((R, C)), steps_used=z(R), num_sampled=z(R))
+        self.seed = torch.as_tensor(sched["seeds"].astype(np.int64), device=dev)
+        self.page_table = torch.as_tensor(sched["page_table"], dtype=torch.int32, device=dev)
+        self.accept = z((R, C), torch.uint8)
+        self.n_accept = z(R)
+        self.phase = np.full(R, WAITING)
+        self.cached = np.zeros(R, np.int64)
+        self.blocks_done = np.zeros(R, np.int64)
+        self.queue = []
+        self.deficit = 0
+        self.scale = 1.0 / math.sqrt(cfg["D"])
+
+    def _schedule(self, it: int):
+        """Phases of this iteration: arrivals join the queue, decode work first, then admission."""
+        cfg, s = self.cfg, self.sched
+        for r in np.nonzero(s["arrival"] == it)[0]:
+            self.queue.append(int(r))
+        decode = int(np.sum((self.phase == DENOISE) | (self.phase == COMMIT))) * cfg["C"]
+        sizes = [int(s["prompt"][r]) for r in self.queue]
+        if self.policy == "deficit":
+            n, self.deficit, tokens = dg_deficit_admit(cfg["token_budget"], decode, sizes, self.deficit)
+        else:                      # admit every waiting prefill at once (no budget)
+            n, tokens = len(sizes), decode + sum(sizes)
+        admitted = self.queue[:n]
+        self.queue = self.queue[n:]
+        for r in admitted:
+            self.phase[r] = PREFILL
+        return admitted, tokens
+
+    def _splits(self):
+        """dg_split rows (request order) for every request scheduled this iteration."""
+        C, rows, out = self.cfg["C"], 0, []
+        for r in range(self.cfg["R"]):
+            ph = self.phase[r]
+            if ph == PREFILL:
+                nc, nv, cached = int(self.sched["prompt"][r]), 0, 0
+            elif ph == DENOISE:
+                nc, nv, cached = 0, C, int(self.cached[r])
+            elif ph == COMMIT:
+                nc, nv, cached = C, 0, int(self.cached[r])
+            else:
+                continue
+            out.append([rows, cached, nc, nv, int(self.sched["page0"][r]), 0])
+            rows += nc + nv
+        return np.array(out, np.int32).reshape(-1, 6), rows
+
+    def step(self, it: int, record: bool = False):
+        cfg = self.cfg
+        R, C, V = cfg["R"], cfg["C"], cfg["V"]
+        admitted, tokens = self._schedule(it)
+        sp, rows = self._splits()
+        if rows > self.t["q"].shape[0]:
+            raise ValueError(f"iteration {it} packs {rows} rows but the Q/K/V pools hold {self.t['q'].shape[0]}")
+        rec = dict(iteration=it, admitted=admitted, tokens=tokens, deficit=self.deficit, rows=rows,
+                   denoise_rows=int(np.sum(self.phase == DENOISE)) * C)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        if rows > 0:
+            spl = torch.as_tensor(sp, device=self.dev)
+            max_rows = int(np.max(sp[:, 2] + sp[:, 3]))
+            max_keys = int(np.max(sp[:, 1] + sp[:, 2] + sp[:, 3]))
+            att = dg_canvas_attention(self.t["q"][:rows], self.t["k"][:rows], self.t["v"][:rows], self.t["k_cache"],
+                                      self.t["v_cache"], self.page_table, spl, max_rows, max_keys, self.scale)
+            if record:
+                rec["splits"] = sp.copy()
+                rec["attention"] = att.float().cpu().numpy()
+        den = torch.as_tensor((self.phase == DENOISE).astype(np.uint8), device=self.dev)
+        pre = torch.as_tensor(((self.phase == DENOISE) | (self.phase == PREFILL)).astype(np.uint8), device=self.dev)
+        st = self.state
+        if bool((self.phase == DENOISE).any()):
+            logits = self.t["logits"][it % cfg["n_pool"]]
+            step_now = st["step_global"].clone()
+            so = dg_denoise_sample(logits, V, C, self.seed, step_now, cfg["temperature"], active=den)
+            dg_entropy_accept(so["entropy"].view(R, C), so["sample"].view(R, C), st["canvas"], V, cfg["budget"],
+                              self.seed, step_now, active=den, accept=self.accept, n_accept=self.n_accept)
+            argmax, entropy = so["argmax"].view(R, C), so["entropy"].view(R, C)
+        else:
+            argmax = torch.zeros((R, C), dtype=torch.int32, device=self.dev)
+            entropy = torch.zeros((R, C), dtype=torch.float32, device=self.dev)
+        if bool(((self.phase == DENOISE) | (self.phase == PREFILL)).any()):
+            st["committed"].zero_()
+            dg_converged(argmax, entropy, V, cfg["k"], cfg["tau"], cfg["max_steps"], self.seed, st, active=pre)
+        ev1.record()
+        committed = st["committed"].cpu().numpy().astype(bool) & (self.phase == DENOISE)
+        rec["gpu_ms"] = (ev0, ev1)
+        rec["committed"] = {int(r): st["out_tokens"][r].cpu().numpy().copy() for r in np.nonzero(committed)[0]}
+        if record:
+            rec["canvas"] = st["canvas"].cpu().numpy().copy()
+        # phase transitions for the next iteration
+        for r in range(R):
+            ph = self.phase[r]
+            if ph == PREFILL:
+                self.cached[r] = int(self.sched["prompt"][r])
+                self.phase[r] = DENOISE
+            elif ph == COMMIT:
+                self.cached[r] += C
+                self.phase[r] = DENOISE if self.blocks_done[r] < cfg["blocks"] else DONE
+            elif ph == DENOISE and committed[r]:
+                self.blocks_done[r] += 1
+                self.phase[r] = COMMIT
+        return rec
+
+    def run(self, max_iters: int = 100000, record: bool = False):
+        log = []
+        for it in range(max_iters):
+            if np.all(self.phase == DONE):
+                break
+            log.append(self.step(it, record))
+        torch.cuda.synchronize()
+        for rec in log:
+            a, b = rec.pop("gpu_ms")
+            rec["gpu_ms"] = a.elapsed_time(b)
+        return log

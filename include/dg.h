@@ -285,6 +285,25 @@ dg_status dg_allowed_probs(const void* logits, int64_t ld, int32_t dtype, int32_
                            float temperature, float* q, int32_t* answer, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * dg_deficit_admit -- one iteration of the deficit token-budget admission of
+ * a serving loop (Sangam page, section on the deficit token-budget scheduler).
+ * Host function: plain host pointers, no GPU work, no stream.
+ * All decode work (decode_tokens: canvas rows and commit-pass rows of the
+ * running requests) is scheduled first.  The waiting prefill at the head of the
+ * first-come-first-served queue is admitted whole when
+ *   (budget - decode_tokens) + *deficit >= queue[0];
+ * then *deficit <- 0 and *n_admitted = 1.  Otherwise *deficit grows by
+ * budget - decode_tokens (negative when decode work overruns the budget) and
+ * *n_admitted = 0.  With an empty queue nothing changes.  Prefills are never
+ * split and at most one is admitted per iteration.
+ *   budget > 0, decode_tokens >= 0, queue [n_queue] token counts (queue[0] > 0),
+ *   deficit in/out, n_admitted out, tokens out (may be NULL): tokens scheduled
+ *   this iteration (decode_tokens plus the admitted prefill).
+ * ------------------------------------------------------------------------ */
+dg_status dg_deficit_admit(int64_t budget, int64_t decode_tokens, const int64_t* queue, int32_t n_queue,
+                           int64_t* deficit, int32_t* n_admitted, int64_t* tokens);
+
+/* ------------------------------------------------------------------------ *
  * dg_verify_prefix -- greedy block verification (DFlash page, section "What
  * DFlash does differently", verification step): accepted[b] = index of the
  * first j with draft[b][j] != target[b][j], or L if the whole block matches.

@@ -294,3 +294,38 @@ def zipf_logits_torch(seed: int, tag, rows: int, V: int, device, alpha_max: floa
         perm = torch.argsort(torch.rand((r1 - r0, V), generator=g, device=device), dim=1)
         out[r0:r1] = (np.sqrt(3.0) * z + alpha[r0:r1, None] * base[perm]).to(dtype)
     return out
+
+
+def serving_schedule_inputs(cfg: dict) -> dict:
+    """Prompt lengths, arrival iterations and the paged layout of the serving loop.
+
+    Request r arrives at iteration (r // burst) * arrival_every (bursts of `burst` requests, 1 if
+    unset) with a prompt of U[P_min, P_max] tokens and
+    owns ceil((P + blocks * C) / page_size) pages (prompt plus every committed block), a contiguous
+    slice of one shuffled page table with two spare pages that nobody owns."""
+    s, R, ps = cfg["seed"], cfg["R"], cfg["page_size"]
+    P = rng_for(s, "serving.prompts").integers(cfg["P_min"], cfg["P_max"] + 1, R).astype(np.int64)
+    need = [-(-(int(p) + cfg["blocks"] * cfg["C"]) // ps) for p in P]
+    n_pages = int(sum(need)) + 2
+    tbl = page_table(s, "serving.pages", n_pages)
+    page0 = np.concatenate([[0], np.cumsum(need)[:-1]]).astype(np.int32)
+    arrival = (np.arange(R, dtype=np.int64) // cfg.get("burst", 1)) * cfg["arrival_every"]
+    return dict(prompt=P, arrival=arrival, page0=page0,
+                page_table=tbl[:int(sum(need))].copy(), n_pages=n_pages,
+                seeds=np.array([(s << 20) + r for r in range(R)], np.uint64),
+                max_rows=int(R * cfg["C"] + cfg["P_max"]))
+
+
+def serving_small_tensors(cfg: dict, sched: dict) -> dict:
+    """Host arrays (bf16 bits) for the small serving loop: Q/K/V row pools, initial caches, logit pools."""
+    s, R, C, V = cfg["seed"], cfg["R"], cfg["C"], cfg["V"]
+    n = sched["max_rows"]
+    Hq, Hkv, D, ps = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page_size"]
+    return dict(
+        q=normal_bf16(s, "serving.q", (n, Hq, D)),
+        k=normal_bf16(s, "serving.k", (n, Hkv, D)),
+        v=normal_bf16(s, "serving.v", (n, Hkv, D)),
+        k_cache=normal_bf16(s, "serving.kc", (sched["n_pages"], Hkv, ps, D)),
+        v_cache=normal_bf16(s, "serving.vc", (sched["n_pages"], Hkv, ps, D)),
+        logits=np.stack([zipf_logits_bf16(s, ("serving.logits", i), R * C, V) for i in range(cfg["n_pool"])]),
+    )

@@ -40,3 +40,22 @@ BLOCK_DRAFT = dict(
 )
 
 ALL = [TINY_LOOP, SINGLE_CANVAS, BATCHED, STRUCTURED_READ, BLOCK_DRAFT]
+
+# Batched serving loop with deficit token-budget admission (Sangam page, deficit scheduler): requests
+# arrive in bursts of `burst` every `arrival_every` iterations with prompts U[P_min, P_max]; each is
+# prefilled whole when
+# admitted, then denoises `blocks` canvases of C tokens (commit pass after each).  Activations (Q/K/V
+# rows) and logits are synthetic pools: the loop exercises scheduling, launch composition, the paged
+# cache and the per-request state, not a trained backbone.
+SERVING = dict(
+    name="serving", seed=0, R=32, C=256, P_min=512, P_max=8192, burst=8, arrival_every=6, page_size=16, Hq=16,
+    Hkv=8, D=256, V=262144, token_budget=8192, blocks=2, budget=8.0, k=3, tau=0.3, max_steps=8,
+    temperature=1.0, n_pool=2,
+)
+
+# The same loop at sizes the oracle runs in seconds (bf16, MFMA attention path).
+SERVING_SMALL = dict(
+    name="serving_small", seed=0, R=6, C=16, P_min=8, P_max=72, arrival_every=1, page_size=16, Hq=4, Hkv=2,
+    D=128, V=2048, token_budget=72, blocks=2, budget=4.0, k=2, tau=0.3, max_steps=4, temperature=1.0,
+    n_pool=3,
+)
