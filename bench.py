@@ -35,8 +35,10 @@ METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
-           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0)
+           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0, e4m3=False)
+E4M3_SCALE = 2.0 ** -7      # the E4M3 table stores E / scale; E ~ N(0, 1) / 8 stays far inside +-448
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
+PE_KERNEL_E4M3 = "gemm_f16_e4m3_splitk_kernel"
 PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp",)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
 
@@ -76,8 +78,9 @@ def source_sha() -> str:
 
 
 def pe_algorithmic_bytes(c=CFG) -> int:
-    """E read once (V x d) + P read once (C x V), both 16-bit, per launch (one canvas)."""
-    return 2 * c["V"] * c["d"] + 2 * c["B"] * c["C"] * c["V"]
+    """E read once (V x d, 16-bit, or 8-bit for the E4M3 table) + P read once (C x V, 16-bit), per
+    launch (one canvas)."""
+    return (1 if c["e4m3"] else 2) * c["V"] * c["d"] + 2 * c["B"] * c["C"] * c["V"]
 
 
 def traffic_from_counters(per_launch_alg: int):
@@ -119,12 +122,17 @@ class Workload:
         # keys the canvas rows see together: the whole request, or the band of a sliding window
         self.key_span = L + C if c["window"] <= 0 else min(L + C, C + 2 * c["window"])
         self.pool = [synth.zipf_logits_torch(s, ("bench.logits", i), C, V, dev) for i in range(c["pool"])]
-        self.E = synth.normal_torch(s, "bench.E", (V, d), 1 / 8, bf, dev)
         self.wg = synth.normal_torch(s, "bench.wg", (d, h), 0.02, bf, dev)
         self.wu = synth.normal_torch(s, "bench.wu", (d, h), 0.02, bf, dev)
         self.wd = synth.normal_torch(s, "bench.wd", (h, d), 0.02, bf, dev)
-        log("preparing the fp16 operand copies")
-        self.prepared = dg.dg_selfcond_prepare(self.E, self.wg, self.wu, self.wd)
+        if c["e4m3"]:
+            self.E = synth.e4m3_table_torch(s, "bench.E8", (V, d), 1 / 8, E4M3_SCALE, dev)
+            log("preparing the E4M3 E^T and fp16 MLP operand copies")
+            self.prepared = dg.dg_selfcond_prepare_e4m3(self.E, self.wg, self.wu, self.wd)
+        else:
+            self.E = synth.normal_torch(s, "bench.E", (V, d), 1 / 8, bf, dev)
+            log("preparing the fp16 operand copies")
+            self.prepared = dg.dg_selfcond_prepare(self.E, self.wg, self.wu, self.wd)
         self.seed = torch.tensor([s], dtype=torch.int64, device=dev)
         z = lambda n, dt=torch.int32: torch.zeros(n, dtype=dt, device=dev)
         self.state = dict(prev_argmax=z((1, C)), unchanged=z(1), step_in_block=torch.full((1,), -1, dtype=torch.int32,
@@ -163,9 +171,14 @@ class Workload:
         rec(3)
         dg.dg_converged(self.so["argmax"], self.so["entropy"], c["V"], c["k"], c["tau"], c["max_steps"], self.seed, s)
         rec(4)
-        dg.dg_selfcond_embed_sc(self.sc_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
-                                s["canvas"], self.E, self.prepared, c["hidden"], x_out=self.x, ws=self.ws_sc,
-                                pe_events=pe_ev)
+        if c["e4m3"]:
+            dg.dg_selfcond_embed_sc_e4m3(self.sc_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
+                                         s["canvas"], self.E, E4M3_SCALE, self.prepared, c["hidden"], x_out=self.x,
+                                         ws=self.ws_sc, pe_events=pe_ev)
+        else:
+            dg.dg_selfcond_embed_sc(self.sc_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
+                                    s["canvas"], self.E, self.prepared, c["hidden"], x_out=self.x, ws=self.ws_sc,
+                                    pe_events=pe_ev)
         rec(5)
 
 
@@ -219,7 +232,11 @@ def cpu_baseline(w: Workload, rows: int):
     kc, vc = f64(w.k_cache), f64(w.v_cache)
     pt = w.page_table.cpu().numpy()
     logits = f64(w.pool[0][:rows])
-    E = w.E.float().cpu().numpy()
+    if c["e4m3"]:
+        from oracle import fp8
+        E = fp8.decode_table(w.E.cpu().numpy(), E4M3_SCALE)
+    else:
+        E = w.E.float().cpu().numpy()
     wg, wu, wd = f64(w.wg), f64(w.wu), f64(w.wd)
     ent_canvas = np.random.default_rng(0).gamma(1.0, 2.0, (1, C)).astype(np.float32)
     threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
@@ -317,6 +334,8 @@ def main():
     ap.add_argument("--serving", action="store_true",
                     help="run the batched serving loop with deficit admission (and admit-on-arrival for "
                          "comparison) instead of the single-canvas step; prints its own JSON line")
+    ap.add_argument("--e4m3", action="store_true",
+                    help="run the step with the E4M3 (FP8) embedding table instead of the bf16 one")
     ap.add_argument("--window", type=int, default=0,
                     help="run the step as a sliding-window layer of this window (0: full attention)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -343,7 +362,7 @@ def main():
     if args.serving:
         print(json.dumps(serving_bench()), flush=True)
         return
-    w = Workload(dict(CFG, window=args.window))
+    w = Workload(dict(CFG, window=args.window, e4m3=args.e4m3))
     c = w.c
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
@@ -369,7 +388,7 @@ def main():
     pe_ms = sum(hev.elapsed_ms(a, b) for a, b in pe_ev) / K
     names = ["canvas_attention", "denoise_sample", "entropy_accept", "converged", "selfcond_embed"]
     brk = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in call_ev) * 1000.0 / K for i, n in enumerate(names)}
-    alg = pe_algorithmic_bytes()
+    alg = pe_algorithmic_bytes(c)
     achieved = alg / (pe_ms * 1e-3) / 1e9
     positions = c["B"] * c["C"]
     kernels = call_rooflines(brk, pe_ms, c)
@@ -384,15 +403,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not c["e4m3"] else "bf16 (E4M3 table, fp16 MFMA)",
         "data": "synthetic",
-        "config": {"workload": "single_canvas" + (f"_window{c['window']}" if c["window"] > 0 else ""), "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],
+        "config": {"workload": "single_canvas" + (f"_window{c['window']}" if c["window"] > 0 else "")
+                   + ("_e4m3" if c["e4m3"] else ""), "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],
                    "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["D"], "page_size": c["page_size"],
                    "d_embed": c["d"], "mlp_hidden": c["hidden"], "logit_pool": c["pool"], "window": c["window"]},
         "steps_per_s": 1000.0 / ms_step,
         "wall_s_timed_region": wall,
-        "roofline": {"kernel": PE_KERNEL, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(alg),
+        "roofline": {"kernel": PE_KERNEL_E4M3 if c["e4m3"] else PE_KERNEL, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if c["e4m3"] else traffic_from_counters(alg),
                      "algorithmic_bytes_per_launch": alg, "avg_launch_us": pe_ms * 1000.0,
                      "source_sha": source_sha()},
         "breakdown_us": brk,

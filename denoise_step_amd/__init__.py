@@ -21,7 +21,8 @@ __all__ = [
     "dg_selfcond_prepared_bytes", "dg_selfcond_prepare", "dg_selfcond_ws_bytes", "dg_selfcond_embed",
     "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
     "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
-    "dg_deficit_admit",
+    "dg_deficit_admit", "dg_e4m3_decode", "dg_selfcond_prepared_bytes_e4m3", "dg_selfcond_prepare_e4m3",
+    "dg_selfcond_embed_sc_e4m3",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -63,6 +64,11 @@ _SIGS = {
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
     "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
     "dg_deficit_admit": (_i32, [_i64, _i64, _p, _i32, _p, _p, _p]),
+    "dg_e4m3_decode": (_i32, [_p, _i64, _f32, _p, _p, _p]),
+    "dg_selfcond_prepared_bytes_e4m3": (_sz, [_i32, _i32, _i32]),
+    "dg_selfcond_prepare_e4m3": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _p, _sz, _p]),
+    "dg_selfcond_embed_sc_e4m3": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _f32, _p, _i32, _i32, _i32, _p, _p, _p,
+                                         _p, _sz, _p, _p, _p]),
     "dg_linear": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p]),
     "dg_gather_rows": (_i32, [_p, _i32, _i32, _i32, _p, _i32, _p, _p]),
 }
@@ -301,6 +307,46 @@ def dg_selfcond_embed_sc(sc_operand, V, row_max, row_lnz, sc_on, canvas, E, prep
     _check(lib().dg_selfcond_embed_sc(_ptr(sc_operand), _ptr(row_max), _ptr(row_lnz), _ptr(sc_on), _ptr(canvas), B,
                                       C, _ptr(E), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
                                       _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_sc")
+    return x_out
+
+
+def dg_e4m3_decode(codes, scale=1.0, out16=None, stream=None):
+    """uint8 E4M3 codes (numel % 8 == 0) -> float32 values times scale (and fp16 values into out16)."""
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(lib().dg_e4m3_decode(_ptr(codes), codes.numel(), float(scale), _ptr(out), _ptr(out16), _stream(stream)),
+           "dg_e4m3_decode")
+    return out
+
+
+def dg_selfcond_prepared_bytes_e4m3(V, d, hidden) -> int:
+    return int(lib().dg_selfcond_prepared_bytes_e4m3(V, d, hidden))
+
+
+def dg_selfcond_prepare_e4m3(E8, w_gate, w_up, w_down, stream=None):
+    """E8: uint8 E4M3 codes [V, d]; MLP weights bf16.  Builds the E4M3 E^T and the fp16 MLP operands."""
+    V, d = E8.shape
+    hidden = w_gate.shape[1]
+    nb = dg_selfcond_prepared_bytes_e4m3(V, d, hidden)
+    prepared = torch.empty(max(nb, 1), dtype=torch.uint8, device=E8.device)
+    _check(lib().dg_selfcond_prepare_e4m3(_ptr(E8), _ptr(w_gate), _ptr(w_up), _ptr(w_down), V, d, hidden,
+                                          _ptr(prepared), nb, _stream(stream)), "dg_selfcond_prepare_e4m3")
+    return prepared
+
+
+def dg_selfcond_embed_sc_e4m3(sc_operand, V, row_max, row_lnz, sc_on, canvas, E8, e_scale, prepared, hidden,
+                              x_out=None, s_out=None, y_out=None, ws=None, stream=None, pe_events=None):
+    """dg_selfcond_embed_sc against an E4M3 table (values e_scale * decode(E8)); x_out is bf16."""
+    B, C = canvas.shape
+    rows = B * C
+    d = E8.shape[1]
+    x_out = torch.empty((rows, d), dtype=torch.bfloat16, device=E8.device) if x_out is None else x_out
+    nb = dg_selfcond_ws_bytes_sc(rows, V, d, hidden)
+    ws = _ws(nb, ws, E8.device)
+    ev0, ev1 = (None, None) if pe_events is None else (int(pe_events[0]), int(pe_events[1]))
+    _check(lib().dg_selfcond_embed_sc_e4m3(_ptr(sc_operand), _ptr(row_max), _ptr(row_lnz), _ptr(sc_on),
+                                           _ptr(canvas), B, C, _ptr(E8), float(e_scale), _ptr(prepared), V, d, hidden,
+                                           _ptr(x_out), _ptr(s_out), _ptr(y_out), _ptr(ws), nb, ev0, ev1,
+                                           _stream(stream)), "dg_selfcond_embed_sc_e4m3")
     return x_out
 
 

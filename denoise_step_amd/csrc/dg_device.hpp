@@ -157,6 +157,29 @@ DG_DEV void dpp_wave_argmax(float& v, int32_t& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// ---------------------------------------------------------------- OCP E4M3 (FP8) codes
+// Conversions by gfx950's instructions; exact, since every E4M3 value is an fp16 (and fp32) value.
+// Byte b of a word holds element b.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+DG_DEV half8 e4m3x8_to_half8(uint32_t lo, uint32_t hi) {
+  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  half8 h;
+  h[0] = a[0]; h[1] = a[1]; h[2] = b[0]; h[3] = b[1];
+  h[4] = c[0]; h[5] = c[1]; h[6] = d[0]; h[7] = d[1];
+  return h;
+}
+
+DG_DEV float4 e4m3x4_to_float4(uint32_t w) {
+  const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return make_float4(a[0], a[1], b[0], b[1]);
+}
+
 // s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
 // lgkmcnt 11:8 left at their maxima).  Used where direct global -> LDS copies issued from inline
 // asm must have landed: the compiler does not count those instructions.

@@ -42,6 +42,7 @@ struct GemmArgs {
   int64_t lda;        // rows of the A operand's blocked layout (M rounded up to 256)
   const _Float16* Bt;
   int64_t ldb;        // rows of Bt (N)
+  const uint8_t* Bt8; // E4M3 right operand (gemm_f16_e4m3_splitk_kernel), same blocked layout in bytes
   float* part;  // [splits][M][N]
   int32_t M, N, K;
   int32_t kchunk;  // K per split (multiple of kGemmStages * kGemmTK)
@@ -95,19 +96,52 @@ DG_DEV void gemm_dma(const _Float16* __restrict__ base, int64_t rows, int row0, 
         : "memory", "m0");
 }
 
+// E4M3 right operand: a K slice of one row is 32 bytes, two 16-byte chunks; chunk c of row r is
+// stored at LDS chunk c ^ f8(r), f8(r) = ((r >> 2) ^ (r >> 3)) & 1.  A B-fragment read has 32 lanes
+// ask for the same 8-byte quarter of 32 consecutive rows; with the flip, every run of 4 rows that
+// would share banks (same r mod 4, or same r mod 8 on a 64-bank array) is split evenly between the
+// two halves of the row, so the read runs at the array's full width.  f8 depends on r mod 16 only.
+DG_DEV int gemm_swz8(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+
+// One copy instruction moves 1 KB = 32 rows x 32 bytes of one K slice; lane i writes LDS chunk i,
+// i.e. row i / 2, chunk i & 1, and fetches source chunk (i & 1) ^ f8(i / 2) of that row.
+DG_DEV uint32_t gemm_lane_offset8() {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane >> 1;
+  return static_cast<uint32_t>(r * 32 + 16 * ((lane & 1) ^ gemm_swz8(r)));
+}
+
+DG_DEV void gemm_dma8(const uint8_t* __restrict__ base, int64_t rows, int row0, int k0, uint32_t lane_off,
+                      uint8_t* lds, int q) {
+  const uint8_t* ub = base + kblk_index(row0 + 32 * q, k0, rows);
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + q * 1024));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt"
+      :
+      : "s"(lds_addr), "v"(lane_off), "s"(ub)
+      : "memory", "m0");
+}
+
 // Issue one stage: A (256 rows) and B (TN rows) as 1-KB instructions shared round-robin by the waves.
 // A has mtiles * 256 rows in its layout (rows past M are read but never stored); Bt has N rows.
-template <int TN>
-DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, int wave, _Float16* as,
-                       _Float16* bs) {
+template <int TN, bool BF8>
+DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, uint32_t off8, int wave,
+                       _Float16* as, _Float16* bs) {
 #pragma unroll
   for (int i = 0; i < kGemmTM / 16 / kGemmWaves; ++i) gemm_dma<false>(g.A, g.lda, m0, k0, off, as, wave + kGemmWaves * i);
+  if constexpr (BF8) {
 #pragma unroll
-  for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma<true>(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
+    for (int i = 0; i < TN / 32 / kGemmWaves; ++i)
+      gemm_dma8(g.Bt8, g.ldb, n0, k0, off8, reinterpret_cast<uint8_t*>(bs), wave + kGemmWaves * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma<true>(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
+  }
 }
 
 // Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.
-template <int TN>
+template <int TN, bool BF8>
 DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __restrict__ bs, int wm, int wn, int lane,
                          floatx16 (&acc)[4][TN / 128]) {
   constexpr int NJ = TN / 128;
@@ -119,8 +153,16 @@ DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __rest
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(wn + j * 32 + (lane & 31), c));
+    for (int j = 0; j < NJ; ++j) {
+      const int row = wn + j * 32 + (lane & 31);
+      if constexpr (BF8) {
+        const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(bs) + row * 32 +
+                                                        16 * ((c >> 1) ^ gemm_swz8(row)) + 8 * (c & 1));
+        b[j] = e4m3x8_to_half8(q.x, q.y);
+      } else {
+        b[j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(row, c));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -129,18 +171,18 @@ DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __rest
 }
 
 // vector-memory instructions a wave issues per stage
-template <int TN>
+template <int TN, bool BF8>
 constexpr int gemm_dma_per_stage() {
-  return (kGemmTM + TN) / 16 / kGemmWaves;
+  return (kGemmTM / 16 + (BF8 ? TN / 32 : TN / 16)) / kGemmWaves;
 }
 
 // Wait until at most `pending` later stages of this wave's copies are still in flight, then
 // barrier.  A bare s_barrier is used instead of __syncthreads(): the latter's release fence would
 // wait for every outstanding copy, including the prefetched stages.  The empty asm statements keep
 // the compiler from moving LDS accesses across the wait and the barrier.
-template <int TN>
+template <int TN, bool BF8>
 DG_DEV void gemm_wait_barrier(int pending) {
-  constexpr int n = gemm_dma_per_stage<TN>();
+  constexpr int n = gemm_dma_per_stage<TN, BF8>();
   asm volatile("" ::: "memory");
   if (pending >= 2)
     __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * n));
@@ -152,16 +194,14 @@ DG_DEV void gemm_wait_barrier(int pending) {
   asm volatile("" ::: "memory");
 }
 
-// ROLE only names the instantiation (0: P.E contraction, 1: MLP GEMMs) so that profilers report the
-// dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
-// of 256).
-template <int ROLE, int TN>
-__global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
+// The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
+template <int TN, bool BF8>
+DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
+  constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
   __shared__ __attribute__((aligned(16))) _Float16 As0[kGemmTM * kGemmTK], As1[kGemmTM * kGemmTK],
       As2[kGemmTM * kGemmTK], As3[kGemmTM * kGemmTK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs0[TN * kGemmTK], Bs1[TN * kGemmTK], Bs2[TN * kGemmTK],
-      Bs3[TN * kGemmTK];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs0[kBs], Bs1[kBs], Bs2[kBs], Bs3[kBs];
   // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
@@ -178,6 +218,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
   const uint32_t off = gemm_lane_offset();
+  const uint32_t off8 = BF8 ? gemm_lane_offset8() : 0u;
 
   floatx16 acc[4][NJ];
 #pragma unroll
@@ -187,18 +228,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (nstage > 0) gemm_issue<TN>(g, m0, n0, k_begin, off, wave, As0, Bs0);
-  if (nstage > 1) gemm_issue<TN>(g, m0, n0, k_begin + kGemmTK, off, wave, As1, Bs1);
-  if (nstage > 2) gemm_issue<TN>(g, m0, n0, k_begin + 2 * kGemmTK, off, wave, As2, Bs2);
+  if (nstage > 0) gemm_issue<TN, BF8>(g, m0, n0, k_begin, off, off8, wave, As0, Bs0);
+  if (nstage > 1) gemm_issue<TN, BF8>(g, m0, n0, k_begin + kGemmTK, off, off8, wave, As1, Bs1);
+  if (nstage > 2) gemm_issue<TN, BF8>(g, m0, n0, k_begin + 2 * kGemmTK, off, off8, wave, As2, Bs2);
   // iteration s: wait for stage s, barrier (stage s visible; every wave is past compute(s - 1), so
   // that stage's buffer may be refilled), issue stage s + 3, compute stage s
 #define DG_GEMM_STEP(S_OFF, AC, BC, AN, BN)                                                   \
   {                                                                                           \
     const int s_ = s + (S_OFF);                                                               \
-    gemm_wait_barrier<TN>(min(2, nstage - 1 - s_));                                           \
+    gemm_wait_barrier<TN, BF8>(min(2, nstage - 1 - s_));                                      \
     if (s_ + 3 < nstage)                                                                      \
-      gemm_issue<TN>(g, m0, n0, k_begin + (s_ + 3) * kGemmTK, off, wave, AN, BN);             \
-    gemm_compute<TN>(AC, BC, wm, wn, lane, acc);                                              \
+      gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s_ + 3) * kGemmTK, off, off8, wave, AN, BN);  \
+    gemm_compute<TN, BF8>(AC, BC, wm, wn, lane, acc);                                         \
   }
   for (int s = 0; s < nstage; s += 4) {
     DG_GEMM_STEP(0, As0, Bs0, As3, Bs3)
@@ -219,6 +260,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
         const int n = n0 + wn + j * 32 + (lane & 31);
         if (m < g.M) out[static_cast<int64_t>(m) * g.N + n] = acc[i][j][e];
       }
+}
+
+// ROLE only names the instantiation (0: P.E contraction, 1: MLP GEMMs) so that profilers report the
+// dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
+// of 256).
+template <int ROLE, int TN>
+__global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
+  gemm_splitk_body<TN, false>(g);
+}
+
+// P.E against an E4M3 embedding table (N a multiple of 256): the E stream is one byte per element.
+__global__ __launch_bounds__(kGemmThreads) void gemm_f16_e4m3_splitk_kernel(GemmArgs g) {
+  gemm_splitk_body<256, true>(g);
 }
 
 struct GemmPlan {
@@ -257,8 +311,8 @@ inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk
 }
 
 inline GemmArgs gemm_args(const _Float16* A, int64_t lda, const _Float16* Bt, int64_t ldb, float* part, int32_t M,
-                          int32_t N, int32_t K, const GemmPlan& p) {
-  return GemmArgs{A, lda, Bt, ldb, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
+                          int32_t N, int32_t K, const GemmPlan& p, const uint8_t* Bt8 = nullptr) {
+  return GemmArgs{A, lda, Bt, ldb, Bt8, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
 }
 
 }  // namespace dg

@@ -138,6 +138,33 @@ extern "C" dg_status dg_philox4x32_10(const uint32_t* ctr, const uint32_t* key, 
   return DG_OK;
 }
 
+namespace dg {
+namespace {
+// 8 codes per thread through both conversions the kernels use (fp32 for the embedding rows, fp16
+// for the GEMM operand)
+__global__ void e4m3_decode_kernel(const uint8_t* __restrict__ codes, int64_t n8, float scale,
+                                   float* __restrict__ out32, _Float16* __restrict__ out16) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint2 q = *reinterpret_cast<const uint2*>(codes + 8 * i);
+  const float4 a = e4m3x4_to_float4(q.x), b = e4m3x4_to_float4(q.y);
+  *reinterpret_cast<float4*>(out32 + 8 * i) = make_float4(a.x * scale, a.y * scale, a.z * scale, a.w * scale);
+  *reinterpret_cast<float4*>(out32 + 8 * i + 4) = make_float4(b.x * scale, b.y * scale, b.z * scale, b.w * scale);
+  if (out16 != nullptr) *reinterpret_cast<half8*>(out16 + 8 * i) = e4m3x8_to_half8(q.x, q.y);
+}
+}  // namespace
+}  // namespace dg
+
+extern "C" dg_status dg_e4m3_decode(const uint8_t* codes, int64_t n, float scale, float* out32, void* out16,
+                                    dg_stream_t stream) {
+  DG_ARG(codes && out32 && n > 0 && n % 8 == 0 && n < (int64_t(1) << 40));
+  DG_UNSUP(aligned16(codes) && aligned16(out32) && (out16 == nullptr || aligned16(out16)));
+  e4m3_decode_kernel<<<static_cast<unsigned>(cdiv(n / 8, 256)), 256, 0, as_stream(stream)>>>(
+      codes, n / 8, scale, out32, reinterpret_cast<_Float16*>(out16));
+  DG_LAUNCHED();
+  return DG_OK;
+}
+
 extern "C" dg_status dg_verify_prefix(const int32_t* draft, const int32_t* target, int32_t B, int32_t L,
                                       int32_t* accepted, dg_stream_t stream) {
   DG_ARG(draft && target && accepted && B > 0 && L > 0);

@@ -53,6 +53,24 @@ __global__ __launch_bounds__(256) void transpose_bf16_to_f16_kernel(const uint16
   }
 }
 
+// E4M3 codes src [K][N] -> dst, the K-blocked byte operand with N rows and Kp columns: element
+// (n, k) = src[k][n] for k < K, code 0 (+0.0) for K <= k < Kp.
+__global__ __launch_bounds__(256) void transpose_e4m3_kernel(const uint8_t* __restrict__ src, int32_t K, int32_t N,
+                                                             int64_t Kp, uint8_t* __restrict__ dst) {
+  __shared__ uint8_t tile[64][65];
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int k = k0 + i, n = n0 + tx;
+    tile[i][tx] = (k < K && n < N) ? src[static_cast<int64_t>(k) * N + n] : uint8_t{0};
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int n = n0 + i, k = k0 + tx;
+    if (n < N && k < Kp) dst[kblk_index(n, k, N)] = tile[tx][i];
+  }
+}
+
 // ---------------------------------------------------------------- bf16 path kernels
 // w is written in the K-blocked layout with Mp rows (the GEMM's left operand).  A workgroup covers
 // 8 rows x 256 columns: each row is read as 512 contiguous bytes and, for each of the 8 K slices of
@@ -137,11 +155,11 @@ __global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* 
                                                         int32_t N, int64_t Mp, const float* __restrict__ row_max,
                                                         const float* __restrict__ row_lnz,
                                                         const float* __restrict__ sc_ref, int32_t nchunk,
-                                                        float* __restrict__ s_out, _Float16* __restrict__ s16,
-                                                        float* __restrict__ s_inv) {
+                                                        float e_scale, float* __restrict__ s_out,
+                                                        _Float16* __restrict__ s16, float* __restrict__ s_inv) {
   __shared__ float red[kReduceThreads / kWave];
   const int r = blockIdx.x;
-  const float f = (1.0f / kProbScale) * __expf(-row_lnz[r]);
+  const float f = (e_scale / kProbScale) * __expf(-row_lnz[r]);
   const float m2 = sc_ref != nullptr ? row_max[r] * 1.4426950408889634f : 0.f;
   float4 acc[C];
 #pragma unroll
@@ -227,10 +245,11 @@ __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict
 }
 
 // x_out = bf16(E[canvas] + (sc_on ? y : 0)), y from the partials of the down GEMM; one thread per
-// 4 consecutive values of a row
+// 4 consecutive values of a row.  E8: E is E4M3 codes, each value times e_scale.
+template <bool E8>
 __global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                            int32_t d, int32_t V, int32_t C,
-                                                           const uint16_t* __restrict__ E,
+                                                           const void* __restrict__ E, float e_scale,
                                                            const int32_t* __restrict__ canvas,
                                                            const uint8_t* __restrict__ sc_on,
                                                            const float* __restrict__ h_inv,
@@ -239,8 +258,14 @@ __global__ __launch_bounds__(256) void embed_reduce_kernel(const float* __restri
   if (idx >= static_cast<int64_t>(M) * d) return;
   const int r = static_cast<int>(idx / d), c = static_cast<int>(idx - static_cast<int64_t>(r) * d);
   const int64_t tok = min(max(canvas[r], 0), V - 1);
-  const uint2 e = *reinterpret_cast<const uint2*>(E + tok * d + c);
-  float4 x = make_float4(bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y));
+  float4 x;
+  if constexpr (E8) {
+    x = e4m3x4_to_float4(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(E) + tok * d + c));
+    x = make_float4(x.x * e_scale, x.y * e_scale, x.z * e_scale, x.w * e_scale);
+  } else {
+    const uint2 e = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(E) + tok * d + c);
+    x = make_float4(bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y));
+  }
   const bool on = sc_on[r / C] != 0;
   if (on || y_out != nullptr) {
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -296,6 +321,17 @@ PreparedLayout prepared_layout(int32_t V, int32_t d, int32_t hidden) {
   p.Kp = pad128(V);
   p.off_et = 0;
   p.off_wgu = round_up(p.off_et + static_cast<size_t>(d) * p.Kp * 2, 256);
+  p.off_wd = round_up(p.off_wgu + static_cast<size_t>(2) * hidden * d * 2, 256);
+  p.bytes = round_up(p.off_wd + static_cast<size_t>(d) * hidden * 2, 256);
+  return p;
+}
+
+// E4M3 table: E^T as bytes (d rows, Kp columns), then the same fp16 MLP operands
+PreparedLayout prepared_layout_e4m3(int32_t V, int32_t d, int32_t hidden) {
+  PreparedLayout p{};
+  p.Kp = pad128(V);
+  p.off_et = 0;
+  p.off_wgu = round_up(p.off_et + static_cast<size_t>(d) * p.Kp, 256);
   p.off_wd = round_up(p.off_wgu + static_cast<size_t>(2) * hidden * d * 2, 256);
   p.bytes = round_up(p.off_wd + static_cast<size_t>(d) * hidden * 2, 256);
   return p;
@@ -367,11 +403,14 @@ void launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 
 // P.E (from the operand w), its reduce, the gated MLP and the embedding: the bf16 path after the
 // probability operand exists.  sc_ref != nullptr: w comes from the sampling pass (per-run references).
+// et8 != nullptr: the table is E4M3 (E holds the codes, values times e_scale) and et8 is its
+// K-blocked transpose; et is then unused.
 dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* sc_ref, int32_t nchunk,
                              const float* row_max, const float* row_lnz, const uint8_t* sc_on, const int32_t* canvas,
                              int32_t rows, int32_t C, const void* E, const _Float16* et, const _Float16* wgu,
                              const _Float16* wd, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,
-                             float* y_out, char* wsb, void* pe_start, void* pe_stop, hipStream_t s) {
+                             float* y_out, char* wsb, void* pe_start, void* pe_stop, hipStream_t s,
+                             const uint8_t* et8 = nullptr, float e_scale = 1.f) {
   const int64_t rows64 = rows;
   auto* part = reinterpret_cast<float*>(wsb + p.off_part);
   auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
@@ -379,16 +418,20 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
   auto* s_inv = reinterpret_cast<float*>(wsb + p.off_sinv);
   auto* h_inv = reinterpret_cast<float*>(wsb + p.off_hinv);
   if (pe_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_start), s) == hipSuccess, DG_E_HIP);
-  launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
+  if (et8 != nullptr)
+    gemm_f16_e4m3_splitk_kernel<<<p.pe.grid, kGemmThreads, 0, s>>>(
+        gemm_args(w, p.Mp, nullptr, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, et8));
+  else
+    launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
   const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
   if (rc == 1)
     pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
-                                                        nchunk, s_out, s16, s_inv);
+                                                        nchunk, e_scale, s_out, s16, s_inv);
   else
     pe_reduce_kernel<2><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
-                                                        nchunk, s_out, s16, s_inv);
+                                                        nchunk, e_scale, s_out, s16, s_inv);
   DG_LAUNCHED();
   launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
@@ -403,9 +446,12 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
   DG_LAUNCHED();
   launch_gemm<1>(p.g2, gemm_args(h16, p.Mp, wd, d, part, rows, d, hidden, p.g2), s);
   DG_LAUNCHED();
-  embed_reduce_kernel<<<blocks_for(rows64 * d / 4), 256, 0, s>>>(part, p.g2.splits, rows, d, V, C,
-                                                                 reinterpret_cast<const uint16_t*>(E), canvas, sc_on,
-                                                                 h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
+  if (et8 != nullptr)
+    embed_reduce_kernel<true><<<blocks_for(rows64 * d / 4), 256, 0, s>>>(
+        part, p.g2.splits, rows, d, V, C, E, e_scale, canvas, sc_on, h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
+  else
+    embed_reduce_kernel<false><<<blocks_for(rows64 * d / 4), 256, 0, s>>>(
+        part, p.g2.splits, rows, d, V, C, E, 1.f, canvas, sc_on, h_inv, reinterpret_cast<uint16_t*>(x_out), y_out);
   DG_LAUNCHED();
   return DG_OK;
 }
@@ -580,4 +626,65 @@ extern "C" dg_status dg_selfcond_embed_sc(const void* sc_operand, const float* r
   const int32_t nchunk = static_cast<int32_t>(cdiv(V, kScChunk));
   return selfcond_bf16_tail(p, w, ref, nchunk, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden,
                             x_out, s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop, as_stream(stream));
+}
+
+extern "C" size_t dg_selfcond_prepared_bytes_e4m3(int32_t V, int32_t d, int32_t hidden) {
+  if (V <= 0 || d <= 0 || hidden <= 0) return 0;
+  return prepared_layout_e4m3(V, d, hidden).bytes;
+}
+
+extern "C" dg_status dg_selfcond_prepare_e4m3(const uint8_t* E8, const void* w_gate, const void* w_up,
+                                              const void* w_down, int32_t V, int32_t d, int32_t hidden,
+                                              void* prepared, size_t prepared_bytes, dg_stream_t stream) {
+  DG_ARG(E8 && w_gate && w_up && w_down && prepared && V > 0 && d > 0 && hidden > 0);
+  DG_UNSUP(d % 256 == 0 && hidden % 128 == 0 && d <= 8192 && hidden <= 8192);
+  const PreparedLayout L = prepared_layout_e4m3(V, d, hidden);
+  DG_REQUIRE(prepared_bytes >= L.bytes, DG_E_WORKSPACE);
+  hipStream_t s = as_stream(stream);
+  char* base = reinterpret_cast<char*>(prepared);
+  auto* et8 = reinterpret_cast<uint8_t*>(base + L.off_et);
+  auto* wgu = reinterpret_cast<_Float16*>(base + L.off_wgu);
+  auto* wd = reinterpret_cast<_Float16*>(base + L.off_wd);
+  // E8 [V][d] -> E8^T (d rows, Kp columns)
+  transpose_e4m3_kernel<<<dim3(static_cast<unsigned>(cdiv(L.Kp, 64)), static_cast<unsigned>(cdiv(d, 64))), 256, 0,
+                          s>>>(E8, V, d, L.Kp, et8);
+  DG_LAUNCHED();
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_gate), d, hidden, d, 0, 2 * hidden,
+                                              wgu);
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(d, 64)), static_cast<unsigned>(cdiv(hidden, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_up), d, hidden, d, hidden,
+                                              2 * hidden, wgu);
+  transpose_bf16_to_f16_kernel<<<dim3(static_cast<unsigned>(cdiv(hidden, 64)), static_cast<unsigned>(cdiv(d, 64))),
+                                 256, 0, s>>>(reinterpret_cast<const uint16_t*>(w_down), hidden, d, hidden, 0, d, wd);
+  DG_LAUNCHED();
+  return DG_OK;
+}
+
+extern "C" dg_status dg_selfcond_embed_sc_e4m3(const void* sc_operand, const float* row_max, const float* row_lnz,
+                                               const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C,
+                                               const uint8_t* E8, float e_scale, const void* prepared, int32_t V,
+                                               int32_t d, int32_t hidden, void* x_out, float* s_out, float* y_out,
+                                               void* ws, size_t ws_bytes, void* pe_start, void* pe_stop,
+                                               dg_stream_t stream) {
+  DG_ARG(sc_operand && row_max && row_lnz && sc_on && canvas && E8 && prepared && x_out);
+  DG_ARG(B > 0 && C > 0 && V > 0 && d > 0 && hidden > 0 && e_scale > 0.f && e_scale < INFINITY);
+  DG_UNSUP(d % 256 == 0 && hidden % 128 == 0 && d <= 8192 && hidden <= 8192);
+  const int64_t rows64 = static_cast<int64_t>(B) * C;
+  DG_ARG(rows64 <= 65535);
+  const int32_t rows = static_cast<int32_t>(rows64);
+  const Bf16Plan p = bf16_plan(rows, V, d, hidden, true);
+  DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
+  const PreparedLayout L = prepared_layout_e4m3(V, d, hidden);
+  const char* pb = reinterpret_cast<const char*>(prepared);
+  const auto* et8 = reinterpret_cast<const uint8_t*>(pb + L.off_et);
+  const auto* wgu = reinterpret_cast<const _Float16*>(pb + L.off_wgu);
+  const auto* wd = reinterpret_cast<const _Float16*>(pb + L.off_wd);
+  const char* ob = reinterpret_cast<const char*>(sc_operand);
+  const auto* w = reinterpret_cast<const _Float16*>(ob);
+  const auto* ref = reinterpret_cast<const float*>(ob + round_up(static_cast<size_t>(p.Mp) * p.Kp * 2, 256));
+  const int32_t nchunk = static_cast<int32_t>(cdiv(V, kScChunk));
+  return selfcond_bf16_tail(p, w, ref, nchunk, row_max, row_lnz, sc_on, canvas, rows, C, E8, nullptr, wgu, wd, V, d,
+                            hidden, x_out, s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop,
+                            as_stream(stream), et8, e_scale);
 }

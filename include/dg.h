@@ -285,6 +285,36 @@ dg_status dg_allowed_probs(const void* logits, int64_t ld, int32_t dtype, int32_
                            float temperature, float* q, int32_t* answer, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * E4M3 embedding-table variant (DiffusionGemma/vLLM page, section "Quantized
+ * checkpoint support": the model ships FP8 weights).  The table is stored as
+ * OCP E4M3 codes E8 [V][d] (uint8, row-major) times one fp32 scale e_scale.
+ *
+ * dg_e4m3_decode: out32[i] = e_scale * value(codes[i]) (f32); out16 (may be
+ *   NULL) = value(codes[i]) as fp16 (exact).  The conversions the kernels use.
+ *   n % 8 == 0; codes, out32, out16 16-byte aligned.
+ * dg_selfcond_prepare_e4m3: builds the K-blocked E8^T byte operand and the
+ *   fp16 MLP operands (w_gate, w_up, w_down bf16 as in dg_selfcond_prepare)
+ *   into `prepared` (dg_selfcond_prepared_bytes_e4m3 bytes).
+ * dg_selfcond_embed_sc_e4m3: dg_selfcond_embed_sc with the table E = e_scale *
+ *   value(E8): s = softmax(x) E on fp16 MFMA with the E4M3 operand converted to
+ *   fp16 after its LDS read (the E stream is 1 byte per element), then the
+ *   MLP and x_out = bf16(E[canvas] + (sc_on ? y : 0)).  Workspace:
+ *   dg_selfcond_ws_bytes_sc.
+ * Supported: d % 256 == 0, hidden % 128 == 0, both <= 8192.
+ * ------------------------------------------------------------------------ */
+dg_status dg_e4m3_decode(const uint8_t* codes, int64_t n, float scale, float* out32, void* out16,
+                         dg_stream_t stream);
+size_t dg_selfcond_prepared_bytes_e4m3(int32_t V, int32_t d, int32_t hidden);
+dg_status dg_selfcond_prepare_e4m3(const uint8_t* E8, const void* w_gate, const void* w_up, const void* w_down,
+                                   int32_t V, int32_t d, int32_t hidden, void* prepared, size_t prepared_bytes,
+                                   dg_stream_t stream);
+dg_status dg_selfcond_embed_sc_e4m3(const void* sc_operand, const float* row_max, const float* row_lnz,
+                                    const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C,
+                                    const uint8_t* E8, float e_scale, const void* prepared, int32_t V, int32_t d,
+                                    int32_t hidden, void* x_out, float* s_out, float* y_out, void* ws,
+                                    size_t ws_bytes, void* pe_start, void* pe_stop, dg_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * dg_deficit_admit -- one iteration of the deficit token-budget admission of
  * a serving loop (Sangam page, section on the deficit token-budget scheduler).
  * Host function: plain host pointers, no GPU work, no stream.

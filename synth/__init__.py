@@ -329,3 +329,24 @@ def serving_small_tensors(cfg: dict, sched: dict) -> dict:
         v_cache=normal_bf16(s, "serving.vc", (sched["n_pages"], Hkv, ps, D)),
         logits=np.stack([zipf_logits_bf16(s, ("serving.logits", i), R * C, V) for i in range(cfg["n_pool"])]),
     )
+
+
+def e4m3_table(seed: int, tag, shape, std: float, scale: float) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of N(0, std^2) / scale values, rounded to nearest by torch's
+    float8_e4m3fn conversion: a table whose values are scale * decode(codes)."""
+    import torch
+    x = normal_f32(seed, tag, shape, std) / np.float32(scale)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_table_torch(seed: int, tag, shape, std: float, scale: float, device, chunk_rows: int = 1 << 14):
+    """e4m3_table drawn with torch's device generator (full-size tables), as a uint8 tensor."""
+    import torch
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    flat = out.view(shape[0], -1)
+    g = _torch_gen(seed, tag, device)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        x = torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device) * (std / scale)
+        flat[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return out

@@ -1,0 +1,101 @@
+"""GPU parity of the E4M3 embedding-table variant (through the C ABI) against the oracle with the
+decoded table: the conversions, the fused operand path at ragged sizes, and sampled rows at full
+size (V = 262144, d = 4096)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import fp8 as ofp8
+from oracle import sampler as osamp
+from oracle import selfcond as osc
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+E_SCALE = 2.0 ** -7     # E ~ N(0, 1) / 8 stored as codes of N(0, 16): far inside E4M3's +-448
+
+
+def test_e4m3_decode_all_codes():
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    print("e4m3 decode of all 256 codes", flush=True)
+    codes = np.tile(np.arange(256, dtype=np.uint8), 2)
+    out16 = torch.empty(codes.size, dtype=torch.float16, device="cuda")
+    got32 = dg.dg_e4m3_decode(P.dev(codes), 0.5, out16=out16).cpu().numpy().astype(np.float64)
+    got16 = out16.float().cpu().numpy().astype(np.float64)
+    ref = ofp8.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got32), nan) and np.array_equal(np.isnan(got16), nan)
+    np.testing.assert_array_equal(got32[~nan], 0.5 * ref[~nan])
+    np.testing.assert_array_equal(got16[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("V,d,hidden,rows_per_req", [(1000, 256, 128, 16), (40000, 256, 256, 16),
+                                                      (70000, 512, 384, 48)])
+def test_selfcond_e4m3_operand_path(V, d, hidden, rows_per_req):
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    print(f"selfcond e4m3 operand path V={V} d={d} h={hidden}", flush=True)
+    B, C = 3, rows_per_req
+    rows = B * C
+    ld = (V + 7) // 8 * 8
+    bits = synth.f32_to_bf16_bits(synth.zipf_logits_f32(8, ("sc8", V), rows, ld))
+    E8 = synth.e4m3_table(8, ("sc8.E", V), (V, d), 1 / 8, E_SCALE)
+    wg, wu = (synth.normal_bf16(8, (t, V), (d, hidden), 0.5) for t in ("sc8.wg", "sc8.wu"))
+    wd = synth.normal_bf16(8, ("sc8.wd", V), (hidden, d), 0.5)
+    canvas = synth.rng_for(8, "sc8.canvas").integers(0, V, (B, C)).astype(np.int32)
+    sc_on = np.array([1, 0, 1], np.uint8)
+    st, op = dg.dg_denoise_sample_sc(P.dev_bf16(bits), V, C, P.dev(np.arange(B, dtype=np.int64)),
+                                     P.dev(np.full(B, 5, np.int32)))
+    prepared = dg.dg_selfcond_prepare_e4m3(P.dev(E8), *(P.dev_bf16(a) for a in (wg, wu, wd)))
+    s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    y_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    x = dg.dg_selfcond_embed_sc_e4m3(op, V, st["row_max"], st["row_lnz"], P.dev(sc_on), P.dev(canvas), P.dev(E8),
+                                     E_SCALE, prepared, hidden, s_out=s_out, y_out=y_out)
+    torch.cuda.synchronize()
+    host_l = synth.bf16_bits_to_f32(bits).astype(np.float64)[:, :V]
+    ref = osamp.denoise_sample(host_l, 1.0, np.arange(B), np.full(B, 5), C)
+    Pm = osc.probs_from_stats(host_l, 1.0, ref.row_max, ref.row_lnz)
+    f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)
+    E = ofp8.decode_table(E8, E_SCALE)
+    rx, rs, ry = osc.selfcond_embed(Pm, canvas, sc_on, E, f(wg), f(wu), f(wd), C, to_bf16=False)
+    es = P.rel_norm_err(s_out.cpu().numpy(), rs)
+    ey = P.rel_norm_err(y_out.cpu().numpy(), ry)
+    print(f"e4m3 operand path: P.E max normwise rel err {es.max():.2e}, MLP {ey.max():.2e}")
+    assert es.max() <= P.TOL_NORM_REL, es.max()
+    assert ey.max() <= P.TOL_NORM_REL, ey.max()
+    P.check_bf16_output(P.host_f64(x), rx)
+
+
+def test_selfcond_e4m3_single_canvas_full_size():
+    """Sampled rows of the full-size step (V = 262144, d = 4096) against the decoded table."""
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    print("selfcond e4m3 full size", flush=True)
+    V, d, hidden, C = 262144, 4096, 1024, 256
+    E8 = synth.e4m3_table_torch(0, "single_canvas.E8", (V, d), 1 / 8, E_SCALE, "cuda")
+    wg = synth.normal_torch(0, "single_canvas.wg", (d, hidden), 0.02, torch.bfloat16, "cuda")
+    wu = synth.normal_torch(0, "single_canvas.wu", (d, hidden), 0.02, torch.bfloat16, "cuda")
+    wd = synth.normal_torch(0, "single_canvas.wd", (hidden, d), 0.02, torch.bfloat16, "cuda")
+    lt = synth.zipf_logits_torch(0, "single_canvas.logits_t", C, V, "cuda")
+    canvas = P.dev(synth.rng_for(0, "single_canvas.canvas").integers(0, V, (1, C)).astype(np.int32))
+    st, op = dg.dg_denoise_sample_sc(lt, V, C, P.dev(np.zeros(1, np.int64)), P.dev(np.zeros(1, np.int32)))
+    prepared = dg.dg_selfcond_prepare_e4m3(E8, wg, wu, wd)
+    s_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
+    y_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
+    x = dg.dg_selfcond_embed_sc_e4m3(op, V, st["row_max"], st["row_lnz"], P.dev(np.array([1], np.uint8)), canvas,
+                                     E8, E_SCALE, prepared, hidden, s_out=s_out, y_out=y_out)
+    torch.cuda.synchronize()
+    rows = [0, 77, 255]
+    host_l = lt[rows].float().cpu().numpy().astype(np.float64)
+    Pm = np.stack([osamp.probabilities(host_l[i], 1.0) for i in range(len(rows))])
+    s_ref = np.zeros((len(rows), d))
+    for v0 in range(0, V, 16384):
+        s_ref += Pm[:, v0:v0 + 16384] @ ofp8.decode_table(E8[v0:v0 + 16384].cpu().numpy(), E_SCALE)
+    err = P.rel_norm_err(s_out.cpu().numpy()[rows], s_ref)
+    print(f"e4m3 full size: P.E max normwise rel err {err.max():.2e} on rows {rows}", flush=True)
+    assert err.max() <= P.TOL_NORM_REL
+    # x = bf16(E[canvas] + y) with E the decoded table row of each sampled position's token
+    tok = canvas.cpu().numpy()[0, rows].astype(np.int64)
+    e_rows = ofp8.decode_table(E8[torch.as_tensor(tok, device="cuda")].cpu().numpy(), E_SCALE)
+    P.check_bf16_output(P.host_f64(x)[rows], e_rows + y_out.cpu().numpy().astype(np.float64)[rows])
