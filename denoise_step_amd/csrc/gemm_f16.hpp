@@ -140,33 +140,44 @@ DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, 
   }
 }
 
-// Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.
+// Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.  Every operand
+// fragment of the stage (both 16-K steps) is read before the first MFMA, so the MFMAs of the first
+// step wait only for their own reads and the second step's reads arrive behind them.
 template <int TN, bool BF8>
 DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __restrict__ bs, int wm, int wn, int lane,
                          floatx16 (&acc)[4][TN / 128]) {
   constexpr int NJ = TN / 128;
+  constexpr int KS = kGemmTK / 16;  // 16-K steps per stage
+  half8 a[KS][4], b[KS][NJ];
+  uint2 b8[KS][NJ];
 #pragma unroll
-  for (int kk = 0; kk < kGemmTK / 8; kk += 2) {  // chunk pair (kk, kk + 1) = 16 K
-    const int c = kk + (lane >> 5);
-    half8 a[4], b[NJ];
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = 2 * ks + (lane >> 5);  // 8-K chunk of this lane
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
+      a[ks][i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int row = wn + j * 32 + (lane & 31);
-      if constexpr (BF8) {
-        const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(bs) + row * 32 +
-                                                        16 * ((c >> 1) ^ gemm_swz8(row)) + 8 * (c & 1));
-        b[j] = e4m3x8_to_half8(q.x, q.y);
-      } else {
-        b[j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(row, c));
-      }
+      if constexpr (BF8)
+        b8[ks][j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(bs) + row * 32 +
+                                                    16 * ((c >> 1) ^ gemm_swz8(row)) + 8 * (c & 1));
+      else
+        b[ks][j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(row, c));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them to their uses)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if constexpr (BF8) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[ks][j] = e4m3x8_to_half8(b8[ks][j].x, b8[ks][j].y);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
   }
 }
 
