@@ -192,7 +192,7 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));
   if (p.nsplit > 1) {
     const size_t n = static_cast<size_t>(p.nsplit) * rows * Hq;
-    p.off_ml = round_up(n * D * sizeof(float), 256);
+    p.off_ml = round_up(n * D * sizeof(uint16_t), 256);
     p.bytes = round_up(p.off_ml + n * sizeof(float2), 256);
   }
   return p;
@@ -263,7 +263,7 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
     a.nsplit = plan.nsplit;
     a.split_keys = plan.split_keys;
     a.out = reinterpret_cast<uint16_t*>(out);
-    a.o_part = reinterpret_cast<float*>(ws);
+    a.o_part = reinterpret_cast<uint16_t*>(ws);
     a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
     a.qtiles = plan.qtiles;
     const int64_t items = static_cast<int64_t>(n_req) * plan.nsplit * Hkv * plan.qtiles;

@@ -69,8 +69,8 @@ struct AttArgs {
   int32_t qtiles;       // row tiles of kAttRows packed rows per request
   int32_t n_items;      // n_req * nsplit * Hkv * qtiles work items
   uint16_t* out;        // [rows][Hq][D] bf16 (nsplit == 1)
-  float* o_part;        // [nsplit][rows][Hq][D] (nsplit > 1)
-  float2* ml_part;      // [nsplit][rows][Hq]    (nsplit > 1)
+  uint16_t* o_part;     // [nsplit][rows][Hq][D] bf16, each split's output normalised by its own l (nsplit > 1)
+  float2* ml_part;      // [nsplit][rows][Hq] (reference max in log2 units, l)  (nsplit > 1)
 };
 
 template <int D>
@@ -389,45 +389,36 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   }
 
   if (!row_ok || !row_in) return;
-  // O^T element e of tile t: d = 32 t + 8 (e / 4) + 4 half + e % 4, row = this lane's row
-  if (a.nsplit == 1) {
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    uint16_t* orow = a.out + (static_cast<int64_t>(row) * a.Hq + h) * D;
+  // O^T element e of tile t: d = 32 t + 8 (e / 4) + 4 half + e % 4, row = this lane's row.  One split:
+  // the output; several: this split's output normalised by its own l, in bf16, and (m, l).
+  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+  const int64_t ridx = static_cast<int64_t>(a.nsplit == 1 ? 0 : split) * a.rows * a.Hq +
+                       static_cast<int64_t>(row) * a.Hq + h;
+  uint16_t* orow = (a.nsplit == 1 ? a.out : a.o_part) + ridx * D;
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t)
+  for (int t = 0; t < kDTiles; ++t)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * t + 8 * g4 + 4 * half;
-        uint2 w;
-        w.x = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 1] * inv)) << 16);
-        w.y = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 2] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + d) = w;
-      }
-  } else {
-    const int64_t ridx = static_cast<int64_t>(split) * a.rows * a.Hq + static_cast<int64_t>(row) * a.Hq + h;
-    float* orow = a.o_part + ridx * D;
-#pragma unroll
-    for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * t + 8 * g4 + 4 * half;
-        *reinterpret_cast<float4*>(orow + d) =
-            make_float4(o[t][4 * g4], o[t][4 * g4 + 1], o[t][4 * g4 + 2], o[t][4 * g4 + 3]);
-      }
-    if (half == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
-  }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * t + 8 * g4 + 4 * half;
+      uint2 w;
+      w.x = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4] * inv)) |
+            (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 1] * inv)) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 2] * inv)) |
+            (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + d) = w;
+    }
+  if (a.nsplit > 1 && half == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
 }
 
-// Combine KV splits: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  Grid
+// Combine KV splits: out = sum_s c_s Ohat_s / sum_s c_s with c_s = 2^(m_s - M) l_s, M = max_s m_s and
+// Ohat_s = O_s / l_s the split's normalised output (so sum_s c_s Ohat_s = sum_s 2^(m_s - M) O_s).  Grid
 // (packed row, 1024-value slice of the row's Hq x D outputs); four consecutive d per thread, every
 // split's loads issued before the sums.  Rows outside every request's range were never written and
 // are skipped.
 constexpr int kMergeSplits = 16;  // the most splits a launch uses
 
 template <int D>
-__global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(256) void attend_merge_kernel(const uint16_t* __restrict__ o_part,
                                                            const float2* __restrict__ ml_part, int32_t nsplit,
                                                            int32_t rows, int32_t Hq,
                                                            const dg_split* __restrict__ splits, int32_t n_req,
@@ -445,12 +436,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restri
     const int h = e / D, d = e - h * D;
     const int64_t rh = static_cast<int64_t>(row) * Hq + h;
     float2 ml[kMergeSplits];
-    float4 ov[kMergeSplits];
+    uint2 ov[kMergeSplits];
 #pragma unroll
     for (int s = 0; s < kMergeSplits; ++s) {
       if (s < nsplit) {
         ml[s] = ml_part[s * plane + rh];
-        ov[s] = *reinterpret_cast<const float4*>(o_part + (s * plane + rh) * D + d);
+        ov[s] = *reinterpret_cast<const uint2*>(o_part + (s * plane + rh) * D + d);
       }
     }
     float M = -INFINITY;
@@ -462,12 +453,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restri
 #pragma unroll
     for (int s = 0; s < kMergeSplits; ++s) {
       if (s < nsplit && ml[s].x != -INFINITY) {
-        const float w = exp2f(ml[s].x - M);
-        L += w * ml[s].y;
-        acc.x += w * ov[s].x;
-        acc.y += w * ov[s].y;
-        acc.z += w * ov[s].z;
-        acc.w += w * ov[s].w;
+        const float c = exp2f(ml[s].x - M) * ml[s].y;
+        L += c;
+        acc.x = fmaf(c, bf16_lo(ov[s].x), acc.x);
+        acc.y = fmaf(c, bf16_hi(ov[s].x), acc.y);
+        acc.z = fmaf(c, bf16_lo(ov[s].y), acc.z);
+        acc.w = fmaf(c, bf16_hi(ov[s].y), acc.w);
       }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
