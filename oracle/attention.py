@@ -39,6 +39,15 @@ scale * q . k, softmax over visible keys only, output = sum p v.  GQA: query
 head h reads KV head h // (Hq / Hkv).  No position encoding is applied (the
 inputs are synthetic Q/K/V).
 
+E4M3 paged cache (canvas_attention_e4m3; DiffusionGemma/vLLM page, section "Quantized checkpoint
+support", the FP8 model): the cache holds OCP E4M3 codes, a cached key or value is
+scale * decode(code) (one scale for K, one for V); the causal rows of a launch are quantised when
+appended (code = encode(x / scale), round to nearest even, saturating); within the launch every
+key at a position >= cached, causal or canvas, is used at input precision (the rows are this
+launch's own activations), and the cache is read only below `cached`.  Reading: the page names
+FP8 weights and fully dynamic activations without fixing where the cache quantises; keeping the
+launch's own rows unquantised follows the canvas rows, which never enter the cache.
+
 Pinned by tests/test_oracle_attention.py: the p0/p1/c0/c1 and the
 three-request visibility fixtures in tests/golden/ (with and without the
 W = 2 window), brute-force dense-mask attention on random shapes (window
@@ -137,3 +146,46 @@ def canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, page_size: i
             hk = h // group
             out[row0:row0 + nr, h] = dense_mask_attention(q[row0:row0 + nr, h], K[:, hk], Vv[:, hk], mask, scale)
     return out, kc, vc
+
+
+def canvas_attention_e4m3(q, k, v, kc8, vc8, k_scale: float, v_scale: float, page_table, splits, page_size: int,
+                          scale: float):
+    """Oracle for one launch over an E4M3 paged cache.
+
+    q [rows, Hq, D]; k, v [rows, Hkv, D] (float arrays); kc8, vc8 [pages, Hkv, page_size, D] uint8 codes;
+    splits as in canvas_attention.  Returns (out [rows, Hq, D] fp64, kc8', vc8' with the causal rows'
+    codes appended).
+    """
+    from . import fp8
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    kc8_new = np.array(kc8, dtype=np.uint8, copy=True)
+    vc8_new = np.array(vc8, dtype=np.uint8, copy=True)
+    kc = fp8.decode_table(kc8, k_scale)          # the cache as it was before this launch's appends
+    vc = fp8.decode_table(vc8, v_scale)
+    rows, Hq, D = q.shape
+    group = Hq // k.shape[1]
+    out = np.zeros((rows, Hq, D))
+    splits = [tuple(int(t) for t in s) + (0,) * (6 - len(s)) for s in splits]
+    for (row0, cached, n_causal, n_canvas, page0, window) in splits:
+        for j in range(n_causal):
+            pos = cached + j
+            page = int(page_table[page0 + pos // page_size])
+            kc8_new[page, :, pos % page_size, :] = fp8.encode_e4m3(k[row0 + j] / k_scale)
+            vc8_new[page, :, pos % page_size, :] = fp8.encode_e4m3(v[row0 + j] / v_scale)
+    for (row0, cached, n_causal, n_canvas, page0, window) in splits:
+        nr = n_causal + n_canvas
+        K = np.zeros((cached + nr, k.shape[1], D))
+        Vv = np.zeros_like(K)
+        for pos in range(cached):
+            page = int(page_table[page0 + pos // page_size])
+            K[pos] = kc[page, :, pos % page_size, :]
+            Vv[pos] = vc[page, :, pos % page_size, :]
+        K[cached:] = k[row0:row0 + nr]
+        Vv[cached:] = v[row0:row0 + nr]
+        mask = visibility_mask(cached, n_causal, n_canvas, window)
+        for h in range(Hq):
+            hk = h // group
+            out[row0:row0 + nr, h] = dense_mask_attention(q[row0:row0 + nr, h], K[:, hk], Vv[:, hk], mask, scale)
+    return out, kc8_new, vc8_new

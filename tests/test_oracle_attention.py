@@ -211,3 +211,38 @@ def test_window_left_edge_is_shared_by_both_row_kinds():
             ref = np.zeros_like(row)
             ref[max(0, pos - w):pos + 1] = True
             np.testing.assert_array_equal(row, ref)
+
+
+@pytest.mark.parametrize("splits,Hq,Hkv,D", CASES)
+def test_e4m3_cache_reduces_to_the_plain_oracle_on_representable_rows(splits, Hq, Hkv, D):
+    """When every fresh K/V value is an exact E4M3 value times the scale, quantising on append is
+    the identity, so the E4M3 oracle equals the plain oracle on the decoded cache, and the appended
+    codes are the rows' own codes."""
+    from oracle import fp8
+    p = synth.attention_problem(15, splits, Hq, Hkv, D, dtype="f32")
+    rng = np.random.default_rng(15)
+    ks, vs = 2.0 ** -4, 2.0 ** -3
+    kc8 = rng.integers(0, 0x7F, p.k_cache.shape).astype(np.uint8) | (rng.integers(0, 2, p.k_cache.shape) * 0x80).astype(np.uint8)
+    vc8 = rng.integers(0, 0x7F, p.v_cache.shape).astype(np.uint8)
+    k8 = rng.integers(0, 0x7F, p.k.shape).astype(np.uint8)
+    v8 = rng.integers(0, 0x7F, p.v.shape).astype(np.uint8) | 0x80
+    k, v = fp8.decode_table(k8, ks), fp8.decode_table(v8, vs)
+    sp = [(p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i]) for i, s in enumerate(p.splits)]
+    q = p.q.astype(np.float64)
+    out8, kn, vn = attention.canvas_attention_e4m3(q, k, v, kc8, vc8, ks, vs, p.page_table, sp, p.page_size, 0.2)
+    ref, rkc, rvc = attention.canvas_attention(q, k, v, fp8.decode_table(kc8, ks), fp8.decode_table(vc8, vs),
+                                               p.page_table, sp, p.page_size, 0.2)
+    np.testing.assert_allclose(out8, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(fp8.decode_table(kn, ks), rkc)
+    np.testing.assert_array_equal(fp8.decode_table(vn, vs), rvc)
+
+
+def test_e4m3_cache_keeps_the_launch_rows_unquantised():
+    """A canvas row over an empty cache sees only this launch's rows, at input precision."""
+    p = synth.attention_problem(16, [(0, 0, 5)], 2, 1, 8, dtype="f32")
+    kc8 = np.zeros(p.k_cache.shape, np.uint8)
+    out8, _, _ = attention.canvas_attention_e4m3(p.q, p.k, p.v, kc8, kc8, 0.5, 0.5, p.page_table,
+                                                 [(0, 0, 0, 5, 0)], p.page_size, 0.3)
+    ref, _, _ = attention.canvas_attention(p.q, p.k, p.v, p.k_cache, p.v_cache, p.page_table, [(0, 0, 0, 5, 0)],
+                                           p.page_size, 0.3)
+    np.testing.assert_allclose(out8, ref, rtol=1e-12, atol=1e-12)
