@@ -37,6 +37,7 @@ MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
            tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0, e4m3=False)
 E4M3_SCALE = 2.0 ** -7      # the E4M3 table stores E / scale; E ~ N(0, 1) / 8 stays far inside +-448
+KV_SCALES = (2.0 ** -4, 2.0 ** -4)   # the E4M3 cache stores K / scale, V / scale (K, V ~ N(0, 1))
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
 PE_KERNEL_E4M3 = "gemm_f16_e4m3_splitk_kernel"
 PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp",)
@@ -115,8 +116,12 @@ class Workload:
         self.k = synth.normal_torch(s, "bench.k", (C, Hkv, D), 1.0, bf, dev)
         self.v = synth.normal_torch(s, "bench.v", (C, Hkv, D), 1.0, bf, dev)
         n_pages = L // ps + 2
-        self.k_cache = synth.normal_torch(s, "bench.kc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
-        self.v_cache = synth.normal_torch(s, "bench.vc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
+        if c["e4m3"]:
+            self.k_cache = synth.e4m3_table_torch(s, "bench.kc8", (n_pages, Hkv, ps, D), 1.0, KV_SCALES[0], dev)
+            self.v_cache = synth.e4m3_table_torch(s, "bench.vc8", (n_pages, Hkv, ps, D), 1.0, KV_SCALES[1], dev)
+        else:
+            self.k_cache = synth.normal_torch(s, "bench.kc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
+            self.v_cache = synth.normal_torch(s, "bench.vc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
         self.page_table = torch.as_tensor(synth.page_table(s, "bench.pages", n_pages)[: L // ps].copy(), device=dev)
         self.splits = torch.tensor([[0, L, 0, C, 0, c["window"]]], dtype=torch.int32, device=dev)
         # keys the canvas rows see together: the whole request, or the band of a sliding window
@@ -159,8 +164,13 @@ class Workload:
         c, dg, s = self.c, self.dg, self.state
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
-        dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
-                               c["C"], self.key_span, self.scale, out=self.att_out)
+        if c["e4m3"]:
+            dg.dg_canvas_attention_e4m3(self.q, self.k, self.v, self.k_cache, self.v_cache, *KV_SCALES,
+                                        self.page_table, self.splits, c["C"], self.key_span, self.scale,
+                                        out=self.att_out)
+        else:
+            dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
+                                   c["C"], self.key_span, self.scale, out=self.att_out)
         rec(1)
         logits = self.pool[t % len(self.pool)]
         dg.dg_denoise_sample_sc(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"], out=self.so,
@@ -229,7 +239,11 @@ def cpu_baseline(w: Workload, rows: int):
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
     q = f64(w.q[:rows])
     k_new, v_new = f64(w.k), f64(w.v)
-    kc, vc = f64(w.k_cache), f64(w.v_cache)
+    if c["e4m3"]:
+        from oracle import fp8
+        kc, vc = (fp8.decode_table(t.cpu().numpy(), sc) for t, sc in zip((w.k_cache, w.v_cache), KV_SCALES))
+    else:
+        kc, vc = f64(w.k_cache), f64(w.v_cache)
     pt = w.page_table.cpu().numpy()
     logits = f64(w.pool[0][:rows])
     if c["e4m3"]:
@@ -329,13 +343,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=128, help="canvas positions in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="canvas positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving", action="store_true",
                     help="run the batched serving loop with deficit admission (and admit-on-arrival for "
                          "comparison) instead of the single-canvas step; prints its own JSON line")
     ap.add_argument("--e4m3", action="store_true",
-                    help="run the step with the E4M3 (FP8) embedding table instead of the bf16 one")
+                    help="run the step with an E4M3 (FP8) paged KV cache and embedding table instead of bf16 ones")
     ap.add_argument("--window", type=int, default=0,
                     help="run the step as a sliding-window layer of this window (0: full attention)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -403,7 +417,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not c["e4m3"] else "bf16 (E4M3 table, fp16 MFMA)",
+        "dtype": "bf16" if not c["e4m3"] else "bf16 (E4M3 KV cache and table; bf16 / fp16 MFMA)",
         "data": "synthetic",
         "config": {"workload": "single_canvas" + (f"_window{c['window']}" if c["window"] > 0 else "")
                    + ("_e4m3" if c["e4m3"] else ""), "B": c["B"], "C": c["C"], "V": c["V"], "prefix": c["L"],

@@ -22,7 +22,7 @@ __all__ = [
     "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
     "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
     "dg_deficit_admit", "dg_e4m3_decode", "dg_selfcond_prepared_bytes_e4m3", "dg_selfcond_prepare_e4m3",
-    "dg_selfcond_embed_sc_e4m3",
+    "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -42,6 +42,8 @@ _SIGS = {
     "dg_canvas_attention_ws_bytes": (_sz, [_i32] * 8),
     "dg_canvas_attention": (_i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _i32, _f32, _i32, _p, _p, _sz, _p]),
+    "dg_canvas_attention_e4m3": (_i32, [_p, _p, _p, _p, _p, _f32, _f32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _f32, _p, _p, _sz, _p]),
     "dg_denoise_sample_ws_bytes": (_sz, [_i32, _i32]),
     "dg_denoise_sample": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _u32, _p, _p, _p, _p, _p, _p,
                                  _sz, _p]),
@@ -173,6 +175,25 @@ def dg_canvas_attention(q, k, v, k_cache, v_cache, page_table, splits, max_rows_
                                      max_rows_per_req, max_keys_per_req, Hq, Hkv, D, page_size, float(scale), dt,
                                      _ptr(out), _ptr(ws) if nb else None, nb, _stream(stream)),
            "dg_canvas_attention")
+    return out
+
+
+def dg_canvas_attention_e4m3(q, k, v, k_cache8, v_cache8, k_scale, v_scale, page_table, splits, max_rows_per_req,
+                             max_keys_per_req, scale, out=None, ws=None, stream=None):
+    """dg_canvas_attention over an E4M3 paged cache: k_cache8 / v_cache8 uint8 codes [pages, Hkv, page, D],
+    values k_scale * code / v_scale * code (powers of two); q, k, v bf16."""
+    rows, Hq, D = q.shape
+    Hkv = k.shape[1]
+    n_pages, _, page_size, _ = k_cache8.shape
+    n_req = splits.shape[0]
+    out = torch.empty_like(q) if out is None else out
+    nb = dg_canvas_attention_ws_bytes(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, DG_BF16)
+    ws = _ws(nb, ws, q.device)
+    _check(lib().dg_canvas_attention_e4m3(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache8), _ptr(v_cache8), float(k_scale),
+                                          float(v_scale), n_pages, _ptr(page_table), page_table.numel(), _ptr(splits),
+                                          n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, page_size,
+                                          float(scale), _ptr(out), _ptr(ws) if nb else None, nb, _stream(stream)),
+           "dg_canvas_attention_e4m3")
     return out
 
 

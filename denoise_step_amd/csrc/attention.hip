@@ -21,6 +21,7 @@
 #include "dg_host.hpp"
 
 #include <algorithm>
+#include <cmath>
 
 namespace dg {
 namespace {
@@ -198,6 +199,58 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   return p;
 }
 
+// Both MFMA entry points: fill the arguments shared by the bf16 and E4M3 caches, launch the kernel
+// and, with several key splits, the merge.
+template <bool E8>
+dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void* k, const void* v, int32_t n_pages,
+                      const int32_t* page_table, int32_t page_table_len, const dg_split* splits, int32_t n_req,
+                      int32_t rows, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, float scale, void* out,
+                      void* ws, hipStream_t s) {
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.n_pages = n_pages;
+  a.page_table = page_table;
+  a.page_table_len = page_table_len;
+  a.splits = splits;
+  a.rows = rows;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.page_size = page_size;
+  a.scale_log2 = scale * kLog2e;
+  a.nsplit = plan.nsplit;
+  a.split_keys = plan.split_keys;
+  a.out = reinterpret_cast<uint16_t*>(out);
+  a.o_part = reinterpret_cast<uint16_t*>(ws);
+  a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
+  a.qtiles = plan.qtiles;
+  const int64_t items = static_cast<int64_t>(n_req) * plan.nsplit * Hkv * plan.qtiles;
+  DG_UNSUP(items <= (int64_t{1} << 30));
+  a.n_items = static_cast<int32_t>(items);
+  const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
+  if (D == 256)
+    attend_mfma_kernel<256, E8><<<grid, kAttThreads, 0, s>>>(a);
+  else
+    attend_mfma_kernel<128, E8><<<grid, kAttThreads, 0, s>>>(a);
+  DG_LAUNCHED();
+  if (plan.nsplit > 1) {
+    const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
+    if (D == 256)
+      attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req, a.out);
+    else
+      attend_merge_kernel<128><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req, a.out);
+    DG_LAUNCHED();
+  }
+  return DG_OK;
+}
+
+bool power_of_two(float x) {
+  if (!(x > 0.f) || !(x < INFINITY)) return false;
+  int e;
+  return std::frexp(x, &e) == 0.5f;
+}
+
 }  // namespace
 }  // namespace dg
 
@@ -243,49 +296,12 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   }
   if (plan.mfma) {
     AttArgs a{};
-    a.q = reinterpret_cast<const uint16_t*>(q);
-    a.k = reinterpret_cast<const uint16_t*>(k);
-    a.v = reinterpret_cast<const uint16_t*>(v);
     a.k_cache = reinterpret_cast<const uint16_t*>(k_cache);
     a.v_cache = reinterpret_cast<const uint16_t*>(v_cache);
     a.k_cache_w = reinterpret_cast<uint16_t*>(k_cache);
     a.v_cache_w = reinterpret_cast<uint16_t*>(v_cache);
-    a.n_pages = n_pages;
-    a.page_table = page_table;
-    a.page_table_len = page_table_len;
-    a.splits = splits;
-    a.rows = rows;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = Hq / Hkv;
-    a.page_size = page_size;
-    a.scale_log2 = scale * kLog2e;
-    a.nsplit = plan.nsplit;
-    a.split_keys = plan.split_keys;
-    a.out = reinterpret_cast<uint16_t*>(out);
-    a.o_part = reinterpret_cast<uint16_t*>(ws);
-    a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
-    a.qtiles = plan.qtiles;
-    const int64_t items = static_cast<int64_t>(n_req) * plan.nsplit * Hkv * plan.qtiles;
-    DG_UNSUP(items <= (int64_t{1} << 30));
-    a.n_items = static_cast<int32_t>(items);
-    const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
-    if (D == 256)
-      attend_mfma_kernel<256><<<grid, kAttThreads, 0, s>>>(a);
-    else
-      attend_mfma_kernel<128><<<grid, kAttThreads, 0, s>>>(a);
-    DG_LAUNCHED();
-    if (plan.nsplit > 1) {
-      const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
-      if (D == 256)
-        attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                       a.out);
-      else
-        attend_merge_kernel<128><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req,
-                                                       a.out);
-      DG_LAUNCHED();
-    }
-    return DG_OK;
+    return launch_mfma<false>(a, plan, q, k, v, n_pages, page_table, page_table_len, splits, n_req, rows, Hq, Hkv, D,
+                              page_size, scale, out, ws, s);
   }
 #define DG_ATT(BF, DD)                                                                                        \
   launch_attend_wave<BF, DD>(q, k, v, k_cache, v_cache, n_pages, page_table, page_table_len, splits, n_req, rows, \
@@ -309,4 +325,32 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   DG_LAUNCHED();
   (void)max_keys_per_req;
   return DG_OK;
+}
+
+extern "C" dg_status dg_canvas_attention_e4m3(const void* q, const void* k, const void* v, uint8_t* k_cache8,
+                                              uint8_t* v_cache8, float k_scale, float v_scale, int32_t n_pages,
+                                              const int32_t* page_table, int32_t page_table_len,
+                                              const dg_split* splits, int32_t n_req, int32_t rows,
+                                              int32_t max_rows_per_req, int32_t max_keys_per_req, int32_t Hq,
+                                              int32_t Hkv, int32_t D, int32_t page_size, float scale, void* out,
+                                              void* ws, size_t ws_bytes, dg_stream_t stream) {
+  DG_ARG(q && k && v && k_cache8 && v_cache8 && page_table && splits && out);
+  DG_ARG(n_pages > 0 && page_table_len > 0 && n_req > 0 && rows > 0 && max_rows_per_req > 0 &&
+         max_keys_per_req > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0);
+  DG_ARG(n_req <= 65535 && max_rows_per_req <= (1 << 20) && Hq <= 65535);
+  DG_UNSUP(power_of_two(k_scale) && power_of_two(v_scale));
+  DG_UNSUP(page_size == 16);
+  DG_UNSUP(D == 128 || D == 256);
+  const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, DG_BF16);
+  DG_UNSUP(plan.split_keys + kAttKeys <= kAttMaxPages * 16);
+  DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
+  AttArgs a{};
+  a.k_cache8 = k_cache8;
+  a.v_cache8 = v_cache8;
+  a.k_cache8_w = k_cache8;
+  a.v_cache8_w = v_cache8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_mfma<true>(a, plan, q, k, v, n_pages, page_table, page_table_len, splits, n_req, rows, Hq, Hkv, D,
+                           page_size, scale, out, ws, as_stream(stream));
 }

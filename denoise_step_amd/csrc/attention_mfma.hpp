@@ -71,13 +71,29 @@ struct AttArgs {
   uint16_t* out;        // [rows][Hq][D] bf16 (nsplit == 1)
   uint16_t* o_part;     // [nsplit][rows][Hq][D] bf16, each split's output normalised by its own l (nsplit > 1)
   float2* ml_part;      // [nsplit][rows][Hq] (reference max in log2 units, l)  (nsplit > 1)
+  // E4M3 cache (attend_mfma_kernel<D, true>): codes in place of k_cache / v_cache, values scale * code
+  const uint8_t* k_cache8;
+  const uint8_t* v_cache8;
+  uint8_t* k_cache8_w;
+  uint8_t* v_cache8_w;
+  float k_scale, v_scale;  // powers of two
 };
 
+template <int D, bool E8>
+struct AttSmem;
 template <int D>
-struct AttSmem {
+struct AttSmem<D, false> {
   uint16_t K[2][kAttKeys * D];
   uint16_t V[2][kAttKeys * D];
   int32_t pages[kAttMaxPages];
+};
+// E4M3 cache: the codes of a block's cached keys land in S (K codes, then V codes, D bytes per key)
+// and are converted into the bf16 block; page ids are read from the table (no room to stage them).
+template <int D>
+struct AttSmem<D, true> {
+  uint16_t K[2][kAttKeys * D];
+  uint16_t V[2][kAttKeys * D];
+  uint8_t S[2 * kAttKeys * D];
 };
 
 // K and V in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ (r & 15)).
@@ -165,6 +181,107 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
   }
 }
 
+// E4M3 cache, block at kb: the codes of its cached keys into S (row r of K at S + r D, of V at
+// S + (64 + r) D; one 1-KB copy = 1024 / D keys), its fresh keys (>= cached) as bf16 rows into the
+// block's slots as in att_load.  A block holding both kinds gets both sets of copies; a copy's lanes
+// whose key is of the other kind fetch a valid key of the right kind (the last cached key, the first
+// fresh row), which the conversion then ignores.  Keys past k_end re-read the last visible key.
+template <int D>
+DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int k_end, uint8_t* s8, uint16_t* kdst,
+                      uint16_t* vdst) {
+  constexpr int kChunks = D / 8;
+  constexpr int kKeysPerCopy = kWave / kChunks;
+  constexpr int kPerWave = kChunks / (kAttThreads / kWave);
+  constexpr int kKeysPerCopy8 = 1024 / D;
+  constexpr int kPerWave8 = kAttKeys / kKeysPerCopy8 / (kAttThreads / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int kl = min(kb + kAttKeys - 1, k_end - 1);
+  if (kb < sp.cached) {
+#pragma unroll
+    for (int i = 0; i < kPerWave8; ++i) {
+      const int q = wave * kPerWave8 + i;
+      const int r = q * kKeysPerCopy8 + lane / (D / 16);
+      const int kk = min(min(kb + r, k_end - 1), sp.cached - 1);
+      const int ti = min(max(sp.page0 + kk / 16, 0), a.page_table_len - 1);
+      const int64_t page = min(max(a.page_table[ti], 0), a.n_pages - 1);
+      const int64_t off = ((page * a.Hkv + hk) * 16 + (kk & 15)) * D + 16 * (lane % (D / 16));
+      const uint32_t klds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s8 + 1024 * q));
+      const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s8 + kAttKeys * D + 1024 * q));
+      const uint8_t* ksrc = a.k_cache8 + off;
+      const uint8_t* vsrc = a.v_cache8 + off;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, off"
+          :
+          : "s"(klds), "v"(ksrc)
+          : "memory", "m0");
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, off"
+          :
+          : "s"(vlds), "v"(vsrc)
+          : "memory", "m0");
+    }
+  }
+  if (kl >= sp.cached) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int q = wave * kPerWave + i;
+      const int r = q * kKeysPerCopy + lane / kChunks;
+      const int c = (lane % kChunks) ^ (r & 15);
+      const int kk = max(min(kb + r, k_end - 1), sp.cached);
+      const int64_t row = min(max(sp.row0 + kk - sp.cached, 0), a.rows - 1);
+      const int64_t off = (row * a.Hkv + hk) * D + 8 * c;
+      const uint32_t klds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
+      const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vdst + kWave * 8 * q));
+      const uint16_t* ksrc = a.k + off;
+      const uint16_t* vsrc = a.v + off;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, off"
+          :
+          : "s"(klds), "v"(ksrc)
+          : "memory", "m0");
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, off"
+          :
+          : "s"(vlds), "v"(vsrc)
+          : "memory", "m0");
+    }
+  }
+}
+
+// The cached keys of the block at kb: codes in S -> bf16 (value * scale, exact for a power-of-two
+// scale) in the block's swizzled slots.  Each thread converts 8-code chunks u = tid + 256 j.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+template <int D>
+DG_DEV void att_convert8(const AttArgs& a, const dg_split& sp, int kb, int k_end, const uint8_t* s8, uint16_t* kdst,
+                         uint16_t* vdst) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int j = 0; j < kAttKeys * kChunks / kAttThreads; ++j) {
+    const int u = threadIdx.x + kAttThreads * j;
+    const int r = u / kChunks, c = u % kChunks;
+    if (min(kb + r, k_end - 1) >= sp.cached) continue;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint2 q = *reinterpret_cast<const uint2*>(s8 + (kv * kAttKeys + r) * D + 8 * c);
+      const float sc = kv == 0 ? a.k_scale : a.v_scale;
+      const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, sc, false);
+      const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, sc, true);
+      const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, sc, false);
+      const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, sc, true);
+      bf16x8 w;
+      w[0] = p0[0]; w[1] = p0[1]; w[2] = p1[0]; w[3] = p1[1];
+      w[4] = p2[0]; w[5] = p2[1]; w[6] = p3[0]; w[7] = p3[1];
+      uint16_t* dst = kv == 0 ? kdst : vdst;
+      *reinterpret_cast<bf16x8*>(dst + 8 * att_kslot<D>(r, c)) = w;
+    }
+  }
+}
+
 // Waits for every outstanding copy, so that after the next barrier K and V of the block are visible.
 DG_DEV void att_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_only(0)); }
 
@@ -210,12 +327,39 @@ DG_DEV void att_append(const AttArgs& a, const dg_split& sp, int hk, int j0, int
   }
 }
 
+// E4M3 cache: the causal rows' K/V quantised into the pages (x / scale, clamped to +-448, nearest
+// even), 8 values per thread and step.
 template <int D>
+DG_DEV void att_append8(const AttArgs& a, const dg_split& sp, int hk, int j0, int j1) {
+  constexpr int kChunks = D / 8;
+  const int n = (j1 - j0) * kChunks;
+  for (int u = threadIdx.x; u < 2 * n; u += kAttThreads) {
+    const bool is_v = u >= n;
+    const int w = is_v ? u - n : u;
+    const int j = j0 + w / kChunks, c = w % kChunks;
+    if (sp.row0 + j < 0 || sp.row0 + j >= a.rows) continue;  // a descriptor outside the packed rows
+    const int pos = sp.cached + j;
+    const int ti = min(max(sp.page0 + pos / 16, 0), a.page_table_len - 1);
+    const int64_t page = min(max(a.page_table[ti], 0), a.n_pages - 1);
+    const int64_t src = ((static_cast<int64_t>(sp.row0) + j) * a.Hkv + hk) * D + 8 * c;
+    const int64_t dst = ((page * a.Hkv + hk) * 16 + (pos & 15)) * D + 8 * c;
+    const uint4 x = *reinterpret_cast<const uint4*>((is_v ? a.v : a.k) + src);
+    const float inv = 1.0f / (is_v ? a.v_scale : a.k_scale);
+    auto q = [&](float f) { return fminf(fmaxf(f * inv, -448.f), 448.f); };
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(x.x)), q(bf16_hi(x.x)), 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(x.y)), q(bf16_hi(x.y)), lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(x.z)), q(bf16_hi(x.z)), 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(x.w)), q(bf16_hi(x.w)), hi, true);
+    *reinterpret_cast<uint2*>((is_v ? a.v_cache8_w : a.k_cache8_w) + dst) = make_uint2(lo, hi);
+  }
+}
+
+template <int D, bool E8>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   constexpr int kDSteps = D / 16;                // MFMA k-steps over D
   constexpr int kDTiles = D / 32;                // 32-wide output tiles over D
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
-  __shared__ __attribute__((aligned(16))) AttSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
 
   // XCD-aware order: the hardware deals workgroup L to XCD L % 8; work item t = (L % 8) * per_xcd +
   // L / 8, t = ((req * nsplit + split) * Hkv + hk) * qtiles + qtile, so the row tiles that read the
@@ -265,10 +409,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
 
   // stage the physical page ids of the split's prefix positions (clamped into range)
   const int page_lo = k_begin / 16;
-  const int page_hi = min((min(k_end, sp.cached) + 15) / 16, page_lo + kAttMaxPages);
-  for (int p = page_lo + tid; p < page_hi; p += kAttThreads) {
-    const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
-    sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
+  if constexpr (!E8) {
+    const int page_hi = min((min(k_end, sp.cached) + 15) / 16, page_lo + kAttMaxPages);
+    for (int p = page_lo + tid; p < page_hi; p += kAttThreads) {
+      const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
+      sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
+    }
   }
 
   // Q fragment (B operand of S^T = K Q^T): 8 consecutive d per MFMA step
@@ -291,14 +437,28 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
 
   __syncthreads();  // page ids visible
   if (k_begin < k_end) {
-    att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
+    if constexpr (E8)
+      att_load8<D>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+    else
+      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
     att_wait();
   }
   __syncthreads();
+  if constexpr (E8) {
+    if (k_begin < k_end && k_begin < sp.cached) {
+      att_convert8<D>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+      __syncthreads();
+    }
+  }
   int buf = 0;
   for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
     const bool more = kb + kAttKeys < k_end;
-    if (more) att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+    if (more) {
+      if constexpr (E8)
+        att_load8<D>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+      else
+        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+    }
     const uint16_t* Kb = sm.K[buf];
     const uint16_t* Vb = sm.V[buf];
     // ---- S^T = K Q^T : two 32-key sub-blocks x 32 rows
@@ -378,6 +538,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     }
     if (more) att_wait();
     __syncthreads();
+    if constexpr (E8) {
+      if (more && kb + kAttKeys < sp.cached) {
+        att_convert8<D>(a, sp, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+        __syncthreads();
+      }
+    }
     buf ^= 1;
   }
 
@@ -385,7 +551,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   if (split == 0) {
     const int j0 = (m_tile0 + a.G - 1) / a.G;
     const int j1 = min(sp.n_causal, (m_tile0 + kAttRows + a.G - 1) / a.G);
-    if (j0 < j1) att_append<D>(a, sp, hk, j0, j1);
+    if (j0 < j1) {
+      if constexpr (E8)
+        att_append8<D>(a, sp, hk, j0, j1);
+      else
+        att_append<D>(a, sp, hk, j0, j1);
+    }
   }
 
   if (!row_ok || !row_in) return;

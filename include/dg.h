@@ -133,6 +133,26 @@ dg_status dg_canvas_attention(const void* q, const void* k, const void* v, void*
                               size_t ws_bytes, dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * dg_canvas_attention_e4m3
+ *
+ * dg_canvas_attention over an E4M3 paged cache (DiffusionGemma/vLLM page,
+ * section "Quantized checkpoint support", the FP8 model): k_cache8 / v_cache8
+ * hold OCP E4M3 codes in the page layout of dg_canvas_attention, a cached key
+ * is k_scale * value(code) (v_scale for values).  Keys at positions >= cached
+ * (this launch's causal and canvas rows) are read from k / v at bf16; the
+ * causal rows are appended as codes: round-to-nearest-even of x / scale,
+ * clamped to +-448.  q, k, v, out: DG_BF16.  k_scale and v_scale must be
+ * powers of two (the conversions are then exact).  Supported: D in {128, 256},
+ * page_size 16; workspace: dg_canvas_attention_ws_bytes(..., DG_BF16).
+ * ------------------------------------------------------------------------ */
+dg_status dg_canvas_attention_e4m3(const void* q, const void* k, const void* v, uint8_t* k_cache8,
+                                   uint8_t* v_cache8, float k_scale, float v_scale, int32_t n_pages,
+                                   const int32_t* page_table, int32_t page_table_len, const dg_split* splits,
+                                   int32_t n_req, int32_t rows, int32_t max_rows_per_req, int32_t max_keys_per_req,
+                                   int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, float scale, void* out,
+                                   void* ws, size_t ws_bytes, dg_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * dg_denoise_sample
  *
  * For every logit row (DiffusionGemma/vLLM page, section "Entropy-based

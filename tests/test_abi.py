@@ -88,3 +88,16 @@ def test_workspace_sizes(L):
     assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 4 * 32      # 4 chunks of 65536 logits per row
     assert L.dg_selfcond_ws_bytes(256, 262144, 4096, 1024, 1) >= 256 * 262144 * 2
     assert L.dg_selfcond_prepared_bytes(262144, 4096, 1024, 1) >= 262144 * 4096 * 2 + 3 * 4096 * 1024 * 2
+
+
+def test_e4m3_attention_validates(L):
+    import ctypes
+    import denoise_step_amd as dg
+    p = ctypes.c_void_p(16)
+    sp = ctypes.c_void_p(32)
+    f = L.dg_canvas_attention_e4m3
+    # non power-of-two scale, unsupported head dim, bad sizes: rejected before any launch
+    args = lambda ks, D, nreq: (p, p, p, p, p, ks, 0.5, 4, p, 4, sp, nreq, 8, 8, 8, 2, 1, D, 16, 0.1, p, None, 0, None)
+    assert f(*args(0.3, 128, 1)) == -2
+    assert f(*args(0.25, 64, 1)) == -2
+    assert f(*args(0.25, 128, 0)) == -1

@@ -102,3 +102,56 @@ def test_attention_sliding_window_tight_key_bound():
     span = max(s[1] + s[2] for s in splits) + 2 * W
     print(f"attention window tight bound span={span}", flush=True)
     run_case(splits, 16, 8, 256, "bf16", seed=51, window=W, max_keys=span)
+
+
+K_SCALE, V_SCALE = 2.0 ** -4, 2.0 ** -3
+
+
+def run_case_e4m3(splits, Hq, Hkv, D, seed=0, window=0):
+    """dg_canvas_attention_e4m3 against oracle.attention.canvas_attention_e4m3: outputs within the bf16
+    tolerance, the appended codes and every other cache byte identical."""
+    import denoise_step_amd as dg
+    torch = P.torch_mod()
+    p = synth.attention_problem(seed, splits, Hq, Hkv, D, dtype="bf16")
+    kc8 = synth.e4m3_table(seed, "att8.kc", p.k_cache.shape, 1.0, K_SCALE)
+    vc8 = synth.e4m3_table(seed, "att8.vc", p.v_cache.shape, 1.0, V_SCALE)
+    q, k, v = (P.dev_bf16(a) for a in (p.q, p.k, p.v))
+    kcd, vcd = P.dev(kc8), P.dev(vc8)
+    sp = np.array([[p.row0[i], s.cached, s.n_causal, s.n_canvas, p.page0[i], window]
+                   for i, s in enumerate(p.splits)], np.int32)
+    max_rows = max(s.n_causal + s.n_canvas for s in p.splits)
+    max_keys = max(s.cached + s.n_causal + s.n_canvas for s in p.splits)
+    scale = 1.0 / np.sqrt(D)
+    out = dg.dg_canvas_attention_e4m3(q, k, v, kcd, vcd, K_SCALE, V_SCALE, P.dev(p.page_table), P.dev(sp), max_rows,
+                                      max_keys, scale)
+    torch.cuda.synchronize()
+    f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)
+    ref, rkc, rvc = oatt.canvas_attention_e4m3(f(p.q), f(p.k), f(p.v), kc8, vc8, K_SCALE, V_SCALE, p.page_table,
+                                               [tuple(r) for r in sp], p.page_size, scale)
+    err = np.abs(P.host_f64(out) - ref).max()
+    assert err <= P.TOL_ATT_BF16, f"max |delta| {err}"
+    assert np.array_equal(kcd.cpu().numpy(), rkc) and np.array_equal(vcd.cpu().numpy(), rvc)
+    return err
+
+
+E4M3_CASES = [
+    ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 128, 0),            # the three-request batch
+    ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 128, 0),
+    ([(300, 40, 70), (1, 0, 129)], 16, 8, 256, 0),               # blocks straddling the cache end
+    ([(100, 0, 33)], 8, 2, 128, 0),
+    ([(0, 200, 56)], 32, 8, 128, 0),
+    ([(1000, 100, 200), (70, 0, 64)], 32, 8, 128, 300),          # sliding window
+    ([(3000, 300, 50)], 16, 8, 256, 0),                          # causal rows appended while keys are split
+]
+
+
+@pytest.mark.parametrize("case", range(len(E4M3_CASES)))
+def test_attention_e4m3_cache(case):
+    splits, Hq, Hkv, D, W = E4M3_CASES[case]
+    print(f"attention e4m3 cache case={case}", flush=True)
+    run_case_e4m3(splits, Hq, Hkv, D, seed=60 + case, window=W)
+
+
+def test_attention_e4m3_cache_single_canvas_full_size():
+    print("attention e4m3 cache full size single canvas", flush=True)
+    run_case_e4m3([(2048, 0, 256)], 16, 8, 256, seed=67)
