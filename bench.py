@@ -226,58 +226,53 @@ def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
     return out
 
 
-def cpu_baseline(w: Workload, rows: int):
-    """Time the oracle, as it stands, on `rows` canvas positions of the same step (host cores)."""
+def cpu_baseline(w: Workload, steps: int):
+    """Time the oracle, as it stands, on `steps` whole steps of the same canvas (host cores)."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_info
 
     from oracle import accept, attention, converged, sampler, selfcond
     c = w.c
     C, V, D = c["C"], c["V"], c["D"]
-    log(f"cpu baseline: copying inputs for {rows} positions to the host")
+    log(f"cpu baseline: copying the inputs of {steps} steps to the host")
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-    q = f64(w.q[:rows])
+    q = f64(w.q)
     k_new, v_new = f64(w.k), f64(w.v)
     if c["e4m3"]:
         from oracle import fp8
         kc, vc = (fp8.decode_table(t.cpu().numpy(), sc) for t, sc in zip((w.k_cache, w.v_cache), KV_SCALES))
-    else:
-        kc, vc = f64(w.k_cache), f64(w.v_cache)
-    pt = w.page_table.cpu().numpy()
-    logits = f64(w.pool[0][:rows])
-    if c["e4m3"]:
-        from oracle import fp8
         E = fp8.decode_table(w.E.cpu().numpy(), E4M3_SCALE)
     else:
+        kc, vc = f64(w.k_cache), f64(w.v_cache)
         E = w.E.float().cpu().numpy()
+    pt = w.page_table.cpu().numpy()
+    pool = [f64(w.pool[t % len(w.pool)]) for t in range(steps)]
     wg, wu, wd = f64(w.wg), f64(w.wu), f64(w.wd)
-    ent_canvas = np.random.default_rng(0).gamma(1.0, 2.0, (1, C)).astype(np.float32)
     threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     log("cpu baseline: timing the oracle")
     t0 = time.perf_counter()
-    K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
-    group = c["Hq"] // c["Hkv"]
-    mask = attention.visibility_mask(c["L"], 0, C, c["window"])[:rows]
-    for h in range(c["Hq"]):
-        attention.dense_mask_attention(q[:, h], K[:, h // group], Vv[:, h // group], mask, 1.0 / math.sqrt(D))
-    so = sampler.denoise_sample(logits, 1.0, [0], [1], rows)
-    st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
-                             unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
-                             step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
-    samp = np.zeros((1, C), np.int64)
-    accept.entropy_accept(ent_canvas, samp, st.canvas, c["budget"], [0], [1], V)
-    converged.converged(np.zeros((1, C), np.int64), ent_canvas, st, c["k"], c["tau"], c["max_steps"], [0], V)
-    P = selfcond.probs_from_stats(logits, 1.0, so.row_max, so.row_lnz)
-    selfcond.selfcond_embed(P, np.zeros((1, rows), np.int64), np.ones(1, np.uint8), E, wg, wu, wd, rows,
-                            to_bf16=True)
+    for t in range(steps):
+        logits = pool[t]
+        K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
+        group = c["Hq"] // c["Hkv"]
+        mask = attention.visibility_mask(c["L"], 0, C, c["window"])
+        for h in range(c["Hq"]):
+            attention.dense_mask_attention(q[:, h], K[:, h // group], Vv[:, h // group], mask, 1.0 / math.sqrt(D))
+        so = sampler.denoise_sample(logits, 1.0, [0], [1 + t], C)
+        st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
+                                 unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
+                                 step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
+        accept.entropy_accept(so.entropy[None, :], so.sample[None, :], st.canvas, c["budget"], [0], [1 + t], V)
+        converged.converged(so.argmax[None, :], so.entropy[None, :], st, c["k"], c["tau"], c["max_steps"], [0], V)
+        P = selfcond.probs_from_stats(logits, 1.0, so.row_max, so.row_lnz)
+        selfcond.selfcond_embed(P, st.canvas, st.sc_on, E, wg, wu, wd, C, to_bf16=True)
     dt = time.perf_counter() - t0
     cores = min(len(os.sched_getaffinity(0)), max(threads, 1))
-    return dict(value=rows / dt, unit="positions/s", cores=cores, kind="oracle",
-                sample=(f"{rows} canvas positions of the single-canvas step on the host in fp64 numpy: attention for "
-                        f"{rows} rows x 16 heads over 2304 keys, sampler over {rows} rows of V=262144 (Philox "
-                        f"Gumbel), accept + converged over the 256-position canvas, P.E + MLP for {rows} rows "
-                        f"against the full 262144 x 4096 table; {dt:.1f} s"))
+    return dict(value=steps * C / dt, unit="positions/s", cores=cores, kind="oracle",
+                sample=(f"{steps} whole steps of the {C}-position canvas ({steps * C} positions) on the host in fp64 "
+                        f"numpy: attention for {C} rows x {c['Hq']} heads over {c['L'] + C} keys, the sampler over "
+                        f"{C} rows of V={V} (Philox Gumbel), accept + converged, P.E + MLP against the full "
+                        f"{V} x {c['d']} table; {dt:.1f} s"))
 
 
 def serving_bench(policies=("deficit", "arrival")) -> dict:
@@ -343,7 +338,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="canvas positions in the oracle's timed sample")
+    ap.add_argument("--cpu-steps", type=int, default=2, help="whole steps of the canvas in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving", action="store_true",
                     help="run the batched serving loop with deficit admission (and admit-on-arrival for "
@@ -434,7 +429,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
