@@ -230,9 +230,9 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
   a.n_items = static_cast<int32_t>(items);
   const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
   if (D == 256)
-    attend_mfma_kernel<256, E8><<<grid, kAttThreads, 0, s>>>(a);
+    attend_mfma16_kernel<256, E8><<<grid, kAtt16Threads, 0, s>>>(a);
   else
-    attend_mfma_kernel<128, E8><<<grid, kAttThreads, 0, s>>>(a);
+    attend_mfma16_kernel<128, E8><<<grid, kAtt16Threads, 0, s>>>(a);
   DG_LAUNCHED();
   if (plan.nsplit > 1) {
     const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));

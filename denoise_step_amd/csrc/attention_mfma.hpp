@@ -3,39 +3,39 @@
 // Work item: (request, KV head, tile of 128 packed query rows, KV split).  A
 // packed query row is m = j * G + g (row j of the request, query head
 // hk * G + g of the KV group), so the G query heads that share a KV head share
-// every K/V tile.  Four wave64s own 32 packed rows each.
+// every K/V tile.  Eight wave64s own 16 packed rows each (two waves per SIMD).
 //
 // K and V blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per
 // lane, no staging registers; each copy reads whole key rows) into the same XOR-swizzled row-major
-// layout, prefetched one block ahead.  The V operand of the PV product needs 8 keys at one d per
-// lane: it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each lane of
-// a 16-lane group one column of the 4 rows x 16 columns its lanes address.
+// layout, prefetched one block ahead.  The V operand of the PV product needs several keys at one d
+// per lane: it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each
+// lane of a 16-lane group one column of the 4 rows x 16 columns its lanes address.
 //
-// Per 64-key block the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-// (A = K from LDS, B = Q preloaded in registers): each lane then holds 16
-// scores of ONE query row, so the online softmax is in-lane plus one xor-32
-// shuffle.  The probabilities stay in registers as the B operand of
-// O^T = V^T P^T (A = V^T, transposing reads of the row-major V block); the
-// key order inside each 16-key MFMA step is permuted consistently on both
-// operands to match the accumulator layout.  O^T accumulates in fp32 (each
-// lane again owns one row, so the rescale is in-lane).  The softmax reference
+// Per 64-key block a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// (A = K from LDS, B = Q preloaded in registers): each lane holds 16 scores of
+// one query row and the row's other 48 scores sit in the three lanes 16, 32 and
+// 48 away, so the online softmax is in-lane plus two lane-group swaps.  The
+// probabilities stay in registers as the B operand of O^T = V^T P^T; the key
+// order inside each 32-key MFMA step is permuted consistently on both operands
+// to match the accumulator layout.  O^T accumulates in fp32 (the lanes of a row
+// share its softmax state, so the rescale is in-lane).  The softmax reference
 // (running max) moves only when a block's maximum exceeds it by more than 2^8,
-// so the rescale of O (and the AGPR round trip it costs) is rare; probabilities
-// are then at most 2^8, which bf16 and the fp32 sums hold as well as values
-// below 1.  The final division uses the same reference, so the result is the
-// same softmax.
+// so the rescale of O is rare; probabilities are then at most 2^8, which bf16
+// and the fp32 sums hold as well as values below 1.  The final division uses
+// the same reference, so the result is the same softmax.
 //
 // Visibility (per request): key index kk (prefix positions first, then causal
 // rows, then canvas rows) is visible to causal row j iff kk <= cached + j, to a
-// canvas row always.  Keys at or past `cached` are read from the k / v inputs
-// (the causal rows' K/V are exactly the values this launch appends to the
-// pages), so the append has no ordering constraint and the same kernel does it:
-// the split-0 workgroup of each row tile writes its causal rows' K/V for its KV
-// head.  Blocks past the last visible key of the tile are never loaded (tiles
-// holding only masked entries are skipped); only blocks that are not fully
-// visible to every row of a wave evaluate the mask.  With several KV splits
-// each split writes unnormalised partials (O, reference max, sum) and a merge
-// kernel combines them with log-sum-exp weights.
+// canvas row always, both cut to the window when the split has one.  Keys at or
+// past `cached` are read from the k / v inputs (the causal rows' K/V are exactly
+// the values this launch appends to the pages), so the append has no ordering
+// constraint and the same kernel does it: the split-0 workgroup of each row
+// tile writes its causal rows' K/V for its KV head.  Blocks outside the tile's
+// key range are never loaded (tiles holding only masked entries are skipped);
+// only blocks that are not fully visible to every row of a wave evaluate the
+// mask.  With several KV splits each split writes its output normalised by its
+// own sum (bf16) with (reference max, sum), and a merge kernel combines them
+// with log-sum-exp weights.
 #pragma once
 #include "dg_device.hpp"
 
@@ -46,7 +46,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttRows = 128;   // packed query rows per workgroup
 constexpr int kAttKeys = 64;    // keys per block
-constexpr int kAttThreads = 256;
 constexpr int kAttMaxPages = 1024;  // page ids of one split staged in LDS (16K keys)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -71,7 +70,7 @@ struct AttArgs {
   uint16_t* out;        // [rows][Hq][D] bf16 (nsplit == 1)
   uint16_t* o_part;     // [nsplit][rows][Hq][D] bf16, each split's output normalised by its own l (nsplit > 1)
   float2* ml_part;      // [nsplit][rows][Hq] (reference max in log2 units, l)  (nsplit > 1)
-  // E4M3 cache (attend_mfma_kernel<D, true>): codes in place of k_cache / v_cache, values scale * code
+  // E4M3 cache (attend_mfma16_kernel<D, true>): codes in place of k_cache / v_cache, values scale * code
   const uint8_t* k_cache8;
   const uint8_t* v_cache8;
   uint8_t* k_cache8_w;
@@ -145,12 +144,12 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, in
 //
 // Copy q fills slots 64 q .. 64 q + 63, i.e. the 64 / (D / 8) keys q * 64 / (D / 8) ...; lane l
 // fetches chunk (l % (D / 8)) ^ (r & 15) of its key r, so each copy reads whole key rows.
-template <int D>
+template <int D, int NT>
 DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
                      int k_end, uint16_t* kdst, uint16_t* vdst) {
   constexpr int kChunks = D / 8;
   constexpr int kKeysPerCopy = kWave / kChunks;
-  constexpr int kPerWave = kChunks / (kAttThreads / kWave);  // copies issued by each wave
+  constexpr int kPerWave = kChunks / (NT / kWave);  // copies issued by each wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: M0 is scalar
   // the page ids of the block's four 16-key groups in one 16-byte read (kb - k_begin is a multiple
@@ -186,14 +185,15 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
 // block's slots as in att_load.  A block holding both kinds gets both sets of copies; a copy's lanes
 // whose key is of the other kind fetch a valid key of the right kind (the last cached key, the first
 // fresh row), which the conversion then ignores.  Keys past k_end re-read the last visible key.
-template <int D>
+template <int D, int NT>
 DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int k_end, uint8_t* s8, uint16_t* kdst,
                       uint16_t* vdst) {
   constexpr int kChunks = D / 8;
   constexpr int kKeysPerCopy = kWave / kChunks;
-  constexpr int kPerWave = kChunks / (kAttThreads / kWave);
+  constexpr int kPerWave = kChunks / (NT / kWave);
   constexpr int kKeysPerCopy8 = 1024 / D;
-  constexpr int kPerWave8 = kAttKeys / kKeysPerCopy8 / (kAttThreads / kWave);
+  constexpr int kPerWave8 = kAttKeys / kKeysPerCopy8 / (NT / kWave);
+  static_assert(kPerWave8 >= 1, "one code copy per wave at least");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int kl = min(kb + kAttKeys - 1, k_end - 1);
@@ -256,13 +256,13 @@ DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int 
 // The cached keys of the block at kb: codes in S -> bf16 (value * scale, exact for a power-of-two
 // scale) in the block's swizzled slots.  Each thread converts 8-code chunks u = tid + 256 j.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-template <int D>
+template <int D, int NT>
 DG_DEV void att_convert8(const AttArgs& a, const dg_split& sp, int kb, int k_end, const uint8_t* s8, uint16_t* kdst,
                          uint16_t* vdst) {
   constexpr int kChunks = D / 8;
 #pragma unroll
-  for (int j = 0; j < kAttKeys * kChunks / kAttThreads; ++j) {
-    const int u = threadIdx.x + kAttThreads * j;
+  for (int j = 0; j < kAttKeys * kChunks / NT; ++j) {
+    const int u = threadIdx.x + NT * j;
     const int r = u / kChunks, c = u % kChunks;
     if (min(kb + r, k_end - 1) >= sp.cached) continue;
 #pragma unroll
@@ -285,33 +285,14 @@ DG_DEV void att_convert8(const AttArgs& a, const dg_split& sp, int kb, int k_end
 // Waits for every outstanding copy, so that after the next barrier K and V of the block are visible.
 DG_DEV void att_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_only(0)); }
 
-// A operand of O^T = V^T P^T for 32-d tile t and 16-key chunk ch: lane l (d = 32 t + l % 32, half
-// h = l / 32) gets the keys of MFMA k-slots 8 h .. 8 h + 7, which the P^T operand maps to keys
-// 16 ch + 4 h + 0..3 and 16 ch + 8 + 4 h + 0..3.  Two transposing reads: in 16-lane group G = l / 16
-// lane t16 = l % 16 addresses key 16 ch + 4 (G / 2) + t16 / 4 (+ 8), d 32 t + 16 (G % 2) + 4 (t16 % 4).
 typedef short short4v __attribute__((ext_vector_type(4)));
-template <int D>
-DG_DEV bf16x8 att_vfrag(const uint16_t* Vb, int t, int ch) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int G = lane >> 4, t16 = lane & 15;
-  const int r1 = 16 * ch + 4 * (G >> 1) + (t16 >> 2);
-  const int col = 32 * t + 16 * (G & 1) + 4 * (t16 & 3);
-  const uint16_t* p1 = Vb + 8 * att_kslot<D>(r1, col >> 3) + (col & 7);
-  const uint16_t* p2 = Vb + 8 * att_kslot<D>(r1 + 8, col >> 3) + (col & 7);
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p2));
-  const short4v lohi[2] = {lo, hi};
-  bf16x8 v;
-  __builtin_memcpy(&v, lohi, sizeof(v));
-  return v;
-}
 
 // Causal rows' K/V of one KV head into the pages at positions cached + j (16-byte chunks).
-template <int D>
+template <int D, int NT>
 DG_DEV void att_append(const AttArgs& a, const dg_split& sp, int hk, int j0, int j1) {
   constexpr int kChunks = D / 8;
   const int n = (j1 - j0) * kChunks;
-  for (int u = threadIdx.x; u < 2 * n; u += kAttThreads) {
+  for (int u = threadIdx.x; u < 2 * n; u += NT) {
     const bool is_v = u >= n;
     const int w = is_v ? u - n : u;
     const int j = j0 + w / kChunks, c = w % kChunks;
@@ -329,11 +310,11 @@ DG_DEV void att_append(const AttArgs& a, const dg_split& sp, int hk, int j0, int
 
 // E4M3 cache: the causal rows' K/V quantised into the pages (x / scale, clamped to +-448, nearest
 // even), 8 values per thread and step.
-template <int D>
+template <int D, int NT>
 DG_DEV void att_append8(const AttArgs& a, const dg_split& sp, int hk, int j0, int j1) {
   constexpr int kChunks = D / 8;
   const int n = (j1 - j0) * kChunks;
-  for (int u = threadIdx.x; u < 2 * n; u += kAttThreads) {
+  for (int u = threadIdx.x; u < 2 * n; u += NT) {
     const bool is_v = u >= n;
     const int w = is_v ? u - n : u;
     const int j = j0 + w / kChunks, c = w % kChunks;
@@ -354,16 +335,65 @@ DG_DEV void att_append8(const AttArgs& a, const dg_split& sp, int hk, int j0, in
   }
 }
 
+// ---------------------------------------------------------------- the attention kernel
+// Eight waves of 16 packed query rows (two waves per SIMD at ~210 registers each, so one wave's
+// softmax and address arithmetic overlap the other's MFMAs), on v_mfma_f32_16x16x32_bf16; each lane
+// keeps its row's online-softmax state (max in log2 units, sum) and P stays in registers as the B
+// operand of the PV product.  Operand layouts (lane l, group g = l / 16, t = l % 16):
+//   S^T tile (16 keys x 16 rows) = K Q^T: A = K (key t, d 8 g .. 8 g + 7 of the 32-d step),
+//     B = Q^T (row t, the same d), C: row t, keys 4 g .. 4 g + 3 of the tile;
+//   O^T tile (16 d x 16 rows) += V^T P^T over a 32-key chunk: MFMA k-slots 8 g .. 8 g + 3 hold keys
+//     4 g .. 4 g + 3 of the chunk's first 16-key tile and slots 8 g + 4 .. 8 g + 7 the same keys of
+//     its second tile, which is exactly the P this lane holds (no exchange); the V^T operand for that
+//     order is two transposing LDS reads (4 keys x 16 d each).
+// A row's 64 scores of a block are spread over the four groups; its max and sum are combined with
+// v_permlane16_swap / v_permlane32_swap (no LDS traffic).
+constexpr int kAtt16Threads = 512;
+
+DG_DEV float quad_group_max(float v) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(r16[0]), __int_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r32[0]), __int_as_float(r32[1]));
+}
+DG_DEV float quad_group_sum(float v) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(r16[0]) + __int_as_float(r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r32[0]) + __int_as_float(r32[1]);
+}
+
+// A operand of O^T += V^T P^T for 16-d tile dt and 32-key chunk ch (see the layout above).
+template <int D>
+DG_DEV bf16x8 att_vfrag16(const uint16_t* Vb, int dt, int ch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, t16 = lane & 15;
+  const int r1 = 32 * ch + 4 * g + (t16 >> 2);
+  const int col = 16 * dt + 4 * (t16 & 3);
+  const uint16_t* p1 = Vb + 8 * att_kslot<D>(r1, col >> 3) + (col & 7);
+  const uint16_t* p2 = Vb + 8 * att_kslot<D>(r1 + 16, col >> 3) + (col & 7);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p2));
+  const short4v lohi[2] = {lo, hi};
+  bf16x8 v;
+  __builtin_memcpy(&v, lohi, sizeof(v));
+  return v;
+}
+
 template <int D, bool E8>
-__global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
-  constexpr int kDSteps = D / 16;                // MFMA k-steps over D
-  constexpr int kDTiles = D / 32;                // 32-wide output tiles over D
+__global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
+  constexpr int NT = kAtt16Threads;
+  constexpr int kDSteps = D / 32;                // MFMA k-steps over D
+  constexpr int kDTiles = D / 16;                // 16-wide output tiles over D
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
   __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
 
   // XCD-aware order: the hardware deals workgroup L to XCD L % 8; work item t = (L % 8) * per_xcd +
   // L / 8, t = ((req * nsplit + split) * Hkv + hk) * qtiles + qtile, so the row tiles that read the
-  // same K/V (same request, KV head and split) run on one XCD and share its L2.
+  // same K/V (same request, KV head and split) run on one XCD and share its L2.  The tile sees keys
+  // [lo of its first row, hi of its last row) (both edges grow with the row); the splits cut that
+  // range from its first 64-aligned block, the last split also taking the one block the alignment
+  // can add beyond nsplit * split_keys.
   const int per_xcd = (a.n_items + 7) / 8;
   const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (t >= a.n_items) return;
@@ -374,10 +404,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int nr = sp.n_causal + sp.n_canvas;
   const int m_tile0 = qtile * kAttRows;
   if (m_tile0 >= nr * a.G) return;
-  // keys seen by the tile's rows: both edges of a row's range grow with the row (rows are ordered
-  // causal then canvas), so the tile sees [lo of its first row, hi of its last row).  The splits
-  // cut that range from its first 64-aligned block; the last split also takes the one block the
-  // alignment can add beyond nsplit * split_keys.
   const int j_last = min(nr - 1, (m_tile0 + kAttRows - 1) / a.G);
   const int tile_lo = att_row_keys(sp, m_tile0 / a.G).x & ~(kAttKeys - 1);
   const int tile_hi = att_row_keys(sp, j_last).y;
@@ -387,20 +413,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int half = lane >> 5;
-  const int m = m_tile0 + wave * 32 + (lane & 31);
+  const int g = lane >> 4, t16 = lane & 15;
+  const int m = m_tile0 + wave * 16 + t16;
   const bool row_ok = m < nr * a.G;
   const int j = row_ok ? m / a.G : 0;
   const int h = hk * a.G + (row_ok ? m % a.G : 0);
   const int row = sp.row0 + j;
-  // a descriptor whose rows fall outside [0, rows) reads clamped rows and writes nothing there
   const bool row_in = row >= 0 && row < a.rows;
   const int row_c = min(max(row, 0), a.rows - 1);
-  // visible keys [lo, hi) of this lane's row; rows past the tile's end compute an unused copy of
-  // row 0 and never force masking
   const int2 rk = row_ok ? att_row_keys(sp, j) : make_int2(0, sp.cached + nr);
   const int lo = rk.x, hi = rk.y;
-  int wave_hi = hi, wave_lo = lo;  // smallest hi and largest lo of the wave's rows
+  int wave_hi = hi, wave_lo = lo;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
@@ -411,42 +434,38 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
   const int page_lo = k_begin / 16;
   if constexpr (!E8) {
     const int page_hi = min((min(k_end, sp.cached) + 15) / 16, page_lo + kAttMaxPages);
-    for (int p = page_lo + tid; p < page_hi; p += kAttThreads) {
+    for (int p = page_lo + tid; p < page_hi; p += NT) {
       const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
       sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
     }
   }
 
-  // Q fragment (B operand of S^T = K Q^T): 8 consecutive d per MFMA step
+  // Q^T fragment (B operand): row t16, d 32 s + 8 g .. + 7
   bf16x8 qf[kDSteps];
   {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(row_c) * a.Hq + h) * D;
 #pragma unroll
-    for (int s = 0; s < kDSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
-    // land Q before the first K/V copy: the compiler does not count the copies, so a wait for Q that
-    // it placed at the first use inside the block loop would also wait for the prefetched block
+    for (int s = 0; s < kDSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   }
 
-  floatx16 o[kDTiles];
+  floatx4 o[kDTiles];
 #pragma unroll
-  for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
-  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and sum of 2^(x - m_ref)
+  for (int dt = 0; dt < kDTiles; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;
 
   __syncthreads();  // page ids visible
   if (k_begin < k_end) {
     if constexpr (E8)
-      att_load8<D>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+      att_load8<D, NT>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
     else
-      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
+      att_load<D, NT>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
     att_wait();
   }
   __syncthreads();
   if constexpr (E8) {
     if (k_begin < k_end && k_begin < sp.cached) {
-      att_convert8<D>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+      att_convert8<D, NT>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
       __syncthreads();
     }
   }
@@ -455,92 +474,83 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     const bool more = kb + kAttKeys < k_end;
     if (more) {
       if constexpr (E8)
-        att_load8<D>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+        att_load8<D, NT>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
       else
-        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+        att_load<D, NT>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
     }
     const uint16_t* Kb = sm.K[buf];
     const uint16_t* Vb = sm.V[buf];
-    // ---- S^T = K Q^T : two 32-key sub-blocks x 32 rows
-    // the two sub-blocks' chains advance together; the K operands of step s + 1 are read while the
-    // MFMAs of step s run (the scheduling groups keep the reads ahead of the MFMAs)
-    floatx16 sc[2];
+    // ---- S^T = K Q^T: four 16-key tiles, K operands of step s + 1 read under the MFMAs of step s
+    floatx4 sc[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int tt = 0; tt < 4; ++tt) sc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[2][4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
-    bf16x8 kf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      kf[0][b] = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), half)]);
+    for (int tt = 0; tt < 4; ++tt)
+      kf[0][tt] = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(16 * tt + t16, g)]);
 #pragma unroll
     for (int s = 0; s < kDSteps; ++s) {
       if (s + 1 < kDSteps) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          kf[(s + 1) & 1][b] =
-              *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(32 * b + (lane & 31), 2 * (s + 1) + half)]);
+        for (int tt = 0; tt < 4; ++tt)
+          kf[(s + 1) & 1][tt] =
+              *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(16 * tt + t16, 4 * (s + 1) + g)]);
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][b], qf[s], sc[b], 0, 0, 0);
+      for (int tt = 0; tt < 4; ++tt) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][tt], qf[s], sc[tt], 0, 0, 0);
     }
+    // ---- softmax; element e of tile tt holds key 16 tt + 4 g + e of this lane's row
+    if (kb + kAttKeys > wave_hi || kb < wave_lo) {
 #pragma unroll
-    for (int s = 0; s < kDSteps; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two DS reads (step s + 1)
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs (step s)
-    }
-    // ---- softmax; element e of sub-block b holds key 32 b + 8 (e / 4) + 4 half + e % 4 of this lane's row
-    if (kb + kAttKeys > wave_hi || kb < wave_lo) {  // some key of the block is masked for some row of the wave
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
-          sc[b][e] = (key >= lo && key < hi) ? sc[b][e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          const int key = kb + 16 * tt + 4 * g + e;
+          sc[tt][e] = (key >= lo && key < hi) ? sc[tt][e] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mb = mx * a.scale_log2;  // block max in log2 units (-inf if the whole block is masked)
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[tt][e]);
+    mx = quad_group_max(mx);
+    const float mb = mx * a.scale_log2;
     const bool grow = mb > m_ref + kRescaleAbove;
-    const bool rescale = grow && m_ref != -INFINITY;  // before the first visible key O and l are zero
+    const bool rescale = grow && m_ref != -INFINITY;
     if (__any(rescale)) {
       const float alpha = rescale ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.f;
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < kDTiles; ++t)
+      for (int dt = 0; dt < kDTiles; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+        for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
     }
     if (grow) m_ref = mb;
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // masked scores give 2^-inf = 0 either way
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
-    bf16x8 pf[4];
+    bf16x8 pf[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[b][e], a.scale_log2, -m_use));
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[tt][e], a.scale_log2, -m_use));
         psum += p;
-        pf[2 * b + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+        pf[tt >> 1][4 * (tt & 1) + e] = static_cast<__bf16>(p);
       }
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run += psum;
-    // ---- O^T += V^T P^T over four 16-key chunks; key slots follow the accumulator layout
+    l_run += quad_group_sum(psum);
+    // ---- O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int t = 0; t < kDTiles; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(att_vfrag<D>(Vb, t, c), pf[c], o[t], 0, 0, 0);
+      for (int dt = 0; dt < kDTiles; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(att_vfrag16<D>(Vb, dt, c), pf[c], o[dt], 0, 0, 0);
     }
     if (more) att_wait();
     __syncthreads();
     if constexpr (E8) {
       if (more && kb + kAttKeys < sp.cached) {
-        att_convert8<D>(a, sp, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+        att_convert8<D, NT>(a, sp, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
         __syncthreads();
       }
     }
@@ -553,32 +563,26 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttArgs a) {
     const int j1 = min(sp.n_causal, (m_tile0 + kAttRows + a.G - 1) / a.G);
     if (j0 < j1) {
       if constexpr (E8)
-        att_append8<D>(a, sp, hk, j0, j1);
+        att_append8<D, NT>(a, sp, hk, j0, j1);
       else
-        att_append<D>(a, sp, hk, j0, j1);
+        att_append<D, NT>(a, sp, hk, j0, j1);
     }
   }
 
   if (!row_ok || !row_in) return;
-  // O^T element e of tile t: d = 32 t + 8 (e / 4) + 4 half + e % 4, row = this lane's row.  One split:
-  // the output; several: this split's output normalised by its own l, in bf16, and (m, l).
+  // O^T tile dt: this lane holds d = 16 dt + 4 g + e (e = 0 .. 3) of its row
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   const int64_t ridx = static_cast<int64_t>(a.nsplit == 1 ? 0 : split) * a.rows * a.Hq +
                        static_cast<int64_t>(row) * a.Hq + h;
   uint16_t* orow = (a.nsplit == 1 ? a.out : a.o_part) + ridx * D;
 #pragma unroll
-  for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * t + 8 * g4 + 4 * half;
-      uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4] * inv)) |
-            (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 1] * inv)) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 2] * inv)) |
-            (static_cast<uint32_t>(f32_to_bf16(o[t][4 * g4 + 3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(orow + d) = w;
-    }
-  if (a.nsplit > 1 && half == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
+  for (int dt = 0; dt < kDTiles; ++dt) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16(o[dt][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][1] * inv)) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16(o[dt][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+  }
+  if (a.nsplit > 1 && g == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
 }
 
 // Combine KV splits: out = sum_s c_s Ohat_s / sum_s c_s with c_s = 2^(m_s - M) l_s, M = max_s m_s and
