@@ -40,6 +40,7 @@ def run_case(splits, Hq, Hkv, D, dtype, seed=0, check_cache=True, window=0, max_
 
 SMALL = [
     ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 32),                # the three-request batch
+    ([(5, 0, 0), (0, 1, 0), (3, 0, 1), (20, 1, 1), (0, 0, 0)], 2, 2, 128),  # empty and one-row requests, G = 1
     ([(0, 2, 2)], 2, 2, 32),                                     # p0 p1 c0 c1
     ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 64),
     ([(100, 0, 33)], 8, 2, 128),
@@ -136,6 +137,7 @@ def run_case_e4m3(splits, Hq, Hkv, D, seed=0, window=0):
 
 E4M3_CASES = [
     ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 128, 0),            # the three-request batch
+    ([(5, 0, 0), (0, 1, 0), (3, 0, 1), (20, 1, 1), (0, 0, 0)], 2, 2, 256, 1),  # empty / one-row requests, W = 1
     ([(37, 0, 16), (5, 21, 3), (0, 17, 0), (64, 16, 0)], 4, 2, 128, 0),
     ([(300, 40, 70), (1, 0, 129)], 16, 8, 256, 0),               # blocks straddling the cache end
     ([(100, 0, 33)], 8, 2, 128, 0),

@@ -21,7 +21,8 @@ def run_gpu(logits_t, V, rows_per_req, seeds, steps, T=1.0, argmax_only=False, a
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("V,ld,T", [(4999, 5000, 1.0), (1024, 1024, 1.0), (20000, 20008, 0.7), (8, 8, 1.3)])
+@pytest.mark.parametrize("V,ld,T", [(4999, 5000, 1.0), (1024, 1024, 1.0), (20000, 20008, 0.7), (8, 8, 1.3),
+                                    (1, 8, 1.0), (17, 24, 1.0), (16385, 16392, 1.0)])
 def test_sampler_small(dtype, V, ld, T):
     print(f"sampler small dtype={dtype} V={V} ld={ld} T={T}", flush=True)
     rows, rpr = 24, 8
