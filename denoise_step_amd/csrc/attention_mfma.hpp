@@ -42,7 +42,6 @@
 namespace dg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttRows = 128;   // packed query rows per workgroup
 constexpr int kAttKeys = 64;    // keys per block
