@@ -184,5 +184,7 @@ DG_DEV float4 e4m3x4_to_float4(uint32_t w) {
 // lgkmcnt 11:8 left at their maxima).  Used where direct global -> LDS copies issued from inline
 // asm must have landed: the compiler does not count those instructions.
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt operand that waits for LDS / scalar-memory counts <= n only (vmcnt and expcnt at their maxima)
+constexpr int lgkmcnt_only(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 
 }  // namespace dg

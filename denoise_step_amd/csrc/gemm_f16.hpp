@@ -10,10 +10,14 @@
 // small, K (the vocabulary) is huge and the right operand E must stream from
 // HBM exactly once:
 //   * workgroup tile 256 x 256 (256 x 128 when N is not a multiple of 256)
-//     with eight wave64s (2 x 4, two per SIMD so one wave's LDS and barrier
-//     waits overlap the other's MFMAs), each wave 128 x 64 as 4 x 2
+//     with eight wave64s (2 x 4), each wave 128 x 64 as 4 x 2
 //     v_mfma_f32_32x32x16_f16 accumulators; a canvas of 256 rows is one M
 //     tile, so every E element is fetched by exactly one workgroup;
+//   * ping-pong schedule: waves w and w + 4 share a SIMD; waves 0-3 run one
+//     half-step ahead of waves 4-7, and at every workgroup barrier the two
+//     groups swap roles, so in each half-step one wave per SIMD issues its
+//     MFMAs while the other reads its next fragments from LDS and issues the
+//     copies of a later stage;
 //   * K advances 32 per stage through four LDS stages filled by direct
 //     global -> LDS copies (no staging registers) issued three stages ahead,
 //     about 96 KB per CU in flight against HBM latency;
@@ -140,22 +144,26 @@ DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, 
   }
 }
 
-// Each wave owns a 128 x (TN / 4) block: 4 x (TN / 128) accumulators of 32 x 32.  Every operand
-// fragment of the stage (both 16-K steps) is read before the first MFMA, so the MFMAs of the first
-// step wait only for their own reads and the second step's reads arrive behind them.
+// Operand fragments of one stage for one wave: both 16-K steps of its 4 A blocks and TN / 128 B
+// blocks of 32 rows.
+template <int TN>
+struct GemmFrag {
+  half8 a[2][4], b[2][TN / 128];
+};
+
+// Read half-step: every fragment of the stage from LDS (E4M3 B fragments converted to fp16 here,
+// so the MFMA half-step issues nothing but MFMAs).
 template <int TN, bool BF8>
-DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __restrict__ bs, int wm, int wn, int lane,
-                         floatx16 (&acc)[4][TN / 128]) {
+DG_DEV void gemm_read(const _Float16* __restrict__ as, const _Float16* __restrict__ bs, int wm, int wn, int lane,
+                      GemmFrag<TN>& f) {
   constexpr int NJ = TN / 128;
-  constexpr int KS = kGemmTK / 16;  // 16-K steps per stage
-  half8 a[KS][4], b[KS][NJ];
-  uint2 b8[KS][NJ];
+  uint2 b8[2][NJ];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < 2; ++ks) {
     const int c = 2 * ks + (lane >> 5);  // 8-K chunk of this lane
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[ks][i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
+      f.a[ks][i] = *reinterpret_cast<const half8*>(as + 8 * gemm_slot(wm + i * 32 + (lane & 31), c));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int row = wn + j * 32 + (lane & 31);
@@ -163,22 +171,27 @@ DG_DEV void gemm_compute(const _Float16* __restrict__ as, const _Float16* __rest
         b8[ks][j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(bs) + row * 32 +
                                                     16 * ((c >> 1) ^ gemm_swz8(row)) + 8 * (c & 1));
       else
-        b[ks][j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(row, c));
+        f.b[ks][j] = *reinterpret_cast<const half8*>(bs + 8 * gemm_slot(row, c));
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them to their uses)
+  if constexpr (BF8) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if constexpr (BF8) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) b[ks][j] = e4m3x8_to_half8(b8[ks][j].x, b8[ks][j].y);
-    }
+      for (int j = 0; j < NJ; ++j) f.b[ks][j] = e4m3x8_to_half8(b8[ks][j].x, b8[ks][j].y);
+  }
+}
+
+// MFMA half-step: the wave's 128 x (TN / 4) block, 4 x (TN / 128) accumulators of 32 x 32, both 16-K steps.
+template <int TN>
+DG_DEV void gemm_mfma(const GemmFrag<TN>& f, floatx16 (&acc)[4][TN / 128]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
-  }
+      for (int j = 0; j < TN / 128; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
 }
 
 // vector-memory instructions a wave issues per stage
@@ -187,21 +200,28 @@ constexpr int gemm_dma_per_stage() {
   return (kGemmTM / 16 + (BF8 ? TN / 32 : TN / 16)) / kGemmWaves;
 }
 
-// Wait until at most `pending` later stages of this wave's copies are still in flight, then
-// barrier.  A bare s_barrier is used instead of __syncthreads(): the latter's release fence would
-// wait for every outstanding copy, including the prefetched stages.  The empty asm statements keep
-// the compiler from moving LDS accesses across the wait and the barrier.
+// Wait until at most `pending` (0..3) later stages of this wave's copies are still in flight.
 template <int TN, bool BF8>
-DG_DEV void gemm_wait_barrier(int pending) {
+DG_DEV void gemm_vmwait(int pending) {
   constexpr int n = gemm_dma_per_stage<TN, BF8>();
-  asm volatile("" ::: "memory");
-  if (pending >= 2)
+  if (pending >= 3)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * n));
+  else if (pending == 2)
     __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * n));
   else if (pending == 1)
     __builtin_amdgcn_s_waitcnt(vmcnt_only(n));
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+}
+
+// A bare s_barrier is used instead of __syncthreads(): the latter's release fence would wait for
+// every outstanding copy, including the prefetched stages.  The empty asm statements and scheduling
+// barriers keep the compiler from moving LDS accesses or MFMAs across it.
+DG_DEV void gemm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 }
 
@@ -209,10 +229,10 @@ DG_DEV void gemm_wait_barrier(int pending) {
 template <int TN, bool BF8>
 DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
+  constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
-  __shared__ __attribute__((aligned(16))) _Float16 As0[kGemmTM * kGemmTK], As1[kGemmTM * kGemmTK],
-      As2[kGemmTM * kGemmTK], As3[kGemmTM * kGemmTK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs0[kBs], Bs1[kBs], Bs2[kBs], Bs3[kBs];
+  __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
   // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
@@ -227,6 +247,7 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   const int nstage = (k_end - k_begin) / kGemmTK;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int group = wave >> 2;  // one wave of each group per SIMD
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
   const uint32_t off = gemm_lane_offset();
   const uint32_t off8 = BF8 ? gemm_lane_offset8() : 0u;
@@ -238,27 +259,34 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  GemmFrag<TN> f;
 
-  if (nstage > 0) gemm_issue<TN, BF8>(g, m0, n0, k_begin, off, off8, wave, As0, Bs0);
-  if (nstage > 1) gemm_issue<TN, BF8>(g, m0, n0, k_begin + kGemmTK, off, off8, wave, As1, Bs1);
-  if (nstage > 2) gemm_issue<TN, BF8>(g, m0, n0, k_begin + 2 * kGemmTK, off, off8, wave, As2, Bs2);
-  // iteration s: wait for stage s, barrier (stage s visible; every wave is past compute(s - 1), so
-  // that stage's buffer may be refilled), issue stage s + 3, compute stage s
-#define DG_GEMM_STEP(S_OFF, AC, BC, AN, BN)                                                   \
-  {                                                                                           \
-    const int s_ = s + (S_OFF);                                                               \
-    gemm_wait_barrier<TN, BF8>(min(2, nstage - 1 - s_));                                      \
-    if (s_ + 3 < nstage)                                                                      \
-      gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s_ + 3) * kGemmTK, off, off8, wave, AN, BN);  \
-    gemm_compute<TN, BF8>(AC, BC, wm, wn, lane, acc);                                         \
+  const int pro = min(kGemmStages, nstage);
+  for (int s = 0; s < pro; ++s)
+    gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
+  gemm_vmwait<TN, BF8>(pro - 1);
+  gemm_barrier();
+  // Every wave runs read(s) | barrier | MFMA(s) | barrier; group 1 starts one barrier late (and
+  // group 0 ends one barrier late), so between two barriers one group reads while the other
+  // multiplies.  Stage s + 3 refills the buffer of stage s - 1, which both groups have read (and
+  // waited for) before the barrier that precedes this half-step.  Before its barrier each wave
+  // waits for its own copies of stage s + 1, which the next read half-step needs.
+  if (group == 1) gemm_barrier();
+  for (int s = 0; s < nstage; ++s) {
+    const int buf = s & (kGemmStages - 1);
+    gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
+    if (s >= 1 && s + kGemmStages - 1 < nstage) {
+      const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
+      gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
+                          Bs + nb * kBs);
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+    gemm_vmwait<TN, BF8>(min(kGemmStages - 2, max(0, nstage - 2 - s)));
+    gemm_barrier();
+    gemm_mfma<TN>(f, acc);
+    gemm_barrier();
   }
-  for (int s = 0; s < nstage; s += 4) {
-    DG_GEMM_STEP(0, As0, Bs0, As3, Bs3)
-    DG_GEMM_STEP(1, As1, Bs1, As0, Bs0)
-    DG_GEMM_STEP(2, As2, Bs2, As1, Bs1)
-    DG_GEMM_STEP(3, As3, Bs3, As2, Bs2)
-  }
-#undef DG_GEMM_STEP
+  if (group == 0) gemm_barrier();
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
 #pragma unroll
