@@ -13,7 +13,8 @@
 //     with eight wave64s (2 x 4), each wave 128 x 64 as 4 x 2
 //     v_mfma_f32_32x32x16_f16 accumulators; a canvas of 256 rows is one M
 //     tile, so every E element is fetched by exactly one workgroup;
-//   * ping-pong schedule: waves w and w + 4 share a SIMD; waves 0-3 run one
+//   * ping-pong schedule for the long-K P.E launches (the short-K MLP GEMMs
+//     keep one barrier per stage): waves w and w + 4 share a SIMD; waves 0-3 run one
 //     half-step ahead of waves 4-7, and at every workgroup barrier the two
 //     groups swap roles, so in each half-step one wave per SIMD issues its
 //     MFMAs while the other reads its next fragments from LDS and issues the
@@ -226,7 +227,10 @@ DG_DEV void gemm_barrier() {
 }
 
 // The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
-template <int TN, bool BF8>
+// PP: ping-pong schedule (long K loops); otherwise all eight waves read and multiply each stage
+// together between one barrier per stage (short K loops, where the ping-pong's extra barriers and
+// its staggered start cost more than they hide).
+template <int TN, bool BF8, bool PP>
 DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
   constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
@@ -261,32 +265,53 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   GemmFrag<TN> f;
 
-  const int pro = min(kGemmStages, nstage);
-  for (int s = 0; s < pro; ++s)
-    gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
-  gemm_vmwait<TN, BF8>(pro - 1);
-  gemm_barrier();
-  // Every wave runs read(s) | barrier | MFMA(s) | barrier; group 1 starts one barrier late (and
-  // group 0 ends one barrier late), so between two barriers one group reads while the other
-  // multiplies.  Stage s + 3 refills the buffer of stage s - 1, which both groups have read (and
-  // waited for) before the barrier that precedes this half-step.  Before its barrier each wave
-  // waits for its own copies of stage s + 1, which the next read half-step needs.
-  if (group == 1) gemm_barrier();
-  for (int s = 0; s < nstage; ++s) {
-    const int buf = s & (kGemmStages - 1);
-    gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
-    if (s >= 1 && s + kGemmStages - 1 < nstage) {
-      const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
-      gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
-                          Bs + nb * kBs);
+  if constexpr (!PP) {
+    // iteration s: wait for stage s, barrier (stage s visible; every wave is past MFMA(s - 1), so
+    // that stage's buffer may be refilled), issue stage s + 3, read and multiply stage s
+    const int pro = min(kGemmStages - 1, nstage);
+    for (int s = 0; s < pro; ++s)
+      gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
+    for (int s = 0; s < nstage; ++s) {
+      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, nstage - 1 - s));
+      gemm_barrier();
+      if (s + kGemmStages - 1 < nstage) {
+        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
+        gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
+                            Bs + nb * kBs);
+      }
+      const int buf = s & (kGemmStages - 1);
+      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them to their uses)
+      gemm_mfma<TN>(f, acc);
     }
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
-    gemm_vmwait<TN, BF8>(min(kGemmStages - 2, max(0, nstage - 2 - s)));
+  } else {
+    const int pro = min(kGemmStages, nstage);
+    for (int s = 0; s < pro; ++s)
+      gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
+    gemm_vmwait<TN, BF8>(pro - 1);
     gemm_barrier();
-    gemm_mfma<TN>(f, acc);
-    gemm_barrier();
+    // Every wave runs read(s) | barrier | MFMA(s) | barrier; group 1 starts one barrier late (and
+    // group 0 ends one barrier late), so between two barriers one group reads while the other
+    // multiplies.  Stage s + 3 refills the buffer of stage s - 1, which both groups have read (and
+    // waited for) before the barrier that precedes this half-step.  Before its barrier each wave
+    // waits for its own copies of stage s + 1, which the next read half-step needs.
+    if (group == 1) gemm_barrier();
+    for (int s = 0; s < nstage; ++s) {
+      const int buf = s & (kGemmStages - 1);
+      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
+      if (s >= 1 && s + kGemmStages - 1 < nstage) {
+        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
+        gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
+                            Bs + nb * kBs);
+      }
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, max(0, nstage - 2 - s)));
+      gemm_barrier();
+      gemm_mfma<TN>(f, acc);
+      gemm_barrier();
+    }
+    if (group == 0) gemm_barrier();
   }
-  if (group == 0) gemm_barrier();
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
 #pragma unroll
@@ -301,17 +326,17 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
       }
 }
 
-// ROLE only names the instantiation (0: P.E contraction, 1: MLP GEMMs) so that profilers report the
-// dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
+// ROLE names the instantiation (0: P.E contraction, ping-pong schedule; 1: MLP GEMMs, one barrier per
+// stage), so that profilers also report the dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
 // of 256).
 template <int ROLE, int TN>
 __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
-  gemm_splitk_body<TN, false>(g);
+  gemm_splitk_body<TN, false, ROLE == 0>(g);
 }
 
 // P.E against an E4M3 embedding table (N a multiple of 256): the E stream is one byte per element.
 __global__ __launch_bounds__(kGemmThreads) void gemm_f16_e4m3_splitk_kernel(GemmArgs g) {
-  gemm_splitk_body<256, true>(g);
+  gemm_splitk_body<256, true, true>(g);
 }
 
 struct GemmPlan {
