@@ -164,18 +164,8 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
     const uint16_t* vsrc = att_row<D>(a, sp, pq, kb, hk, kk, true) + 8 * c;
     const uint32_t klds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
     const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vdst + kWave * 8 * q));
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(klds), "v"(ksrc)
-        : "memory", "m0");
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(vlds), "v"(vsrc)
-        : "memory", "m0");
+    lds_copy16(klds, ksrc);
+    lds_copy16(vlds, vsrc);
   }
 }
 
@@ -209,18 +199,8 @@ DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int 
       const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s8 + kAttKeys * D + 1024 * q));
       const uint8_t* ksrc = a.k_cache8 + off;
       const uint8_t* vsrc = a.v_cache8 + off;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "global_load_lds_dwordx4 %1, off"
-          :
-          : "s"(klds), "v"(ksrc)
-          : "memory", "m0");
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "global_load_lds_dwordx4 %1, off"
-          :
-          : "s"(vlds), "v"(vsrc)
-          : "memory", "m0");
+      lds_copy16(klds, ksrc);
+      lds_copy16(vlds, vsrc);
     }
   }
   if (kl >= sp.cached) {
@@ -236,18 +216,8 @@ DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int 
       const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vdst + kWave * 8 * q));
       const uint16_t* ksrc = a.k + off;
       const uint16_t* vsrc = a.v + off;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "global_load_lds_dwordx4 %1, off"
-          :
-          : "s"(klds), "v"(ksrc)
-          : "memory", "m0");
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "global_load_lds_dwordx4 %1, off"
-          :
-          : "s"(vlds), "v"(vsrc)
-          : "memory", "m0");
+      lds_copy16(klds, ksrc);
+      lds_copy16(vlds, vsrc);
     }
   }
 }

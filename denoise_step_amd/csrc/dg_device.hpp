@@ -180,6 +180,23 @@ DG_DEV float4 e4m3x4_to_float4(uint32_t w) {
   return make_float4(a[0], a[1], b[0], b[1]);
 }
 
+// Direct global -> LDS copies (global_load_lds_dwordx4): each lane fetches 16 bytes and lane i's bytes
+// land at LDS address lds + 16 i.  lds must be wave-uniform; it is passed in M0 through a register
+// constraint, so the compiler sets M0 itself and knows it is in use.  Issued from inline asm, the
+// copies are tracked only by the explicit vmcnt waits of the code that issues them.
+DG_DEV void lds_copy16(uint32_t lds, const void* src) {  // per-lane 64-bit source address
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// the same with a wave-uniform base and a per-lane 32-bit byte offset; NT marks the load non-temporal
+template <bool NT>
+DG_DEV void lds_copy16(uint32_t lds, const void* base, uint32_t lane_off) {
+  if constexpr (NT)
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
+}
+
 // s_waitcnt immediate that waits for vmcnt <= n only (vmcnt in bits 3:0 and 15:14; expcnt 6:4 and
 // lgkmcnt 11:8 left at their maxima).  Used where direct global -> LDS copies issued from inline
 // asm must have landed: the compiler does not count those instructions.

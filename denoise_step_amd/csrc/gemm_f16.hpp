@@ -74,9 +74,9 @@ DG_DEV uint32_t gemm_lane_offset() {
   return static_cast<uint32_t>(((lane >> 2) * 32 + 8 * c) * 2);
 }
 
-// The copy is issued from inline asm (M0 = LDS destination, scalar base + per-lane 32-bit offset) so
-// that its completion is tracked only by the explicit vmcnt waits of the pipeline below; the main
-// loop issues no other vector-memory instruction, so those counts are exact.
+// The copy (lds_copy16: scalar base + per-lane 32-bit offset) is tracked only by the explicit vmcnt
+// waits of the pipeline below; the main loop issues no other vector-memory instruction, so those
+// counts are exact.
 // NT marks the load non-temporal: used for the right operand, which every workgroup streams once
 // (E^T is read by exactly one tile per K range), so it does not evict the left operand that the
 // workgroups of the other N tiles re-read from L2.
@@ -85,20 +85,7 @@ DG_DEV void gemm_dma(const _Float16* __restrict__ base, int64_t rows, int row0, 
                      _Float16* lds, int q) {
   const char* ub = reinterpret_cast<const char*>(base) + kblk_index(row0 + 16 * q, k0, rows) * 2;
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + q * kWave * 8));
-  if constexpr (NT)
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %2 nt"
-        :
-        : "s"(lds_addr), "v"(lane_off), "s"(ub)
-        : "memory", "m0");
-  else
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
-        :
-        : "s"(lds_addr), "v"(lane_off), "s"(ub)
-        : "memory", "m0");
+  lds_copy16<NT>(lds_addr, ub, lane_off);
 }
 
 // E4M3 right operand: a K slice of one row is 32 bytes, two 16-byte chunks; chunk c of row r is
@@ -120,12 +107,7 @@ DG_DEV void gemm_dma8(const uint8_t* __restrict__ base, int64_t rows, int row0, 
                       uint8_t* lds, int q) {
   const uint8_t* ub = base + kblk_index(row0 + 32 * q, k0, rows);
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + q * 1024));
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt"
-      :
-      : "s"(lds_addr), "v"(lane_off), "s"(ub)
-      : "memory", "m0");
+  lds_copy16<true>(lds_addr, ub, lane_off);
 }
 
 // Issue one stage: A (256 rows) and B (TN rows) as 1-KB instructions shared round-robin by the waves.
