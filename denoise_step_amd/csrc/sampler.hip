@@ -130,7 +130,7 @@ DG_DEV float load1(const void* row, int64_t idx) {
 // Per-lane state of the streaming pass.
 struct LaneState {
   float av;     // largest logit seen
-  int64_t ag;   // first index of the 8-logit group holding it (-1: none)
+  int32_t ag;   // first index of the 8-logit group holding it (-1: none; a row index fits in int32)
   SoftState ss;
   float kv;     // best first-level key (log2 units)
   int32_t kb;   // its block
@@ -176,16 +176,16 @@ DG_DEV void sample_iteration(const char* row, int64_t E, int32_t V, float c, uin
   for (int q = 0; q < kRounds; ++q) {
     float v = l[q][0];
 #pragma unroll
-    for (int j = 1; j < kGroup; ++j) v = fmaxf(v, l[q][j]);  // chains of 3-input maxima
+    for (int j = 1; j < kGroup; ++j) v = __builtin_elementwise_maximum(v, l[q][j]);  // v_maximum3_f32 chains
     gm[q] = v;
     const bool better = v > ls.av;
     ls.av = better ? v : ls.av;
-    ls.ag = better ? E + q * (kSampleThreads * kGroup) + kGroup * t : ls.ag;
+    ls.ag = better ? static_cast<int32_t>(E) + q * (kSampleThreads * kGroup) + kGroup * t : ls.ag;
   }
   if constexpr (!ARGMAX_ONLY) {
     float mx = gm[0];
 #pragma unroll
-    for (int q = 1; q < kRounds; ++q) mx = fmaxf(mx, gm[q]);
+    for (int q = 1; q < kRounds; ++q) mx = __builtin_elementwise_maximum(mx, gm[q]);
     // reference of this iteration's exponentials: shared by the lane pair (the pair's running max in
     // base 2), or by the whole workgroup (the iteration's max) when the operand is written
     float m;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_partial_kernel(
 
   // the argmax travels as (value, first index of its 8-logit group); the merge resolves the index
   float av = ls.av;
-  int32_t ai = ls.ag >= 0 ? static_cast<int32_t>(ls.ag) : 0x7FFFFFFF;
+  int32_t ai = ls.ag >= 0 ? ls.ag : 0x7FFFFFFF;
   SoftState ss = ls.ss;
   float kv = ls.kv;
   int32_t kb = ls.kb;
