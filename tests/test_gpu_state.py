@@ -29,7 +29,7 @@ def test_philox_device_matches_oracle():
     assert np.array_equal(got, philox.philox4x32_10(ctr, key))
 
 
-@pytest.mark.parametrize("C", [1, 16, 100, 256, 1000, 1024])
+@pytest.mark.parametrize("C", [1, 16, 64, 65, 100, 256, 300, 512, 1000, 1024])  # every workgroup size, both sides of its edges
 def test_entropy_accept_matches_oracle(C):
     import denoise_step_amd as dg
     torch = P.torch_mod()
