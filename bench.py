@@ -336,8 +336,10 @@ def serving_bench(policies=("deficit", "arrival")) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU's clocks settle within the first ~50 steps (~35 ms of this load): 5 warmup steps time the
+    # ramp (measured 679-687 us per step), 50 or more the steady state (648-655 us per step)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-steps", type=int, default=2, help="whole steps of the canvas in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving", action="store_true",
