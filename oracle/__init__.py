@@ -17,9 +17,11 @@ Modules
   verify     greedy longest-matching-prefix block verification
   backbone   the one-layer fp32 backbone of the tiny closed loop
   loop       the tiny closed denoise loop
+  admission  deficit token-budget admission of a serving loop
+  serving    the batched serving loop composed from the parts above
+  fp8        OCP E4M3 decoding and encoding
 
-Parity status per function is listed in each module header; every function
-here is pinned by a ``-m "not gpu"`` test against closed forms, brute force,
-invariants or an independent library routine, except where a header says
-"parity unpinned".
+Every function here is pinned by a ``-m "not gpu"`` test against values the
+pages fix, hand-worked traces, closed forms, brute force, invariants or an
+independent library routine; each module header names its pins.
 """

@@ -7,8 +7,11 @@ reads K/V.  Layer: q, k, v = x Wq, x Wk, x Wv; h = x + Attn(q, k, v) Wo;
 logits = scale * h E^T (tied embedding / LM head).  Readings: no
 normalisation layer, no position encoding, no sqrt(d) embedding scale.
 
-Parity status: a composition of oracle.attention (pinned) and plain numpy
-matmuls; the layer itself is pinned only through its parts.
+Pinned by tests/test_oracle_traces.py against the hand-worked traces of
+tests/golden/backbone_trace.txt: uniform attention under zero scores, a 1:3
+weighting from a score difference of ln 3, the residual, the causal prefill
+and commit passes that append K/V, the canvas pass that sees every key and
+writes none, the orientation of Wv and Wo, and the tied LM head h E^T.
 """
 from __future__ import annotations
 

@@ -8,8 +8,13 @@ writes the block's K/V and emits its tokens) and section
 cases).  Each denoise step runs, in order: backbone (decoder) -> sampler ->
 entropy-budget accept -> convergence -> self-conditioning for the next step.
 
-Parity status: "parity unpinned" beyond the composition of its pinned parts
-(the pages print no trajectory); determinism is checked by a test.
+Pinned by tests/test_oracle_traces.py: two constructed inputs with closed-form
+dynamics (a one-hot case whose block converges after k + 1 steps with the
+prefill canvas as its tokens and its commit pass appended after the prefix;
+an equal-entropy case where the budget accepts exactly two positions per step,
+the others are renoised from Philox RENOISE at the step's global step, and the
+block runs to the cap and restarts from Philox INIT); tests/test_oracle_loop.py
+checks determinism and the dynamics the workload's constants imply.
 """
 from __future__ import annotations
 

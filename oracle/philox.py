@@ -19,9 +19,12 @@ Keying
       stream GUMBEL_INNER = 3 : element level, inside the winning block: vocabulary element i
                                  uses word i & 3 of counter c0 = i >> 2
   step is the request's global step counter, never reset between blocks.
-  The block map (b -> c0, word) is a bijection: the four blocks p, p + 128, p + 256, p + 384 of
-  each run of 512 blocks share one counter, so one Philox call serves four blocks that lie 128
-  blocks apart (the GPU pass gives them to one lane).
+  The block map (b -> c0, word) is a bijection onto (counter, word) pairs, so every block of a
+  position gets its own Philox output word and the block noise values are independent; the four
+  blocks p, p + 128, p + 256, p + 384 of each run of 512 blocks share one counter (words 0..3),
+  so a pass that reads the row in runs of 128 blocks draws the noise of four blocks with one
+  Philox call.  Any bijection gives the same law of the draw; this one is fixed so that the two
+  sides of a parity test draw identical noise.
 
 Mappings
   uniform(w) = (2 * (w >> 9) + 1) * 2**-24         in (0, 1); exact in fp32

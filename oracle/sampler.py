@@ -15,22 +15,29 @@ Philox streams of ``oracle.philox``.  Also returned: m = max_i x_i and
 ln Z = ln sum_i exp(x_i - m), which define p_i = exp(x_i - m - ln Z) for the
 self-conditioning step.
 
-The Gumbel-max candidate is drawn in two levels over blocks of 16 consecutive
-vocabulary ids (the last block of a row may be shorter):
-  1. block b has log-mass L_b = ln sum_{i in b} exp(x_i) and noise G_b; the
-     winning block is b* = argmax_b (L_b + G_b);
-  2. inside b*, the candidate is argmax_{i in b*} (x_i + g_i) with fresh noise g.
-The maximum of Gumbel-perturbed values over a set is itself Gumbel-distributed
-with location the set's log-mass, and its argmax is independent of that
-maximum, so b* is drawn with probability Z_b / Z and the candidate with
-probability exp(x_i) / Z overall: the same law as the flat argmax_i (x_i + g_i)
-over the row, with one noise value per 16 ids at the first level.  A row of at
-most 16 ids is a single block, where the draw is the flat Gumbel-max.
+Two forms of the Gumbel-max candidate:
+  * ``flat_gumbel_candidate`` is the trick as the page states it: one Gumbel
+    value g_i per vocabulary id and the candidate argmax_i (x_i + g_i).  Its law
+    is softmax(x) (the Gumbel-max theorem).
+  * ``gumbel_candidate`` is the draw the step computes (a reading of the page,
+    which fixes no noise layout): two levels over blocks of 16 consecutive
+    ids (the last block of a row may be shorter).  Block b has log-mass
+    L_b = ln sum_{i in b} exp(x_i) and its own noise G_b; the winning block is
+    b* = argmax_b (L_b + G_b); inside b* the candidate is argmax_{i in b*}
+    (x_i + g_i) with per-id noise.  The maximum of Gumbel-perturbed values over
+    a set is Gumbel with the set's log-mass as location, independent of which
+    element attains it, so b* is drawn with probability Z_b / Z and the
+    candidate with probability exp(x_i) / Z: the flat draw's law, with one
+    noise value per 16 ids at the first level.  The per-id noise g_i is the
+    flat draw's own, so a row of at most 16 ids (one block) gives exactly the
+    flat candidate.
 
 Pinned by tests/test_oracle_sampler.py: entropy closed forms (uniform row ->
 ln V, one-hot -> 0, two-point, k equal maxima -> ln k), shift invariance,
-sum p = 1, argmax == numpy.argmax, and a chi-square test that Gumbel-max
-samples follow softmax(x).
+sum p = 1, argmax == numpy.argmax, chi-square tests that the flat candidate
+follows softmax(x), that the two-level candidate follows softmax(x) and its
+block the block masses (up to V = 262144 on peaked and diffuse Zipf rows),
+that both draws give the same law, and that one block reduces to the flat draw.
 """
 from __future__ import annotations
 
@@ -82,12 +89,19 @@ def _top2_gap(v: np.ndarray) -> float:
     return float(v[i] - np.max(rest))
 
 
-def gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int):
-    """Two-level Gumbel-max candidate for one row of scaled logits x (fp64).
+def flat_gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int):
+    """The Gumbel-max trick as stated: argmax_i (x_i + g_i), one Gumbel value per id.
 
-    Returns (candidate id, key gap): the gap is the smaller of the top-2 gaps of
-    the block keys and of the keys inside the winning block (near-tie accounting).
+    g_i is the per-id noise of ``philox.inner_gumbels`` (stream GUMBEL_INNER).  Returns
+    (candidate id, top-2 gap of the keys).
     """
+    x = np.asarray(x, dtype=np.float64)
+    key = x + philox.inner_gumbels(seed, pos, step, 0, x.size)
+    return int(np.argmax(key)), _top2_gap(key)
+
+
+def block_log_mass(x: np.ndarray) -> np.ndarray:
+    """L_b = ln sum_{i in b} exp(x_i) over blocks of 16 consecutive ids (the last may be shorter)."""
     x = np.asarray(x, dtype=np.float64)
     V = x.size
     nb = (V + philox.GUMBEL_BLOCK - 1) // philox.GUMBEL_BLOCK
@@ -95,8 +109,21 @@ def gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int):
     xb[:V] = x
     xb = xb.reshape(nb, philox.GUMBEL_BLOCK)
     mb = np.max(xb, axis=1)
-    log_mass = mb + np.log(np.sum(np.exp(xb - mb[:, None]), axis=1))
-    bkey = log_mass + philox.block_gumbels(seed, pos, step, nb)
+    return mb + np.log(np.sum(np.exp(xb - mb[:, None]), axis=1))
+
+
+def gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int, log_mass=None):
+    """Two-level Gumbel-max candidate for one row of scaled logits x (fp64).
+
+    log_mass: ``block_log_mass(x)`` when the caller already has it (draws over many positions
+    of one row).  Returns (candidate id, key gap): the gap is the smaller of the top-2 gaps of
+    the block keys and of the keys inside the winning block (near-tie accounting).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    V = x.size
+    if log_mass is None:
+        log_mass = block_log_mass(x)
+    bkey = log_mass + philox.block_gumbels(seed, pos, step, log_mass.size)
     b = int(np.argmax(bkey))
     lo, hi = b * philox.GUMBEL_BLOCK, min((b + 1) * philox.GUMBEL_BLOCK, V)
     ikey = x[lo:hi] + philox.inner_gumbels(seed, pos, step, lo, hi)
@@ -104,8 +131,10 @@ def gumbel_candidate(x: np.ndarray, seed: int, pos: int, step: int):
 
 
 def denoise_sample(logits: np.ndarray, temperature: float, seeds, steps, rows_per_req: int,
-                   argmax_only: bool = False, active=None) -> SampleOut:
+                   argmax_only: bool = False, active=None, draw: str = "two_level") -> SampleOut:
     """Sampler over logit rows.
+
+    draw: "two_level" (the step's draw, ``gumbel_candidate``) or "flat" (``flat_gumbel_candidate``).
 
     logits: [rows, V] (already decoded to float; bf16 inputs are exact in fp64).
     Row r belongs to request r // rows_per_req at canvas position r % rows_per_req;
@@ -132,7 +161,8 @@ def denoise_sample(logits: np.ndarray, temperature: float, seeds, steps, rows_pe
         out.entropy[r] = H
         out.row_max[r] = m
         out.row_lnz[r] = np.log(Z)
-        out.sample[r], out.key_gap[r] = gumbel_candidate(x, int(seeds[req]), pos, int(steps[req]))
+        cand = flat_gumbel_candidate if draw == "flat" else gumbel_candidate
+        out.sample[r], out.key_gap[r] = cand(x, int(seeds[req]), pos, int(steps[req]))
     return out
 
 

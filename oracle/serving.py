@@ -16,8 +16,9 @@ page (section on the deficit token-budget scheduler) for admission and the Diffu
   6. transitions: prefill -> denoise; a committed block -> commit pass next iteration; after the
      commit pass of its last block a request is done.
 
-Parity status: "parity unpinned" beyond the composition of its pinned parts (admission, attention,
-sampler, accept, converged); no page prints a serving trajectory.
+Pinned by tests/test_oracle_traces.py against the hand-worked schedule of
+tests/golden/serving_trace.txt (admissions, tokens and deficit per iteration, the split of every
+launch, the commit iterations, the first canvases and where each causal pass's K/V land).
 """
 from __future__ import annotations
 

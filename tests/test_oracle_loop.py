@@ -1,4 +1,4 @@
-"""The tiny closed loop: determinism and the dynamics its constants imply (parity unpinned beyond parts)."""
+"""The tiny closed loop: determinism and the dynamics its constants imply (hand-worked traces: test_oracle_traces.py)."""
 import numpy as np
 
 import synth

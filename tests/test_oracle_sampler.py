@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 from scipy import stats
 
+import synth
 from oracle import sampler
 
 NEG = -1.0e4  # exp(NEG - max) underflows to exactly 0 in fp64
@@ -86,13 +87,85 @@ def test_gumbel_max_follows_softmax():
 
 
 def test_single_block_is_flat_gumbel_max():
-    from oracle import philox
+    """A row of at most 16 ids is one block: the two-level draw is the flat draw, id for id."""
     rng = np.random.default_rng(7)
     for V in (1, 5, 12, 16):
         x = rng.normal(0, 2, V)
         for pos in range(20):
             cand, _ = sampler.gumbel_candidate(x, 99, pos, 4)
-            assert cand == int(np.argmax(x + philox.inner_gumbels(99, pos, 4, 0, V)))
+            assert cand == sampler.flat_gumbel_candidate(x, 99, pos, 4)[0]
+
+
+def _rank_buckets(p: np.ndarray, n: int, n_tail: int = 12, cell: float = 25.0):
+    """Chi-square cells for n draws from p: every id expected >= `cell` times on its own (the top
+    ids), the rest in order of decreasing probability cut into about `n_tail` buckets of equal mass.
+    Returns (cell of each id, expected count per cell)."""
+    order = np.argsort(-p, kind="stable")
+    cells = np.empty(p.size, np.int64)
+    top = int(np.sum(p[order] * n >= cell))
+    cells[order[:top]] = np.arange(top)
+    rest = order[top:]
+    cum = np.cumsum(p[rest]) / max(np.sum(p[rest]), 1e-300)
+    cells[rest] = top + np.minimum((cum * n_tail).astype(np.int64), n_tail - 1)
+    expect = np.bincount(cells, weights=p, minlength=top + n_tail) * n
+    return cells, expect
+
+
+def _chi2_pvalue(cells, expect, draws):
+    obs = np.bincount(cells[np.asarray(draws)], minlength=expect.size)
+    keep = expect > 0
+    return stats.chisquare(obs[keep], expect[keep] * obs.sum() / expect[keep].sum()).pvalue
+
+
+def test_flat_draw_follows_softmax():
+    """The Gumbel-max theorem for the flat draw, on a Zipf row of 4096 ids over 4000 positions."""
+    x = synth.bf16_bits_to_f32(synth.zipf_logits_bf16(0, "flat-law", 1, 4096)[0]).astype(np.float64)
+    n = 4000
+    draws = [sampler.flat_gumbel_candidate(x, 5, pos, 2)[0] for pos in range(n)]
+    cells, expect = _rank_buckets(sampler.probabilities(x, 1.0), n)
+    assert _chi2_pvalue(cells, expect, draws) > 1e-4
+
+
+def test_two_level_and_flat_draws_have_one_law():
+    """Both draws on one row of 2048 ids (128 blocks), 4000 positions each: a two-sample
+    chi-square test over probability-rank cells finds no difference, and each follows softmax."""
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1.5, 2048)
+    x[rng.choice(2048, 6, replace=False)] += 4.0
+    n = 4000
+    lm = sampler.block_log_mass(x)
+    two = [sampler.gumbel_candidate(x, 8, pos, 3, log_mass=lm)[0] for pos in range(n)]
+    flat = [sampler.flat_gumbel_candidate(x, 8, pos, 3)[0] for pos in range(n)]
+    cells, expect = _rank_buckets(sampler.probabilities(x, 1.0), n)
+    table = np.stack([np.bincount(cells[two], minlength=expect.size),
+                      np.bincount(cells[flat], minlength=expect.size)])
+    table = table[:, table.sum(axis=0) > 0]
+    assert stats.chi2_contingency(table).pvalue > 1e-4
+    assert _chi2_pvalue(cells, expect, two) > 1e-4 and _chi2_pvalue(cells, expect, flat) > 1e-4
+
+
+@pytest.mark.parametrize("kind", ["peaked", "diffuse"])
+def test_two_level_law_at_full_vocabulary(kind):
+    """V = 262144 on the benchmark's Zipf rows: of 16 generated rows, the lowest-entropy one (a few
+    ids carry most of the mass) and the highest (mass spread over the whole vocabulary).  Over
+    3000 positions the candidates follow softmax(x) -- the top ids one by one, the rest in
+    equal-mass probability-rank buckets -- and their blocks follow the block masses Z_b / Z."""
+    V, n = 262144, 3000
+    rows = synth.bf16_bits_to_f32(synth.zipf_logits_bf16(0, "law-262144", 16, V)).astype(np.float64)
+    H = [sampler.softmax_stats(r)[3] for r in rows]
+    x = rows[int(np.argmin(H) if kind == "peaked" else np.argmax(H))]
+    lm = sampler.block_log_mass(x)
+    draws = np.array([sampler.gumbel_candidate(x, 21, pos, 6, log_mass=lm)[0] for pos in range(n)])
+    p = sampler.probabilities(x, 1.0)
+    cells, expect = _rank_buckets(p, n)
+    assert _chi2_pvalue(cells, expect, draws) > 1e-4
+    pb = p.reshape(-1, 16).sum(axis=1)
+    bcells, bexpect = _rank_buckets(pb, n)
+    assert _chi2_pvalue(bcells, bexpect, draws // 16) > 1e-4
+    if kind == "peaked":
+        assert expect.size > 13          # several ids are cells of their own
+    else:
+        assert np.max(p) * n < 25        # no id reaches a cell of its own: all mass in rank buckets
 
 
 def test_two_level_draw_follows_softmax_across_blocks():

@@ -47,6 +47,24 @@ def test_mlp_zero_and_linearity_of_up_branch():
     np.testing.assert_allclose(selfcond.gated_mlp(s, wg, wu, wd), ref.numpy(), rtol=1e-12)
 
 
+def test_geglu_gate_up_down_order_hand_worked():
+    """Which projection goes through the GELU, and the orientation of all three weights, from a
+    hand-worked case.  Pre-activations of magnitude >= 10 saturate the tanh in fp64, so the GELU
+    passes z >= 10 through unchanged and sends z <= -10 to 0 exactly:
+      s = (1, 0): gate = (10, 10), up = (3, 5)  -> hidden (30, 50) -> y = 30 (1, 2) + 50 (4, 8) = (230, 460)
+      s = (0, 1): gate = (-12, 11), up = (2, 9) -> hidden (0, 99)  -> y = 99 (4, 8) = (396, 792)
+    Swapping gate and up, or transposing any of the three matrices, gives other values (e.g. a
+    transposed W_gate: (30, 60) for the first row; a transposed W_down: (130, 520))."""
+    wg = np.array([[10.0, 10.0], [-12.0, 11.0]])
+    wu = np.array([[3.0, 5.0], [2.0, 9.0]])
+    wd = np.array([[1.0, 2.0], [4.0, 8.0]])
+    y = selfcond.gated_mlp(np.eye(2), wg, wu, wd)
+    np.testing.assert_array_equal(y, [[230.0, 460.0], [396.0, 792.0]])
+    for bad in (selfcond.gated_mlp(np.eye(2), wu, wg, wd), selfcond.gated_mlp(np.eye(2), wg.T, wu, wd),
+                selfcond.gated_mlp(np.eye(2), wg, wu.T, wd), selfcond.gated_mlp(np.eye(2), wg, wu, wd.T)):
+        assert np.abs(bad - y).max() > 1.0
+
+
 def test_selfcond_off_is_plain_lookup_and_bf16_rounding():
     rng = np.random.default_rng(4)
     E = rng.normal(0, 1 / 8, (50, 8))
