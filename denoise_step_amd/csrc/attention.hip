@@ -168,9 +168,21 @@ void launch_attend_wave(const void* q, const void* k, const void* v, const void*
                                                      scale, out);
 }
 
+// Host bounds of the MFMA path.  A request's splits depend on its own descriptor (att_nsplit), which
+// the host does not see; from the launch bounds it sizes the grid (work items) and the split
+// partials so that every set of descriptors within them fits:
+//   a request has at most ns_hi = att_nsplit(1, nb_max) splits (the rule grows with the keys and
+//   shrinks with the rows), and a split request at most kAttTargetItems / (Hkv qt) + 1 splits plus
+//   the ones its key span forces, so over the launch
+//     items      <= n_req kAttTargetItems + Hkv extra (ceil(rows G / 128) + n_req)
+//     split rows <= n_req ceil(128 kAttTargetItems / Hq) + extra rows
+//   with extra = 1 + ceil(nb_max / kAttMaxSplitBlocks); each bound also <= the plain product.
+// The grid holds at most kAttMaxGrid workgroups (a few per CU); each walks its items in turn.
+constexpr int64_t kAttMaxGrid = 4096;
+
 struct AttPlan {
   bool mfma;
-  int32_t qtiles, nsplit, split_keys;
+  int64_t item_cap, part_cap, grid;
   size_t off_ml, bytes;
 };
 
@@ -179,20 +191,21 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   AttPlan p{};
   p.mfma = dtype == DG_BF16 && (D == 128 || D == 256);
   if (!p.mfma) return p;
-  const int32_t G = Hq / Hkv;
-  p.qtiles = static_cast<int32_t>(cdiv(static_cast<int64_t>(max_rows) * G, kAttRows));
-  const int32_t nblocks = static_cast<int32_t>(cdiv(max_keys, kAttKeys));
-  const int64_t base = static_cast<int64_t>(n_req) * Hkv * p.qtiles;
-  // about one workgroup per CU, at least 2 key blocks per split
-  int32_t nsplit = static_cast<int32_t>(std::min<int64_t>(cdiv(256, base), std::max(1, nblocks / 2)));
-  // a split's page ids are staged in LDS: at most kAttMaxPages pages (16 keys each) per split
-  nsplit = std::max<int32_t>(nsplit, static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys,
-                                                               static_cast<int64_t>(kAttMaxPages - 8) * 16)));
-  nsplit = std::max(1, std::min(nsplit, kMergeSplits));
-  p.split_keys = static_cast<int32_t>(cdiv(nblocks, nsplit)) * kAttKeys;
-  p.nsplit = static_cast<int32_t>(cdiv(static_cast<int64_t>(nblocks) * kAttKeys, p.split_keys));
-  if (p.nsplit > 1) {
-    const size_t n = static_cast<size_t>(p.nsplit) * rows * Hq;
+  const int64_t G = Hq / Hkv;
+  const int64_t qt_max = cdiv(static_cast<int64_t>(max_rows) * G, kAttRows);
+  const int64_t nb_max = cdiv(max_keys, kAttKeys);
+  const int64_t ns_hi = att_nsplit(1, nb_max, Hkv);
+  const int64_t extra = 1 + cdiv(nb_max, kAttMaxSplitBlocks);
+  p.item_cap = std::min<int64_t>(static_cast<int64_t>(n_req) * ns_hi * Hkv * qt_max,
+                                 static_cast<int64_t>(n_req) * kAttTargetItems +
+                                     Hkv * extra * (cdiv(static_cast<int64_t>(rows) * G, kAttRows) + n_req));
+  p.grid = round_up(static_cast<size_t>(std::min<int64_t>(p.item_cap, kAttMaxGrid)), 8);
+  p.part_cap = ns_hi < 2 ? 0
+                         : std::min<int64_t>(ns_hi * rows, static_cast<int64_t>(n_req) *
+                                                                   cdiv(static_cast<int64_t>(kAttRows) * kAttTargetItems, Hq) +
+                                                               extra * rows);
+  if (p.part_cap > 0) {
+    const size_t n = static_cast<size_t>(p.part_cap) * Hq;
     p.off_ml = round_up(n * D * sizeof(uint16_t), 256);
     p.bytes = round_up(p.off_ml + n * sizeof(float2), 256);
   }
@@ -219,27 +232,24 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
   a.G = Hq / Hkv;
   a.page_size = page_size;
   a.scale_log2 = scale * kLog2e;
-  a.nsplit = plan.nsplit;
-  a.split_keys = plan.split_keys;
+  a.n_req = n_req;
+  a.item_cap = plan.item_cap;
+  a.part_cap = plan.part_cap;
   a.out = reinterpret_cast<uint16_t*>(out);
   a.o_part = reinterpret_cast<uint16_t*>(ws);
   a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
-  a.qtiles = plan.qtiles;
-  const int64_t items = static_cast<int64_t>(n_req) * plan.nsplit * Hkv * plan.qtiles;
-  DG_UNSUP(items <= (int64_t{1} << 30));
-  a.n_items = static_cast<int32_t>(items);
-  const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
+  const dim3 grid(static_cast<unsigned>(plan.grid));
   if (D == 256)
     attend_mfma16_kernel<256, E8><<<grid, kAtt16Threads, 0, s>>>(a);
   else
     attend_mfma16_kernel<128, E8><<<grid, kAtt16Threads, 0, s>>>(a);
   DG_LAUNCHED();
-  if (plan.nsplit > 1) {
+  if (plan.part_cap > 0) {
     const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
     if (D == 256)
-      attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req, a.out);
+      attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a);
     else
-      attend_merge_kernel<128><<<mgrid, 256, 0, s>>>(a.o_part, a.ml_part, plan.nsplit, rows, Hq, splits, n_req, a.out);
+      attend_merge_kernel<128><<<mgrid, 256, 0, s>>>(a);
     DG_LAUNCHED();
   }
   return DG_OK;
@@ -279,8 +289,9 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   DG_UNSUP(page_size == 16);
   DG_UNSUP(D == 32 || D == 64 || D == 128 || D == 256);
   const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
-  // a split's page ids (its keys plus one alignment block) must fit the staged list
-  DG_UNSUP(!plan.mfma || plan.split_keys + kAttKeys <= kAttMaxPages * 16);
+  // a request's splits (at most kMergeSplits, each with its keys plus one alignment block) must fit
+  // the staged page list
+  DG_UNSUP(!plan.mfma || cdiv(max_keys_per_req, kAttKeys) <= static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks);
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
   const bool bf = dtype == DG_BF16;
@@ -342,7 +353,7 @@ extern "C" dg_status dg_canvas_attention_e4m3(const void* q, const void* k, cons
   DG_UNSUP(page_size == 16);
   DG_UNSUP(D == 128 || D == 256);
   const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, DG_BF16);
-  DG_UNSUP(plan.split_keys + kAttKeys <= kAttMaxPages * 16);
+  DG_UNSUP(cdiv(max_keys_per_req, kAttKeys) <= static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks);
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   AttArgs a{};
   a.k_cache8 = k_cache8;

@@ -36,6 +36,14 @@
 // mask.  With several KV splits each split writes its output normalised by its
 // own sum (bf16) with (reference max, sum), and a merge kernel combines them
 // with log-sum-exp weights.
+//
+// Batch invariance: how a request's keys are cut into splits depends on that
+// request's own descriptor only (its rows, cached keys and window), never on
+// the other requests of the launch, so a request's output is bitwise the same
+// alone or in any batch.  Work items are numbered request by request; each
+// workgroup recomputes the per-request item counts of the launch (a wave-wide
+// prefix sum over the descriptors) to find its item, so the grid holds no
+// empty items beyond a rounding to the XCD count.
 #pragma once
 #include "dg_device.hpp"
 
@@ -47,6 +55,29 @@ constexpr int kAttRows = 128;   // packed query rows per workgroup
 constexpr int kAttKeys = 64;    // keys per block
 constexpr int kAttMaxPages = 1024;  // page ids of one split staged in LDS (16K keys)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMergeSplits = 16;     // the most splits of one request
+constexpr int kAttTargetItems = 256;  // work items a request alone is split into at most (one per CU)
+constexpr int kAttMaxSplitBlocks = kAttMaxPages / 4 - 1;  // a split's pages plus one block fit the staged list
+
+// Keys a request's rows see together: the whole request, or at most its rows plus two windows.
+__host__ __device__ inline int64_t att_span(int64_t cached, int64_t nr, int64_t window) {
+  const int64_t n_total = cached + nr;
+  return window > 0 ? (n_total < nr + 2 * window ? n_total : nr + 2 * window) : n_total;
+}
+
+// KV splits of a request with qt row tiles per KV head and nb 64-key blocks (its own shape only):
+// enough splits that the request alone gives about kAttTargetItems work items, at least 4 blocks
+// per split, at most kMergeSplits, and few enough blocks per split for the staged page list.
+__host__ __device__ inline int32_t att_nsplit(int64_t qt, int64_t nb, int32_t Hkv) {
+  int64_t n = nb / 4;
+  const int64_t want = (kAttTargetItems + Hkv * qt - 1) / (Hkv * qt);
+  n = n < want ? n : want;
+  n = n < kMergeSplits ? n : kMergeSplits;
+  const int64_t need = (nb + kAttMaxSplitBlocks - 1) / kAttMaxSplitBlocks;
+  n = n > need ? n : need;
+  n = n < 1 ? 1 : n;
+  return static_cast<int32_t>(n < kMergeSplits ? n : kMergeSplits);
+}
 
 struct AttArgs {
   const uint16_t* q;
@@ -60,15 +91,14 @@ struct AttArgs {
   const int32_t* page_table;
   int32_t page_table_len;
   const dg_split* splits;
-  int32_t rows, Hq, Hkv, G, page_size;
+  int32_t n_req, rows, Hq, Hkv, G, page_size;
   float scale_log2;     // scale * log2(e)
-  int32_t nsplit;       // KV splits
-  int32_t split_keys;   // keys per split (multiple of kAttKeys)
-  int32_t qtiles;       // row tiles of kAttRows packed rows per request
-  int32_t n_items;      // n_req * nsplit * Hkv * qtiles work items
-  uint16_t* out;        // [rows][Hq][D] bf16 (nsplit == 1)
-  uint16_t* o_part;     // [nsplit][rows][Hq][D] bf16, each split's output normalised by its own l (nsplit > 1)
-  float2* ml_part;      // [nsplit][rows][Hq] (reference max in log2 units, l)  (nsplit > 1)
+  int64_t item_cap;     // work items the grid holds (the host bound)
+  int64_t part_cap;     // split rows the workspace holds
+  uint16_t* out;        // [rows][Hq][D] bf16 (requests with one split write here directly)
+  uint16_t* o_part;     // [split rows][Hq][D] bf16: split s of a split request, its row j at part_off + s nr + j,
+                        // the split's output normalised by its own l
+  float2* ml_part;      // [split rows][Hq] (reference max in log2 units, l)
   // E4M3 cache (attend_mfma16_kernel<D, true>): codes in place of k_cache / v_cache, values scale * code
   const uint8_t* k_cache8;
   const uint8_t* v_cache8;
@@ -118,6 +148,103 @@ DG_DEV int2 att_row_keys(const dg_split& sp, int j) {
     if (!causal) hi = min(hi, p + w + 1);
   }
   return make_int2(lo, hi);
+}
+
+// ---------------------------------------------------------------- per-request plan and work items
+// A request's plan from its own descriptor: rows nr (clamped to the launch), row tiles qt of
+// kAttRows packed rows per KV head, splits ns and keys per split sk (a multiple of kAttKeys).  A
+// request without rows, or whose key span is beyond what kMergeSplits staged splits hold, has no
+// work (ns = 0): a bad descriptor yields a wrong result, never an out-of-range access.
+struct AttReqPlan {
+  int32_t nr, qt, ns, sk;
+};
+
+DG_DEV AttReqPlan att_req_plan(const AttArgs& a, const dg_split& sp) {
+  AttReqPlan p{0, 0, 0, kAttKeys};
+  int64_t nr = static_cast<int64_t>(max(sp.n_causal, 0)) + max(sp.n_canvas, 0);
+  nr = nr < a.rows ? nr : a.rows;
+  const int64_t nb = (att_span(max(sp.cached, 0), nr, sp.window) + kAttKeys - 1) / kAttKeys;
+  if (nr == 0 || nb > static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks) return p;
+  p.nr = static_cast<int32_t>(nr);
+  p.qt = static_cast<int32_t>((nr * a.G + kAttRows - 1) / kAttRows);
+  const int32_t ns = att_nsplit(p.qt, nb, a.Hkv);
+  p.sk = static_cast<int32_t>((nb + ns - 1) / ns) * kAttKeys;
+  p.ns = static_cast<int32_t>((nb * kAttKeys + p.sk - 1) / p.sk);
+  return p;
+}
+
+DG_DEV int64_t wave_incl_scan(int64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Work items of request r: its splits x KV heads x row tiles, item (s Hkv + hk) qt + qtile; split
+// rows (partials) of a split request: ns nr.  Both numbered request by request.
+DG_DEV void att_req_counts(const AttArgs& a, int r, AttReqPlan& p, int64_t& items, int64_t& part) {
+  items = part = 0;
+  p = AttReqPlan{0, 0, 0, kAttKeys};
+  if (r < a.n_req) {
+    p = att_req_plan(a, a.splits[r]);
+    items = static_cast<int64_t>(p.ns) * a.Hkv * p.qt;
+    part = p.ns > 1 ? static_cast<int64_t>(p.ns) * p.nr : 0;
+  }
+}
+
+// Launch totals (every lane of the calling wave gets them); false when they exceed what the
+// grid or the workspace holds (descriptors inconsistent with the host bounds: nothing is done).
+DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t ni = 0, np = 0;
+  for (int r0 = 0; r0 < a.n_req; r0 += kWave) {
+    AttReqPlan p;
+    int64_t items, part;
+    att_req_counts(a, r0 + lane, p, items, part);
+    ni += __shfl(wave_incl_scan(items), kWave - 1, kWave);
+    np += __shfl(wave_incl_scan(part), kWave - 1, kWave);
+  }
+  n_items = ni;
+  return ni <= a.item_cap && np <= a.part_cap;
+}
+
+struct AttItem {
+  int32_t req, split, hk, qtile;
+  AttReqPlan p;
+  int64_t part_off;  // first split row of the request (split requests)
+};
+
+// Item t (< the launch's item total) -> its request, split, KV head and row tile.
+DG_DEV AttItem att_find(const AttArgs& a, int64_t t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  AttItem it{0, 0, 0, 0, AttReqPlan{0, 0, 0, kAttKeys}, 0};
+  int64_t base_i = 0, base_p = 0;
+  for (int r0 = 0; r0 < a.n_req; r0 += kWave) {
+    AttReqPlan p;
+    int64_t items, part;
+    att_req_counts(a, r0 + lane, p, items, part);
+    const int64_t inc_i = wave_incl_scan(items), inc_p = wave_incl_scan(part);
+    const int64_t first = base_i + inc_i - items;
+    const uint64_t own = __ballot(items > 0 && t >= first && t < first + items);
+    if (own) {
+      const int src = __ffsll(static_cast<unsigned long long>(own)) - 1;
+      it.req = r0 + src;
+      it.p = AttReqPlan{__shfl(p.nr, src, kWave), __shfl(p.qt, src, kWave), __shfl(p.ns, src, kWave),
+                        __shfl(p.sk, src, kWave)};
+      it.part_off = __shfl(base_p + inc_p - part, src, kWave);
+      const int64_t local = t - __shfl(first, src, kWave);
+      it.qtile = static_cast<int32_t>(local % it.p.qt);
+      it.hk = static_cast<int32_t>((local / it.p.qt) % a.Hkv);
+      it.split = static_cast<int32_t>(local / (static_cast<int64_t>(it.p.qt) * a.Hkv));
+      return it;
+    }
+    base_i += __shfl(inc_i, kWave - 1, kWave);
+    base_p += __shfl(inc_p, kWave - 1, kWave);
+  }
+  return it;
 }
 
 // Key kk (kb <= kk < kb + 64) of a request: prefix positions (kk < cached) live in the page of
@@ -349,35 +476,27 @@ DG_DEV bf16x8 att_vfrag16(const uint16_t* Vb, int dt, int ch) {
   return v;
 }
 
+// One work item: row tile `qtile` of request it.req, KV head it.hk, key split it.split.
 template <int D, bool E8>
-__global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
+DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it) {
   constexpr int NT = kAtt16Threads;
   constexpr int kDSteps = D / 32;                // MFMA k-steps over D
   constexpr int kDTiles = D / 16;                // 16-wide output tiles over D
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
-  __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
 
-  // XCD-aware order: the hardware deals workgroup L to XCD L % 8; work item t = (L % 8) * per_xcd +
-  // L / 8, t = ((req * nsplit + split) * Hkv + hk) * qtiles + qtile, so the row tiles that read the
-  // same K/V (same request, KV head and split) run on one XCD and share its L2.  The tile sees keys
-  // [lo of its first row, hi of its last row) (both edges grow with the row); the splits cut that
-  // range from its first 64-aligned block, the last split also taking the one block the alignment
-  // can add beyond nsplit * split_keys.
-  const int per_xcd = (a.n_items + 7) / 8;
-  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (t >= a.n_items) return;
-  const int qtile = t % a.qtiles;
-  const int hk = (t / a.qtiles) % a.Hkv;
-  const int split = (t / (a.qtiles * a.Hkv)) % a.nsplit;
-  const dg_split sp = a.splits[t / (a.qtiles * a.Hkv * a.nsplit)];
-  const int nr = sp.n_causal + sp.n_canvas;
+  // The tile sees keys [lo of its first row, hi of its last row) (both edges grow with the row); the
+  // splits cut that range from its first 64-aligned block, the last split also taking the one block
+  // the alignment can add beyond ns * sk.
+  const int qtile = it.qtile, hk = it.hk, split = it.split;
+  const dg_split sp = a.splits[it.req];
+  const int nr = it.p.nr;
+  const bool split_req = it.p.ns > 1;
   const int m_tile0 = qtile * kAttRows;
-  if (m_tile0 >= nr * a.G) return;
   const int j_last = min(nr - 1, (m_tile0 + kAttRows - 1) / a.G);
   const int tile_lo = att_row_keys(sp, m_tile0 / a.G).x & ~(kAttKeys - 1);
   const int tile_hi = att_row_keys(sp, j_last).y;
-  const int k_begin = tile_lo + split * a.split_keys;
-  const int k_end = min(tile_hi, k_begin + a.split_keys + (split == a.nsplit - 1 ? kAttKeys : 0));
+  const int k_begin = tile_lo + split * it.p.sk;
+  const int k_end = min(tile_hi, k_begin + it.p.sk + (split == it.p.ns - 1 ? kAttKeys : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -538,79 +657,118 @@ __global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a)
     }
   }
 
-  if (!row_ok || !row_in) return;
-  // O^T tile dt: this lane holds d = 16 dt + 4 g + e (e = 0 .. 3) of its row
-  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-  const int64_t ridx = static_cast<int64_t>(a.nsplit == 1 ? 0 : split) * a.rows * a.Hq +
-                       static_cast<int64_t>(row) * a.Hq + h;
-  uint16_t* orow = (a.nsplit == 1 ? a.out : a.o_part) + ridx * D;
+  if (row_ok && row_in) {
+    // O^T tile dt: this lane holds d = 16 dt + 4 g + e (e = 0 .. 3) of its row
+    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+    const int64_t ridx = split_req ? (it.part_off + static_cast<int64_t>(split) * nr + j) * a.Hq + h
+                                   : static_cast<int64_t>(row) * a.Hq + h;
+    uint16_t* orow = (split_req ? a.o_part : a.out) + ridx * D;
 #pragma unroll
-  for (int dt = 0; dt < kDTiles; ++dt) {
-    uint2 w;
-    w.x = static_cast<uint32_t>(f32_to_bf16(o[dt][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][1] * inv)) << 16);
-    w.y = static_cast<uint32_t>(f32_to_bf16(o[dt][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      uint2 w;
+      w.x = static_cast<uint32_t>(f32_to_bf16(o[dt][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][1] * inv)) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16(o[dt][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+    }
+    if (split_req && g == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
   }
-  if (a.nsplit > 1 && g == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
 }
 
-// Combine KV splits: out = sum_s c_s Ohat_s / sum_s c_s with c_s = 2^(m_s - M) l_s, M = max_s m_s and
-// Ohat_s = O_s / l_s the split's normalised output (so sum_s c_s Ohat_s = sum_s 2^(m_s - M) O_s).  Grid
-// (packed row, 1024-value slice of the row's Hq x D outputs); four consecutive d per thread, every
-// split's loads issued before the sums.  Rows outside every request's range were never written and
-// are skipped.
-constexpr int kMergeSplits = 16;  // the most splits a launch uses
+// XCD-aware order: the hardware deals workgroup b to XCD b % 8.  The launch's items are cut into 8
+// contiguous ranges, one per XCD, and the workgroups of XCD x walk range x with a stride, so the row
+// tiles that read the same K/V (same request, split and KV head, consecutive items) run on one XCD
+// and share its L2.  Each workgroup first recomputes the launch totals from the descriptors.
+template <int D, bool E8>
+__global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
+  __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
+  int64_t n_items;
+  if (!att_totals(a, n_items)) return;
+  const int64_t per_xcd = (n_items + 7) / 8;
+  const int64_t lo = (blockIdx.x % 8) * per_xcd;
+  const int64_t hi = min(n_items, lo + per_xcd);
+  const int64_t stride = gridDim.x / 8;  // the grid is a multiple of 8
+  for (int64_t t = lo + blockIdx.x / 8; t < hi; t += stride) {
+    const AttItem it = att_find(a, t);
+    if (it.p.ns == 0) break;  // not reached for t below the total
+    att_run_item<D, E8>(a, sm, it);
+    __syncthreads();          // the next item overwrites the LDS blocks and page list
+  }
+}
 
+// Combine the KV splits of a split request: out = sum_s c_s Ohat_s / sum_s c_s with
+// c_s = 2^(m_s - M) l_s, M = max_s m_s and Ohat_s = O_s / l_s the split's normalised output (so
+// sum_s c_s Ohat_s = sum_s 2^(m_s - M) O_s).  Grid (packed row, 1024-value slice of the row's Hq x D
+// outputs); the workgroup finds the request owning its row and that request's first split row from
+// the same per-request counts as the attention kernel (a block-wide prefix over the descriptors);
+// rows of one-split requests (written by the attention kernel) and rows of no request are skipped.
+// Four consecutive d per thread, every split's loads issued before the sums.
 template <int D>
-__global__ __launch_bounds__(256) void attend_merge_kernel(const uint16_t* __restrict__ o_part,
-                                                           const float2* __restrict__ ml_part, int32_t nsplit,
-                                                           int32_t rows, int32_t Hq,
-                                                           const dg_split* __restrict__ splits, int32_t n_req,
-                                                           uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttArgs a) {
   const int row = blockIdx.x;
-  int owned = 0;
-  for (int r = threadIdx.x; r < n_req; r += 256) {
-    const dg_split sp = splits[r];
-    owned |= (row >= sp.row0 && row < sp.row0 + sp.n_causal + sp.n_canvas) ? 1 : 0;
-  }
-  if (!__syncthreads_or(owned)) return;
-  const int64_t plane = static_cast<int64_t>(rows) * Hq;  // (row, head) pairs per split
-  const int e = blockIdx.y * 1024 + 4 * threadIdx.x;
-  if (e < Hq * D) {
-    const int h = e / D, d = e - h * D;
-    const int64_t rh = static_cast<int64_t>(row) * Hq + h;
-    float2 ml[kMergeSplits];
-    uint2 ov[kMergeSplits];
-#pragma unroll
-    for (int s = 0; s < kMergeSplits; ++s) {
-      if (s < nsplit) {
-        ml[s] = ml_part[s * plane + rh];
-        ov[s] = *reinterpret_cast<const uint2*>(o_part + (s * plane + rh) * D + d);
-      }
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  __shared__ int64_t s_wave[4];
+  __shared__ int64_t s_off;
+  __shared__ int32_t s_ns, s_nr, s_row0;
+  if (tid == 0) s_ns = 0;
+  int64_t base = 0;
+  for (int r0 = 0; r0 < a.n_req; r0 += 256) {
+    AttReqPlan p;
+    int64_t items, part;
+    att_req_counts(a, r0 + tid, p, items, part);
+    const int32_t row0 = r0 + tid < a.n_req ? a.splits[r0 + tid].row0 : 0;
+    const int64_t inc = wave_incl_scan(part);
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    int64_t before = base;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    if (part > 0 && row >= row0 && row < row0 + p.nr) {
+      s_off = before + inc - part;
+      s_ns = p.ns;
+      s_nr = p.nr;
+      s_row0 = row0;
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMergeSplits; ++s)
-      if (s < nsplit) M = fmaxf(M, ml[s].x);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int s = 0; s < kMergeSplits; ++s) {
-      if (s < nsplit && ml[s].x != -INFINITY) {
-        const float c = exp2f(ml[s].x - M) * ml[s].y;
-        L += c;
-        acc.x = fmaf(c, bf16_lo(ov[s].x), acc.x);
-        acc.y = fmaf(c, bf16_hi(ov[s].x), acc.y);
-        acc.z = fmaf(c, bf16_lo(ov[s].y), acc.z);
-        acc.w = fmaf(c, bf16_hi(ov[s].y), acc.w);
-      }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint2 wv;
-    wv.x = static_cast<uint32_t>(f32_to_bf16(acc.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
-    wv.y = static_cast<uint32_t>(f32_to_bf16(acc.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
-    *reinterpret_cast<uint2*>(out + rh * D + d) = wv;
+    base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
   }
+  __syncthreads();
+  const int32_t ns = s_ns;
+  if (ns < 2 || base > a.part_cap) return;
+  const int64_t e = static_cast<int64_t>(blockIdx.y) * 1024 + 4 * tid;
+  if (e >= static_cast<int64_t>(a.Hq) * D) return;
+  const int h = static_cast<int>(e / D), d = static_cast<int>(e - static_cast<int64_t>(h) * D);
+  const int64_t first = s_off + (row - s_row0);  // split row of split 0
+  float2 ml[kMergeSplits];
+  uint2 ov[kMergeSplits];
+#pragma unroll
+  for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
+    if (sidx < ns) {
+      const int64_t ridx = (first + static_cast<int64_t>(sidx) * s_nr) * a.Hq + h;
+      ml[sidx] = a.ml_part[ridx];
+      ov[sidx] = *reinterpret_cast<const uint2*>(a.o_part + ridx * D + d);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sidx = 0; sidx < kMergeSplits; ++sidx)
+    if (sidx < ns) M = fmaxf(M, ml[sidx].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
+    if (sidx < ns && ml[sidx].x != -INFINITY) {
+      const float c = exp2f(ml[sidx].x - M) * ml[sidx].y;
+      L += c;
+      acc.x = fmaf(c, bf16_lo(ov[sidx].x), acc.x);
+      acc.y = fmaf(c, bf16_hi(ov[sidx].x), acc.y);
+      acc.z = fmaf(c, bf16_lo(ov[sidx].y), acc.z);
+      acc.w = fmaf(c, bf16_hi(ov[sidx].y), acc.w);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint2 wv;
+  wv.x = static_cast<uint32_t>(f32_to_bf16(acc.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+  wv.y = static_cast<uint32_t>(f32_to_bf16(acc.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+  if (row < a.rows) *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(row) * a.Hq + h) * D + d) = wv;
 }
 
 }  // namespace dg

@@ -407,16 +407,17 @@ struct SamplePlan {
   int32_t nsplit, iters;
 };
 
-// About 1024 workgroups per launch (4 per CU); a workgroup runs `iters` iterations of 16384
-// logits (measured on the 256 x 262144 step: 1024 workgroups of 4 iterations beat 4096 of 1 by
-// 15 %, the per-workgroup reductions being amortised over more logits).
-SamplePlan plan_sample(int32_t rows, int32_t V) {
+// A row is cut into chunks of kChunkIters iterations (65536 logits) whatever the launch holds, so a
+// row's statistics are summed in the same order in every batch it can be part of (batch-invariant
+// per request); only the number of workgroups grows with the rows.  Four iterations per workgroup:
+// on the 256 x 262144 step, 1024 workgroups of 4 iterations beat 4096 of 1 by 15 % (the
+// per-workgroup reductions are amortised over more logits).
+constexpr int32_t kChunkIters = 4;
+
+SamplePlan plan_sample(int32_t V) {
   const int32_t row_iters = static_cast<int32_t>(cdiv(V, kIterElems));
-  int32_t nsplit = static_cast<int32_t>(cdiv(1024, rows));
-  nsplit = max(1, min(nsplit, row_iters));
-  const int32_t iters = static_cast<int32_t>(cdiv(row_iters, nsplit));
-  nsplit = static_cast<int32_t>(cdiv(row_iters, iters));
-  return {nsplit, iters};
+  const int32_t iters = min(row_iters, kChunkIters);
+  return {static_cast<int32_t>(cdiv(row_iters, iters)), iters};
 }
 
 // Shared by dg_denoise_sample and dg_denoise_sample_sc (so.w != nullptr: also writes the operand).
@@ -437,7 +438,7 @@ dg_status denoise_sample_impl(const void* logits, int64_t ld, int32_t dtype, int
   }
   const size_t need = dg_denoise_sample_ws_bytes(rows, V);
   DG_REQUIRE(ws != nullptr && ws_bytes >= need, DG_E_WORKSPACE);
-  const SamplePlan p = plan_sample(rows, V);
+  const SamplePlan p = plan_sample(V);
   hipStream_t s = as_stream(stream);
   Partial* part = reinterpret_cast<Partial*>(ws);
   const dim3 grid(p.nsplit, rows);
@@ -476,7 +477,7 @@ using namespace dg;
 
 extern "C" size_t dg_denoise_sample_ws_bytes(int32_t rows, int32_t V) {
   if (rows <= 0 || V <= 0) return 0;
-  const SamplePlan p = plan_sample(rows, V);
+  const SamplePlan p = plan_sample(V);
   return static_cast<size_t>(rows) * p.nsplit * sizeof(Partial);
 }
 

@@ -105,7 +105,11 @@ def test_converged_lockstep_histories(C):
             if not active[b]:
                 continue
             if ref.mean_gap[b] < P.MEAN_TIE and got["committed"][b] != ref.committed[b]:
-                pytest.skip("mean-entropy near-tie")
+                # a mean entropy within 1e-3 of tau: counted; the oracle continues from the GPU's state
+                P.report_tie("mean_entropy")
+                for f in ("canvas", "prev_argmax", "unchanged", "step_in_block", "step_global", "sc_on"):
+                    getattr(st, f)[b] = got[f][b]
+                continue
             assert got["committed"][b] == ref.committed[b], (t, b)
             assert got["num_sampled"][b] == ref.num_sampled[b], (t, b)
             if ref.committed[b]:

@@ -1,8 +1,8 @@
 """The tiny closed loop on the GPU (through the C ABI) against the oracle loop, free-running.
 
 Trajectories must be identical until the first counted near-tie (argmax or Gumbel-key gap
-< 1e-5, running entropy within 1e-3 of the budget, mean entropy within 1e-3 of tau,
-or two entropies at the acceptance cut within 1e-3); after one, divergence is reported.
+< 1e-5, running entropy within 1e-3 of the budget, mean entropy within 1e-3 of tau, or
+the last accepted and first rejected entropies within 1e-3); after one, divergence is reported.
 """
 import numpy as np
 import pytest
@@ -16,12 +16,23 @@ pytestmark = pytest.mark.gpu
 
 
 def _near_tie(o):
-    if np.any((o["argmax_gap"] > 0) & (o["argmax_gap"] < P.TIE_GAP)) or np.any(o["key_gap"] < P.TIE_GAP):
-        return True
-    if o["budget_gap"] < P.BUDGET_TIE or o["mean_gap"] < P.MEAN_TIE:
-        return True
-    h = np.sort(o["entropy"])
-    return bool(np.any(np.diff(h) < 1e-3) and o["n_accept"] > 0)
+    """The tie class of step o, or None: argmax / Gumbel-key gaps, the running entropy at the
+    budget, the mean entropy at tau, or the two entropies at the acceptance cut (the last accepted
+    and the first rejected position in (entropy, position) order) within 1e-3."""
+    if np.any((o["argmax_gap"] > 0) & (o["argmax_gap"] < P.TIE_GAP)):
+        return "argmax_gap"
+    if np.any(o["key_gap"] < P.TIE_GAP):
+        return "gumbel_key_gap"
+    if o["budget_gap"] < P.BUDGET_TIE:
+        return "budget"
+    if o["mean_gap"] < P.MEAN_TIE:
+        return "mean_entropy"
+    h = np.asarray(o["entropy"])
+    order = np.lexsort((np.arange(h.size), h))
+    n = o["n_accept"]
+    if 0 < n < h.size and h[order[n]] - h[order[n - 1]] < 1e-3:
+        return "accept_cut"
+    return None
 
 
 @pytest.mark.parametrize("scale", [4.0, 8.0, 32.0])
@@ -39,7 +50,8 @@ def test_tiny_loop_free_run(scale):
                 and g["n_accept"] == o["n_accept"] and np.array_equal(g["canvas"], o["canvas"])
                 and g["committed"] == o["committed"])
         if not same:
-            assert tie, f"trajectories diverge at step {t} without a near-tie"
+            assert tie is not None, f"trajectories diverge at step {t} without a near-tie"
+            P.report_tie(tie)
             P.report_tie("tiny_loop_divergence")
             return
         assert P.rel_norm_err(g["x_next"], o["x_next"]).max() < 1e-4, t
