@@ -183,6 +183,7 @@ constexpr int64_t kAttMaxGrid = 4096;
 struct AttPlan {
   bool mfma;
   int64_t item_cap, part_cap, grid;
+  bool fits;  // items are numbered in 32 bits inside a request
   size_t off_ml, bytes;
 };
 
@@ -194,12 +195,13 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   const int64_t G = Hq / Hkv;
   const int64_t qt_max = cdiv(static_cast<int64_t>(max_rows) * G, kAttRows);
   const int64_t nb_max = cdiv(max_keys, kAttKeys);
-  const int64_t ns_hi = att_nsplit(1, nb_max, Hkv);
+  const int64_t ns_hi = att_nsplit<int64_t>(1, nb_max, Hkv);
   const int64_t extra = 1 + cdiv(nb_max, kAttMaxSplitBlocks);
   p.item_cap = std::min<int64_t>(static_cast<int64_t>(n_req) * ns_hi * Hkv * qt_max,
                                  static_cast<int64_t>(n_req) * kAttTargetItems +
                                      Hkv * extra * (cdiv(static_cast<int64_t>(rows) * G, kAttRows) + n_req));
   p.grid = round_up(static_cast<size_t>(std::min<int64_t>(p.item_cap, kAttMaxGrid)), 8);
+  p.fits = p.item_cap < (int64_t{1} << 31);
   p.part_cap = ns_hi < 2 ? 0
                          : std::min<int64_t>(ns_hi * rows, static_cast<int64_t>(n_req) *
                                                                    cdiv(static_cast<int64_t>(kAttRows) * kAttTargetItems, Hq) +
@@ -291,7 +293,8 @@ extern "C" dg_status dg_canvas_attention(const void* q, const void* k, const voi
   const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, dtype);
   // a request's splits (at most kMergeSplits, each with its keys plus one alignment block) must fit
   // the staged page list
-  DG_UNSUP(!plan.mfma || cdiv(max_keys_per_req, kAttKeys) <= static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks);
+  DG_UNSUP(!plan.mfma || (plan.fits && cdiv(max_keys_per_req, kAttKeys) <=
+                                             static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks));
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   hipStream_t s = as_stream(stream);
   const bool bf = dtype == DG_BF16;
@@ -353,7 +356,7 @@ extern "C" dg_status dg_canvas_attention_e4m3(const void* q, const void* k, cons
   DG_UNSUP(page_size == 16);
   DG_UNSUP(D == 128 || D == 256);
   const AttPlan plan = plan_attention(n_req, rows, max_rows_per_req, max_keys_per_req, Hq, Hkv, D, DG_BF16);
-  DG_UNSUP(cdiv(max_keys_per_req, kAttKeys) <= static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks);
+  DG_UNSUP(plan.fits && cdiv(max_keys_per_req, kAttKeys) <= static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks);
   DG_REQUIRE(plan.bytes == 0 || (ws != nullptr && ws_bytes >= plan.bytes), DG_E_WORKSPACE);
   AttArgs a{};
   a.k_cache8 = k_cache8;

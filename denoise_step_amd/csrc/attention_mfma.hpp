@@ -68,15 +68,19 @@ __host__ __device__ inline int64_t att_span(int64_t cached, int64_t nr, int64_t 
 // KV splits of a request with qt row tiles per KV head and nb 64-key blocks (its own shape only):
 // enough splits that the request alone gives about kAttTargetItems work items, at least 4 blocks
 // per split, at most kMergeSplits, and few enough blocks per split for the staged page list.
-__host__ __device__ inline int32_t att_nsplit(int64_t qt, int64_t nb, int32_t Hkv) {
-  int64_t n = nb / 4;
-  const int64_t want = (kAttTargetItems + Hkv * qt - 1) / (Hkv * qt);
+template <typename I>
+__host__ __device__ inline I att_nsplit(I qt, I nb, I Hkv) {
+  // ceil(kAttTargetItems / (Hkv qt)), without forming a product that could overflow
+  const I want = (qt >= kAttTargetItems || Hkv >= kAttTargetItems || Hkv * qt >= kAttTargetItems)
+                     ? I(1)
+                     : (kAttTargetItems + Hkv * qt - 1) / (Hkv * qt);
+  I n = nb / 4;
   n = n < want ? n : want;
-  n = n < kMergeSplits ? n : kMergeSplits;
-  const int64_t need = (nb + kAttMaxSplitBlocks - 1) / kAttMaxSplitBlocks;
+  n = n < kMergeSplits ? n : I(kMergeSplits);
+  const I need = (nb + kAttMaxSplitBlocks - 1) / kAttMaxSplitBlocks;
   n = n > need ? n : need;
-  n = n < 1 ? 1 : n;
-  return static_cast<int32_t>(n < kMergeSplits ? n : kMergeSplits);
+  n = n < 1 ? I(1) : n;
+  return n < kMergeSplits ? n : I(kMergeSplits);
 }
 
 struct AttArgs {
@@ -161,15 +165,17 @@ struct AttReqPlan {
 
 DG_DEV AttReqPlan att_req_plan(const AttArgs& a, const dg_split& sp) {
   AttReqPlan p{0, 0, 0, kAttKeys};
-  int64_t nr = static_cast<int64_t>(max(sp.n_causal, 0)) + max(sp.n_canvas, 0);
-  nr = nr < a.rows ? nr : a.rows;
-  const int64_t nb = (att_span(max(sp.cached, 0), nr, sp.window) + kAttKeys - 1) / kAttKeys;
-  if (nr == 0 || nb > static_cast<int64_t>(kMergeSplits) * kAttMaxSplitBlocks) return p;
-  p.nr = static_cast<int32_t>(nr);
-  p.qt = static_cast<int32_t>((nr * a.G + kAttRows - 1) / kAttRows);
-  const int32_t ns = att_nsplit(p.qt, nb, a.Hkv);
-  p.sk = static_cast<int32_t>((nb + ns - 1) / ns) * kAttKeys;
-  p.ns = static_cast<int32_t>((nb * kAttKeys + p.sk - 1) / p.sk);
+  const int32_t nr = min(static_cast<int32_t>(min(static_cast<int64_t>(max(sp.n_causal, 0)) + max(sp.n_canvas, 0),
+                                                  static_cast<int64_t>(a.rows))), a.rows);
+  const int64_t nb64 = (att_span(max(sp.cached, 0), nr, sp.window) + kAttKeys - 1) / kAttKeys;
+  const int64_t qt64 = (static_cast<int64_t>(nr) * a.G + kAttRows - 1) / kAttRows;
+  if (nr == 0 || nb64 > kMergeSplits * kAttMaxSplitBlocks || qt64 > (1 << 24)) return p;
+  const int32_t nb = static_cast<int32_t>(nb64);
+  p.nr = nr;
+  p.qt = static_cast<int32_t>(qt64);
+  const int32_t ns = att_nsplit<int32_t>(p.qt, nb, a.Hkv);
+  p.sk = (nb + ns - 1) / ns * kAttKeys;
+  p.ns = (nb * kAttKeys + p.sk - 1) / p.sk;
   return p;
 }
 
@@ -195,8 +201,14 @@ DG_DEV void att_req_counts(const AttArgs& a, int r, AttReqPlan& p, int64_t& item
   }
 }
 
-// Launch totals (every lane of the calling wave gets them); false when they exceed what the
-// grid or the workspace holds (descriptors inconsistent with the host bounds: nothing is done).
+struct AttItem {
+  int32_t req, split, hk, qtile;
+  AttReqPlan p;
+  int64_t part_off;  // first split row of the request (split requests)
+};
+
+// Launch totals (every lane of the calling wave gets them); false when they exceed what the grid
+// or the workspace holds (descriptors inconsistent with the host bounds: nothing is done).
 DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t ni = 0, np = 0;
@@ -211,11 +223,25 @@ DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items) {
   return ni <= a.item_cap && np <= a.part_cap;
 }
 
-struct AttItem {
-  int32_t req, split, hk, qtile;
-  AttReqPlan p;
-  int64_t part_off;  // first split row of the request (split requests)
-};
+// The request of item t among the 64 requests from r0 (per lane: its request's plan p, items, part
+// and the inclusive scans of items and part), or false when none of them holds it.
+DG_DEV bool att_pick(const AttArgs& a, int64_t t, int r0, const AttReqPlan& p, int64_t items, int64_t part,
+                     int64_t first, int64_t part_first, AttItem& it) {
+  const uint64_t own = __ballot(items > 0 && t >= first && t < first + items);
+  if (!own) return false;
+  const int src = __ffsll(static_cast<unsigned long long>(own)) - 1;
+  it.req = r0 + src;
+  it.p = AttReqPlan{__shfl(p.nr, src, kWave), __shfl(p.qt, src, kWave), __shfl(p.ns, src, kWave),
+                    __shfl(p.sk, src, kWave)};
+  it.part_off = __shfl(part_first, src, kWave);
+  // local < the request's items <= item_cap < 2^31
+  const int32_t local = static_cast<int32_t>(t - __shfl(first, src, kWave));
+  it.qtile = local % it.p.qt;
+  const int32_t rest = local / it.p.qt;
+  it.hk = rest % a.Hkv;
+  it.split = rest / a.Hkv;
+  return true;
+}
 
 // Item t (< the launch's item total) -> its request, split, KV head and row tile.
 DG_DEV AttItem att_find(const AttArgs& a, int64_t t) {
@@ -227,20 +253,7 @@ DG_DEV AttItem att_find(const AttArgs& a, int64_t t) {
     int64_t items, part;
     att_req_counts(a, r0 + lane, p, items, part);
     const int64_t inc_i = wave_incl_scan(items), inc_p = wave_incl_scan(part);
-    const int64_t first = base_i + inc_i - items;
-    const uint64_t own = __ballot(items > 0 && t >= first && t < first + items);
-    if (own) {
-      const int src = __ffsll(static_cast<unsigned long long>(own)) - 1;
-      it.req = r0 + src;
-      it.p = AttReqPlan{__shfl(p.nr, src, kWave), __shfl(p.qt, src, kWave), __shfl(p.ns, src, kWave),
-                        __shfl(p.sk, src, kWave)};
-      it.part_off = __shfl(base_p + inc_p - part, src, kWave);
-      const int64_t local = t - __shfl(first, src, kWave);
-      it.qtile = static_cast<int32_t>(local % it.p.qt);
-      it.hk = static_cast<int32_t>((local / it.p.qt) % a.Hkv);
-      it.split = static_cast<int32_t>(local / (static_cast<int64_t>(it.p.qt) * a.Hkv));
-      return it;
-    }
+    if (att_pick(a, t, r0, p, items, part, base_i + inc_i - items, base_p + inc_p - part, it)) return it;
     base_i += __shfl(inc_i, kWave - 1, kWave);
     base_p += __shfl(inc_p, kWave - 1, kWave);
   }
@@ -681,17 +694,35 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
 template <int D, bool E8>
 __global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
   __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
+  // requests 0 .. 63: their plans and prefix sums stay in registers (one pass for launches of up to
+  // 64 requests; larger launches rescan the descriptors per item)
+  const int lane = threadIdx.x & (kWave - 1);
+  AttReqPlan p0;
+  int64_t items0, part0;
+  att_req_counts(a, lane, p0, items0, part0);
+  const int64_t inc_i0 = wave_incl_scan(items0), inc_p0 = wave_incl_scan(part0);
+  const bool one_pass = a.n_req <= kWave;
   int64_t n_items;
-  if (!att_totals(a, n_items)) return;
+  if (one_pass) {
+    n_items = __shfl(inc_i0, kWave - 1, kWave);
+    if (n_items > a.item_cap || __shfl(inc_p0, kWave - 1, kWave) > a.part_cap) return;
+  } else if (!att_totals(a, n_items)) {
+    return;
+  }
   const int64_t per_xcd = (n_items + 7) / 8;
   const int64_t lo = (blockIdx.x % 8) * per_xcd;
   const int64_t hi = min(n_items, lo + per_xcd);
   const int64_t stride = gridDim.x / 8;  // the grid is a multiple of 8
   for (int64_t t = lo + blockIdx.x / 8; t < hi; t += stride) {
-    const AttItem it = att_find(a, t);
-    if (it.p.ns == 0) break;  // not reached for t below the total
+    AttItem it{0, 0, 0, 0, AttReqPlan{0, 0, 0, kAttKeys}, 0};
+    if (one_pass) {
+      if (!att_pick(a, t, 0, p0, items0, part0, inc_i0 - items0, inc_p0 - part0, it)) break;
+    } else {
+      it = att_find(a, t);
+      if (it.p.ns == 0) break;  // not reached for t below the total
+    }
     att_run_item<D, E8>(a, sm, it);
-    __syncthreads();          // the next item overwrites the LDS blocks and page list
+    __syncthreads();  // the next item overwrites the LDS blocks and page list
   }
 }
 
