@@ -22,7 +22,8 @@ __all__ = [
     "dg_allowed_probs", "dg_verify_prefix", "dg_linear", "dg_gather_rows", "EXPORTED",
     "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
     "dg_deficit_admit", "dg_e4m3_decode", "dg_selfcond_prepared_bytes_e4m3", "dg_selfcond_prepare_e4m3",
-    "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3",
+    "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3", "dg_denoise_sample_noalloc",
+    "dg_denoise_sample_noalloc_max_bytes",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -47,6 +48,9 @@ _SIGS = {
     "dg_denoise_sample_ws_bytes": (_sz, [_i32, _i32]),
     "dg_denoise_sample": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _u32, _p, _p, _p, _p, _p, _p,
                                  _sz, _p]),
+    "dg_denoise_sample_noalloc_max_bytes": (_sz, []),
+    "dg_denoise_sample_noalloc": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _u32, _p, _p, _p, _p, _p,
+                                         _p]),
     "dg_entropy_accept": (_i32, [_p, _p, _i32, _i32, _i32, _f64, _p, _p, _p, _p, _p, _p, _p]),
     "dg_converged": (_i32, [_p, _p, _i32, _i32, _i32, _i32, _f64, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                             _p, _p]),
@@ -221,6 +225,25 @@ def dg_denoise_sample(logits, V, rows_per_req, seed, step, temperature=1.0, acti
                                    DG_SAMPLE_ARGMAX_ONLY if argmax_only else 0, _ptr(g("entropy")),
                                    _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")), _ptr(g("row_lnz")),
                                    _ptr(ws), nb, _stream(stream)), "dg_denoise_sample")
+    return out
+
+
+def dg_denoise_sample_noalloc_max_bytes() -> int:
+    return int(lib().dg_denoise_sample_noalloc_max_bytes())
+
+
+def dg_denoise_sample_noalloc(logits, V, rows_per_req, seed, step, out, temperature=1.0, active=None,
+                              argmax_only=False, stream=None):
+    """dg_denoise_sample without a workspace (the library's fixed per-device scratch); `out` holds the
+    caller's preallocated output tensors (argmax, and entropy / sample / row_max / row_lnz unless
+    argmax_only), so the call allocates nothing."""
+    rows, ld = logits.shape
+    g = out.get
+    _check(lib().dg_denoise_sample_noalloc(_ptr(logits), ld, _dtype_code(logits), rows, V, rows_per_req, _ptr(seed),
+                                           _ptr(step), _ptr(active), float(temperature),
+                                           DG_SAMPLE_ARGMAX_ONLY if argmax_only else 0, _ptr(g("entropy")),
+                                           _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")),
+                                           _ptr(g("row_lnz")), _stream(stream)), "dg_denoise_sample_noalloc")
     return out
 
 

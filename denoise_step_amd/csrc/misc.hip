@@ -126,6 +126,7 @@ extern "C" const char* dg_status_str(dg_status s) {
     case DG_E_UNSUPPORTED: return "unsupported dtype, size or alignment";
     case DG_E_WORKSPACE: return "workspace missing or too small";
     case DG_E_HIP: return "HIP launch error";
+    case DG_E_SCRATCH: return "input larger than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

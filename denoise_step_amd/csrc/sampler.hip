@@ -28,6 +28,8 @@
 // lanes with wave64 shuffles and LDS; a second small kernel merges the chunks
 // of a row (associative, lowest-index tie-breaks at every level) and draws
 // the element inside the winning block.
+#include <mutex>
+
 #include "dg_device.hpp"
 #include "dg_host.hpp"
 
@@ -512,4 +514,43 @@ extern "C" dg_status dg_denoise_sample_sc(const void* logits, int64_t ld, int32_
                  static_cast<int32_t>(cdiv(V, kIterElems)), 0};
   return denoise_sample_impl(logits, ld, dtype, rows, V, rows_per_req, seed, step, active, temperature, 0, entropy,
                              argmax, sample, row_max, row_lnz, ws, ws_bytes, so, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// dg_denoise_sample with its chunk partials in a fixed device array instead of a caller workspace,
+// for callers that cannot allocate.  Each GPU holds its own copy of the array (a static __device__
+// symbol); its address on the current device is looked up once per device with
+// hipGetSymbolAddress and passed to the kernels like a workspace.  The partials are written in
+// full before they are read, so nothing needs clearing between calls.
+namespace dg {
+namespace {
+constexpr size_t kScratchPartials = 262144;  // 8 MiB: rows * chunks per row (V = 262144: 4 chunks, 65536 rows)
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) Partial scratch[kScratchPartials];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+std::once_flag g_scratch_once[kScratchDevices];
+}  // namespace
+}  // namespace dg
+
+extern "C" size_t dg_denoise_sample_noalloc_max_bytes(void) { return sizeof(Partial) * kScratchPartials; }
+
+extern "C" dg_status dg_denoise_sample_noalloc(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                                               int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
+                                               const uint8_t* active, float temperature, uint32_t flags,
+                                               float* entropy, int32_t* argmax, int32_t* sample, float* row_max,
+                                               float* row_lnz, dg_stream_t stream) {
+  DG_ARG(rows > 0 && V > 0);
+  DG_REQUIRE(dg_denoise_sample_ws_bytes(rows, V) <= sizeof(Partial) * kScratchPartials, DG_E_SCRATCH);
+  int dev = -1;
+  DG_REQUIRE(hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kScratchDevices, DG_E_HIP);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  DG_REQUIRE(g_scratch_err[dev] == hipSuccess && g_scratch_ptr[dev] != nullptr, DG_E_HIP);
+  return denoise_sample_impl(logits, ld, dtype, rows, V, rows_per_req, seed, step, active, temperature, flags, entropy,
+                             argmax, sample, row_max, row_lnz, g_scratch_ptr[dev], sizeof(Partial) * kScratchPartials,
+                             ScOut{nullptr, 0, 0, nullptr, 0, 0}, stream);
 }

@@ -26,9 +26,14 @@
  *     buffers (token ids, split descriptors, page ids) are not validated on the
  *     host; page ids and token ids are clamped into range on the device so that a
  *     bad value yields a wrong result, never an out-of-bounds access.
- *   - Results are bitwise deterministic for a given input and launch shape.
+ *   - Results are bitwise deterministic and batch-invariant per request: a
+ *     request's outputs depend on its own inputs only, not on the other
+ *     requests of a launch, the host-side bounds or the physical page ids
+ *     (single-pass-reads page, section on judging the saved launch per request).
  *   - bf16 data is the top 16 bits of an IEEE fp32 (round to nearest even).
- *   - No entry point keeps state between calls; the library is thread-safe.
+ *   - No entry point keeps state between calls and the library is thread-safe,
+ *     except dg_denoise_sample_noalloc, whose per-device scratch array is
+ *     shared by every call on that device.
  */
 #ifndef DG_H
 #define DG_H
@@ -48,7 +53,8 @@ enum {
   DG_E_ARG = -1,          /* null pointer, bad size, inconsistent shapes          */
   DG_E_UNSUPPORTED = -2,  /* dtype / head_dim / page size / alignment not supported */
   DG_E_WORKSPACE = -3,    /* workspace missing or smaller than the *_ws_bytes size  */
-  DG_E_HIP = -4           /* a HIP launch reported an error                          */
+  DG_E_HIP = -4,          /* a HIP launch reported an error                          */
+  DG_E_SCRATCH = -5       /* larger than the fixed scratch of an allocation-free entry point */
 };
 
 enum { DG_F32 = 0, DG_BF16 = 1 };
@@ -181,6 +187,26 @@ dg_status dg_denoise_sample(const void* logits, int64_t ld, int32_t dtype, int32
                             const uint8_t* active, float temperature, uint32_t flags, float* entropy,
                             int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz, void* ws,
                             size_t ws_bytes, dg_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * dg_denoise_sample_noalloc -- dg_denoise_sample for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and results, with its chunk
+ * partials in a fixed device array of dg_denoise_sample_noalloc_max_bytes()
+ * bytes (8 MiB) that each GPU holds until the process ends, instead of a
+ * caller workspace.  Arguments as dg_denoise_sample minus ws / ws_bytes.
+ * Calls whose dg_denoise_sample_ws_bytes(rows, V) exceeds the maximum return
+ * DG_E_SCRATCH and launch nothing (V = 262144: up to 65535 rows).  The call
+ * allocates nothing; every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (concurrent streams or threads) race.  The first
+ * call on a device looks the array's address up (hipGetSymbolAddress).
+ * ------------------------------------------------------------------------ */
+size_t dg_denoise_sample_noalloc_max_bytes(void);
+dg_status dg_denoise_sample_noalloc(const void* logits, int64_t ld, int32_t dtype, int32_t rows, int32_t V,
+                                    int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
+                                    const uint8_t* active, float temperature, uint32_t flags, float* entropy,
+                                    int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz,
+                                    dg_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * dg_denoise_sample_sc

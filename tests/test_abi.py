@@ -101,3 +101,16 @@ def test_e4m3_attention_validates(L):
     assert f(*args(0.3, 128, 1)) == -2
     assert f(*args(0.25, 64, 1)) == -2
     assert f(*args(0.25, 128, 0)) == -1
+
+
+def test_noalloc_sampler_rejects_sizes_beyond_its_scratch(L):
+    """The allocation-free sampler checks its fixed scratch on the host before anything else: a
+    launch needing more chunk partials than the array holds returns DG_E_SCRATCH (-5) and launches
+    nothing (V = 2^20 is 16 chunks of 65536 ids per row; 16385 rows need 262160 > 262144)."""
+    assert L.dg_denoise_sample_noalloc_max_bytes() == 8 << 20
+    assert L.dg_denoise_sample_ws_bytes(16385, 1 << 20) > L.dg_denoise_sample_noalloc_max_bytes()
+    call = lambda rows, V: L.dg_denoise_sample_noalloc(64, V, 1, rows, V, rows, 64, 64, None, 1.0, 0, 64, 64, 64, 64,
+                                                       64, None)
+    assert call(16385, 1 << 20) == -5
+    assert L.dg_status_str(-5).startswith(b"input larger than the fixed scratch")
+    assert call(0, 1 << 20) == -1
