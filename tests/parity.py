@@ -124,3 +124,21 @@ def sampler_oracle_row(row, seed, pos, step):
                            sample=np.array([cand]), row_max=np.array([m]),
                            row_lnz=np.array([np.log(Z)]), argmax_gap=np.array([srt[-1] - srt[-2]]),
                            key_gap=np.array([key_gap]))
+
+
+def oracle_pe_slabs(Pm: np.ndarray, table_rows, V: int, slab: int = 16384) -> np.ndarray:
+    """s = P . E in fp64 by the oracle's prob_embed, summed over slabs of `slab` table rows so that
+    the full 262144 x 4096 table never sits in host memory at once; table_rows(v0, v1) returns the
+    fp64 rows v0 .. v1 - 1 of E."""
+    from oracle import selfcond as _osc
+    s = None
+    for v0 in range(0, V, slab):
+        v1 = min(V, v0 + slab)
+        part = _osc.prob_embed(Pm[:, v0:v1], table_rows(v0, v1))
+        s = part if s is None else s + part
+    return s
+
+
+def torch_table_rows(E):
+    """table_rows for a device bf16 / fp32 table (exact fp64 copies of its rows)."""
+    return lambda v0, v1: E[v0:v1].float().cpu().numpy().astype(np.float64)

@@ -84,11 +84,13 @@ def test_selfcond_f32_tiny_sizes(w_std):
     assert P.rel_norm_err(x.cpu().numpy(), rx).max() <= 1e-5
 
 
-def test_selfcond_single_canvas_full_size_sampled_rows():
-    """256 canvas rows, V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096, in the bench's launch configuration."""
+def test_selfcond_single_canvas_full_size_all_rows():
+    """256 canvas rows, V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096, in the bench's launch
+    configuration: the sampler statistics, s = P.E, the MLP output y and x_next of every row
+    against the oracle (fp64 P.E over slabs of the table)."""
     import denoise_step_amd as dg
     torch = P.torch_mod()
-    print("selfcond full size", flush=True)
+    print("selfcond full size, every row", flush=True)
     V, d, hidden, C = 262144, 4096, 1024, 256
     E = synth.normal_torch(0, "single_canvas.E", (V, d), 1 / 8, torch.bfloat16, "cuda")
     wg = synth.normal_torch(0, "single_canvas.wg", (d, hidden), 0.02, torch.bfloat16, "cuda")
@@ -103,22 +105,20 @@ def test_selfcond_single_canvas_full_size_sampled_rows():
     x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], P.dev(np.array([1], np.uint8)), P.dev(canvas), E,
                              wg, wu, wd, prepared, s_out=s_out, y_out=y_out)
     torch.cuda.synchronize()
-    rows = [0, 77, 128, 255]
-    host_l = lt[rows].float().cpu().numpy().astype(np.float64)
-    Pm = np.stack([osamp.probabilities(host_l[i], 1.0) for i in range(len(rows))])
-    Eh = E.float().cpu().numpy()
-    s_ref = np.zeros((len(rows), d))
-    for v0 in range(0, V, 16384):                      # fp64 P.E in chunks of the table
-        s_ref += Pm[:, v0:v0 + 16384] @ Eh[v0:v0 + 16384].astype(np.float64)
-    es = P.rel_norm_err(s_out.cpu().numpy()[rows], s_ref)
-    assert es.max() <= P.TOL_NORM_REL, es
+    host_l = lt.float().cpu().numpy().astype(np.float64)
+    ref = osamp.denoise_sample(host_l, 1.0, [0], [0], C)
+    P.check_sampler_rows({k: v.cpu().numpy() for k, v in st.items()}, ref, list(range(C)))
+    Pm = osc.probs_from_stats(host_l, 1.0, ref.row_max, ref.row_lnz)
+    s_ref = P.oracle_pe_slabs(Pm, P.torch_table_rows(E), V)
+    es = P.rel_norm_err(s_out.cpu().numpy(), s_ref)
+    assert es.max() <= P.TOL_NORM_REL, es.max()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     y_ref = osc.gated_mlp(s_ref, f(wg), f(wu), f(wd))
-    ey = P.rel_norm_err(y_out.cpu().numpy()[rows], y_ref)
-    print(f"full size: P.E max normwise rel err {es.max():.2e}, MLP {ey.max():.2e}")
-    assert ey.max() <= P.TOL_NORM_REL, ey
-    x_ref = Eh[canvas[0, rows]].astype(np.float64) + y_ref
-    P.check_bf16_output(P.host_f64(x)[rows], x_ref)
+    ey = P.rel_norm_err(y_out.cpu().numpy(), y_ref)
+    print(f"full size, {C} rows: P.E max normwise rel err {es.max():.2e}, MLP {ey.max():.2e}")
+    assert ey.max() <= P.TOL_NORM_REL, ey.max()
+    x_ref = f(E[torch.as_tensor(canvas[0].astype(np.int64), device="cuda")]) + y_ref
+    P.check_bf16_output(P.host_f64(x), x_ref)
 
 
 @pytest.mark.parametrize("V,d,hidden,rows_per_req", [(1000, 128, 128, 16), (40000, 256, 256, 16),
@@ -202,12 +202,17 @@ def test_selfcond_operand_path_single_canvas_full_size():
     ey = P.rel_norm_err(outs[1][1].cpu().numpy(), outs[0][1].cpu().numpy().astype(np.float64))
     print(f"operand vs logits path: s {es.max():.2e}, y {ey.max():.2e}")
     assert es.max() <= P.TOL_NORM_REL and ey.max() <= P.TOL_NORM_REL
-    # sampled rows against the oracle, as in the full-size test of the logits path
-    rows = [0, 77, 255]
-    host_l = lt[rows].float().cpu().numpy().astype(np.float64)
-    Pm = np.stack([osamp.probabilities(host_l[i], 1.0) for i in range(len(rows))])
-    Eh = E.float().cpu().numpy()
-    s_ref = np.zeros((len(rows), d))
-    for v0 in range(0, V, 16384):
-        s_ref += Pm[:, v0:v0 + 16384] @ Eh[v0:v0 + 16384].astype(np.float64)
-    assert P.rel_norm_err(outs[1][0].cpu().numpy()[rows], s_ref).max() <= P.TOL_NORM_REL
+    # every row against the oracle: the sampler outputs, s, y and x_next
+    host_l = lt.float().cpu().numpy().astype(np.float64)
+    ref = osamp.denoise_sample(host_l, 1.0, [0], [0], C)
+    P.check_sampler_rows({k: v.cpu().numpy() for k, v in st_b.items()}, ref, list(range(C)))
+    Pm = osc.probs_from_stats(host_l, 1.0, ref.row_max, ref.row_lnz)
+    s_ref = P.oracle_pe_slabs(Pm, P.torch_table_rows(E), V)
+    es = P.rel_norm_err(outs[1][0].cpu().numpy(), s_ref)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    y_ref = osc.gated_mlp(s_ref, f(wg), f(wu), f(wd))
+    ey = P.rel_norm_err(outs[1][1].cpu().numpy(), y_ref)
+    print(f"operand path, {C} rows against the oracle: s {es.max():.2e}, y {ey.max():.2e}")
+    assert es.max() <= P.TOL_NORM_REL and ey.max() <= P.TOL_NORM_REL
+    x_ref = f(E[canvas[0].long()]) + y_ref
+    P.check_bf16_output(P.host_f64(outs[1][2]), x_ref)
