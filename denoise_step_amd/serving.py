@@ -2,7 +2,8 @@
 
 Each iteration (Sangam page, section on the deficit token-budget scheduler, for the admission;
 DiffusionGemma/vLLM page, sections "Two modes, one set of weights" and "Dynamic per-sequence
-causal attention", for the phases that share one launch):
+causal attention", for the phases that share one launch; section "Self-conditioning" for the
+feedback into the next step):
   * decode work is scheduled first: every request that denoises a canvas (C canvas rows) or runs
     the commit pass of its last block (C causal rows);
   * dg_deficit_admit decides whether the prefill at the head of the arrival queue enters, whole;
@@ -10,8 +11,15 @@ causal attention", for the phases that share one launch):
     commit rows causal with K/V appended to the request's pages, canvas rows bidirectional);
   * the denoising requests run dg_denoise_sample -> dg_entropy_accept -> dg_converged; a request
     admitted this iteration gets its first random canvas from dg_converged's prefill case;
+  * with self-conditioning, the sampling pass also writes the probability operand
+    (dg_denoise_sample_sc) and dg_selfcond_embed_sc turns it into the next step's canvas
+    embedding x_next = E[canvas] + (sc_on ? MLP(softmax . E) : 0), after dg_converged has set the
+    new canvas and sc_on (off for a block that just committed and restarted);
   * a committed block is followed by its commit pass in the next iteration; after `blocks` blocks
     the request leaves.
+A steady-state start (`start`) puts every request in the denoising phase from the first iteration,
+over a prefix already in its pages and at its own step (the batched workload: requests at different
+steps, each block committing at its cap, running its commit pass and restarting).
 Activations and logits come from synthetic pools (no trained backbone): the loop exercises the
 scheduling, the launch composition, the paged cache and the per-request state.  All arithmetic
 runs in libdg; this module keeps the request phases and sequences the calls.
@@ -23,14 +31,22 @@ import math
 import numpy as np
 import torch
 
-from . import dg_canvas_attention, dg_converged, dg_deficit_admit, dg_denoise_sample, dg_entropy_accept
+from . import (dg_canvas_attention, dg_converged, dg_deficit_admit, dg_denoise_sample, dg_denoise_sample_sc,
+               dg_denoise_sample_ws_bytes, dg_entropy_accept, dg_selfcond_embed_sc, dg_selfcond_operand_bytes,
+               dg_selfcond_ws_bytes_sc)
 
 WAITING, PREFILL, DENOISE, COMMIT, DONE = range(5)
 
 
 class ServingLoop:
-    def __init__(self, cfg: dict, sched: dict, tensors: dict, device="cuda", policy: str = "deficit"):
-        """tensors: q/k/v row pools, k_cache/v_cache, logits pools [n_pool, R*C, V] (torch on `device`)."""
+    def __init__(self, cfg: dict, sched: dict, tensors: dict, device="cuda", policy: str = "deficit",
+                 selfcond: dict | None = None, start: dict | None = None):
+        """tensors: q/k/v row pools, k_cache/v_cache, logits pools [n_pool, R*C, V] (torch on `device`).
+        selfcond: dict(E [V, d] bf16, prepared = dg_selfcond_prepare(E, ...), hidden): run the
+        self-conditioning of every denoise iteration (x_next in self.x).
+        start: dict(cached, step_in_block, step_global), one int per request: every request starts
+        denoising over `cached` tokens already in its pages, with a canvas drawn by dg_converged's
+        prefill case at step_global - 1 and then those counters (sc_on = step_in_block > 0)."""
         self.cfg, self.sched, self.policy = cfg, sched, policy
         dev = torch.device(device)
         self.dev = dev
@@ -51,12 +67,39 @@ class ServingLoop:
         self.queue = []
         self.deficit = 0
         self.scale = 1.0 / math.sqrt(cfg["D"])
+        V = cfg["V"]
+        self.so = dict(entropy=torch.empty(R * C, dtype=torch.float32, device=dev), argmax=z(R * C),
+                       sample=z(R * C), row_max=torch.empty(R * C, dtype=torch.float32, device=dev),
+                       row_lnz=torch.empty(R * C, dtype=torch.float32, device=dev))
+        self.ws_s = torch.empty(dg_denoise_sample_ws_bytes(R * C, V), dtype=torch.uint8, device=dev)
+        self.sc = selfcond
+        if selfcond is not None:
+            E = selfcond["E"]
+            # zero-filled once: rows of requests that do not denoise keep finite (earlier) values
+            self.operand = torch.zeros(dg_selfcond_operand_bytes(R * C, V), dtype=torch.uint8, device=dev)
+            self.ws_sc = torch.empty(dg_selfcond_ws_bytes_sc(R * C, V, E.shape[1], selfcond["hidden"]),
+                                     dtype=torch.uint8, device=dev)
+            self.x = torch.zeros((R * C, E.shape[1]), dtype=E.dtype, device=dev)
+        if start is not None:
+            st = self.state
+            st["step_global"].copy_(torch.as_tensor(np.asarray(start["step_global"]) - 1, dtype=torch.int32))
+            zi = torch.zeros((R, C), dtype=torch.int32, device=dev)
+            dg_converged(zi, torch.zeros((R, C), dtype=torch.float32, device=dev), V, cfg["k"], cfg["tau"],
+                         cfg["max_steps"], self.seed, st)                  # prefill case: first canvases
+            sib = np.asarray(start["step_in_block"], np.int32)
+            st["step_in_block"].copy_(torch.as_tensor(sib))
+            st["sc_on"].copy_(torch.as_tensor((sib > 0).astype(np.uint8)))
+            self.phase[:] = DENOISE
+            self.cached[:] = np.asarray(start["cached"], np.int64)
+        self.steady = start is not None
+        self.last = {}
 
     def _schedule(self, it: int):
         """Phases of this iteration: arrivals join the queue, decode work first, then admission."""
         cfg, s = self.cfg, self.sched
-        for r in np.nonzero(s["arrival"] == it)[0]:
-            self.queue.append(int(r))
+        if not self.steady:                       # a steady-state start has admitted every request
+            for r in np.nonzero(s["arrival"] == it)[0]:
+                self.queue.append(int(r))
         decode = int(np.sum((self.phase == DENOISE) | (self.phase == COMMIT))) * cfg["C"]
         sizes = [int(s["prompt"][r]) for r in self.queue]
         if self.policy == "deficit":
@@ -109,10 +152,17 @@ class ServingLoop:
         den = torch.as_tensor((self.phase == DENOISE).astype(np.uint8), device=self.dev)
         pre = torch.as_tensor(((self.phase == DENOISE) | (self.phase == PREFILL)).astype(np.uint8), device=self.dev)
         st = self.state
-        if bool((self.phase == DENOISE).any()):
+        denoising = bool((self.phase == DENOISE).any())
+        if denoising:
             logits = self.t["logits"][it % cfg["n_pool"]]
             step_now = st["step_global"].clone()
-            so = dg_denoise_sample(logits, V, C, self.seed, step_now, cfg["temperature"], active=den)
+            so = self.so
+            if self.sc is not None:
+                dg_denoise_sample_sc(logits, V, C, self.seed, step_now, cfg["temperature"], active=den, out=so,
+                                     ws=self.ws_s, sc_operand=self.operand)
+            else:
+                dg_denoise_sample(logits, V, C, self.seed, step_now, cfg["temperature"], active=den, out=so,
+                                  ws=self.ws_s)
             dg_entropy_accept(so["entropy"].view(R, C), so["sample"].view(R, C), st["canvas"], V, cfg["budget"],
                               self.seed, step_now, active=den, accept=self.accept, n_accept=self.n_accept)
             argmax, entropy = so["argmax"].view(R, C), so["entropy"].view(R, C)
@@ -122,12 +172,18 @@ class ServingLoop:
         if bool(((self.phase == DENOISE) | (self.phase == PREFILL)).any()):
             st["committed"].zero_()
             dg_converged(argmax, entropy, V, cfg["k"], cfg["tau"], cfg["max_steps"], self.seed, st, active=pre)
+        if denoising and self.sc is not None:
+            dg_selfcond_embed_sc(self.operand, V, self.so["row_max"], self.so["row_lnz"], st["sc_on"], st["canvas"],
+                                 self.sc["E"], self.sc["prepared"], self.sc["hidden"], x_out=self.x, ws=self.ws_sc)
         ev1.record()
+        self.last = dict(denoise=self.phase == DENOISE, attention=att if rows > 0 else None)
         committed = st["committed"].cpu().numpy().astype(bool) & (self.phase == DENOISE)
         rec["gpu_ms"] = (ev0, ev1)
         rec["committed"] = {int(r): st["out_tokens"][r].cpu().numpy().copy() for r in np.nonzero(committed)[0]}
         if record:
             rec["canvas"] = st["canvas"].cpu().numpy().copy()
+            if self.sc is not None and denoising:
+                rec["x_next"] = self.x.float().cpu().numpy().copy()
         # phase transitions for the next iteration
         for r in range(R):
             ph = self.phase[r]

@@ -15,6 +15,12 @@ page (section on the deficit token-budget scheduler) for admission and the Diffu
      prefill case of the convergence step;
   6. transitions: prefill -> denoise; a committed block -> commit pass next iteration; after the
      commit pass of its last block a request is done.
+With self-conditioning (DiffusionGemma/vLLM page, section "Self-conditioning"), each iteration with
+denoising requests also forms the next step's canvas embedding of their rows from this iteration's
+softmax, after the convergence step: x_next = E[canvas] + (sc_on ? MLP(P . E) : 0).
+A steady-state start puts every request in the denoising phase over its cached prefix, with its
+first canvas from the prefill case at global step g0 - 1 and the counters (step in block s0, global
+step g0, self-conditioning on when s0 > 0).
 
 Pinned by tests/test_oracle_traces.py against the hand-worked schedule of
 tests/golden/serving_trace.txt (admissions, tokens and deficit per iteration, the split of every
@@ -25,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import accept as acc_mod
-from . import admission, attention, converged as conv_mod, sampler
+from . import admission, attention, converged as conv_mod, sampler, selfcond as sc_mod
 
 
 def _bf16(a):
@@ -33,9 +39,12 @@ def _bf16(a):
     return a.view(np.float32).astype(np.float64)
 
 
-def serving_loop(cfg: dict, sched: dict, tensors: dict, max_iters: int = 10000) -> list:
+def serving_loop(cfg: dict, sched: dict, tensors: dict, max_iters: int = 10000, selfcond: dict | None = None,
+                 start: dict | None = None) -> list:
     """Returns one record per iteration: admitted ids, tokens, deficit, launch splits, attention
-    output [rows, Hq, D], commits {request: tokens}, canvas [R, C] after the iteration."""
+    output [rows, Hq, D], commits {request: tokens}, canvas [R, C] after the iteration, and with
+    selfcond (fp64 E [V, d], w_gate, w_up, w_down) x_next [R * C, d] (rows of denoising requests;
+    NaN elsewhere).  start: dict(cached, step_in_block, step_global) per request."""
     R, C, V, ps = cfg["R"], cfg["C"], cfg["V"], cfg["page_size"]
     q, k, v = _bf16(tensors["q"]), _bf16(tensors["k"]), _bf16(tensors["v"])
     kc, vc = _bf16(tensors["k_cache"]), _bf16(tensors["v_cache"])
@@ -49,12 +58,21 @@ def serving_loop(cfg: dict, sched: dict, tensors: dict, max_iters: int = 10000) 
     phase = ["waiting"] * R
     cached = [0] * R
     blocks = [0] * R
+    if start is not None:
+        state.step_global[:] = np.asarray(start["step_global"], np.int64) - 1
+        conv_mod.converged(np.zeros((R, C), np.int64), np.zeros((R, C)), state, cfg["k"], cfg["tau"],
+                           cfg["max_steps"], seeds, V)                    # prefill case: first canvases
+        state.step_in_block[:] = np.asarray(start["step_in_block"], np.int64)
+        state.sc_on[:] = (state.step_in_block > 0).astype(np.uint8)
+        phase = ["denoise"] * R
+        cached = [int(c) for c in start["cached"]]
     queue, deficit = [], 0
     log = []
     for it in range(max_iters):
         if all(p == "done" for p in phase):
             break
-        queue += [r for r in range(R) if arrival[r] == it]
+        if start is None:                          # a steady-state start has admitted every request
+            queue += [r for r in range(R) if arrival[r] == it]
         decode = C * sum(p in ("denoise", "commit") for p in phase)
         n, deficit, tokens = admission.admit(cfg["token_budget"], decode, [int(prompt[r]) for r in queue], deficit)
         admitted, queue = queue[:n], queue[n:]
@@ -97,6 +115,12 @@ def serving_loop(cfg: dict, sched: dict, tensors: dict, max_iters: int = 10000) 
                                     active=act)
             rec["mean_gap"] = co.mean_gap
         rec["canvas"] = state.canvas.copy()
+        if selfcond is not None and den.any():
+            P = sc_mod.probs_from_stats(_bf16(logits[it % cfg["n_pool"]]), cfg["temperature"], so.row_max, so.row_lnz)
+            x, _s, _y = sc_mod.selfcond_embed(P, state.canvas, state.sc_on, selfcond["E"], selfcond["w_gate"],
+                                              selfcond["w_up"], selfcond["w_down"], C, to_bf16=False)
+            x[~np.repeat(den, C)] = np.nan
+            rec["x_next"] = x
         for r in range(R):
             if phase[r] == "prefill":
                 cached[r] = int(prompt[r])

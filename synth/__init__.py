@@ -350,3 +350,12 @@ def e4m3_table_torch(seed: int, tag, shape, std: float, scale: float, device, ch
         x = torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device) * (std / scale)
         flat[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
     return out
+
+
+def batched_loop_start(cfg: dict, sched: dict) -> dict:
+    """Steady-state start of the batched loop: request r holds its prompt as a cached prefix and sits
+    at step 2r of its block (mod the step cap) and global step 2r + 1 (its first canvas drawn at
+    global step 2r)."""
+    R = cfg["R"]
+    r = np.arange(R, dtype=np.int64)
+    return dict(cached=sched["prompt"].copy(), step_in_block=(2 * r) % cfg["max_steps"], step_global=2 * r + 1)

@@ -57,5 +57,16 @@ SERVING = dict(
 SERVING_SMALL = dict(
     name="serving_small", seed=0, R=6, C=16, P_min=8, P_max=72, arrival_every=1, page_size=16, Hq=4, Hkv=2,
     D=128, V=2048, token_budget=72, blocks=2, budget=4.0, k=2, tau=0.3, max_steps=4, temperature=1.0,
-    n_pool=3,
+    n_pool=3, d=128, hidden=128,
+)
+
+# The batched workload as a steady-state loop (every request already holds its prefix of
+# U[P_min, P_max] tokens and denoises from the first iteration; request r starts at step 2r of its
+# block and global step 2r + 1, so one block reaches the 64-step cap every two iterations, runs its
+# commit pass and restarts), with self-conditioning.  Pages are sized for the prefix plus `blocks`
+# committed blocks.
+BATCHED_LOOP = dict(
+    name="batched_loop", seed=0, R=32, C=256, P_min=512, P_max=8192, arrival_every=1, page_size=16, Hq=16,
+    Hkv=8, D=256, V=262144, token_budget=8192, blocks=2, budget=8.0, k=3, tau=0.3, max_steps=64,
+    temperature=1.0, n_pool=2, d=4096, hidden=1024,
 )

@@ -181,3 +181,33 @@ def test_serving_trace_matches_hand_schedule():
     np.testing.assert_array_equal(kc[0, 0, 10:14], kf[0:4, 0])   # its commit pass (it 6, rows 0..3)
     np.testing.assert_array_equal(kc[1, 0, :3], kf[4:7, 0])      # request 2 prefill (it 4, rows 4..6)
     np.testing.assert_array_equal(kc[1, 0, 3:7], kf[0:4, 0])     # its commit pass (it 7, rows 0..3)
+
+
+def test_serving_steady_start_hand_schedule():
+    """A steady-state start (every request already holds its prefix and denoises from the first
+    iteration, at its own step): two requests, C = 4, prefixes 5 and 9, steps in block 0 and 3 of
+    a 4-step block, global steps 1 and 7.  Worked out by hand: request 1 is at its last step, so it
+    commits in iteration 0, runs its commit pass (4 causal rows after its 9 cached) in iteration 1
+    and denoises again from iteration 2 over 13 cached tokens; request 0 commits in iteration 3.
+    The first canvases are the prefill case's Philox INIT tokens at global steps 0 and 6; arrivals
+    are ignored; with self-conditioning off for request 0 (step 0) and on for request 1 (step 3)."""
+    cfg = dict(R=2, C=4, V=64, page_size=16, Hq=2, Hkv=1, D=8, token_budget=8, blocks=2, budget=4.0, k=2,
+               tau=0.0, max_steps=4, temperature=1.0, n_pool=1)
+    sched = dict(prompt=np.array([5, 9]), arrival=np.array([0, 0]), page0=np.array([0, 1], np.int32),
+                 page_table=np.array([1, 0], np.int32), seeds=np.array([21, 22], np.uint64))
+    rng = np.random.default_rng(9)
+    bf = lambda shape: (rng.normal(0, 1, shape).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    tensors = dict(q=bf((8, 2, 8)), k=bf((8, 1, 8)), v=bf((8, 1, 8)), k_cache=bf((2, 1, 16, 8)),
+                   v_cache=bf((2, 1, 16, 8)), logits=bf((1, 8, 64)))
+    start = dict(cached=[5, 9], step_in_block=[0, 3], step_global=[1, 7])
+    log, _ = serving.serving_loop(cfg, sched, tensors, max_iters=5, start=start)
+    split = lambda rec: [tuple(int(v) for v in s[:4]) for s in rec["splits"]]
+    assert split(log[0]) == [(0, 5, 0, 4), (4, 9, 0, 4)]
+    assert sorted(log[0]["committed"]) == [1]
+    assert split(log[1]) == [(0, 5, 0, 4), (4, 9, 4, 0)]
+    assert split(log[2]) == [(0, 5, 0, 4), (4, 13, 0, 4)]
+    assert sorted(log[3]["committed"]) == [0]
+    assert split(log[4]) == [(0, 5, 4, 0), (4, 13, 0, 4)]
+    assert all(rec["admitted"] == [] for rec in log)
+    # request 1's block committed the canvas it was sampling; its restart canvas is INIT at global step 7
+    assert np.array_equal(log[0]["canvas"][1], philox.random_tokens(22, 7, np.arange(4), 64, philox.INIT))
