@@ -197,20 +197,21 @@ def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
 
     attention: MFMA work 4 D Hq per visible (query row, key) pair: every one of the C canvas rows sees
     the L cached keys and all C canvas keys (in a sliding-window layer of window W, canvas row j at
-    position L + j sees positions L + j - W .. L + j + W inside the request); sampler: the logit
-    bytes (2 V per row, read once); P.E: 2 C V d FLOP on fp16 MFMA and its algorithmic bytes
-    (E + P, 16-bit)."""
+    position L + j sees positions L + j - W .. L + j + W inside the request); sampler (the fused call:
+    streaming kernel + chunk merge): the logits read once (2 V per row) plus the fp16 probability
+    operand it writes (2 V per row, rows padded to 256); P.E: 2 C V d FLOP on fp16 MFMA and its
+    algorithmic bytes (E + P, 16-bit)."""
     C, V, d, L, W = c["B"] * c["C"], c["V"], c["d"], c["L"], c["window"]
     pairs = C * (L + C)
     if W > 0:
         pairs = c["B"] * sum(min(L + c["C"], L + j + W + 1) - max(0, L + j - W) for j in range(c["C"]))
     att_flop = 4.0 * c["D"] * c["Hq"] * pairs
-    samp_bytes = 2.0 * C * V
+    samp_bytes = 2.0 * C * V + 2.0 * (-(-C // 256) * 256) * V      # logits read once + the fp16 operand written
     pe_flop = 2.0 * C * V * d
     out = {
         "canvas_attention": {"us": brk["canvas_attention"], "bound": "mfma",
                              "tflops": att_flop / (brk["canvas_attention"] * 1e-6) / 1e12},
-        "denoise_sample": {"us": brk["denoise_sample"], "bound": "hbm",
+        "denoise_sample": {"us": brk["denoise_sample"], "bound": "hbm", "bytes": samp_bytes,
                            "gbs": samp_bytes / (brk["denoise_sample"] * 1e-6) / 1e9},
         "pe_contraction": {"us": pe_ms * 1000.0, "bound": "hbm",
                            "gbs": pe_algorithmic_bytes(c) / (pe_ms * 1e-3) / 1e9,
@@ -250,6 +251,7 @@ def cpu_baseline(w: Workload, steps: int):
     wg, wu, wd = f64(w.wg), f64(w.wu), f64(w.wd)
     threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     log("cpu baseline: timing the oracle")
+    oracle_samples = []
     t0 = time.perf_counter()
     for t in range(steps):
         logits = pool[t]
@@ -259,6 +261,7 @@ def cpu_baseline(w: Workload, steps: int):
         for h in range(c["Hq"]):
             attention.dense_mask_attention(q[:, h], K[:, h // group], Vv[:, h // group], mask, 1.0 / math.sqrt(D))
         so = sampler.denoise_sample(logits, 1.0, [0], [1 + t], C)
+        oracle_samples.append(so)
         st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
                                  unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
                                  step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
@@ -268,6 +271,7 @@ def cpu_baseline(w: Workload, steps: int):
         selfcond.selfcond_embed(P, st.canvas, st.sc_on, E, wg, wu, wd, C, to_bf16=True)
     dt = time.perf_counter() - t0
     cores = min(len(os.sched_getaffinity(0)), max(threads, 1))
+    w.parity = sampler_parity(w, oracle_samples)
     return dict(value=steps * C / dt, unit="positions/s", cores=cores, kind="oracle",
                 sample=(f"{steps} whole steps of the {C}-position canvas ({steps * C} positions) on the host in fp64 "
                         f"numpy: attention for {C} rows x {c['Hq']} heads over {c['L'] + C} keys, the sampler over "
@@ -275,17 +279,55 @@ def cpu_baseline(w: Workload, steps: int):
                         f"{V} x {c['d']} table; {dt:.1f} s"))
 
 
+TIE_GAP, TOL_ENTROPY = 1e-5, 1e-3
+
+
+def sampler_parity(w: Workload, oracle_samples) -> dict:
+    """The GPU sampler (the step's fused call) on the logits, seeds and steps of the oracle's timed
+    sample, compared row by row: argmax and candidate bit-exact except near-ties (top-2 gap of the
+    logits or of the Gumbel keys below 1e-5, counted by class), entropy within 1e-3 nats."""
+    import numpy as np
+    import torch
+    dg, c = w.dg, w.c
+    C, V = c["C"], c["V"]
+    ties = {"argmax_gap": 0, "gumbel_key_gap": 0}
+    bad = {"argmax": 0, "sample": 0, "entropy": 0}
+    worst_h = 0.0
+    for t, ref in enumerate(oracle_samples):
+        step = torch.full((1,), 1 + t, dtype=torch.int32, device="cuda")
+        out, _ = dg.dg_denoise_sample_sc(w.pool[t % len(w.pool)], V, C, w.seed, step, c["temperature"])
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        for r in range(C):
+            if got["argmax"][r] != ref.argmax[r]:
+                if 0 < ref.argmax_gap[r] < TIE_GAP:
+                    ties["argmax_gap"] += 1
+                else:
+                    bad["argmax"] += 1
+            if got["sample"][r] != ref.sample[r]:
+                if ref.key_gap[r] < TIE_GAP:
+                    ties["gumbel_key_gap"] += 1
+                else:
+                    bad["sample"] += 1
+        err = np.abs(got["entropy"].astype(np.float64) - ref.entropy)
+        worst_h = max(worst_h, float(err.max()))
+        bad["entropy"] += int(np.sum(err > TOL_ENTROPY))
+    return {"rows": C * len(oracle_samples), "near_ties": ties, "mismatches": bad, "entropy_max_abs_err": worst_h}
+
+
 def serving_bench(policies=("deficit", "arrival")) -> dict:
     """The batched serving loop (32 requests in bursts of 8, prompts U[512, 8192], 256-token
     canvases, two blocks each, V = 262144, 8192 tokens per iteration) run to completion once per
     admission policy: deficit admission, and admitting every waiting prefill at once.  A decode
     iteration's time is what every running request waits for its next step (the decode stall).  Per iteration: one mixed
-    attention launch, then sampler / accept / convergence for the denoising requests; GPU time from
+    attention launch, then sampler / accept / convergence and self-conditioning (P.E over the 8192
+    canvas rows, d = 4096, MLP 4096 -> 1024 -> 4096) for the denoising requests; GPU time from
     events around each iteration's launches (the host reads the commit flags once per iteration)."""
     import numpy as np
     import torch
 
     import synth
+    from denoise_step_amd import dg_selfcond_prepare as dg_prepare
     from denoise_step_amd.serving import ServingLoop
     from synth.configs import SERVING as cfg
     dev = torch.device("cuda:0")
@@ -300,12 +342,17 @@ def serving_bench(policies=("deficit", "arrival")) -> dict:
                 v=synth.normal_torch(s, "serving.v", (n, cfg["Hkv"], cfg["D"]), 1.0, bf, dev),
                 logits=torch.stack([synth.zipf_logits_torch(s, ("serving.logits", i), R * C, V, dev)
                                     for i in range(cfg["n_pool"])]))
+    E = synth.normal_torch(s, "serving.E", (V, cfg["d"]), 1 / 8, bf, dev)
+    wts = [synth.normal_torch(s, tag, sh, 0.02, bf, dev)
+           for tag, sh in (("serving.wg", (cfg["d"], cfg["hidden"])), ("serving.wu", (cfg["d"], cfg["hidden"])),
+                           ("serving.wd", (cfg["hidden"], cfg["d"])))]
+    sc = dict(E=E, prepared=dg_prepare(E, *wts), hidden=cfg["hidden"])
     out = {}
     for pol in policies:
         t = dict(base, k_cache=torch.zeros((sched["n_pages"], cfg["Hkv"], cfg["page_size"], cfg["D"]), dtype=bf,
                                            device=dev))
         t["v_cache"] = torch.zeros_like(t["k_cache"])
-        loop = ServingLoop(cfg, sched, t, device=dev, policy=pol)
+        loop = ServingLoop(cfg, sched, t, device=dev, policy=pol, selfcond=sc)
         log(f"serving: running the loop with {pol} admission")
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
@@ -329,17 +376,357 @@ def serving_bench(policies=("deficit", "arrival")) -> dict:
             "config": {"workload": "serving", "requests": R, "C": C, "V": V, "prompt": [cfg["P_min"], cfg["P_max"]],
                        "arrival_every": cfg["arrival_every"], "token_budget": cfg["token_budget"],
                        "blocks": cfg["blocks"], "max_steps": cfg["max_steps"], "heads_q": cfg["Hq"],
-                       "heads_kv": cfg["Hkv"], "head_dim": cfg["D"]},
+                       "heads_kv": cfg["Hkv"], "head_dim": cfg["D"], "d_embed": cfg["d"], "mlp_hidden": cfg["hidden"],
+                       "self_conditioning": True},
             "policies": out}
 
+
+
+# ------------------------------------------------------------------ batched, structured-read, block-draft lines
+def _json_line(metric, value, unit, K, W, ms_total, config, roofline, cpu, extra=None, dtype="bf16"):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
+           "ms_per_step": ms_total / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dtype, "data": "synthetic", "config": config, "steps_per_s": 1000.0 * K / ms_total,
+           "roofline": roofline, "cpu_baseline": cpu}
+    out.update(extra or {})
+    return out
+
+
+def _cores(threads):
+    return min(len(os.sched_getaffinity(0)), max(threads, 1))
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    info = threadpool_info()
+    return max(int(i.get("num_threads", 1)) for i in info) if info else 1
+
+
+def bench_batched(K: int, W: int, cpu: bool) -> dict:
+    """One iteration of the batched workload as a steady-state loop: 32 requests over prefixes
+    U[512, 8192] in shuffled pages, each denoising a 256-token canvas at its own step (request r at
+    step 2r of its 64-step block), so a block commits every other iteration and its 256-row commit
+    pass shares the next launch; per iteration one mixed attention launch (16/8 heads x 256), the
+    fused sampler over 8192 rows of V = 262144, accept, convergence and self-conditioning
+    (P.E over 8192 rows, d = 4096, MLP 4096 -> 1024 -> 4096).  Logits rotate through 4 sets
+    (17 GB).  Dominant kernel: P.E, bound by MFMA (2 x 8192 x V x d per launch)."""
+    import numpy as np
+    import torch
+
+    import denoise_step_amd as dg
+    import synth
+    from denoise_step_amd.serving import ServingLoop
+    from synth.configs import BATCHED_LOOP
+    cfg = dict(BATCHED_LOOP, n_pool=4, blocks=2)
+    R, C, V, d, h = cfg["R"], cfg["C"], cfg["V"], cfg["d"], cfg["hidden"]
+    Hq, Hkv, D, ps = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page_size"]
+    sched = synth.serving_schedule_inputs(cfg)
+    start = synth.batched_loop_start(cfg, sched)
+    n = R * C
+    bf = torch.bfloat16
+    log("batched: generating the row pools, caches, 4 logit sets and the table on the GPU")
+    g = lambda tag, shape, std=1.0: synth.normal_torch(cfg["seed"], ("bench.batched", tag), shape, std, bf, "cuda")
+    t = dict(q=g("q", (n, Hq, D)), k=g("k", (n, Hkv, D)), v=g("v", (n, Hkv, D)),
+             k_cache=g("kc", (sched["n_pages"], Hkv, ps, D)), v_cache=g("vc", (sched["n_pages"], Hkv, ps, D)))
+    t["logits"] = torch.empty((cfg["n_pool"], n, V), dtype=bf, device="cuda")
+    for i in range(cfg["n_pool"]):
+        t["logits"][i] = synth.zipf_logits_torch(cfg["seed"], ("bench.batched.logits", i), n, V, "cuda")
+    E = g("E", (V, d), 1 / 8)
+    w = [g(tag, sh, 0.02) for tag, sh in (("wg", (d, h)), ("wu", (d, h)), ("wd", (h, d)))]
+    prepared = dg.dg_selfcond_prepare(E, *w)
+    loop = ServingLoop(cfg, sched, t, selfcond=dict(E=E, prepared=prepared, hidden=h), start=start)
+    log(f"batched: warmup {W} iterations")
+    for it in range(W):
+        loop.step(it)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"batched: timing {K} iterations")
+    positions = 0
+    t0.record()
+    for i in range(K):
+        rec = loop.step(W + i, pe_events=pe_ev[i])
+        positions += rec["denoise_rows"]
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    pe_ms = sum(hev.elapsed_ms(a, b) for a, b in pe_ev) / K
+    pe_flop = 2.0 * n * V * d
+    achieved = pe_flop / (pe_ms * 1e-3) / 1e12
+    roof = {"kernel": PE_KERNEL, "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None, "algorithmic_flop_per_launch": pe_flop,
+            "avg_launch_us": pe_ms * 1000.0}
+    cpu_line = None
+    if cpu:
+        cpu_line = _cpu_batched(loop, t, E, w, cfg, sched)
+    return _json_line("canvas positions denoised/sec (batched: 32 x 256 canvases, V=262144) + % MFMA roofline",
+                      positions / (ms * 1e-3), "positions/s", K, W, ms,
+                      {"workload": "batched", "requests": R, "C": C, "V": V, "prefix": [cfg["P_min"], cfg["P_max"]],
+                       "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "d_embed": d, "mlp_hidden": h,
+                       "max_steps": cfg["max_steps"], "logit_pool": cfg["n_pool"], "self_conditioning": True},
+                      roof, cpu_line, {"positions_per_iteration": positions / K})
+
+
+def _cpu_batched(loop, t, E, w, cfg, sched):
+    """The oracle on one request's denoise iteration (its attention over its own pages, sampler,
+    accept, convergence, P.E + MLP of its 256 rows) of the same loop state and inputs."""
+    import numpy as np
+    import torch
+
+    from oracle import accept, attention, converged, sampler, selfcond
+    C, V, D, ps = cfg["C"], cfg["V"], cfg["D"], cfg["page_size"]
+    f = lambda x: x.float().cpu().numpy().astype(np.float64)
+    r = 0
+    sp, _ = loop._splits()
+    i = [k for k in range(sp.shape[0]) if sp[k, 4] == sched["page0"][r]][0]
+    row0, cached, nc, nv = (int(x) for x in sp[i][:4])
+    p0, p1 = int(sched["page0"][r]), int(sched["page0"][r + 1])
+    pt = torch.as_tensor(sched["page_table"][p0:p1].astype(np.int64), device="cuda")
+    sl = slice(row0, row0 + nc + nv)
+    q, k, v = f(t["q"][sl]), f(t["k"][sl]), f(t["v"][sl])
+    kc, vc = f(t["k_cache"][pt]), f(t["v_cache"][pt])
+    logits = f(t["logits"][0][r * C:(r + 1) * C])
+    Eh = E.float().cpu().numpy()
+    wh = [f(x) for x in w]
+    seed = int(sched["seeds"][r])
+    log("cpu baseline: timing the oracle on one request's iteration")
+    threads = _blas_threads()
+    t0 = time.perf_counter()
+    attention.canvas_attention(q, k, v, kc, vc, np.arange(kc.shape[0], dtype=np.int32), [(0, cached, nc, nv, 0)], ps,
+                               1.0 / math.sqrt(D))
+    so = sampler.denoise_sample(logits, 1.0, [seed], [1], C)
+    st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
+                             unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
+                             step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
+    accept.entropy_accept(so.entropy[None, :], so.sample[None, :], st.canvas, cfg["budget"], [seed], [1], V)
+    converged.converged(so.argmax[None, :], so.entropy[None, :], st, cfg["k"], cfg["tau"], cfg["max_steps"], [seed], V)
+    P = selfcond.probs_from_stats(logits, 1.0, so.row_max, so.row_lnz)
+    selfcond.selfcond_embed(P, st.canvas, st.sc_on, Eh, *wh, C, to_bf16=True)
+    dt = time.perf_counter() - t0
+    return dict(value=C / dt, unit="positions/s", cores=_cores(threads), kind="oracle",
+                sample=(f"one request's iteration of the batched loop on the host in fp64 numpy: attention for its "
+                        f"{nc + nv} rows x {cfg['Hq']} heads over {cached + nc + nv} keys, the sampler over {C} rows "
+                        f"of V={V}, accept + converged, P.E + MLP for {C} rows against the full table; {dt:.1f} s"))
+
+
+def bench_structured_read(K: int, W: int, cpu: bool) -> dict:
+    """One single-pass structured read over 64 requests: each launch holds the request's final
+    2048-token prompt chunk (causal rows, K/V appended to its pages) and its 256-row canvas
+    (bidirectional, read-only), 16/8 heads x 256; then the allowed-choice readout of 8 slots per
+    request (2-5 allowed ids) over V = 262144 slot logits.  Dominant kernel: the attention, bound by
+    MFMA: 4 D Hq FLOP per visible (row, key) pair (causal triangle plus the canvas block)."""
+    import numpy as np
+    import torch
+
+    import denoise_step_amd as dg
+    import synth
+    from synth.configs import STRUCTURED_READ as cfg
+    B, C, V, nc = cfg["B"], cfg["C"], cfg["V"], cfg["n_causal"]
+    Hq, Hkv, D, ps = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page_size"]
+    lay = synth.paged_layout(cfg["seed"], synth.structured_read_splits(cfg), ps, tag="bench.sread")
+    bf = torch.bfloat16
+    log("structured read: generating inputs on the GPU")
+    g = lambda tag, shape: synth.normal_torch(cfg["seed"], ("bench.sread", tag), shape, 1.0, bf, "cuda")
+    q, k, v = g("q", (lay.rows, Hq, D)), g("k", (lay.rows, Hkv, D)), g("v", (lay.rows, Hkv, D))
+    kc, vc = g("kc", (lay.n_pages, Hkv, ps, D)), g("vc", (lay.n_pages, Hkv, ps, D))
+    pt = torch.as_tensor(lay.page_table, device="cuda")
+    sp = torch.as_tensor(lay.split_array(), device="cuda")
+    rng = synth.rng_for(cfg["seed"], "bench.sread.slots")
+    n_slots = B * cfg["slots"]
+    counts = rng.integers(cfg["min_ids"], cfg["max_ids"] + 1, n_slots)
+    offsets = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+    ids = torch.as_tensor(np.concatenate([rng.choice(V, c, replace=False) for c in counts]).astype(np.int32),
+                          device="cuda")
+    slot_row = torch.arange(n_slots, dtype=torch.int32, device="cuda")
+    slot_logits = synth.zipf_logits_torch(cfg["seed"], "bench.sread.logits", n_slots, V, "cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, dg.dg_canvas_attention_ws_bytes(B, lay.rows, nc + C, nc + C, Hq, Hkv, D, dg.DG_BF16)),
+                     dtype=torch.uint8, device="cuda")
+    qv = torch.empty(int(counts.sum()), dtype=torch.float32, device="cuda")
+    ans = torch.empty(n_slots, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record()
+        dg.dg_canvas_attention(q, k, v, kc, vc, pt, sp, nc + C, nc + C, scale, out=out, ws=ws)
+        if ev is not None:
+            ev[1].record()
+        dg.dg_allowed_probs(slot_logits, V, slot_row, offsets, ids, 1.0, q=qv, answer=ans)
+
+    log(f"structured read: warmup {W}")
+    for _ in range(W):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        one(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    att_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    pairs = B * (nc * (nc + 1) // 2 + C * (nc + C))
+    flop = 4.0 * D * Hq * pairs
+    achieved = flop / (att_ms * 1e-3) / 1e12
+    roof = {"kernel": "attend_mfma16_kernel<256, false>", "bound": "mfma", "achieved": achieved,
+            "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None,
+            "algorithmic_flop_per_launch": flop, "avg_launch_us": att_ms * 1000.0}
+    cpu_line = None
+    if cpu:
+        from oracle import attention, readout
+        f = lambda x: x.float().cpu().numpy().astype(np.float64)
+        r0, nr = int(lay.row0[0]), nc + C
+        pages = torch.as_tensor(lay.pages_of(0).astype(np.int64), device="cuda")
+        qh, kh, vh = f(q[r0:r0 + nr]), f(k[r0:r0 + nr]), f(v[r0:r0 + nr])
+        kch, vch = f(kc[pages]), f(vc[pages])
+        sl = f(slot_logits[:cfg["slots"]])
+        off = offsets[:cfg["slots"] + 1].cpu().numpy()
+        idh = ids[:int(off[-1])].cpu().numpy()
+        threads = _blas_threads()
+        log("cpu baseline: timing the oracle on one request")
+        tc = time.perf_counter()
+        attention.canvas_attention(qh, kh, vh, kch, vch, np.arange(kch.shape[0], dtype=np.int32), [(0, 0, nc, C, 0)],
+                                   ps, scale)
+        readout.allowed_probs(sl, off, idh)
+        dt = time.perf_counter() - tc
+        cpu_line = dict(value=C / dt, unit="positions/s", cores=_cores(threads), kind="oracle",
+                        sample=(f"one request of the launch on the host in fp64 numpy: attention for its {nc} causal "
+                                f"+ {C} canvas rows x {Hq} heads (K/V appended), the readout of its {cfg['slots']} "
+                                f"slots; {dt:.1f} s"))
+    return _json_line("canvas positions read/sec (structured read: 64 x (2048 causal + 256 canvas), V=262144) "
+                      "+ % MFMA roofline", B * C / (ms * 1e-3), "positions/s", K, W, ms,
+                      {"workload": "structured_read", "requests": B, "causal_rows": nc, "C": C, "V": V,
+                       "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "slots": cfg["slots"]},
+                      roof, cpu_line, {"attention_us": att_ms * 1000.0})
+
+
+def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
+    """One parallel-drafting pass: 5 draft layers of attention (128 requests x 16 draft rows over
+    injected context U[256, 4096], 32 query / 8 KV heads x 128, each layer its own K/V), the
+    argmax-only sampler over 2048 x 151936 bf16 logits and greedy verification of the 128 blocks
+    against targets whose first mismatch is geometric(0.2).  Dominant work: the attention, bound by
+    HBM (the context K/V is read once per layer)."""
+    import numpy as np
+    import torch
+
+    import denoise_step_amd as dg
+    import synth
+    from synth.configs import BLOCK_DRAFT as cfg
+    B, L16, V, layers = cfg["B"], cfg["block"], cfg["V"], cfg["layers"]
+    Hq, Hkv, D, ps = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page_size"]
+    bf = torch.bfloat16
+    log("block draft: generating 5 layers of context K/V and the logits on the GPU")
+    lays, L = [], []
+    for layer in range(layers):
+        lay = synth.paged_layout(cfg["seed"], synth.block_draft_splits(cfg), ps, tag=("bench.draft", layer))
+        g = lambda tag, shape: synth.normal_torch(cfg["seed"], ("bench.draft", layer, tag), shape, 1.0, bf, "cuda")
+        L.append(dict(q=g("q", (lay.rows, Hq, D)), k=g("k", (lay.rows, Hkv, D)), v=g("v", (lay.rows, Hkv, D)),
+                      kc=g("kc", (lay.n_pages, Hkv, ps, D)), vc=g("vc", (lay.n_pages, Hkv, ps, D)),
+                      pt=torch.as_tensor(lay.page_table, device="cuda"),
+                      sp=torch.as_tensor(lay.split_array(), device="cuda"),
+                      max_keys=max(s.cached + s.n_causal + s.n_canvas for s in lay.splits)))
+        L[-1]["out"] = torch.empty_like(L[-1]["q"])
+        L[-1]["ws"] = torch.empty(max(1, dg.dg_canvas_attention_ws_bytes(B, lay.rows, L16, L[-1]["max_keys"], Hq, Hkv,
+                                                                        D, dg.DG_BF16)), dtype=torch.uint8,
+                                  device="cuda")
+        lays.append(lay)
+    logits = synth.zipf_logits_torch(cfg["seed"], "bench.draft.logits", B * L16, V, "cuda")
+    amax = torch.empty(B * L16, dtype=torch.int32, device="cuda")
+    ws_s = torch.empty(dg.dg_denoise_sample_ws_bytes(B * L16, V), dtype=torch.uint8, device="cuda")
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for x in L:
+            dg.dg_canvas_attention(x["q"], x["k"], x["v"], x["kc"], x["vc"], x["pt"], x["sp"], L16, x["max_keys"],
+                                   scale, out=x["out"], ws=x["ws"])
+        if ev is not None:
+            ev[1].record()
+        dg.dg_denoise_sample(logits, V, L16, None, None, 1.0, argmax_only=True, out=dict(argmax=amax), ws=ws_s)
+        dg.dg_verify_prefix(amax.view(B, L16), target, accepted=acc)
+
+    # targets: the draft argmax with its first mismatch at a geometric(0.2) offset (later ids random)
+    dg.dg_denoise_sample(logits, V, L16, None, None, 1.0, argmax_only=True, out=dict(argmax=amax), ws=ws_s)
+    draft = amax.view(B, L16).cpu().numpy()
+    rng = synth.rng_for(cfg["seed"], "bench.draft.targets")
+    gmm = rng.geometric(cfg["p_mismatch"], B) - 1
+    tgt = draft.copy()
+    for b in range(B):
+        if gmm[b] < L16:
+            tgt[b, gmm[b]] = (draft[b, gmm[b]] + 1 + rng.integers(0, V - 1)) % V
+            tgt[b, gmm[b] + 1:] = rng.integers(0, V, L16 - 1 - gmm[b])
+    target = torch.as_tensor(tgt, device="cuda")
+    log(f"block draft: warmup {W}")
+    for _ in range(W):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        one(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    att_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    kv_bytes = sum(2 * 2 * Hkv * D * sum(s.cached + s.n_causal + s.n_canvas for s in lay.splits) for lay in lays)
+    achieved = kv_bytes / (att_ms * 1e-3) / 1e9
+    roof = {"kernel": "attend_mfma16_kernel<128, false> (5 layers)", "bound": "hbm", "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "algorithmic_bytes_per_pass": kv_bytes, "avg_pass_attention_us": att_ms * 1000.0}
+    assert np.array_equal(acc.cpu().numpy(), np.minimum(gmm, L16)), "verification disagrees with its construction"
+    cpu_line = None
+    if cpu:
+        from oracle import attention, verify
+        f = lambda x: x.float().cpu().numpy().astype(np.float64)
+        reqs = (0, 1, 2, 3)
+        host = []
+        for x, lay in zip(L, lays):
+            for r in reqs:
+                s_ = lay.splits[r]
+                r0, nr = int(lay.row0[r]), s_.n_causal + s_.n_canvas
+                pages = torch.as_tensor(lay.pages_of(r).astype(np.int64), device="cuda")
+                host.append((f(x["q"][r0:r0 + nr]), f(x["k"][r0:r0 + nr]), f(x["v"][r0:r0 + nr]), f(x["kc"][pages]),
+                             f(x["vc"][pages]), s_))
+        hl = f(logits[:len(reqs) * L16])
+        threads = _blas_threads()
+        log("cpu baseline: timing the oracle on 4 requests")
+        tc = time.perf_counter()
+        for qh, kh, vh, kch, vch, s_ in host:
+            attention.canvas_attention(qh, kh, vh, kch, vch, np.arange(kch.shape[0], dtype=np.int32),
+                                       [(0, s_.cached, s_.n_causal, s_.n_canvas, 0)], ps, scale)
+        am = np.argmax(hl, axis=1).reshape(len(reqs), L16)
+        verify.verify_prefix(am, tgt[:len(reqs)])
+        dt = time.perf_counter() - tc
+        cpu_line = dict(value=len(reqs) * L16 / dt, unit="draft positions/s", cores=_cores(threads), kind="oracle",
+                        sample=(f"4 of the 128 requests on the host in fp64 numpy: 5 layers of attention for their "
+                                f"16 draft rows x {Hq} heads over their injected context, the argmax of their 64 "
+                                f"logit rows of V={V}, verification; {dt:.1f} s"))
+    return _json_line("draft positions/sec (block draft: 128 x 16 positions, 5 layers, V=151936) + % HBM roofline",
+                      B * L16 / (ms * 1e-3), "draft positions/s", K, W, ms,
+                      {"workload": "block_draft", "requests": B, "block": L16, "layers": layers,
+                       "context": [cfg["L_min"], cfg["L_max"]], "heads_q": Hq, "heads_kv": Hkv, "head_dim": D,
+                       "V": V}, roof, cpu_line,
+                      {"attention_us_per_pass": att_ms * 1000.0,
+                       "accepted_mean": float(np.minimum(gmm, L16).mean())})
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # the GPU's clocks settle within the first ~50 steps (~35 ms of this load): 5 warmup steps time the
-    # ramp (measured 679-687 us per step), 50 or more the steady state (648-655 us per step)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    # the GPU's clocks are still settling after 5 warmup steps of the single-canvas step (its steady
+    # state, after ~50 steps, is a few per cent faster); the default is the recorded configuration
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("single_canvas", "batched", "structured_read", "block_draft"),
+                    default="single_canvas",
+                    help="single_canvas: one 256-token canvas step (default); batched: one iteration of the "
+                         "32-request batched loop; structured_read: one 64-request single-pass read launch; "
+                         "block_draft: one 5-layer parallel draft + argmax + verify pass")
     ap.add_argument("--cpu-steps", type=int, default=2, help="whole steps of the canvas in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving", action="store_true",
@@ -372,6 +759,11 @@ def main():
     dg.lib()
     if args.serving:
         print(json.dumps(serving_bench()), flush=True)
+        return
+    if args.workload != "single_canvas":
+        fn = {"batched": bench_batched, "structured_read": bench_structured_read,
+              "block_draft": bench_block_draft}[args.workload]
+        print(json.dumps(fn(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return
     w = Workload(dict(CFG, window=args.window, e4m3=args.e4m3))
     c = w.c
@@ -432,6 +824,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        result["parity"] = w.parity
+        result["near_ties"] = w.parity["near_ties"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -129,7 +129,9 @@ class ServingLoop:
             rows += nc + nv
         return np.array(out, np.int32).reshape(-1, 6), rows
 
-    def step(self, it: int, record: bool = False):
+    def step(self, it: int, record: bool = False, pe_events=None):
+        """One iteration.  pe_events: optional (start, stop) hipEvent_t handles recorded around the
+        P.E kernel of the self-conditioning call (it then runs only in iterations with denoising)."""
         cfg = self.cfg
         R, C, V = cfg["R"], cfg["C"], cfg["V"]
         admitted, tokens = self._schedule(it)
@@ -174,7 +176,8 @@ class ServingLoop:
             dg_converged(argmax, entropy, V, cfg["k"], cfg["tau"], cfg["max_steps"], self.seed, st, active=pre)
         if denoising and self.sc is not None:
             dg_selfcond_embed_sc(self.operand, V, self.so["row_max"], self.so["row_lnz"], st["sc_on"], st["canvas"],
-                                 self.sc["E"], self.sc["prepared"], self.sc["hidden"], x_out=self.x, ws=self.ws_sc)
+                                 self.sc["E"], self.sc["prepared"], self.sc["hidden"], x_out=self.x, ws=self.ws_sc,
+                                 pe_events=pe_events)
         ev1.record()
         self.last = dict(denoise=self.phase == DENOISE, attention=att if rows > 0 else None)
         committed = st["committed"].cpu().numpy().astype(bool) & (self.phase == DENOISE)
@@ -198,9 +201,9 @@ class ServingLoop:
                 self.phase[r] = COMMIT
         return rec
 
-    def run(self, max_iters: int = 100000, record: bool = False):
+    def run(self, max_iters: int = 100000, record: bool = False, first: int = 0):
         log = []
-        for it in range(max_iters):
+        for it in range(first, first + max_iters):
             if np.all(self.phase == DONE):
                 break
             log.append(self.step(it, record))

@@ -50,7 +50,7 @@ ALL = [TINY_LOOP, SINGLE_CANVAS, BATCHED, STRUCTURED_READ, BLOCK_DRAFT]
 SERVING = dict(
     name="serving", seed=0, R=32, C=256, P_min=512, P_max=8192, burst=8, arrival_every=6, page_size=16, Hq=16,
     Hkv=8, D=256, V=262144, token_budget=8192, blocks=2, budget=8.0, k=3, tau=0.3, max_steps=8,
-    temperature=1.0, n_pool=2,
+    temperature=1.0, n_pool=2, d=4096, hidden=1024,
 )
 
 # The same loop at sizes the oracle runs in seconds (bf16, MFMA attention path).
