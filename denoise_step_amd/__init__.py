@@ -23,7 +23,8 @@ __all__ = [
     "dg_selfcond_operand_bytes", "dg_denoise_sample_sc", "dg_selfcond_ws_bytes_sc", "dg_selfcond_embed_sc",
     "dg_deficit_admit", "dg_e4m3_decode", "dg_selfcond_prepared_bytes_e4m3", "dg_selfcond_prepare_e4m3",
     "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3", "dg_denoise_sample_noalloc",
-    "dg_denoise_sample_noalloc_max_bytes",
+    "dg_denoise_sample_noalloc_max_bytes", "dg_lmhead_ws_bytes", "dg_lmhead_operand_bytes",
+    "dg_lmhead_denoise_sample", "dg_selfcond_embed_lm",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -66,6 +67,12 @@ _SIGS = {
                                     _p, _sz, _p]),
     "dg_selfcond_ws_bytes_sc": (_sz, [_i32, _i32, _i32, _i32]),
     "dg_selfcond_embed_sc": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz,
+                                    _p, _p, _p]),
+    "dg_lmhead_ws_bytes": (_sz, [_i32, _i32, _i32]),
+    "dg_lmhead_operand_bytes": (_sz, [_i32, _i32]),
+    "dg_lmhead_denoise_sample": (_i32, [_p, _i64, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _f32, _p, _p, _p, _p,
+                                        _p, _p, _sz, _p, _sz, _p]),
+    "dg_selfcond_embed_lm": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz,
                                     _p, _p, _p]),
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
     "dg_verify_prefix": (_i32, [_p, _p, _i32, _i32, _p, _p]),
@@ -351,6 +358,56 @@ def dg_selfcond_embed_sc(sc_operand, V, row_max, row_lnz, sc_on, canvas, E, prep
     _check(lib().dg_selfcond_embed_sc(_ptr(sc_operand), _ptr(row_max), _ptr(row_lnz), _ptr(sc_on), _ptr(canvas), B,
                                       C, _ptr(E), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
                                       _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_sc")
+    return x_out
+
+
+def dg_lmhead_ws_bytes(rows, V, d) -> int:
+    return int(lib().dg_lmhead_ws_bytes(rows, V, d))
+
+
+def dg_lmhead_operand_bytes(rows, V) -> int:
+    return int(lib().dg_lmhead_operand_bytes(rows, V))
+
+
+def dg_lmhead_denoise_sample(h, E, scale, rows_per_req, seed, step, temperature=1.0, active=None, out=None, ws=None,
+                             operand=None, stream=None):
+    """The LM head logits = scale h E^T fused with the sampler (h [rows][d] and E [V][d] bf16); returns
+    (outputs, operand) with the operand for dg_selfcond_embed_lm."""
+    rows, ldh = h.shape
+    V, d = E.shape
+    dev = h.device
+    if out is None:
+        out = dict(argmax=torch.empty(rows, dtype=torch.int32, device=dev),
+                   entropy=torch.empty(rows, dtype=torch.float32, device=dev),
+                   sample=torch.empty(rows, dtype=torch.int32, device=dev),
+                   row_max=torch.empty(rows, dtype=torch.float32, device=dev),
+                   row_lnz=torch.empty(rows, dtype=torch.float32, device=dev))
+    nb = dg_lmhead_ws_bytes(rows, V, d)
+    ws = _ws(nb, ws, dev)
+    ob = dg_lmhead_operand_bytes(rows, V)
+    operand = _ws(ob, operand, dev)
+    g = out.get
+    _check(lib().dg_lmhead_denoise_sample(_ptr(h), ldh, _ptr(E), rows, V, d, float(scale), rows_per_req, _ptr(seed),
+                                          _ptr(step), _ptr(active), float(temperature), _ptr(g("entropy")),
+                                          _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")),
+                                          _ptr(g("row_lnz")), _ptr(ws), nb, _ptr(operand), ob, _stream(stream)),
+           "dg_lmhead_denoise_sample")
+    return out, operand
+
+
+def dg_selfcond_embed_lm(lm_operand, V, row_max, row_lnz, sc_on, canvas, E, prepared, hidden, x_out=None,
+                         s_out=None, y_out=None, ws=None, stream=None, pe_events=None):
+    """dg_selfcond_embed on the operand written by dg_lmhead_denoise_sample."""
+    B, C = canvas.shape
+    rows = B * C
+    d = E.shape[1]
+    x_out = torch.empty((rows, d), dtype=E.dtype, device=E.device) if x_out is None else x_out
+    nb = dg_selfcond_ws_bytes_sc(rows, V, d, hidden)
+    ws = _ws(nb, ws, E.device)
+    ev0, ev1 = (None, None) if pe_events is None else (int(pe_events[0]), int(pe_events[1]))
+    _check(lib().dg_selfcond_embed_lm(_ptr(lm_operand), _ptr(row_max), _ptr(row_lnz), _ptr(sc_on), _ptr(canvas), B,
+                                      C, _ptr(E), _ptr(prepared), V, d, hidden, _ptr(x_out), _ptr(s_out),
+                                      _ptr(y_out), _ptr(ws), nb, ev0, ev1, _stream(stream)), "dg_selfcond_embed_lm")
     return x_out
 
 

@@ -157,6 +157,54 @@ DG_DEV void dpp_wave_argmax(float& v, int32_t& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// ---------------------------------------------------------------- softmax state and Gumbel keys
+// Online softmax state in base 2 relative to a reference m (the running maximum in a streaming
+// pass): Z = sum 2^(x2 - m), S = sum 2^(x2 - m) (x2 - m), x2 = x log2(e).
+struct SoftState {
+  float m, Z, S;
+};
+
+DG_DEV float exp2f_fast(float d) { return __builtin_amdgcn_exp2f(d); }
+
+// merge b into a (each relative to its own reference); Z == 0 marks an empty state
+DG_DEV void soft_merge(SoftState& a, SoftState b) {
+  if (b.Z == 0.f) return;
+  if (a.Z == 0.f) {
+    a = b;
+    return;
+  }
+  const float m = fmaxf(a.m, b.m);
+  const float da = a.m - m, db = b.m - m;
+  const float fa = exp2f_fast(da), fb = exp2f_fast(db);
+  a.S = fa * (a.S + da * a.Z) + fb * (b.S + db * b.Z);
+  a.Z = fa * a.Z + fb * b.Z;
+  a.m = m;
+}
+
+// Softmax state of the whole wave: every lane's (Z, S) rescaled to the wave's largest reference, then summed.
+DG_DEV SoftState dpp_wave_soft(SoftState s) {
+  const float M = dpp_wave_max(s.m);
+  float Z = 0.f, S = 0.f;
+  if (s.Z != 0.f) {
+    const float d = s.m - M;
+    const float f = exp2f_fast(d);
+    Z = f * s.Z;
+    S = f * (s.S + d * s.Z);
+  }
+  return SoftState{M, dpp_wave_sum(Z), dpp_wave_sum(S)};
+}
+
+// Gumbel-max key in log2 units.  With u = (2a + 1) 2^-24 (a = w >> 9, exact in fp32),
+// g = -ln(-ln u) and x2 = x log2(e):
+//   (x + g) log2(e) = x2 - log2(-log2 u) - log2(ln 2),
+// so argmax (x + g) = argmax (x2 - log2(-log2 u)) (a positive rescale and a shift).
+// Both logs are the hardware base-2 logarithm on normal inputs (u >= 2^-24, -log2 u >= 2^-24 / ln 2).
+DG_DEV float gumbel_key2(float x2, uint32_t w) {
+  const float u = fmaf(static_cast<float>(w >> 9), 0x1.0p-23f, 0x1.0p-24f);
+  const float L = -__builtin_amdgcn_logf(u);
+  return x2 - __builtin_amdgcn_logf(L);
+}
+
 // ---------------------------------------------------------------- OCP E4M3 (FP8) codes
 // Conversions by gfx950's instructions; exact, since every E4M3 value is an fp16 (and fp32) value.
 // Byte b of a word holds element b.

@@ -49,6 +49,7 @@ struct GemmArgs {
   int64_t ldb;        // rows of Bt (N)
   const uint8_t* Bt8; // E4M3 right operand (gemm_f16_e4m3_splitk_kernel), same blocked layout in bytes
   float* part;  // [splits][M][N]
+  const int8_t* a_exp;  // scaled left operand (gemm_f16_scaled_splitk_kernel): exponents [tiles][lda]
   int32_t M, N, K;
   int32_t kchunk;  // K per split (multiple of kGemmStages * kGemmTK)
   int32_t mtiles, ntiles, splits;
@@ -165,16 +166,24 @@ DG_DEV void gemm_read(const _Float16* __restrict__ as, const _Float16* __restric
   }
 }
 
+typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
+
 // MFMA half-step: the wave's 128 x (TN / 4) block, 4 x (TN / 128) accumulators of 32 x 32, both 16-K steps.
-template <int TN>
+// BF16: the fragments hold bf16 bit patterns (v_mfma_f32_32x32x16_bf16), else fp16.
+template <int TN, bool BF16 = false>
 DG_DEV void gemm_mfma(const GemmFrag<TN>& f, floatx16 (&acc)[4][TN / 128]) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < TN / 128; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN / 128; ++j) {
+        if constexpr (BF16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_g, f.a[ks][i]),
+                                                              __builtin_bit_cast(bf16x8_g, f.b[ks][j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
+      }
 }
 
 // vector-memory instructions a wave issues per stage
@@ -208,17 +217,118 @@ DG_DEV void gemm_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
+// Operand source of the main loop for the K-blocked operands of GemmArgs: issue(s, as, bs) starts
+// the copies of stage s (K offset s * kGemmTK of the workgroup's range) into the given LDS buffers;
+// fix(f, s) adjusts the fragments of stage s after their LDS read (nothing here).
+template <int TN, bool BF8>
+struct GemmSrc {
+  const GemmArgs& g;
+  int m0, n0, k_begin;
+  uint32_t off, off8;
+  int wave;
+  DG_DEV void issue(int s, _Float16* as, _Float16* bs) const {
+    gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, as, bs);
+  }
+  DG_DEV void fix(GemmFrag<TN>&, int) const {}
+};
+
+// Left operand scaled per (row, vocabulary tile) by an exact power of two: fragment rows of stage s
+// are multiplied by 2^e with e = exps[tile(s)][row], the tile of a K offset o inside the split being
+// 32 (o / 8192) + (o mod 2048) / 64 (the id-to-tile map of the LM-head tiles, whose 256 ids are four
+// runs of 64 spaced 2048 apart inside an 8192-id group).  exps holds the split's 64 tiles x 256 rows
+// in LDS.
+template <int TN>
+struct GemmScaledSrc : GemmSrc<TN, false> {
+  const int8_t* exps;
+  int wm, lane;
+  DG_DEV void fix(GemmFrag<TN>& f, int s) const {
+    const int8_t* e = exps + (32 * (s >> 8) + ((s & 63) >> 1)) * kGemmTM + wm + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 sc = static_cast<_Float16>(ldexpf(1.f, e[32 * i]));  // exact; 0 below 2^-25
+      f.a[0][i] = f.a[0][i] * sc;
+      f.a[1][i] = f.a[1][i] * sc;
+    }
+  }
+};
+
+// The main loop over nstage stages of K into acc (zeroed here).
 // PP: ping-pong schedule (long K loops); otherwise all eight waves read and multiply each stage
 // together between one barrier per stage (short K loops, where the ping-pong's extra barriers and
 // its staggered start cost more than they hide).
-template <int TN, bool BF8, bool PP>
+template <int TN, bool BF8, bool PP, bool BF16, class Src>
+DG_DEV void gemm_main(const Src& src, int nstage, _Float16* As, _Float16* Bs, int wm, int wn, int lane, int group,
+                      floatx16 (&acc)[4][TN / 128]) {
+  constexpr int NJ = TN / 128;
+  constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
+  constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  GemmFrag<TN> f;
+
+  if constexpr (!PP) {
+    // iteration s: wait for stage s, barrier (stage s visible; every wave is past MFMA(s - 1), so
+    // that stage's buffer may be refilled), issue stage s + 3, read and multiply stage s
+    const int pro = min(kGemmStages - 1, nstage);
+    for (int s = 0; s < pro; ++s) src.issue(s, As + s * kAs, Bs + s * kBs);
+    for (int s = 0; s < nstage; ++s) {
+      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, nstage - 1 - s));
+      gemm_barrier();
+      if (s + kGemmStages - 1 < nstage) {
+        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
+        src.issue(s + kGemmStages - 1, As + nb * kAs, Bs + nb * kBs);
+      }
+      const int buf = s & (kGemmStages - 1);
+      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
+      src.fix(f, s);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them to their uses)
+      gemm_mfma<TN, BF16>(f, acc);
+    }
+  } else {
+    const int pro = min(kGemmStages, nstage);
+    for (int s = 0; s < pro; ++s) src.issue(s, As + s * kAs, Bs + s * kBs);
+    gemm_vmwait<TN, BF8>(pro - 1);
+    gemm_barrier();
+    // Every wave runs read(s) | barrier | MFMA(s) | barrier; group 1 starts one barrier late (and
+    // group 0 ends one barrier late), so between two barriers one group reads while the other
+    // multiplies.  Stage s + 3 refills the buffer of stage s - 1, which both groups have read (and
+    // waited for) before the barrier that precedes this half-step.  Before its barrier each wave
+    // waits for its own copies of stage s + 1, which the next read half-step needs.
+    if (group == 1) gemm_barrier();
+    for (int s = 0; s < nstage; ++s) {
+      const int buf = s & (kGemmStages - 1);
+      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
+      src.fix(f, s);
+      if (s >= 1 && s + kGemmStages - 1 < nstage) {
+        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
+        src.issue(s + kGemmStages - 1, As + nb * kAs, Bs + nb * kBs);
+      }
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, max(0, nstage - 2 - s)));
+      gemm_barrier();
+      gemm_mfma<TN, BF16>(f, acc);
+      gemm_barrier();
+    }
+    if (group == 0) gemm_barrier();
+  }
+}
+
+// The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
+// SCALED: the left operand is scaled per (row, tile) by the exponents g.a_exp (GemmScaledSrc), one
+// split per 16384 ids of K.
+template <int TN, bool BF8, bool PP, bool SCALED = false>
 DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
   constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
+  constexpr int kExp = SCALED ? 64 * kGemmTM : 16;            // exponent bytes of a split's tiles
   __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
+  __shared__ __attribute__((aligned(16))) int8_t Xs[kExp];
   // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
@@ -235,64 +345,20 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int group = wave >> 2;  // one wave of each group per SIMD
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
-  const uint32_t off = gemm_lane_offset();
-  const uint32_t off8 = BF8 ? gemm_lane_offset8() : 0u;
+  const GemmSrc<TN, BF8> base{g, m0, n0, k_begin, gemm_lane_offset(), BF8 ? gemm_lane_offset8() : 0u, wave};
 
   floatx16 acc[4][NJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  GemmFrag<TN> f;
-
-  if constexpr (!PP) {
-    // iteration s: wait for stage s, barrier (stage s visible; every wave is past MFMA(s - 1), so
-    // that stage's buffer may be refilled), issue stage s + 3, read and multiply stage s
-    const int pro = min(kGemmStages - 1, nstage);
-    for (int s = 0; s < pro; ++s)
-      gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
-    for (int s = 0; s < nstage; ++s) {
-      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, nstage - 1 - s));
-      gemm_barrier();
-      if (s + kGemmStages - 1 < nstage) {
-        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
-        gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
-                            Bs + nb * kBs);
-      }
-      const int buf = s & (kGemmStages - 1);
-      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them to their uses)
-      gemm_mfma<TN>(f, acc);
+  if constexpr (SCALED) {
+    // the split's 64 tiles x 256 rows of exponents (16 bytes per load), before any copy is issued
+    for (int q = threadIdx.x; q < 64 * kGemmTM / 16; q += kGemmThreads) {
+      const int tl = q / (kGemmTM / 16), r16 = q % (kGemmTM / 16);
+      *reinterpret_cast<uint4*>(Xs + tl * kGemmTM + 16 * r16) =
+          *reinterpret_cast<const uint4*>(g.a_exp + (static_cast<int64_t>(split) * 64 + tl) * g.lda + m0 + 16 * r16);
     }
+    __syncthreads();
+    gemm_main<TN, BF8, PP, false>(GemmScaledSrc<TN>{base, Xs, wm, lane}, nstage, As, Bs, wm, wn, lane, group, acc);
   } else {
-    const int pro = min(kGemmStages, nstage);
-    for (int s = 0; s < pro; ++s)
-      gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, As + s * kAs, Bs + s * kBs);
-    gemm_vmwait<TN, BF8>(pro - 1);
-    gemm_barrier();
-    // Every wave runs read(s) | barrier | MFMA(s) | barrier; group 1 starts one barrier late (and
-    // group 0 ends one barrier late), so between two barriers one group reads while the other
-    // multiplies.  Stage s + 3 refills the buffer of stage s - 1, which both groups have read (and
-    // waited for) before the barrier that precedes this half-step.  Before its barrier each wave
-    // waits for its own copies of stage s + 1, which the next read half-step needs.
-    if (group == 1) gemm_barrier();
-    for (int s = 0; s < nstage; ++s) {
-      const int buf = s & (kGemmStages - 1);
-      gemm_read<TN, BF8>(As + buf * kAs, Bs + buf * kBs, wm, wn, lane, f);
-      if (s >= 1 && s + kGemmStages - 1 < nstage) {
-        const int nb = (s + kGemmStages - 1) & (kGemmStages - 1);
-        gemm_issue<TN, BF8>(g, m0, n0, k_begin + (s + kGemmStages - 1) * kGemmTK, off, off8, wave, As + nb * kAs,
-                            Bs + nb * kBs);
-      }
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
-      gemm_vmwait<TN, BF8>(min(kGemmStages - 2, max(0, nstage - 2 - s)));
-      gemm_barrier();
-      gemm_mfma<TN>(f, acc);
-      gemm_barrier();
-    }
-    if (group == 0) gemm_barrier();
+    gemm_main<TN, BF8, PP, false>(base, nstage, As, Bs, wm, wn, lane, group, acc);
   }
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
@@ -316,9 +382,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
   gemm_splitk_body<TN, false, ROLE == 0>(g);
 }
 
-// P.E against an E4M3 embedding table (N a multiple of 256): the E stream is one byte per element.
-__global__ __launch_bounds__(kGemmThreads) void gemm_f16_e4m3_splitk_kernel(GemmArgs g) {
-  gemm_splitk_body<256, true, true>(g);
+// P.E from the operand of the fused LM head (kchunk 16384, exponents in g.a_exp).
+template <int TN>
+__global__ __launch_bounds__(kGemmThreads) void gemm_f16_scaled_splitk_kernel(GemmArgs g) {
+  gemm_splitk_body<TN, false, true, true>(g);
 }
 
 struct GemmPlan {
@@ -357,8 +424,9 @@ inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk
 }
 
 inline GemmArgs gemm_args(const _Float16* A, int64_t lda, const _Float16* Bt, int64_t ldb, float* part, int32_t M,
-                          int32_t N, int32_t K, const GemmPlan& p, const uint8_t* Bt8 = nullptr) {
-  return GemmArgs{A, lda, Bt, ldb, Bt8, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
+                          int32_t N, int32_t K, const GemmPlan& p, const uint8_t* Bt8 = nullptr,
+                          const int8_t* a_exp = nullptr) {
+  return GemmArgs{A, lda, Bt, ldb, Bt8, part, a_exp, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
 }
 
 }  // namespace dg

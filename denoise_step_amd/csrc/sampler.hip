@@ -51,52 +51,6 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 32, "partial layout");
 
-// Online softmax state in base 2: m = max x2, Z = sum 2^(x2 - m), S = sum 2^(x2 - m) (x2 - m).
-struct SoftState {
-  float m, Z, S;
-};
-
-DG_DEV float exp2f_fast(float d) { return __builtin_amdgcn_exp2f(d); }
-
-// merge b into a (both relative to their own max); Z == 0 marks an empty state
-DG_DEV void soft_merge(SoftState& a, SoftState b) {
-  if (b.Z == 0.f) return;
-  if (a.Z == 0.f) {
-    a = b;
-    return;
-  }
-  const float m = fmaxf(a.m, b.m);
-  const float da = a.m - m, db = b.m - m;
-  const float fa = exp2f_fast(da), fb = exp2f_fast(db);
-  a.S = fa * (a.S + da * a.Z) + fb * (b.S + db * b.Z);
-  a.Z = fa * a.Z + fb * b.Z;
-  a.m = m;
-}
-
-// Softmax state of the whole wave: every lane's (Z, S) rescaled to the wave's max, then summed.
-DG_DEV SoftState dpp_wave_soft(SoftState s) {
-  const float M = dpp_wave_max(s.m);
-  float Z = 0.f, S = 0.f;
-  if (s.Z != 0.f) {
-    const float d = s.m - M;
-    const float f = exp2f_fast(d);
-    Z = f * s.Z;
-    S = f * (s.S + d * s.Z);
-  }
-  return SoftState{M, dpp_wave_sum(Z), dpp_wave_sum(S)};
-}
-
-// Gumbel-max key in log2 units.  With u = (2a + 1) 2^-24 (a = w >> 9, exact in fp32),
-// g = -ln(-ln u) and x2 = x log2(e):
-//   (x + g) log2(e) = x2 - log2(-log2 u) - log2(ln 2),
-// so argmax (x + g) = argmax (x2 - log2(-log2 u)) (a positive rescale and a shift).
-// Both logs are the hardware base-2 logarithm on normal inputs (u >= 2^-24, -log2 u >= 2^-24 / ln 2).
-DG_DEV float gumbel_key2(float x2, uint32_t w) {
-  const float u = fmaf(static_cast<float>(w >> 9), 0x1.0p-23f, 0x1.0p-24f);
-  const float L = -__builtin_amdgcn_logf(u);
-  return x2 - __builtin_amdgcn_logf(L);
-}
-
 // value of the neighbouring lane (lane ^ 1), one DPP move
 DG_DEV float pair_swap(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));

@@ -33,6 +33,11 @@ constexpr float kProbScale = 32768.0f;  // 2^15
 
 int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
 
+// P.E against an E4M3 embedding table (N a multiple of 256): the E stream is one byte per element.
+__global__ __launch_bounds__(kGemmThreads) void gemm_f16_e4m3_splitk_kernel(GemmArgs g) {
+  gemm_splitk_body<256, true, true>(g);
+}
+
 // ---------------------------------------------------------------- prepare
 // dst = fp16(src^T) placed at rows row_off .. row_off + N - 1 of a K-blocked operand with R rows:
 // element (row_off + n, k) = src[k][n] for k < K (rows of src), zero for K <= k < Kp.
@@ -150,13 +155,27 @@ DG_DEV void store4_f16(_Float16* dst, int r, int n, int64_t Mp, float4 v, float 
 constexpr int kReduceThreads = 1024;
 // With sc_ref (the operand written by the sampling pass), split k's probabilities are relative to
 // 2^ref[r][k] instead of the row max, so its partial is weighted by 2^(ref[r][k] - row_max log2 e).
+// Operand of the fused LM head (lm.w != nullptr): its values are relative to a power of two per
+// 256-id tile, so a row's largest probability carries up to 2^-11 relative rounding, where the
+// sampling pass's operand holds it exactly (2^15); the term of the argmax id i* is replaced by its
+// exact value: s += (2^15 - g w~ 2^e) E[i*] in operand units, with w~ the stored value, e its tile's
+// exponent and g its split's weight.
+struct LmTop {
+  const _Float16* w;  // operand [Kp / 32][Mp][32]
+  const int8_t* exps; // [tiles][Mp]
+  const int32_t* top; // [rows]
+  const uint16_t* E;  // [V][N] bf16
+  int32_t V;
+};
+
 template <int C>
 __global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* __restrict__ part, int32_t splits, int32_t M,
                                                         int32_t N, int64_t Mp, const float* __restrict__ row_max,
                                                         const float* __restrict__ row_lnz,
                                                         const float* __restrict__ sc_ref, int32_t nchunk,
                                                         float e_scale, float* __restrict__ s_out,
-                                                        _Float16* __restrict__ s16, float* __restrict__ s_inv) {
+                                                        _Float16* __restrict__ s16, float* __restrict__ s_inv,
+                                                        LmTop lm) {
   __shared__ float red[kReduceThreads / kWave];
   const int r = blockIdx.x;
   const float f = (e_scale / kProbScale) * __expf(-row_lnz[r]);
@@ -164,6 +183,22 @@ __global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* 
   float4 acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (lm.w != nullptr && lm.top[r] >= 0 && lm.top[r] < lm.V) {  // out of range only for non-finite logits
+    const int64_t i = lm.top[r];
+    const int64_t t = 32 * (i >> 13) + ((i & 2047) >> 6);  // the LM-head tile of id i
+    const float wt = static_cast<float>(lm.w[((i >> 5) * Mp + r) * 32 + (i & 31)]);
+    const float g = exp2f(sc_ref[static_cast<int64_t>(r) * nchunk + (i >> 14)] - m2);
+    const float coef = kProbScale - g * ldexpf(wt, lm.exps[t * Mp + r]);
+    const uint16_t* er = lm.E + i * N;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int n = 4 * (threadIdx.x + kReduceThreads * c);
+      if (n < N) {
+        const uint2 e = *reinterpret_cast<const uint2*>(er + n);
+        acc[c] = make_float4(coef * bf16_lo(e.x), coef * bf16_hi(e.x), coef * bf16_lo(e.y), coef * bf16_hi(e.y));
+      }
+    }
+  }
 #pragma unroll 8
   for (int k = 0; k < splits; ++k) {
     const float* p = part + (static_cast<int64_t>(k) * M + r) * N;
@@ -410,7 +445,8 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
                              int32_t rows, int32_t C, const void* E, const _Float16* et, const _Float16* wgu,
                              const _Float16* wd, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,
                              float* y_out, char* wsb, void* pe_start, void* pe_stop, hipStream_t s,
-                             const uint8_t* et8 = nullptr, float e_scale = 1.f) {
+                             const uint8_t* et8 = nullptr, float e_scale = 1.f, const int8_t* a_exp = nullptr,
+                             const int32_t* top = nullptr) {
   const int64_t rows64 = rows;
   auto* part = reinterpret_cast<float*>(wsb + p.off_part);
   auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
@@ -421,17 +457,25 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
   if (et8 != nullptr)
     gemm_f16_e4m3_splitk_kernel<<<p.pe.grid, kGemmThreads, 0, s>>>(
         gemm_args(w, p.Mp, nullptr, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, et8));
+  else if (a_exp != nullptr && p.pe.tn == 256)
+    gemm_f16_scaled_splitk_kernel<256><<<p.pe.grid, kGemmThreads, 0, s>>>(
+        gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, nullptr, a_exp));
+  else if (a_exp != nullptr)
+    gemm_f16_scaled_splitk_kernel<128><<<p.pe.grid, kGemmThreads, 0, s>>>(
+        gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, nullptr, a_exp));
   else
     launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
   const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
+  const LmTop lm = a_exp != nullptr ? LmTop{w, a_exp, top, reinterpret_cast<const uint16_t*>(E), V}
+                                     : LmTop{nullptr, nullptr, nullptr, nullptr, 0};
   if (rc == 1)
     pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
-                                                        nchunk, e_scale, s_out, s16, s_inv);
+                                                        nchunk, e_scale, s_out, s16, s_inv, lm);
   else
     pe_reduce_kernel<2><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
-                                                        nchunk, e_scale, s_out, s16, s_inv);
+                                                        nchunk, e_scale, s_out, s16, s_inv, lm);
   DG_LAUNCHED();
   launch_gemm<1>(p.g1, gemm_args(s16, p.Mp, wgu, 2 * hidden, part, rows, 2 * hidden, d, p.g1), s);
   DG_LAUNCHED();
@@ -626,6 +670,33 @@ extern "C" dg_status dg_selfcond_embed_sc(const void* sc_operand, const float* r
   const int32_t nchunk = static_cast<int32_t>(cdiv(V, kScChunk));
   return selfcond_bf16_tail(p, w, ref, nchunk, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden,
                             x_out, s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop, as_stream(stream));
+}
+
+extern "C" dg_status dg_selfcond_embed_lm(const void* lm_operand, const float* row_max, const float* row_lnz,
+                                          const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C,
+                                          const void* E, const void* prepared, int32_t V, int32_t d, int32_t hidden,
+                                          void* x_out, float* s_out, float* y_out, void* ws, size_t ws_bytes,
+                                          void* pe_start, void* pe_stop, dg_stream_t stream) {
+  DG_ARG(lm_operand && row_max && row_lnz && sc_on && canvas && E && prepared && x_out);
+  DG_ARG(B > 0 && C > 0 && V > 0 && d > 0 && hidden > 0);
+  DG_UNSUP(V % 16 == 0 && d % 128 == 0 && hidden % 128 == 0 && d <= 8192 && hidden <= 8192);
+  const int64_t rows64 = static_cast<int64_t>(B) * C;
+  DG_ARG(rows64 <= 65535);
+  const int32_t rows = static_cast<int32_t>(rows64);
+  const Bf16Plan p = bf16_plan(rows, V, d, hidden, true);
+  DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
+  const PreparedLayout L = prepared_layout(V, d, hidden);
+  const char* pb = reinterpret_cast<const char*>(prepared);
+  const auto* et = reinterpret_cast<const _Float16*>(pb + L.off_et);
+  const auto* wgu = reinterpret_cast<const _Float16*>(pb + L.off_wgu);
+  const auto* wd = reinterpret_cast<const _Float16*>(pb + L.off_wd);
+  const LmOperandLayout O = lm_operand_layout(rows, V);
+  const char* ob = reinterpret_cast<const char*>(lm_operand);
+  return selfcond_bf16_tail(p, reinterpret_cast<const _Float16*>(ob), reinterpret_cast<const float*>(ob + O.off_ref),
+                            O.nrun, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden, x_out,
+                            s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop, as_stream(stream), nullptr,
+                            1.f, reinterpret_cast<const int8_t*>(ob + O.off_exp),
+                            reinterpret_cast<const int32_t*>(ob + O.off_top));
 }
 
 extern "C" size_t dg_selfcond_prepared_bytes_e4m3(int32_t V, int32_t d, int32_t hidden) {

@@ -359,3 +359,31 @@ def batched_loop_start(cfg: dict, sched: dict) -> dict:
     R = cfg["R"]
     r = np.arange(R, dtype=np.int64)
     return dict(cached=sched["prompt"].copy(), step_in_block=(2 * r) % cfg["max_steps"], step_global=2 * r + 1)
+
+
+# ---------------------------------------------------------------- LM-head inputs
+# A hidden state with a planted direction: h_r = a_r E[t_r] + b n_r with a_r ~ U[0, a_max],
+# t_r uniform over the vocabulary and n_r ~ N(0, I), rounded to bf16.  With E ~ N(0, 1/64) the
+# logit of t_r stands about a_r d / 64 above the others, whose spread is about
+# sqrt(a_r^2 d / 4096 + b^2 d / 64): rows range from diffuse (a_r ~ 0) to peaked.
+
+def lmhead_hidden_bf16(seed: int, tag, E_bits: np.ndarray, rows: int, a_max: float, b: float) -> np.ndarray:
+    """h [rows][d] as bf16 bits from the bf16 table E_bits [V][d] (numpy)."""
+    g = rng_for(seed, tag, "h")
+    V, d = E_bits.shape
+    a = g.random(rows) * a_max
+    t = g.integers(0, V, rows)
+    h = a[:, None] * bf16_bits_to_f32(E_bits[t]).astype(np.float64) + b * g.standard_normal((rows, d))
+    return f32_to_bf16_bits(h.astype(np.float32))
+
+
+def lmhead_hidden_torch(seed: int, tag, E, rows: int, a_max: float, b: float):
+    """The same recipe drawn with torch's device generator from a device bf16 table E [V][d]."""
+    import torch
+    g = _torch_gen(seed, (tag, "h") if not isinstance(tag, tuple) else tag + ("h",), E.device)
+    V, d = E.shape
+    a = torch.rand(rows, generator=g, device=E.device) * a_max
+    t = torch.randint(0, V, (rows,), generator=g, device=E.device)
+    n = torch.randn((rows, d), generator=g, device=E.device)
+    return (a[:, None] * E[t].float() + b * n).to(torch.bfloat16)
+

@@ -70,3 +70,17 @@ BATCHED_LOOP = dict(
     Hkv=8, D=256, V=262144, token_budget=8192, blocks=2, budget=8.0, k=3, tau=0.3, max_steps=64,
     temperature=1.0, n_pool=2, d=4096, hidden=1024,
 )
+
+# The LM head fused with the sampler (logits = scale h E^T never stored): h from
+# synth.lmhead_hidden_*, E ~ N(0, 1/64) bf16.  Small: two requests of 20 rows over a vocabulary of
+# 16464 ids (two P.E runs, the second ragged, and LM-head tiles past V) with d = 256.  Full: the
+# single canvas (256 rows, V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096).
+LMHEAD_SMALL = dict(
+    name="lmhead_small", seed=0, B=2, C=20, V=16464, d=256, hidden=128, scale=4.0, a_max=1.5, b=0.125,
+    temperature=0.8, e_std=1.0 / 8.0, w_std=0.5,
+)
+
+LMHEAD = dict(
+    name="lmhead_single_canvas", seed=0, B=1, C=256, V=262144, d=4096, hidden=1024, scale=1.0, a_max=0.4, b=0.125,
+    temperature=1.0, e_std=1.0 / 8.0, w_std=0.02,
+)

@@ -12,7 +12,7 @@ def pytest_configure(config):
 
 
 TIE_CLASSES = ("argmax_gap", "gumbel_key_gap", "budget", "mean_entropy", "accept_cut", "allowed_argmax",
-               "tiny_loop_divergence", "serving_divergence")
+               "tiny_loop_divergence", "serving_divergence", "lmhead_argmax_gap", "lmhead_key_gap")
 
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):

@@ -84,6 +84,30 @@ def test_fused_operand_entry_points_validate(L):
     assert L.dg_selfcond_ws_bytes_sc(256, 262144, 4096, 1024) > 0
 
 
+def test_lmhead_entry_points_validate(L):
+    # h, ldh, E, rows, V, d, scale, rows_per_req, seed, step, active, T, 5 outputs, ws, ws_bytes, operand, bytes, stream
+    call = lambda V=16384, d=256, scale=1.0, rows=32, rpr=16, ldh=256, wsb=1 << 30, opb=1 << 30, h=64: \
+        L.dg_lmhead_denoise_sample(h, ldh, 64, rows, V, d, scale, rpr, 64, 64, None, 1.0, 64, 64, 64, 64, 64, 64,
+                                   wsb, 64, opb, None)
+    assert call(h=None) == -1
+    assert call(V=16392) == -2                   # V % 16 != 0
+    assert call(d=200, ldh=200) == -2            # d % 128 != 0
+    assert call(scale=0.0) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(rpr=5) == -1                     # rows % rows_per_req != 0
+    assert call(ldh=128) == -1                   # ldh < d
+    assert call(ldh=260) == -2                   # ldh % 8 != 0
+    assert call(wsb=1) == -3
+    assert call(opb=1) == -3
+    assert L.dg_lmhead_ws_bytes(256, 262144, 4096) >= 256 * 4096 * 2 + 256 * 1024 * 32
+    assert L.dg_lmhead_operand_bytes(256, 262144) >= L.dg_selfcond_operand_bytes(256, 262144) + 1024 * 256
+    emb = lambda op=64, V=1024, wsb=1 << 30: L.dg_selfcond_embed_lm(op, 64, 64, 64, 64, 1, 16, 64, 64, V, 128, 128,
+                                                                    64, None, None, 64, wsb, None, None, None)
+    assert emb(op=None) == -1
+    assert emb(V=1000) == -2
+    assert emb(wsb=1) == -3
+
+
 def test_workspace_sizes(L):
     assert L.dg_denoise_sample_ws_bytes(256, 262144) == 256 * 4 * 32      # 4 chunks of 65536 logits per row
     assert L.dg_selfcond_ws_bytes(256, 262144, 4096, 1024, 1) >= 256 * 262144 * 2
