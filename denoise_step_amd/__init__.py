@@ -24,7 +24,8 @@ __all__ = [
     "dg_deficit_admit", "dg_e4m3_decode", "dg_selfcond_prepared_bytes_e4m3", "dg_selfcond_prepare_e4m3",
     "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3", "dg_denoise_sample_noalloc",
     "dg_denoise_sample_noalloc_max_bytes", "dg_lmhead_ws_bytes", "dg_lmhead_operand_bytes",
-    "dg_lmhead_denoise_sample", "dg_selfcond_embed_lm",
+    "dg_lmhead_denoise_sample", "dg_selfcond_embed_lm", "dg_lmhead_prepared_bytes", "dg_lmhead_prepare",
+    "dg_lmhead_denoise_sample_traced",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -70,8 +71,12 @@ _SIGS = {
                                     _p, _p, _p]),
     "dg_lmhead_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "dg_lmhead_operand_bytes": (_sz, [_i32, _i32]),
+    "dg_lmhead_prepared_bytes": (_sz, [_i32, _i32]),
+    "dg_lmhead_prepare": (_i32, [_p, _i32, _i32, _p, _sz, _p]),
     "dg_lmhead_denoise_sample": (_i32, [_p, _i64, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _f32, _p, _p, _p, _p,
                                         _p, _p, _sz, _p, _sz, _p]),
+    "dg_lmhead_denoise_sample_traced": (_i32, [_p, _i64, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _f32, _p, _p,
+                                               _p, _p, _p, _p, _sz, _p, _sz, _p, _p, _p]),
     "dg_selfcond_embed_lm": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz,
                                     _p, _p, _p]),
     "dg_allowed_probs": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p]),
@@ -369,12 +374,26 @@ def dg_lmhead_operand_bytes(rows, V) -> int:
     return int(lib().dg_lmhead_operand_bytes(rows, V))
 
 
-def dg_lmhead_denoise_sample(h, E, scale, rows_per_req, seed, step, temperature=1.0, active=None, out=None, ws=None,
-                             operand=None, stream=None):
-    """The LM head logits = scale h E^T fused with the sampler (h [rows][d] and E [V][d] bf16); returns
-    (outputs, operand) with the operand for dg_selfcond_embed_lm."""
-    rows, ldh = h.shape
+def dg_lmhead_prepared_bytes(V, d) -> int:
+    return int(lib().dg_lmhead_prepared_bytes(V, d))
+
+
+def dg_lmhead_prepare(E, prepared=None, stream=None):
+    """The table E [V][d] bf16 re-laid for dg_lmhead_denoise_sample (uint8 device buffer)."""
     V, d = E.shape
+    nb = dg_lmhead_prepared_bytes(V, d)
+    prepared = _ws(nb, prepared, E.device)
+    _check(lib().dg_lmhead_prepare(_ptr(E), V, d, _ptr(prepared), nb, _stream(stream)), "dg_lmhead_prepare")
+    return prepared
+
+
+def dg_lmhead_denoise_sample(h, prepared, V, scale, rows_per_req, seed, step, temperature=1.0, active=None, out=None,
+                             ws=None, operand=None, stream=None, events=None):
+    """The LM head logits = scale h E^T fused with the sampler (h [rows][d] bf16, prepared from
+    dg_lmhead_prepare); returns (outputs, operand) with the operand for dg_selfcond_embed_lm.
+    events: optional (start, stop) hipEvent_t handles recorded around the fused LM-head kernel."""
+    rows, ldh = h.shape
+    d = ldh
     dev = h.device
     if out is None:
         out = dict(argmax=torch.empty(rows, dtype=torch.int32, device=dev),
@@ -387,11 +406,12 @@ def dg_lmhead_denoise_sample(h, E, scale, rows_per_req, seed, step, temperature=
     ob = dg_lmhead_operand_bytes(rows, V)
     operand = _ws(ob, operand, dev)
     g = out.get
-    _check(lib().dg_lmhead_denoise_sample(_ptr(h), ldh, _ptr(E), rows, V, d, float(scale), rows_per_req, _ptr(seed),
-                                          _ptr(step), _ptr(active), float(temperature), _ptr(g("entropy")),
-                                          _ptr(g("argmax")), _ptr(g("sample")), _ptr(g("row_max")),
-                                          _ptr(g("row_lnz")), _ptr(ws), nb, _ptr(operand), ob, _stream(stream)),
-           "dg_lmhead_denoise_sample")
+    ev0, ev1 = (None, None) if events is None else (int(events[0]), int(events[1]))
+    _check(lib().dg_lmhead_denoise_sample_traced(_ptr(h), ldh, _ptr(prepared), rows, V, d, float(scale), rows_per_req,
+                                                 _ptr(seed), _ptr(step), _ptr(active), float(temperature),
+                                                 _ptr(g("entropy")), _ptr(g("argmax")), _ptr(g("sample")),
+                                                 _ptr(g("row_max")), _ptr(g("row_lnz")), _ptr(ws), nb, _ptr(operand),
+                                                 ob, ev0, ev1, _stream(stream)), "dg_lmhead_denoise_sample_traced")
     return out, operand
 
 

@@ -29,15 +29,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 // Operand written by dg_lmhead_denoise_sample (dg_lmhead_operand_bytes) and read by
-// dg_selfcond_embed_lm: w [Kp / 32][Mp][32] fp16 and ref [rows][nrun] f32 as in the
-// self-conditioning operand of the sampling pass (one run per 16384 ids), then the per-tile
-// exponents [64 nrun][Mp] int8 (tile t of the LM head covers ids 8192 (t / 32) + 64 (t % 32) +
-// 2048 j + [0, 64), j = 0..3; run k holds tiles 64 k .. 64 k + 63), then each row's argmax id
-// [rows] i32 (its probability enters P.E exactly).
+// dg_selfcond_embed_lm: the self-conditioning operand of the sampling pass (w [Kp / 32][Mp][32]
+// fp16, then ref [rows][nrun] f32, one run per 16384 ids, the refs integers here), then each
+// row's argmax id [rows] i32.
 struct LmOperandLayout {
   int64_t Mp, Kp;
   int32_t nrun;
-  size_t off_ref, off_exp, off_top, bytes;
+  size_t off_ref, off_top, bytes;
 };
 
 inline LmOperandLayout lm_operand_layout(int32_t rows, int32_t V) {
@@ -46,8 +44,7 @@ inline LmOperandLayout lm_operand_layout(int32_t rows, int32_t V) {
   L.Kp = cdiv(V, 128) * 128;
   L.nrun = static_cast<int32_t>(cdiv(V, 16384));
   L.off_ref = round_up(static_cast<size_t>(L.Mp) * L.Kp * 2, 256);
-  L.off_exp = round_up(L.off_ref + static_cast<size_t>(rows) * L.nrun * 4, 256);
-  L.off_top = round_up(L.off_exp + static_cast<size_t>(64) * L.nrun * L.Mp, 256);
+  L.off_top = round_up(L.off_ref + static_cast<size_t>(rows) * L.nrun * 4, 256);
   L.bytes = round_up(L.off_top + static_cast<size_t>(rows) * 4, 256);
   return L;
 }

@@ -49,7 +49,6 @@ struct GemmArgs {
   int64_t ldb;        // rows of Bt (N)
   const uint8_t* Bt8; // E4M3 right operand (gemm_f16_e4m3_splitk_kernel), same blocked layout in bytes
   float* part;  // [splits][M][N]
-  const int8_t* a_exp;  // scaled left operand (gemm_f16_scaled_splitk_kernel): exponents [tiles][lda]
   int32_t M, N, K;
   int32_t kchunk;  // K per split (multiple of kGemmStages * kGemmTK)
   int32_t mtiles, ntiles, splits;
@@ -232,26 +231,6 @@ struct GemmSrc {
   DG_DEV void fix(GemmFrag<TN>&, int) const {}
 };
 
-// Left operand scaled per (row, vocabulary tile) by an exact power of two: fragment rows of stage s
-// are multiplied by 2^e with e = exps[tile(s)][row], the tile of a K offset o inside the split being
-// 32 (o / 8192) + (o mod 2048) / 64 (the id-to-tile map of the LM-head tiles, whose 256 ids are four
-// runs of 64 spaced 2048 apart inside an 8192-id group).  exps holds the split's 64 tiles x 256 rows
-// in LDS.
-template <int TN>
-struct GemmScaledSrc : GemmSrc<TN, false> {
-  const int8_t* exps;
-  int wm, lane;
-  DG_DEV void fix(GemmFrag<TN>& f, int s) const {
-    const int8_t* e = exps + (32 * (s >> 8) + ((s & 63) >> 1)) * kGemmTM + wm + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 sc = static_cast<_Float16>(ldexpf(1.f, e[32 * i]));  // exact; 0 below 2^-25
-      f.a[0][i] = f.a[0][i] * sc;
-      f.a[1][i] = f.a[1][i] * sc;
-    }
-  }
-};
-
 // The main loop over nstage stages of K into acc (zeroed here).
 // PP: ping-pong schedule (long K loops); otherwise all eight waves read and multiply each stage
 // together between one barrier per stage (short K loops, where the ping-pong's extra barriers and
@@ -318,17 +297,13 @@ DG_DEV void gemm_main(const Src& src, int nstage, _Float16* As, _Float16* Bs, in
 }
 
 // The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
-// SCALED: the left operand is scaled per (row, tile) by the exponents g.a_exp (GemmScaledSrc), one
-// split per 16384 ids of K.
-template <int TN, bool BF8, bool PP, bool SCALED = false>
+template <int TN, bool BF8, bool PP>
 DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
   constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
-  constexpr int kExp = SCALED ? 64 * kGemmTM : 16;            // exponent bytes of a split's tiles
   __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
-  __shared__ __attribute__((aligned(16))) int8_t Xs[kExp];
   // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
@@ -345,21 +320,11 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int group = wave >> 2;  // one wave of each group per SIMD
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
-  const GemmSrc<TN, BF8> base{g, m0, n0, k_begin, gemm_lane_offset(), BF8 ? gemm_lane_offset8() : 0u, wave};
 
   floatx16 acc[4][NJ];
-  if constexpr (SCALED) {
-    // the split's 64 tiles x 256 rows of exponents (16 bytes per load), before any copy is issued
-    for (int q = threadIdx.x; q < 64 * kGemmTM / 16; q += kGemmThreads) {
-      const int tl = q / (kGemmTM / 16), r16 = q % (kGemmTM / 16);
-      *reinterpret_cast<uint4*>(Xs + tl * kGemmTM + 16 * r16) =
-          *reinterpret_cast<const uint4*>(g.a_exp + (static_cast<int64_t>(split) * 64 + tl) * g.lda + m0 + 16 * r16);
-    }
-    __syncthreads();
-    gemm_main<TN, BF8, PP, false>(GemmScaledSrc<TN>{base, Xs, wm, lane}, nstage, As, Bs, wm, wn, lane, group, acc);
-  } else {
-    gemm_main<TN, BF8, PP, false>(base, nstage, As, Bs, wm, wn, lane, group, acc);
-  }
+  gemm_main<TN, BF8, PP, false>(GemmSrc<TN, BF8>{g, m0, n0, k_begin, gemm_lane_offset(),
+                                                  BF8 ? gemm_lane_offset8() : 0u, wave},
+                                nstage, As, Bs, wm, wn, lane, group, acc);
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
 #pragma unroll
@@ -382,11 +347,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs 
   gemm_splitk_body<TN, false, ROLE == 0>(g);
 }
 
-// P.E from the operand of the fused LM head (kchunk 16384, exponents in g.a_exp).
-template <int TN>
-__global__ __launch_bounds__(kGemmThreads) void gemm_f16_scaled_splitk_kernel(GemmArgs g) {
-  gemm_splitk_body<TN, false, true, true>(g);
-}
 
 struct GemmPlan {
   int32_t splits, kchunk, mtiles, ntiles, tn;
@@ -424,9 +384,8 @@ inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk
 }
 
 inline GemmArgs gemm_args(const _Float16* A, int64_t lda, const _Float16* Bt, int64_t ldb, float* part, int32_t M,
-                          int32_t N, int32_t K, const GemmPlan& p, const uint8_t* Bt8 = nullptr,
-                          const int8_t* a_exp = nullptr) {
-  return GemmArgs{A, lda, Bt, ldb, Bt8, part, a_exp, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
+                          int32_t N, int32_t K, const GemmPlan& p, const uint8_t* Bt8 = nullptr) {
+  return GemmArgs{A, lda, Bt, ldb, Bt8, part, M, N, K, p.kchunk, p.mtiles, p.ntiles, p.splits};
 }
 
 }  // namespace dg

@@ -10,17 +10,19 @@
 // ids inside the winning block words i & 3 of counter i >> 2 (stream 3).
 //
 // gfx950 design.  One workgroup per (256 rows, 256 ids) tile, the whole d contraction on
-// v_mfma_f32_32x32x16_bf16 with the pipeline and ping-pong schedule of the P.E GEMM: h is copied
-// once into the K-blocked layout (shared by every tile through L2), E is read as stored ([V][d]
-// rows; each 16-id group of a stage is 16 rows x 64 bytes, one direct global -> LDS copy).  A
-// tile's 256 ids are four runs of 64 ids spaced 2048 apart inside a group of 8192 ids: the 16
+// v_mfma_f32_32x32x16_bf16 with the pipeline and ping-pong schedule of the P.E GEMM.  Both operands
+// are bf16 in the K-blocked layout (h copied per call, E prepared once by dg_lmhead_prepare), so
+// each 16-id group of a stage is one contiguous kilobyte (the table as stored, [V][d], would give
+// 64-byte pieces 8 KB apart, which all workgroups fetch from the same few HBM channels at once).
+// A tile's 256 ids are four runs of 64 ids spaced 2048 apart inside a group of 8192 ids: the 16
 // Gumbel blocks of a row then share four Philox counters (one call per lane).  After the main loop
 // the tile's logits go through LDS, 128 rows at a time; four lanes per row then compute the tile's
 // partial softmax state (relative to ref = ceil of the tile's largest base-2 logit), argmax, best
 // Gumbel block and the draw inside that block, and write the fp16 operand w = 2^15 2^(x2 - ref).
 // A merge kernel combines a row's tiles and derives, per 16384-id run of P.E, the run's reference
-// R (the largest tile ref) and each tile's exponent ref - R, by which P.E scales the tile's
-// operand rows exactly (powers of two).
+// R (the largest tile ref) and each tile's exponent ref - R; a streaming pass then multiplies every
+// tile's operand values by 2^(ref - R) (exact), which leaves the operand of the sampling pass
+// (values relative to one reference per run) for the P.E GEMM.
 #include "dg_device.hpp"
 #include "dg_host.hpp"
 #include "gemm_f16.hpp"
@@ -46,7 +48,7 @@ static_assert(sizeof(LmPartial) == 32, "partial layout");
 struct LmArgs {
   const _Float16* hk;  // h as bf16 bit patterns, K-blocked with Mp rows
   int64_t Mp;
-  const uint16_t* E;   // [V][d] bf16
+  const _Float16* Ek;  // E as bf16 bit patterns, K-blocked with V rows
   int32_t rows, V, d;
   int64_t Kp;
   int32_t mtiles, ntiles;
@@ -70,27 +72,25 @@ __global__ __launch_bounds__(256) void lm_h_kblk_kernel(const uint16_t* __restri
   *reinterpret_cast<uint4*>(hk + kblk_index(r, k, Mp)) = v;
 }
 
-// Operand source of the LM-head main loop: A = hk (K-blocked), B = the tile's 256 rows of E.
-// 16-id group q of the tile holds ids id_base + 2048 (q / 4) + 16 (q % 4) + [0, 16); groups past V
-// read rows 0..15 instead (their logits are discarded).  Lane i of a copy fetches row i / 4 of the
-// group, 16-byte chunk (i % 4) ^ f(i / 4) of the stage's 64 bytes (the LDS swizzle of the GEMM).
+// Operand source of the LM-head main loop: A = hk, B = the tile's 256 rows of Ek (both K-blocked).
+// 16-id group q of the tile holds ids id_base + 2048 (q / 4) + 16 (q % 4) + [0, 16), one contiguous
+// kilobyte per stage; groups past V read ids 0..15 instead (their logits are discarded).
 struct LmSrc {
   const LmArgs& a;
   int m0;
   int64_t id_base;
-  uint32_t off_a, off_b;
+  uint32_t off;
   int wave;
   DG_DEV void issue(int s, _Float16* as, _Float16* bs) const {
     const int k0 = s * kGemmTK;
 #pragma unroll
     for (int i = 0; i < kGemmTM / 16 / kGemmWaves; ++i)
-      gemm_dma<false>(a.hk, a.Mp, m0, k0, off_a, as, wave + kGemmWaves * i);
+      gemm_dma<false>(a.hk, a.Mp, m0, k0, off, as, wave + kGemmWaves * i);
 #pragma unroll
     for (int i = 0; i < 256 / 16 / kGemmWaves; ++i) {
       const int q = wave + kGemmWaves * i;
       const int64_t id0 = id_base + 2048 * (q >> 2) + 16 * (q & 3);
-      const char* src = reinterpret_cast<const char*>(a.E) + ((id0 < a.V ? id0 : 0) * a.d + k0) * 2;
-      lds_copy16<true>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bs + q * kWave * 8)), src, off_b);
+      gemm_dma<true>(a.Ek, a.V, static_cast<int>(id0 < a.V ? id0 : 0), k0, off, bs + q * kWave * 8, 0);
     }
   }
   DG_DEV void fix(GemmFrag<256>&, int) const {}
@@ -235,13 +235,10 @@ __global__ __launch_bounds__(kGemmThreads) void lmhead_sample_kernel(LmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int group = wave >> 2;
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * 64;
-  const int lr = lane >> 2;
-  const uint32_t off_b =
-      static_cast<uint32_t>(lr * a.d * 2 + 16 * ((lane & 3) ^ gemm_swz(lr)));
 
   floatx16 acc[4][2];
-  gemm_main<256, false, true, true>(LmSrc{a, m0, id_base, gemm_lane_offset(), off_b, wave}, a.d / kGemmTK, As, Bs, wm,
-                                    wn, lane, group, acc);
+  gemm_main<256, false, true, true>(LmSrc{a, m0, id_base, gemm_lane_offset(), wave}, a.d / kGemmTK, As, Bs, wm, wn,
+                                    lane, group, acc);
 
   // Epilogue: the tile's logits through LDS in two halves of 128 rows.  The even waves hold rows
   // 0..127 (wm = 0): they store them and, four lanes per row, process them while the odd waves
@@ -319,10 +316,46 @@ __global__ __launch_bounds__(kWave) void lmhead_merge_kernel(const LmPartial* __
   }
 }
 
+// w *= 2^e per (row, LM-head tile), e = exps[tile][row] <= 0 (exact for powers of two, except that
+// values below fp16's normal range round), so that every value is relative to its run's reference.
+// Thread g covers 16 ids (32 bytes) of one row: K block g / (2 Mp), row (g / 2) % Mp, half g % 2, so
+// consecutive threads cover consecutive memory.  Tiles with e == 0 (the largest of each run) are
+// left as they are.
+__global__ __launch_bounds__(256) void lm_rescale_kernel(_Float16* __restrict__ w, int64_t Mp, int64_t Kp, int32_t rows,
+                                                         const int8_t* __restrict__ exps) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= Kp / 16 * Mp) return;
+  const int64_t kb = g / (2 * Mp);
+  const int64_t r = (g >> 1) % Mp;
+  if (r >= rows) return;
+  const int64_t id = kb * 32 + 16 * (g & 1);
+  const int e = exps[(32 * (id >> 13) + ((id & 2047) >> 6)) * Mp + r];
+  if (e == 0) return;
+  half8* p = reinterpret_cast<half8*>(w + (kb * Mp + r) * 32 + 16 * (g & 1));
+  const float sc = ldexpf(1.f, e);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    half8 v = p[k];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = static_cast<_Float16>(static_cast<float>(v[j]) * sc);
+    p[k] = v;
+  }
+}
+
+// E [V][d] bf16 -> Ek, K-blocked with V rows; 8 elements per thread.
+__global__ __launch_bounds__(256) void lm_prepare_kernel(const uint16_t* __restrict__ E, int32_t V, int32_t d,
+                                                         uint16_t* __restrict__ Ek) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= static_cast<int64_t>(V) * d) return;
+  const int64_t v = i / d;
+  const int32_t k = static_cast<int32_t>(i - v * d);
+  *reinterpret_cast<uint4*>(Ek + kblk_index(v, k, V)) = *reinterpret_cast<const uint4*>(E + i);
+}
+
 struct LmPlan {
   int64_t Mp, Kp;
   int32_t mtiles, ntiles;
-  size_t off_hk, off_part, bytes;
+  size_t off_hk, off_part, off_exp, bytes;
 };
 
 LmPlan lm_plan(int32_t rows, int32_t V, int32_t d) {
@@ -333,7 +366,9 @@ LmPlan lm_plan(int32_t rows, int32_t V, int32_t d) {
   p.ntiles = static_cast<int32_t>(32 * cdiv(V, 8192));
   p.off_hk = 0;
   p.off_part = round_up(static_cast<size_t>(p.Mp) * d * 2, 256);
-  p.bytes = round_up(p.off_part + static_cast<size_t>(rows) * p.ntiles * sizeof(LmPartial), 256);
+  p.off_exp = round_up(p.off_part + static_cast<size_t>(rows) * p.ntiles * sizeof(LmPartial), 256);
+  // exponents of 64 tiles per run (the last run may hold fewer LM-head tiles)
+  p.bytes = round_up(p.off_exp + static_cast<size_t>(64) * cdiv(V, 16384) * p.Mp, 256);
   return p;
 }
 
@@ -341,6 +376,22 @@ LmPlan lm_plan(int32_t rows, int32_t V, int32_t d) {
 }  // namespace dg
 
 using namespace dg;
+
+extern "C" size_t dg_lmhead_prepared_bytes(int32_t V, int32_t d) {
+  if (V <= 0 || d <= 0) return 0;
+  return static_cast<size_t>(V) * d * 2;
+}
+
+extern "C" dg_status dg_lmhead_prepare(const void* E, int32_t V, int32_t d, void* prepared, size_t prepared_bytes,
+                                       dg_stream_t stream) {
+  DG_ARG(E && prepared && V > 0 && d > 0);
+  DG_UNSUP(V % 16 == 0 && d % 128 == 0 && aligned16(E) && aligned16(prepared));
+  DG_REQUIRE(prepared_bytes >= dg_lmhead_prepared_bytes(V, d), DG_E_WORKSPACE);
+  lm_prepare_kernel<<<static_cast<unsigned>(cdiv(static_cast<int64_t>(V) * d / 8, 256)), 256, 0, as_stream(stream)>>>(
+      reinterpret_cast<const uint16_t*>(E), V, d, reinterpret_cast<uint16_t*>(prepared));
+  DG_LAUNCHED();
+  return DG_OK;
+}
 
 extern "C" size_t dg_lmhead_ws_bytes(int32_t rows, int32_t V, int32_t d) {
   if (rows <= 0 || V <= 0 || d <= 0) return 0;
@@ -352,17 +403,18 @@ extern "C" size_t dg_lmhead_operand_bytes(int32_t rows, int32_t V) {
   return lm_operand_layout(rows, V).bytes;
 }
 
-extern "C" dg_status dg_lmhead_denoise_sample(const void* h, int64_t ldh, const void* E, int32_t rows, int32_t V,
-                                              int32_t d, float scale, int32_t rows_per_req, const uint64_t* seed,
-                                              const int32_t* step, const uint8_t* active, float temperature,
-                                              float* entropy, int32_t* argmax, int32_t* sample, float* row_max,
-                                              float* row_lnz, void* ws, size_t ws_bytes, void* operand,
-                                              size_t operand_bytes, dg_stream_t stream) {
-  DG_ARG(h && E && seed && step && entropy && argmax && sample && row_max && row_lnz && operand);
+extern "C" dg_status dg_lmhead_denoise_sample_traced(const void* h, int64_t ldh, const void* prepared, int32_t rows,
+                                                     int32_t V, int32_t d, float scale, int32_t rows_per_req,
+                                                     const uint64_t* seed, const int32_t* step, const uint8_t* active,
+                                                     float temperature, float* entropy, int32_t* argmax,
+                                                     int32_t* sample, float* row_max, float* row_lnz, void* ws,
+                                                     size_t ws_bytes, void* operand, size_t operand_bytes,
+                                                     void* k_start, void* k_stop, dg_stream_t stream) {
+  DG_ARG(h && prepared && seed && step && entropy && argmax && sample && row_max && row_lnz && operand);
   DG_ARG(rows > 0 && V > 0 && d > 0 && rows_per_req > 0 && rows % rows_per_req == 0 && rows <= 65535 && ldh >= d);
   DG_ARG(scale > 0.f && scale < INFINITY && temperature > 0.f && temperature < INFINITY);
   DG_UNSUP(V % 16 == 0 && V <= (1 << 30) && d % 128 == 0 && d <= 16384);
-  DG_UNSUP(ldh % 8 == 0 && aligned16(h) && aligned16(E));
+  DG_UNSUP(ldh % 8 == 0 && aligned16(h) && aligned16(prepared));
   const LmPlan p = lm_plan(rows, V, d);
   const LmOperandLayout L = lm_operand_layout(rows, V);
   DG_REQUIRE(ws != nullptr && ws_bytes >= p.bytes, DG_E_WORKSPACE);
@@ -372,19 +424,35 @@ extern "C" dg_status dg_lmhead_denoise_sample(const void* h, int64_t ldh, const 
   char* ob = reinterpret_cast<char*>(operand);
   auto* hk = reinterpret_cast<uint16_t*>(wsb + p.off_hk);
   auto* part = reinterpret_cast<LmPartial*>(wsb + p.off_part);
+  auto* exps = reinterpret_cast<int8_t*>(wsb + p.off_exp);
+  auto* w = reinterpret_cast<_Float16*>(ob);
   lm_h_kblk_kernel<<<static_cast<unsigned>(cdiv(p.Mp * d / 8, 256)), 256, 0, s>>>(
       reinterpret_cast<const uint16_t*>(h), ldh, rows, d, p.Mp, hk);
   DG_LAUNCHED();
-  const LmArgs a{reinterpret_cast<const _Float16*>(hk), p.Mp, reinterpret_cast<const uint16_t*>(E), rows, V, d, p.Kp,
-                 p.mtiles, p.ntiles, scale * 1.4426950408889634f / temperature, rows_per_req, seed, step,
-                 reinterpret_cast<_Float16*>(ob), part};
+  const LmArgs a{reinterpret_cast<const _Float16*>(hk), p.Mp, reinterpret_cast<const _Float16*>(prepared), rows, V, d,
+                 p.Kp, p.mtiles, p.ntiles, scale * 1.4426950408889634f / temperature, rows_per_req, seed, step, w,
+                 part};
   const int64_t total = static_cast<int64_t>(p.mtiles) * p.ntiles;
+  if (k_start != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(k_start), s) == hipSuccess, DG_E_HIP);
   lmhead_sample_kernel<<<static_cast<unsigned>(cdiv(total, kGemmXcds) * kGemmXcds), kGemmThreads, 0, s>>>(a);
   DG_LAUNCHED();
+  if (k_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(k_stop), s) == hipSuccess, DG_E_HIP);
   lmhead_merge_kernel<<<rows, kWave, 0, s>>>(part, p.ntiles, L.nrun, V, p.Mp, rows_per_req, active, entropy, argmax,
-                                             sample, row_max, row_lnz, reinterpret_cast<float*>(ob + L.off_ref),
-                                             reinterpret_cast<int8_t*>(ob + L.off_exp),
+                                             sample, row_max, row_lnz, reinterpret_cast<float*>(ob + L.off_ref), exps,
                                              reinterpret_cast<int32_t*>(ob + L.off_top));
   DG_LAUNCHED();
+  lm_rescale_kernel<<<static_cast<unsigned>(cdiv(p.Kp / 16 * p.Mp, 256)), 256, 0, s>>>(w, p.Mp, p.Kp, rows, exps);
+  DG_LAUNCHED();
   return DG_OK;
+}
+
+extern "C" dg_status dg_lmhead_denoise_sample(const void* h, int64_t ldh, const void* prepared, int32_t rows, int32_t V,
+                                              int32_t d, float scale, int32_t rows_per_req, const uint64_t* seed,
+                                              const int32_t* step, const uint8_t* active, float temperature,
+                                              float* entropy, int32_t* argmax, int32_t* sample, float* row_max,
+                                              float* row_lnz, void* ws, size_t ws_bytes, void* operand,
+                                              size_t operand_bytes, dg_stream_t stream) {
+  return dg_lmhead_denoise_sample_traced(h, ldh, prepared, rows, V, d, scale, rows_per_req, seed, step, active,
+                                         temperature, entropy, argmax, sample, row_max, row_lnz, ws, ws_bytes, operand,
+                                         operand_bytes, nullptr, nullptr, stream);
 }

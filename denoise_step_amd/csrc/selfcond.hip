@@ -155,14 +155,13 @@ DG_DEV void store4_f16(_Float16* dst, int r, int n, int64_t Mp, float4 v, float 
 constexpr int kReduceThreads = 1024;
 // With sc_ref (the operand written by the sampling pass), split k's probabilities are relative to
 // 2^ref[r][k] instead of the row max, so its partial is weighted by 2^(ref[r][k] - row_max log2 e).
-// Operand of the fused LM head (lm.w != nullptr): its values are relative to a power of two per
-// 256-id tile, so a row's largest probability carries up to 2^-11 relative rounding, where the
-// sampling pass's operand holds it exactly (2^15); the term of the argmax id i* is replaced by its
-// exact value: s += (2^15 - g w~ 2^e) E[i*] in operand units, with w~ the stored value, e its tile's
-// exponent and g its split's weight.
+// Operand of the fused LM head (lm.w != nullptr): its values were written relative to an integer
+// power of two per 256-id tile and rescaled exactly to the run's integer reference, so a row's
+// largest probability carries up to 2^-11 relative rounding, where the sampling pass's operand
+// holds it exactly (2^15); the term of the argmax id i* is replaced by its exact value:
+// s += (2^15 - g w~) E[i*] in operand units, with w~ the stored value and g its split's weight.
 struct LmTop {
   const _Float16* w;  // operand [Kp / 32][Mp][32]
-  const int8_t* exps; // [tiles][Mp]
   const int32_t* top; // [rows]
   const uint16_t* E;  // [V][N] bf16
   int32_t V;
@@ -185,10 +184,9 @@ __global__ __launch_bounds__(kReduceThreads) void pe_reduce_kernel(const float* 
   for (int c = 0; c < C; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (lm.w != nullptr && lm.top[r] >= 0 && lm.top[r] < lm.V) {  // out of range only for non-finite logits
     const int64_t i = lm.top[r];
-    const int64_t t = 32 * (i >> 13) + ((i & 2047) >> 6);  // the LM-head tile of id i
     const float wt = static_cast<float>(lm.w[((i >> 5) * Mp + r) * 32 + (i & 31)]);
     const float g = exp2f(sc_ref[static_cast<int64_t>(r) * nchunk + (i >> 14)] - m2);
-    const float coef = kProbScale - g * ldexpf(wt, lm.exps[t * Mp + r]);
+    const float coef = kProbScale - g * wt;
     const uint16_t* er = lm.E + i * N;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -445,8 +443,7 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
                              int32_t rows, int32_t C, const void* E, const _Float16* et, const _Float16* wgu,
                              const _Float16* wd, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,
                              float* y_out, char* wsb, void* pe_start, void* pe_stop, hipStream_t s,
-                             const uint8_t* et8 = nullptr, float e_scale = 1.f, const int8_t* a_exp = nullptr,
-                             const int32_t* top = nullptr) {
+                             const uint8_t* et8 = nullptr, float e_scale = 1.f, const int32_t* lm_top = nullptr) {
   const int64_t rows64 = rows;
   auto* part = reinterpret_cast<float*>(wsb + p.off_part);
   auto* s16 = reinterpret_cast<_Float16*>(wsb + p.off_s16);
@@ -457,19 +454,13 @@ dg_status selfcond_bf16_tail(const Bf16Plan& p, const _Float16* w, const float* 
   if (et8 != nullptr)
     gemm_f16_e4m3_splitk_kernel<<<p.pe.grid, kGemmThreads, 0, s>>>(
         gemm_args(w, p.Mp, nullptr, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, et8));
-  else if (a_exp != nullptr && p.pe.tn == 256)
-    gemm_f16_scaled_splitk_kernel<256><<<p.pe.grid, kGemmThreads, 0, s>>>(
-        gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, nullptr, a_exp));
-  else if (a_exp != nullptr)
-    gemm_f16_scaled_splitk_kernel<128><<<p.pe.grid, kGemmThreads, 0, s>>>(
-        gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe, nullptr, a_exp));
   else
     launch_gemm<0>(p.pe, gemm_args(w, p.Mp, et, d, part, rows, d, static_cast<int32_t>(p.Kp), p.pe), s);
   DG_LAUNCHED();
   if (pe_stop != nullptr) DG_REQUIRE(hipEventRecord(reinterpret_cast<hipEvent_t>(pe_stop), s) == hipSuccess, DG_E_HIP);
   const int rc = static_cast<int>(cdiv(d, 4 * kReduceThreads)), hc = static_cast<int>(cdiv(hidden, 1024));
-  const LmTop lm = a_exp != nullptr ? LmTop{w, a_exp, top, reinterpret_cast<const uint16_t*>(E), V}
-                                     : LmTop{nullptr, nullptr, nullptr, nullptr, 0};
+  const LmTop lm = lm_top != nullptr ? LmTop{w, lm_top, reinterpret_cast<const uint16_t*>(E), V}
+                                      : LmTop{nullptr, nullptr, nullptr, 0};
   if (rc == 1)
     pe_reduce_kernel<1><<<rows, kReduceThreads, 0, s>>>(part, p.pe.splits, rows, d, p.Mp, row_max, row_lnz, sc_ref,
                                                         nchunk, e_scale, s_out, s16, s_inv, lm);
@@ -695,8 +686,7 @@ extern "C" dg_status dg_selfcond_embed_lm(const void* lm_operand, const float* r
   return selfcond_bf16_tail(p, reinterpret_cast<const _Float16*>(ob), reinterpret_cast<const float*>(ob + O.off_ref),
                             O.nrun, row_max, row_lnz, sc_on, canvas, rows, C, E, et, wgu, wd, V, d, hidden, x_out,
                             s_out, y_out, reinterpret_cast<char*>(ws), pe_start, pe_stop, as_stream(stream), nullptr,
-                            1.f, reinterpret_cast<const int8_t*>(ob + O.off_exp),
-                            reinterpret_cast<const int32_t*>(ob + O.off_top));
+                            1.f, reinterpret_cast<const int32_t*>(ob + O.off_top));
 }
 
 extern "C" size_t dg_selfcond_prepared_bytes_e4m3(int32_t V, int32_t d, int32_t hidden) {

@@ -329,33 +329,49 @@ dg_status dg_selfcond_embed_sc(const void* sc_operand, const float* row_max, con
  * probability operand of the self-conditioning contraction (section
  * "Self-conditioning"), which dg_selfcond_embed_lm consumes.  The [rows][V]
  * logits are never written to memory.
- *   h [rows][ldh] bf16 (ldh >= d, ldh % 8 == 0, 16-byte aligned);
- *   E [V][d] bf16 row-major (16-byte aligned); V % 16 == 0, d % 128 == 0,
- *   d <= 16384; scale > 0, temperature > 0 (finite); rows <= 65535,
- *   rows % rows_per_req == 0; seed [rows / rows_per_req] u64, step i32 (the
- *   Gumbel noise of row r is keyed by (seed, r % rows_per_req, step) of its
- *   request); active [rows / rows_per_req] u8 or NULL: the five outputs of
- *   inactive requests' rows are not written (the operand covers every row).
+ * dg_lmhead_prepare: E [V][d] bf16 row-major -> `prepared`
+ *   (dg_lmhead_prepared_bytes(V, d) bytes, caller-owned, opaque: the table
+ *   re-laid for the kernel's copies), once per table.
+ * dg_lmhead_denoise_sample:
+ *   h [rows][ldh] bf16 (ldh >= d, ldh % 8 == 0, 16-byte aligned); prepared
+ *   from dg_lmhead_prepare; V % 16 == 0, d % 128 == 0, d <= 16384; scale > 0,
+ *   temperature > 0 (finite); rows <= 65535, rows % rows_per_req == 0;
+ *   seed [rows / rows_per_req] u64, step i32 (the Gumbel noise of row r is
+ *   keyed by (seed, r % rows_per_req, step) of its request); active
+ *   [rows / rows_per_req] u8 or NULL: the five outputs of inactive requests'
+ *   rows are not written (the operand covers every row).
  *   entropy, row_max, row_lnz [rows] f32; argmax, sample [rows] i32.
- * Workspace: dg_lmhead_ws_bytes(rows, V, d) bytes.  operand: caller-owned,
- * dg_lmhead_operand_bytes(rows, V) bytes, opaque (fp16 probabilities scaled
- * per 256-id tile by a power of two, with per-tile exponents and per-run
- * references).  Argmax ties resolve to the lowest id.  Not bitwise equal to
- * dg_denoise_sample on bf16-rounded logits: these logits keep fp32.
+ *   Workspace: dg_lmhead_ws_bytes(rows, V, d) bytes.  operand: caller-owned,
+ *   dg_lmhead_operand_bytes(rows, V) bytes, opaque (fp16 probabilities
+ *   relative to one power of two per 16384-id run, those references, each
+ *   row's argmax).  Argmax ties resolve to the lowest id.  Not bitwise equal
+ *   to dg_denoise_sample on bf16-rounded logits: these logits keep fp32.
+ * dg_lmhead_denoise_sample_traced: the same; when k_start / k_stop
+ *   (hipEvent_t) are non-NULL they are recorded on `stream` immediately before
+ *   and after the fused LM-head kernel, the call's dominant launch.
  * ------------------------------------------------------------------------ */
+size_t dg_lmhead_prepared_bytes(int32_t V, int32_t d);
+dg_status dg_lmhead_prepare(const void* E, int32_t V, int32_t d, void* prepared, size_t prepared_bytes,
+                            dg_stream_t stream);
 size_t dg_lmhead_ws_bytes(int32_t rows, int32_t V, int32_t d);
 size_t dg_lmhead_operand_bytes(int32_t rows, int32_t V);
-dg_status dg_lmhead_denoise_sample(const void* h, int64_t ldh, const void* E, int32_t rows, int32_t V, int32_t d,
-                                   float scale, int32_t rows_per_req, const uint64_t* seed, const int32_t* step,
-                                   const uint8_t* active, float temperature, float* entropy, int32_t* argmax,
-                                   int32_t* sample, float* row_max, float* row_lnz, void* ws, size_t ws_bytes,
-                                   void* operand, size_t operand_bytes, dg_stream_t stream);
+dg_status dg_lmhead_denoise_sample(const void* h, int64_t ldh, const void* prepared, int32_t rows, int32_t V,
+                                   int32_t d, float scale, int32_t rows_per_req, const uint64_t* seed,
+                                   const int32_t* step, const uint8_t* active, float temperature, float* entropy,
+                                   int32_t* argmax, int32_t* sample, float* row_max, float* row_lnz, void* ws,
+                                   size_t ws_bytes, void* operand, size_t operand_bytes, dg_stream_t stream);
+dg_status dg_lmhead_denoise_sample_traced(const void* h, int64_t ldh, const void* prepared, int32_t rows, int32_t V,
+                                          int32_t d, float scale, int32_t rows_per_req, const uint64_t* seed,
+                                          const int32_t* step, const uint8_t* active, float temperature,
+                                          float* entropy, int32_t* argmax, int32_t* sample, float* row_max,
+                                          float* row_lnz, void* ws, size_t ws_bytes, void* operand,
+                                          size_t operand_bytes, void* k_start, void* k_stop, dg_stream_t stream);
 
 /* dg_selfcond_embed_lm: dg_selfcond_embed_sc on the operand written by dg_lmhead_denoise_sample of
- * the same step (row_max / row_lnz are that call's outputs): s = softmax(x) E with each 256-id
- * tile's probabilities scaled exactly by its power of two inside the P.E kernel, then the gated MLP
- * and x_out = bf16(E[canvas] + (sc_on ? y : 0)).  V % 16 == 0; other arguments, the workspace
- * (dg_selfcond_ws_bytes_sc) and pe_start / pe_stop as in dg_selfcond_embed_sc. */
+ * the same step (row_max / row_lnz are that call's outputs): s = softmax(x) E (each row's largest
+ * probability entering exactly), then the gated MLP and x_out = bf16(E[canvas] + (sc_on ? y : 0)).
+ * E is the bf16 table [V][d]; prepared from dg_selfcond_prepare.  V % 16 == 0; other arguments,
+ * the workspace (dg_selfcond_ws_bytes_sc) and pe_start / pe_stop as in dg_selfcond_embed_sc. */
 dg_status dg_selfcond_embed_lm(const void* lm_operand, const float* row_max, const float* row_lnz,
                                const uint8_t* sc_on, const int32_t* canvas, int32_t B, int32_t C, const void* E,
                                const void* prepared, int32_t V, int32_t d, int32_t hidden, void* x_out, float* s_out,

@@ -100,7 +100,13 @@ def test_lmhead_entry_points_validate(L):
     assert call(wsb=1) == -3
     assert call(opb=1) == -3
     assert L.dg_lmhead_ws_bytes(256, 262144, 4096) >= 256 * 4096 * 2 + 256 * 1024 * 32
-    assert L.dg_lmhead_operand_bytes(256, 262144) >= L.dg_selfcond_operand_bytes(256, 262144) + 1024 * 256
+    assert L.dg_lmhead_operand_bytes(256, 262144) >= L.dg_selfcond_operand_bytes(256, 262144) + 256 * 4
+    assert L.dg_lmhead_prepared_bytes(262144, 4096) == 262144 * 4096 * 2
+    prep = lambda V=16384, d=256, nb=1 << 30, E=64: L.dg_lmhead_prepare(E, V, d, 64, nb, None)
+    assert prep(E=None) == -1
+    assert prep(V=100) == -2
+    assert prep(d=96) == -2
+    assert prep(nb=16) == -3
     emb = lambda op=64, V=1024, wsb=1 << 30: L.dg_selfcond_embed_lm(op, 64, 64, 64, 64, 1, 16, 64, 64, V, 128, 128,
                                                                     64, None, None, 64, wsb, None, None, None)
     assert emb(op=None) == -1

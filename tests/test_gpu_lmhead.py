@@ -67,7 +67,7 @@ def test_lmhead_small(B, C, V, d):
     steps = np.arange(B, dtype=np.int32) + 4
     scale, T = cfg["scale"] * 256 / d, cfg["temperature"]
     Et, ht, wgt, wut, wdt = (P.dev_bf16(a) for a in (E, h, wg, wu, wd))
-    st, op = dg.dg_lmhead_denoise_sample(ht, Et, scale, C, P.dev(seeds), P.dev(steps), T)
+    st, op = dg.dg_lmhead_denoise_sample(ht, dg.dg_lmhead_prepare(Et), V, scale, C, P.dev(seeds), P.dev(steps), T)
     prepared = dg.dg_selfcond_prepare(Et, wgt, wut, wdt)
     s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
     y_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
@@ -102,8 +102,8 @@ def test_lmhead_inactive_rows_untouched():
                entropy=P.dev(np.full(B * C, -7.0, np.float32)), row_max=P.dev(np.full(B * C, -7.0, np.float32)),
                row_lnz=P.dev(np.full(B * C, -7.0, np.float32)))
     seeds, steps = np.array([1, 2], np.int64), np.array([0, 0], np.int32)
-    dg.dg_lmhead_denoise_sample(P.dev_bf16(h), P.dev_bf16(E), 8.0, C, P.dev(seeds), P.dev(steps), 1.0,
-                                active=P.dev(np.array([0, 1], np.uint8)), out=out)
+    dg.dg_lmhead_denoise_sample(P.dev_bf16(h), dg.dg_lmhead_prepare(P.dev_bf16(E)), V, 8.0, C, P.dev(seeds),
+                                P.dev(steps), 1.0, active=P.dev(np.array([0, 1], np.uint8)), out=out)
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in out.items()}
     for k, v in got.items():
@@ -129,7 +129,8 @@ def test_lmhead_single_canvas_full_size_all_rows():
     canvas = P.dev(synth.rng_for(0, "single_canvas.canvas").integers(0, V, (1, C)).astype(np.int32))
     seeds, steps = np.array([11], np.int64), np.array([3], np.int32)
     on = P.dev(np.array([1], np.uint8))
-    st, op = dg.dg_lmhead_denoise_sample(h, E, cfg["scale"], C, P.dev(seeds), P.dev(steps), cfg["temperature"])
+    st, op = dg.dg_lmhead_denoise_sample(h, dg.dg_lmhead_prepare(E), V, cfg["scale"], C, P.dev(seeds), P.dev(steps),
+                                         cfg["temperature"])
     prepared = dg.dg_selfcond_prepare(E, wg, wu, wd)
     s_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
     y_out = torch.empty((C, d), dtype=torch.float32, device="cuda")
