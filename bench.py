@@ -12,6 +12,11 @@ logits of successive steps rotate through a pool of distinct sets (768 MiB,
 three times the 256 MB Infinity Cache) so that no step reads them from cache.
 The logits stand in for the LM head output of a real backbone.
 
+--workload single_canvas_lmhead runs the same step from the backbone's last hidden states h
+(256 x 4096 bf16): dg_lmhead_denoise_sample computes the LM head logits = h E^T on MFMA and
+samples them in the same kernel (the logits never reach HBM), and dg_selfcond_embed_lm runs P.E
+from its operand; its roofline is the fused LM-head kernel's (2 C V d FLOP per launch, bf16 MFMA).
+
 Prints ONE JSON line (see --help).  The P.E contraction kernel, the step's
 dominant launch, is timed with HIP events recorded around it on the launch
 stream over the whole timed region; its roofline fraction uses the algorithmic
@@ -35,13 +40,20 @@ METRIC = "canvas positions denoised/sec (C=256, V=262144) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 CFG = dict(B=1, C=256, L=2048, page_size=16, Hq=16, Hkv=8, D=256, V=262144, d=4096, hidden=1024, budget=8.0, k=3,
-           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0, e4m3=False)
+           tau=0.3, max_steps=64, temperature=1.0, pool=6, seed=0, window=0, e4m3=False, lmhead=False)
+# the LM-head variant: hidden states h = a E[t] + b n (a ~ U[0, 0.4], b = 1/8) and logits = h E^T
+LMHEAD = dict(scale=1.0, a_max=0.4, b=0.125)
+LM_KERNEL = "lmhead_sample_kernel"
 E4M3_SCALE = 2.0 ** -7      # the E4M3 table stores E / scale; E ~ N(0, 1) / 8 stays far inside +-448
 KV_SCALES = (2.0 ** -4, 2.0 ** -4)   # the E4M3 cache stores K / scale, V / scale (K, V ~ N(0, 1))
 PE_KERNEL = "gemm_f16_splitk_kernel<0>"
 PE_KERNEL_E4M3 = "gemm_f16_e4m3_splitk_kernel"
 PE_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp",)
+LM_SOURCES = ("denoise_step_amd/csrc/gemm_f16.hpp", "denoise_step_amd/csrc/lmhead.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pe_gemm_single_canvas_counters.json")
+LM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "lmhead_single_canvas_counters.json")
+METRIC_LMHEAD = ("canvas positions denoised/sec with the LM head in the step (C=256, V=262144, d=4096) "
+                 "+ % MFMA roofline")
 
 
 class HipEvents:
@@ -70,9 +82,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha() -> str:
+def source_sha(sources=PE_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in PE_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -92,6 +104,18 @@ def traffic_from_counters(per_launch_alg: int):
         rec = json.load(f)
     if rec.get("source_sha") != source_sha():
         return None                      # the kernel changed since the counters were taken
+    return int(rec["hbm_bytes_per_dispatch"])
+
+
+def lm_traffic_from_counters():
+    """HBM bytes per launch of the fused LM-head kernel from the committed counter summary, if it
+    matches the current sources."""
+    if not os.path.exists(LM_COUNTERS_FILE):
+        return None
+    with open(LM_COUNTERS_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(LM_SOURCES):
+        return None
     return int(rec["hbm_bytes_per_dispatch"])
 
 
@@ -126,7 +150,8 @@ class Workload:
         self.splits = torch.tensor([[0, L, 0, C, 0, c["window"]]], dtype=torch.int32, device=dev)
         # keys the canvas rows see together: the whole request, or the band of a sliding window
         self.key_span = L + C if c["window"] <= 0 else min(L + C, C + 2 * c["window"])
-        self.pool = [synth.zipf_logits_torch(s, ("bench.logits", i), C, V, dev) for i in range(c["pool"])]
+        if not c["lmhead"]:
+            self.pool = [synth.zipf_logits_torch(s, ("bench.logits", i), C, V, dev) for i in range(c["pool"])]
         self.wg = synth.normal_torch(s, "bench.wg", (d, h), 0.02, bf, dev)
         self.wu = synth.normal_torch(s, "bench.wu", (d, h), 0.02, bf, dev)
         self.wd = synth.normal_torch(s, "bench.wd", (h, d), 0.02, bf, dev)
@@ -138,6 +163,14 @@ class Workload:
             self.E = synth.normal_torch(s, "bench.E", (V, d), 1 / 8, bf, dev)
             log("preparing the fp16 operand copies")
             self.prepared = dg.dg_selfcond_prepare(self.E, self.wg, self.wu, self.wd)
+        if c["lmhead"]:
+            # the step starts from the backbone's last hidden states (one set per step of the pool)
+            self.hpool = [synth.lmhead_hidden_torch(s, ("bench.h", i), self.E, C, LMHEAD["a_max"], LMHEAD["b"])
+                          for i in range(c["pool"])]
+            log("preparing the LM-head layout of the table")
+            self.lm_prepared = dg.dg_lmhead_prepare(self.E)
+            self.ws_lm = torch.empty(dg.dg_lmhead_ws_bytes(C, V, d), dtype=torch.uint8, device=dev)
+            self.lm_operand = torch.empty(dg.dg_lmhead_operand_bytes(C, V), dtype=torch.uint8, device=dev)
         self.seed = torch.tensor([s], dtype=torch.int64, device=dev)
         z = lambda n, dt=torch.int32: torch.zeros(n, dtype=dt, device=dev)
         self.state = dict(prev_argmax=z((1, C)), unchanged=z(1), step_in_block=torch.full((1,), -1, dtype=torch.int32,
@@ -159,8 +192,9 @@ class Workload:
         self.scale = 1.0 / math.sqrt(D)
         torch.cuda.synchronize()
 
-    def step(self, t: int, ev=None, pe_ev=None):
-        """One denoise step.  ev: optional list of 6 events recorded between the calls."""
+    def step(self, t: int, ev=None, pe_ev=None, lm_ev=None):
+        """One denoise step.  ev: optional list of 6 events recorded between the calls; pe_ev / lm_ev:
+        hipEvent_t pairs recorded around the P.E and the fused LM-head kernels."""
         c, dg, s = self.c, self.dg, self.state
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
@@ -172,16 +206,25 @@ class Workload:
             dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
                                    c["C"], self.key_span, self.scale, out=self.att_out)
         rec(1)
-        logits = self.pool[t % len(self.pool)]
-        dg.dg_denoise_sample_sc(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"], out=self.so,
-                                ws=self.ws_s, sc_operand=self.sc_operand)
+        if c["lmhead"]:
+            dg.dg_lmhead_denoise_sample(self.hpool[t % len(self.hpool)], self.lm_prepared, c["V"], LMHEAD["scale"],
+                                        c["C"], self.seed, s["step_global"], c["temperature"], out=self.so,
+                                        ws=self.ws_lm, operand=self.lm_operand, events=lm_ev)
+        else:
+            logits = self.pool[t % len(self.pool)]
+            dg.dg_denoise_sample_sc(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"],
+                                    out=self.so, ws=self.ws_s, sc_operand=self.sc_operand)
         rec(2)
         dg.dg_entropy_accept(self.so["entropy"], self.so["sample"], s["canvas"], c["V"], c["budget"], self.seed,
                              s["step_global"], accept=self.accept, n_accept=self.n_accept)
         rec(3)
         dg.dg_converged(self.so["argmax"], self.so["entropy"], c["V"], c["k"], c["tau"], c["max_steps"], self.seed, s)
         rec(4)
-        if c["e4m3"]:
+        if c["lmhead"]:
+            dg.dg_selfcond_embed_lm(self.lm_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
+                                    s["canvas"], self.E, self.prepared, c["hidden"], x_out=self.x, ws=self.ws_sc,
+                                    pe_events=pe_ev)
+        elif c["e4m3"]:
             dg.dg_selfcond_embed_sc_e4m3(self.sc_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
                                          s["canvas"], self.E, E4M3_SCALE, self.prepared, c["hidden"], x_out=self.x,
                                          ws=self.ws_sc, pe_events=pe_ev)
@@ -247,14 +290,18 @@ def cpu_baseline(w: Workload, steps: int):
         kc, vc = f64(w.k_cache), f64(w.v_cache)
         E = w.E.float().cpu().numpy()
     pt = w.page_table.cpu().numpy()
-    pool = [f64(w.pool[t % len(w.pool)]) for t in range(steps)]
+    if c["lmhead"]:
+        from oracle import backbone
+        hpool = [f64(w.hpool[t % len(w.hpool)]) for t in range(steps)]
+    else:
+        pool = [f64(w.pool[t % len(w.pool)]) for t in range(steps)]
     wg, wu, wd = f64(w.wg), f64(w.wu), f64(w.wd)
     threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     log("cpu baseline: timing the oracle")
     oracle_samples = []
     t0 = time.perf_counter()
     for t in range(steps):
-        logits = pool[t]
+        logits = backbone.lm_head(hpool[t], E, LMHEAD["scale"]) if c["lmhead"] else pool[t]
         K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
         group = c["Hq"] // c["Hkv"]
         mask = attention.visibility_mask(c["L"], 0, C, c["window"])
@@ -272,10 +319,11 @@ def cpu_baseline(w: Workload, steps: int):
     dt = time.perf_counter() - t0
     cores = min(len(os.sched_getaffinity(0)), max(threads, 1))
     w.parity = sampler_parity(w, oracle_samples)
+    lm = f"the LM head h E^T ({C} x {c['d']} x {V}), " if c["lmhead"] else ""
     return dict(value=steps * C / dt, unit="positions/s", cores=cores, kind="oracle",
                 sample=(f"{steps} whole steps of the {C}-position canvas ({steps * C} positions) on the host in fp64 "
-                        f"numpy: attention for {C} rows x {c['Hq']} heads over {c['L'] + C} keys, the sampler over "
-                        f"{C} rows of V={V} (Philox Gumbel), accept + converged, P.E + MLP against the full "
+                        f"numpy: attention for {C} rows x {c['Hq']} heads over {c['L'] + C} keys, {lm}the sampler "
+                        f"over {C} rows of V={V} (Philox Gumbel), accept + converged, P.E + MLP against the full "
                         f"{V} x {c['d']} table; {dt:.1f} s"))
 
 
@@ -285,7 +333,8 @@ TIE_GAP, TOL_ENTROPY = 1e-5, 1e-3
 def sampler_parity(w: Workload, oracle_samples) -> dict:
     """The GPU sampler (the step's fused call) on the logits, seeds and steps of the oracle's timed
     sample, compared row by row: argmax and candidate bit-exact except near-ties (top-2 gap of the
-    logits or of the Gumbel keys below 1e-5, counted by class), entropy within 1e-3 nats."""
+    logits or of the Gumbel keys below 1e-5, or 1e-3 for the fused LM head, counted by class),
+    entropy within 1e-3 nats."""
     import numpy as np
     import torch
     dg, c = w.dg, w.c
@@ -293,19 +342,25 @@ def sampler_parity(w: Workload, oracle_samples) -> dict:
     ties = {"argmax_gap": 0, "gumbel_key_gap": 0}
     bad = {"argmax": 0, "sample": 0, "entropy": 0}
     worst_h = 0.0
+    # the fused LM head keeps fp32 logits (accumulation error ~2e-5 at |x| = 25): its tie band is 1e-3
+    gap = 1e-3 if c["lmhead"] else TIE_GAP
     for t, ref in enumerate(oracle_samples):
         step = torch.full((1,), 1 + t, dtype=torch.int32, device="cuda")
-        out, _ = dg.dg_denoise_sample_sc(w.pool[t % len(w.pool)], V, C, w.seed, step, c["temperature"])
+        if c["lmhead"]:
+            out, _ = dg.dg_lmhead_denoise_sample(w.hpool[t % len(w.hpool)], w.lm_prepared, V, LMHEAD["scale"], C,
+                                                 w.seed, step, c["temperature"])
+        else:
+            out, _ = dg.dg_denoise_sample_sc(w.pool[t % len(w.pool)], V, C, w.seed, step, c["temperature"])
         torch.cuda.synchronize()
         got = {k: v.cpu().numpy() for k, v in out.items()}
         for r in range(C):
             if got["argmax"][r] != ref.argmax[r]:
-                if 0 < ref.argmax_gap[r] < TIE_GAP:
+                if 0 < ref.argmax_gap[r] < gap:
                     ties["argmax_gap"] += 1
                 else:
                     bad["argmax"] += 1
             if got["sample"][r] != ref.sample[r]:
-                if ref.key_gap[r] < TIE_GAP:
+                if ref.key_gap[r] < gap:
                     ties["gumbel_key_gap"] += 1
                 else:
                     bad["sample"] += 1
@@ -441,6 +496,7 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
     torch.cuda.synchronize()
     hev = HipEvents()
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
+    lm_ev = [(hev.create(), hev.create()) for _ in range(K)] if lmhead else [None] * K
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"batched: timing {K} iterations")
     positions = 0
@@ -722,11 +778,13 @@ def main():
     # the GPU's clocks are still settling after 5 warmup steps of the single-canvas step (its steady
     # state, after ~50 steps, is a few per cent faster); the default is the recorded configuration
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("single_canvas", "batched", "structured_read", "block_draft"),
+    ap.add_argument("--workload", choices=("single_canvas", "single_canvas_lmhead", "batched", "structured_read",
+                                           "block_draft"),
                     default="single_canvas",
-                    help="single_canvas: one 256-token canvas step (default); batched: one iteration of the "
-                         "32-request batched loop; structured_read: one 64-request single-pass read launch; "
-                         "block_draft: one 5-layer parallel draft + argmax + verify pass")
+                    help="single_canvas: one 256-token canvas step (default); single_canvas_lmhead: the same step "
+                         "from the backbone's hidden states, the LM head fused with the sampler; batched: one "
+                         "iteration of the 32-request batched loop; structured_read: one 64-request single-pass "
+                         "read launch; block_draft: one 5-layer parallel draft + argmax + verify pass")
     ap.add_argument("--cpu-steps", type=int, default=2, help="whole steps of the canvas in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving", action="store_true",
@@ -760,12 +818,16 @@ def main():
     if args.serving:
         print(json.dumps(serving_bench()), flush=True)
         return
-    if args.workload != "single_canvas":
+    if args.workload not in ("single_canvas", "single_canvas_lmhead"):
         fn = {"batched": bench_batched, "structured_read": bench_structured_read,
               "block_draft": bench_block_draft}[args.workload]
         print(json.dumps(fn(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return
-    w = Workload(dict(CFG, window=args.window, e4m3=args.e4m3))
+    lmhead = args.workload == "single_canvas_lmhead"
+    if lmhead and (args.e4m3 or args.window):
+        print("the LM-head step runs with the bf16 table and full attention", file=sys.stderr)
+        sys.exit(2)
+    w = Workload(dict(CFG, window=args.window, e4m3=args.e4m3, lmhead=lmhead))
     c = w.c
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
@@ -774,6 +836,7 @@ def main():
     K = args.steps
     hev = HipEvents()
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
+    lm_ev = [(hev.create(), hev.create()) for _ in range(K)] if lmhead else [None] * K
     # events between the calls of every timed step (on the launch stream): per-call GPU time
     call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -782,7 +845,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record()
     for t in range(K):
-        w.step(args.warmup + t, ev=call_ev[t], pe_ev=pe_ev[t])
+        w.step(args.warmup + t, ev=call_ev[t], pe_ev=pe_ev[t], lm_ev=lm_ev[t])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -822,8 +885,26 @@ def main():
         "breakdown_us": brk,
         "kernels": kernels,
     }
+    if lmhead:
+        # the dominant kernel is the fused LM head: 2 C V d FLOP on bf16 MFMA per launch
+        lm_ms = sum(hev.elapsed_ms(a, b) for a, b in lm_ev) / K
+        lm_flop = 2.0 * positions * c["V"] * c["d"]
+        lm_tf = lm_flop / (lm_ms * 1e-3) / 1e12
+        result["metric"] = METRIC_LMHEAD
+        result["config"]["workload"] = "single_canvas_lmhead"
+        result["config"]["lm_head"] = {"scale": LMHEAD["scale"], "hidden": "a E[t] + b n, a ~ U[0, 0.4], b = 1/8"}
+        del result["config"]["logit_pool"]
+        result["roofline"] = {"kernel": LM_KERNEL, "bound": "mfma", "achieved": lm_tf, "peak": MFMA_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": lm_tf / MFMA_PEAK_TFLOPS,
+                              "traffic": lm_traffic_from_counters(),
+                              "algorithmic_flop_per_launch": lm_flop, "avg_launch_us": lm_ms * 1000.0,
+                              "source_sha": source_sha(LM_SOURCES)}
+        result["breakdown_us"]["lmhead_denoise_sample"] = result["breakdown_us"].pop("denoise_sample")
+        kernels["lmhead_sample_kernel"] = {"us": lm_ms * 1000.0, "bound": "mfma", "tflops": lm_tf,
+                                           "mfma_frac": lm_tf / MFMA_PEAK_TFLOPS}
+        del kernels["denoise_sample"]
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        result["cpu_baseline"] = cpu_baseline(w, 1 if lmhead else args.cpu_steps)
         result["parity"] = w.parity
         result["near_ties"] = w.parity["near_ties"]
     else:
