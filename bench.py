@@ -4,7 +4,7 @@
 One step = one pass of the whole hot path over one 256-token canvas
 (16 query / 8 KV heads, head_dim 256, 2048-token paged bf16 prefix,
 V = 262144, d = 4096, MLP 4096 -> 1024 -> 4096):
-    dg_canvas_attention -> dg_denoise_sample_sc -> dg_entropy_accept -> dg_converged -> dg_selfcond_embed_sc
+    dg_canvas_attention -> dg_denoise_sample_sc -> dg_accept_converged -> dg_selfcond_embed_sc
 (the sampling pass also writes the self-conditioning probability operand, so the logits are read
 once per step)
 Every input is synthetic and already resident in HBM when timing starts; the
@@ -193,7 +193,7 @@ class Workload:
         torch.cuda.synchronize()
 
     def step(self, t: int, ev=None, pe_ev=None, lm_ev=None):
-        """One denoise step.  ev: optional list of 6 events recorded between the calls; pe_ev / lm_ev:
+        """One denoise step.  ev: optional list of 5 events recorded between the calls; pe_ev / lm_ev:
         hipEvent_t pairs recorded around the P.E and the fused LM-head kernels."""
         c, dg, s = self.c, self.dg, self.state
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
@@ -215,11 +215,9 @@ class Workload:
             dg.dg_denoise_sample_sc(logits, c["V"], c["C"], self.seed, s["step_global"], c["temperature"],
                                     out=self.so, ws=self.ws_s, sc_operand=self.sc_operand)
         rec(2)
-        dg.dg_entropy_accept(self.so["entropy"], self.so["sample"], s["canvas"], c["V"], c["budget"], self.seed,
-                             s["step_global"], accept=self.accept, n_accept=self.n_accept)
+        dg.dg_accept_converged(self.so["entropy"], self.so["sample"], self.so["argmax"], c["V"], c["budget"], c["k"],
+                               c["tau"], c["max_steps"], self.seed, s, accept=self.accept, n_accept=self.n_accept)
         rec(3)
-        dg.dg_converged(self.so["argmax"], self.so["entropy"], c["V"], c["k"], c["tau"], c["max_steps"], self.seed, s)
-        rec(4)
         if c["lmhead"]:
             dg.dg_selfcond_embed_lm(self.lm_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
                                     s["canvas"], self.E, self.prepared, c["hidden"], x_out=self.x, ws=self.ws_sc,
@@ -232,7 +230,7 @@ class Workload:
             dg.dg_selfcond_embed_sc(self.sc_operand, c["V"], self.so["row_max"], self.so["row_lnz"], s["sc_on"],
                                     s["canvas"], self.E, self.prepared, c["hidden"], x_out=self.x, ws=self.ws_sc,
                                     pe_events=pe_ev)
-        rec(5)
+        rec(4)
 
 
 def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
@@ -259,8 +257,7 @@ def call_rooflines(brk: dict, pe_ms: float, c=CFG) -> dict:
         "pe_contraction": {"us": pe_ms * 1000.0, "bound": "hbm",
                            "gbs": pe_algorithmic_bytes(c) / (pe_ms * 1e-3) / 1e9,
                            "tflops": pe_flop / (pe_ms * 1e-3) / 1e12},
-        "entropy_accept": {"us": brk["entropy_accept"], "bound": "latency"},
-        "converged": {"us": brk["converged"], "bound": "latency"},
+        "accept_converged": {"us": brk["accept_converged"], "bound": "latency"},
     }
     for k in out.values():
         if "tflops" in k:
@@ -838,7 +835,7 @@ def main():
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
     lm_ev = [(hev.create(), hev.create()) for _ in range(K)] if lmhead else [None] * K
     # events between the calls of every timed step (on the launch stream): per-call GPU time
-    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {K} steps")
     torch.cuda.synchronize()
@@ -852,7 +849,7 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
     pe_ms = sum(hev.elapsed_ms(a, b) for a, b in pe_ev) / K
-    names = ["canvas_attention", "denoise_sample", "entropy_accept", "converged", "selfcond_embed"]
+    names = ["canvas_attention", "denoise_sample", "accept_converged", "selfcond_embed"]
     brk = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in call_ev) * 1000.0 / K for i, n in enumerate(names)}
     alg = pe_algorithmic_bytes(c)
     achieved = alg / (pe_ms * 1e-3) / 1e9

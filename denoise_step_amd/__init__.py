@@ -25,7 +25,7 @@ __all__ = [
     "dg_selfcond_embed_sc_e4m3", "dg_canvas_attention_e4m3", "dg_denoise_sample_noalloc",
     "dg_denoise_sample_noalloc_max_bytes", "dg_lmhead_ws_bytes", "dg_lmhead_operand_bytes",
     "dg_lmhead_denoise_sample", "dg_selfcond_embed_lm", "dg_lmhead_prepared_bytes", "dg_lmhead_prepare",
-    "dg_lmhead_denoise_sample_traced",
+    "dg_lmhead_denoise_sample_traced", "dg_accept_converged",
 ]
 
 DG_F32, DG_BF16 = 0, 1
@@ -56,6 +56,8 @@ _SIGS = {
     "dg_entropy_accept": (_i32, [_p, _p, _i32, _i32, _i32, _f64, _p, _p, _p, _p, _p, _p, _p]),
     "dg_converged": (_i32, [_p, _p, _i32, _i32, _i32, _i32, _f64, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                             _p, _p]),
+    "dg_accept_converged": (_i32, [_p, _p, _p, _i32, _i32, _i32, _f64, _i32, _f64, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                   _p, _p, _p, _p, _p, _p, _p, _p]),
     "dg_selfcond_prepared_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "dg_selfcond_prepare": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _sz, _p]),
     "dg_selfcond_ws_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -304,6 +306,20 @@ def dg_converged(argmax, entropy, V, k, tau, max_steps, seed, state: dict, activ
                               _ptr(s["step_global"]), _ptr(s["canvas"]), _ptr(s["sc_on"]), _ptr(s["committed"]),
                               _ptr(s["out_tokens"]), _ptr(s["steps_used"]), _ptr(s["num_sampled"]),
                               _stream(stream)), "dg_converged")
+
+
+def dg_accept_converged(entropy, sample, argmax, V, budget, k, tau, max_steps, seed, state: dict, active=None,
+                        accept=None, n_accept=None, stream=None):
+    """dg_entropy_accept then dg_converged in one launch (prefill case: dg_converged only); state as in
+    dg_converged (updated in place, canvas included)."""
+    B, C = state["canvas"].shape
+    s = state
+    _check(lib().dg_accept_converged(_ptr(entropy), _ptr(sample), _ptr(argmax), B, C, V, float(budget), int(k),
+                                     float(tau), int(max_steps), _ptr(seed), _ptr(active), _ptr(s["prev_argmax"]),
+                                     _ptr(s["unchanged"]), _ptr(s["step_in_block"]), _ptr(s["step_global"]),
+                                     _ptr(s["canvas"]), _ptr(s["sc_on"]), _ptr(s["committed"]), _ptr(s["out_tokens"]),
+                                     _ptr(s["steps_used"]), _ptr(s["num_sampled"]), _ptr(accept), _ptr(n_accept),
+                                     _stream(stream)), "dg_accept_converged")
 
 
 def dg_selfcond_prepared_bytes(V, d, hidden, dtype) -> int:

@@ -9,8 +9,8 @@ feedback into the next step):
   * dg_deficit_admit decides whether the prefill at the head of the arrival queue enters, whole;
   * one dg_canvas_attention launch covers every scheduled request in its own phase (prefill and
     commit rows causal with K/V appended to the request's pages, canvas rows bidirectional);
-  * the denoising requests run dg_denoise_sample -> dg_entropy_accept -> dg_converged; a request
-    admitted this iteration gets its first random canvas from dg_converged's prefill case;
+  * the denoising requests run dg_denoise_sample -> dg_accept_converged (acceptance + convergence in
+    one launch); a request admitted this iteration gets its first random canvas from its prefill case;
   * with self-conditioning, the sampling pass also writes the probability operand
     (dg_denoise_sample_sc) and dg_selfcond_embed_sc turns it into the next step's canvas
     embedding x_next = E[canvas] + (sc_on ? MLP(softmax . E) : 0), after dg_converged has set the
@@ -31,8 +31,8 @@ import math
 import numpy as np
 import torch
 
-from . import (dg_canvas_attention, dg_converged, dg_deficit_admit, dg_denoise_sample, dg_denoise_sample_sc,
-               dg_denoise_sample_ws_bytes, dg_entropy_accept, dg_selfcond_embed_sc, dg_selfcond_operand_bytes,
+from . import (dg_accept_converged, dg_canvas_attention, dg_converged, dg_deficit_admit, dg_denoise_sample,
+               dg_denoise_sample_sc, dg_denoise_sample_ws_bytes, dg_selfcond_embed_sc, dg_selfcond_operand_bytes,
                dg_selfcond_ws_bytes_sc)
 
 WAITING, PREFILL, DENOISE, COMMIT, DONE = range(5)
@@ -165,15 +165,15 @@ class ServingLoop:
             else:
                 dg_denoise_sample(logits, V, C, self.seed, step_now, cfg["temperature"], active=den, out=so,
                                   ws=self.ws_s)
-            dg_entropy_accept(so["entropy"].view(R, C), so["sample"].view(R, C), st["canvas"], V, cfg["budget"],
-                              self.seed, step_now, active=den, accept=self.accept, n_accept=self.n_accept)
-            argmax, entropy = so["argmax"].view(R, C), so["entropy"].view(R, C)
+            argmax, entropy, sample = so["argmax"].view(R, C), so["entropy"].view(R, C), so["sample"].view(R, C)
         else:
-            argmax = torch.zeros((R, C), dtype=torch.int32, device=self.dev)
+            argmax = sample = torch.zeros((R, C), dtype=torch.int32, device=self.dev)
             entropy = torch.zeros((R, C), dtype=torch.float32, device=self.dev)
         if bool(((self.phase == DENOISE) | (self.phase == PREFILL)).any()):
             st["committed"].zero_()
-            dg_converged(argmax, entropy, V, cfg["k"], cfg["tau"], cfg["max_steps"], self.seed, st, active=pre)
+            # denoising requests: acceptance then the convergence test; admitted ones: the prefill case
+            dg_accept_converged(entropy, sample, argmax, V, cfg["budget"], cfg["k"], cfg["tau"], cfg["max_steps"],
+                                self.seed, st, active=pre, accept=self.accept, n_accept=self.n_accept)
         if denoising and self.sc is not None:
             dg_selfcond_embed_sc(self.operand, V, self.so["row_max"], self.so["row_lnz"], st["sc_on"], st["canvas"],
                                  self.sc["E"], self.sc["prepared"], self.sc["hidden"], x_out=self.x, ws=self.ws_sc,

@@ -3,7 +3,7 @@
 One request, one fp32 layer (the two-mode backbone of the DiffusionGemma/vLLM
 page, section "Two modes, one set of weights"): encoder prefill of the prompt
 (causal, K/V written), prefill case of the sampler (random canvas), denoise
-steps (decoder pass -> dg_denoise_sample -> dg_entropy_accept -> dg_converged
+steps (decoder pass -> dg_denoise_sample -> dg_accept_converged (acceptance + convergence)
 -> dg_selfcond_embed) until the canvas commits, then the encoder commit pass
 that appends the block's K/V.  Every step of the arithmetic runs in libdg;
 this module only allocates tensors and sequences the calls.
@@ -14,7 +14,7 @@ import math
 
 import torch
 
-from . import (dg_canvas_attention, dg_converged, dg_denoise_sample, dg_entropy_accept, dg_gather_rows, dg_linear,
+from . import (dg_accept_converged, dg_canvas_attention, dg_converged, dg_denoise_sample, dg_gather_rows, dg_linear,
                dg_selfcond_embed)
 
 
@@ -71,9 +71,8 @@ class TinyLoop:
             h = self._layer(x, P0, 0, C)                            # decoder pass over the canvas
             logits = dg_linear(h, self.E, trans_b=True, alpha=self.scale)
             so = dg_denoise_sample(logits, V, C, self.seed, step_now, cfg["temperature"])
-            dg_entropy_accept(so["entropy"], so["sample"], s["canvas"], V, cfg["budget"], self.seed, step_now,
-                              accept=accept, n_accept=n_acc)
-            dg_converged(so["argmax"], so["entropy"], V, cfg["k"], cfg["tau"], cfg["max_steps"], self.seed, s)
+            dg_accept_converged(so["entropy"], so["sample"], so["argmax"], V, cfg["budget"], cfg["k"], cfg["tau"],
+                                cfg["max_steps"], self.seed, s, accept=accept, n_accept=n_acc)
             x = dg_selfcond_embed(logits, V, so["row_max"], so["row_lnz"], s["sc_on"], s["canvas"], self.E,
                                   self.w["w_gate"], self.w["w_up"], self.w["w_down"], None, cfg["temperature"])
             committed = bool(s["committed"].item())

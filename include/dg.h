@@ -267,6 +267,19 @@ dg_status dg_converged(const int32_t* argmax, const float* entropy, int32_t B, i
                        int32_t* canvas, uint8_t* sc_on, uint8_t* committed, int32_t* out_tokens,
                        int32_t* steps_used, int32_t* num_sampled, dg_stream_t stream);
 
+/* dg_accept_converged: dg_entropy_accept followed by dg_converged in one launch (one workgroup per
+ * request).  A request in its prefill case (step_in_block < 0) gets only dg_converged's prefill;
+ * every other active request gets the acceptance (renoise keyed by its current step_global, as
+ * dg_entropy_accept with step = step_global) and then the convergence test on the accepted canvas.
+ * Arguments as in the two entry points (accept and n_accept may be NULL; budget not NaN); results
+ * are bitwise those of the two calls in sequence. */
+dg_status dg_accept_converged(const float* entropy, const int32_t* sample, const int32_t* argmax, int32_t B,
+                              int32_t C, int32_t V, double budget, int32_t k, double tau, int32_t max_steps,
+                              const uint64_t* seed, const uint8_t* active, int32_t* prev_argmax, int32_t* unchanged,
+                              int32_t* step_in_block, int32_t* step_global, int32_t* canvas, uint8_t* sc_on,
+                              uint8_t* committed, int32_t* out_tokens, int32_t* steps_used, int32_t* num_sampled,
+                              uint8_t* accept, int32_t* n_accept, dg_stream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * dg_selfcond_embed
  *
