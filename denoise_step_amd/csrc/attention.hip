@@ -184,7 +184,7 @@ struct AttPlan {
   bool mfma;
   int64_t item_cap, part_cap, grid;
   bool fits;  // items are numbered in 32 bits inside a request
-  size_t off_ml, bytes;
+  size_t off_ml, off_np, bytes;
 };
 
 AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t max_keys, int32_t Hq, int32_t Hkv,
@@ -209,7 +209,8 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   if (p.part_cap > 0) {
     const size_t n = static_cast<size_t>(p.part_cap) * Hq;
     p.off_ml = round_up(n * D * sizeof(uint16_t), 256);
-    p.bytes = round_up(p.off_ml + n * sizeof(float2), 256);
+    p.off_np = round_up(p.off_ml + n * sizeof(float2), 256);
+    p.bytes = p.off_np + 256;
   }
   return p;
 }
@@ -240,6 +241,7 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
   a.out = reinterpret_cast<uint16_t*>(out);
   a.o_part = reinterpret_cast<uint16_t*>(ws);
   a.ml_part = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + plan.off_ml);
+  a.n_part = plan.part_cap > 0 ? reinterpret_cast<int64_t*>(reinterpret_cast<char*>(ws) + plan.off_np) : nullptr;
   const dim3 grid(static_cast<unsigned>(plan.grid));
   if (D == 256)
     attend_mfma16_kernel<256, E8><<<grid, kAtt16Threads, 0, s>>>(a);
@@ -247,7 +249,8 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
     attend_mfma16_kernel<128, E8><<<grid, kAtt16Threads, 0, s>>>(a);
   DG_LAUNCHED();
   if (plan.part_cap > 0) {
-    const dim3 mgrid(rows, static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
+    const dim3 mgrid(static_cast<unsigned>(std::min<int64_t>(rows, 2048)),
+                     static_cast<unsigned>(cdiv(static_cast<int64_t>(Hq) * D, 1024)));
     if (D == 256)
       attend_merge_kernel<256><<<mgrid, 256, 0, s>>>(a);
     else

@@ -103,6 +103,7 @@ struct AttArgs {
   uint16_t* o_part;     // [split rows][Hq][D] bf16: split s of a split request, its row j at part_off + s nr + j,
                         // the split's output normalised by its own l
   float2* ml_part;      // [split rows][Hq] (reference max in log2 units, l)
+  int64_t* n_part;      // split rows of the launch, written by the attention kernel for the merge (with ml_part)
   // E4M3 cache (attend_mfma16_kernel<D, true>): codes in place of k_cache / v_cache, values scale * code
   const uint8_t* k_cache8;
   const uint8_t* v_cache8;
@@ -209,9 +210,10 @@ struct AttItem {
 
 // Launch totals (every lane of the calling wave gets them); false when they exceed what the grid
 // or the workspace holds (descriptors inconsistent with the host bounds: nothing is done).
-DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items) {
+DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items, int64_t& np) {
   const int lane = threadIdx.x & (kWave - 1);
-  int64_t ni = 0, np = 0;
+  int64_t ni = 0;
+  np = 0;
   for (int r0 = 0; r0 < a.n_req; r0 += kWave) {
     AttReqPlan p;
     int64_t items, part;
@@ -702,13 +704,18 @@ __global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a)
   att_req_counts(a, lane, p0, items0, part0);
   const int64_t inc_i0 = wave_incl_scan(items0), inc_p0 = wave_incl_scan(part0);
   const bool one_pass = a.n_req <= kWave;
-  int64_t n_items;
+  int64_t n_items, n_part;
+  bool ok;
   if (one_pass) {
     n_items = __shfl(inc_i0, kWave - 1, kWave);
-    if (n_items > a.item_cap || __shfl(inc_p0, kWave - 1, kWave) > a.part_cap) return;
-  } else if (!att_totals(a, n_items)) {
-    return;
+    n_part = __shfl(inc_p0, kWave - 1, kWave);
+    ok = n_items <= a.item_cap && n_part <= a.part_cap;
+  } else {
+    ok = att_totals(a, n_items, n_part);
   }
+  // the merge kernel has nothing to do when no request of the launch is split (or nothing is done)
+  if (a.n_part != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.n_part = ok ? n_part : 0;
+  if (!ok) return;
   const int64_t per_xcd = (n_items + 7) / 8;
   const int64_t lo = (blockIdx.x % 8) * per_xcd;
   const int64_t hi = min(n_items, lo + per_xcd);
@@ -728,78 +735,83 @@ __global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a)
 
 // Combine the KV splits of a split request: out = sum_s c_s Ohat_s / sum_s c_s with
 // c_s = 2^(m_s - M) l_s, M = max_s m_s and Ohat_s = O_s / l_s the split's normalised output (so
-// sum_s c_s Ohat_s = sum_s 2^(m_s - M) O_s).  Grid (packed row, 1024-value slice of the row's Hq x D
-// outputs); the workgroup finds the request owning its row and that request's first split row from
-// the same per-request counts as the attention kernel (a block-wide prefix over the descriptors);
-// rows of one-split requests (written by the attention kernel) and rows of no request are skipped.
-// Four consecutive d per thread, every split's loads issued before the sums.
+// sum_s c_s Ohat_s = sum_s 2^(m_s - M) O_s).  Grid (row stride, 1024-value slice of the row's Hq x D
+// outputs): a workgroup walks rows blockIdx.x, + gridDim.x, ...; for each it finds the request
+// owning the row and that request's first split row from the same per-request counts as the
+// attention kernel (a block-wide prefix over the descriptors); rows of one-split requests (written
+// by the attention kernel) and rows of no request are skipped, and the whole launch returns at once
+// when the attention kernel counted no split rows.  Four consecutive d per thread, every split's
+// loads issued before the sums.
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttArgs a) {
-  const int row = blockIdx.x;
+  if (*a.n_part == 0) return;  // no split request in this launch
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   __shared__ int64_t s_wave[4];
   __shared__ int64_t s_off;
   __shared__ int32_t s_ns, s_nr, s_row0;
-  if (tid == 0) s_ns = 0;
-  int64_t base = 0;
-  for (int r0 = 0; r0 < a.n_req; r0 += 256) {
-    AttReqPlan p;
-    int64_t items, part;
-    att_req_counts(a, r0 + tid, p, items, part);
-    const int32_t row0 = r0 + tid < a.n_req ? a.splits[r0 + tid].row0 : 0;
-    const int64_t inc = wave_incl_scan(part);
-    if (lane == kWave - 1) s_wave[wave] = inc;
-    __syncthreads();
-    int64_t before = base;
-    for (int w = 0; w < wave; ++w) before += s_wave[w];
-    if (part > 0 && row >= row0 && row < row0 + p.nr) {
-      s_off = before + inc - part;
-      s_ns = p.ns;
-      s_nr = p.nr;
-      s_row0 = row0;
-    }
-    base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    __syncthreads();
-  }
-  __syncthreads();
-  const int32_t ns = s_ns;
-  if (ns < 2 || base > a.part_cap) return;
   const int64_t e = static_cast<int64_t>(blockIdx.y) * 1024 + 4 * tid;
-  if (e >= static_cast<int64_t>(a.Hq) * D) return;
-  const int h = static_cast<int>(e / D), d = static_cast<int>(e - static_cast<int64_t>(h) * D);
-  const int64_t first = s_off + (row - s_row0);  // split row of split 0
-  float2 ml[kMergeSplits];
-  uint2 ov[kMergeSplits];
-#pragma unroll
-  for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
-    if (sidx < ns) {
-      const int64_t ridx = (first + static_cast<int64_t>(sidx) * s_nr) * a.Hq + h;
-      ml[sidx] = a.ml_part[ridx];
-      ov[sidx] = *reinterpret_cast<const uint2*>(a.o_part + ridx * D + d);
+  const bool has_e = e < static_cast<int64_t>(a.Hq) * D;
+  const int h = has_e ? static_cast<int>(e / D) : 0, d = has_e ? static_cast<int>(e - static_cast<int64_t>(h) * D) : 0;
+  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    if (tid == 0) s_ns = 0;
+    int64_t base = 0;
+    for (int r0 = 0; r0 < a.n_req; r0 += 256) {
+      AttReqPlan p;
+      int64_t items, part;
+      att_req_counts(a, r0 + tid, p, items, part);
+      const int32_t row0 = r0 + tid < a.n_req ? a.splits[r0 + tid].row0 : 0;
+      const int64_t inc = wave_incl_scan(part);
+      if (lane == kWave - 1) s_wave[wave] = inc;
+      __syncthreads();
+      int64_t before = base;
+      for (int w = 0; w < wave; ++w) before += s_wave[w];
+      if (part > 0 && row >= row0 && row < row0 + p.nr) {
+        s_off = before + inc - part;
+        s_ns = p.ns;
+        s_nr = p.nr;
+        s_row0 = row0;
+      }
+      base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+      __syncthreads();
     }
-  }
-  float M = -INFINITY;
+    const int32_t ns = s_ns;
+    const int64_t first = s_off + (row - s_row0);  // split row of split 0
+    const int32_t nr = s_nr;
+    __syncthreads();  // the shared values are read before the next row resets them
+    if (ns < 2 || base > a.part_cap || !has_e) continue;  // block-uniform except has_e (no barrier follows)
+    float2 ml[kMergeSplits];
+    uint2 ov[kMergeSplits];
 #pragma unroll
-  for (int sidx = 0; sidx < kMergeSplits; ++sidx)
-    if (sidx < ns) M = fmaxf(M, ml[sidx].x);
-  float L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
-    if (sidx < ns && ml[sidx].x != -INFINITY) {
-      const float c = exp2f(ml[sidx].x - M) * ml[sidx].y;
-      L += c;
-      acc.x = fmaf(c, bf16_lo(ov[sidx].x), acc.x);
-      acc.y = fmaf(c, bf16_hi(ov[sidx].x), acc.y);
-      acc.z = fmaf(c, bf16_lo(ov[sidx].y), acc.z);
-      acc.w = fmaf(c, bf16_hi(ov[sidx].y), acc.w);
+    for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
+      if (sidx < ns) {
+        const int64_t ridx = (first + static_cast<int64_t>(sidx) * nr) * a.Hq + h;
+        ml[sidx] = a.ml_part[ridx];
+        ov[sidx] = *reinterpret_cast<const uint2*>(a.o_part + ridx * D + d);
+      }
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sidx = 0; sidx < kMergeSplits; ++sidx)
+      if (sidx < ns) M = fmaxf(M, ml[sidx].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sidx = 0; sidx < kMergeSplits; ++sidx) {
+      if (sidx < ns && ml[sidx].x != -INFINITY) {
+        const float c = exp2f(ml[sidx].x - M) * ml[sidx].y;
+        L += c;
+        acc.x = fmaf(c, bf16_lo(ov[sidx].x), acc.x);
+        acc.y = fmaf(c, bf16_hi(ov[sidx].x), acc.y);
+        acc.z = fmaf(c, bf16_lo(ov[sidx].y), acc.z);
+        acc.w = fmaf(c, bf16_hi(ov[sidx].y), acc.w);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 wv;
+    wv.x = static_cast<uint32_t>(f32_to_bf16(acc.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
+    wv.y = static_cast<uint32_t>(f32_to_bf16(acc.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(row) * a.Hq + h) * D + d) = wv;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint2 wv;
-  wv.x = static_cast<uint32_t>(f32_to_bf16(acc.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.y * inv)) << 16);
-  wv.y = static_cast<uint32_t>(f32_to_bf16(acc.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc.w * inv)) << 16);
-  if (row < a.rows) *reinterpret_cast<uint2*>(a.out + (static_cast<int64_t>(row) * a.Hq + h) * D + d) = wv;
 }
 
 }  // namespace dg
