@@ -493,7 +493,6 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
     torch.cuda.synchronize()
     hev = HipEvents()
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
-    lm_ev = [(hev.create(), hev.create()) for _ in range(K)] if lmhead else [None] * K
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"batched: timing {K} iterations")
     positions = 0
