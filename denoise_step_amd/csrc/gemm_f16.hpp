@@ -77,9 +77,10 @@ DG_DEV uint32_t gemm_lane_offset() {
 // The copy (lds_copy16: scalar base + per-lane 32-bit offset) is tracked only by the explicit vmcnt
 // waits of the pipeline below; the main loop issues no other vector-memory instruction, so those
 // counts are exact.
-// NT marks the load non-temporal: used for the right operand, which every workgroup streams once
-// (E^T is read by exactly one tile per K range), so it does not evict the left operand that the
-// workgroups of the other N tiles re-read from L2.
+// NT marks the load non-temporal: used for the right operand when there is one M tile (E^T is then
+// read by exactly one tile per K range), so it does not evict the left operand that the workgroups
+// of the other N tiles re-read from L2 (BNT); with several M tiles every B chunk is re-read by each
+// of them and is loaded normally.
 template <bool NT>
 DG_DEV void gemm_dma(const _Float16* __restrict__ base, int64_t rows, int row0, int k0, uint32_t lane_off,
                      _Float16* lds, int q) {
@@ -112,7 +113,7 @@ DG_DEV void gemm_dma8(const uint8_t* __restrict__ base, int64_t rows, int row0, 
 
 // Issue one stage: A (256 rows) and B (TN rows) as 1-KB instructions shared round-robin by the waves.
 // A has mtiles * 256 rows in its layout (rows past M are read but never stored); Bt has N rows.
-template <int TN, bool BF8>
+template <int TN, bool BF8, bool BNT = true>
 DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, uint32_t off8, int wave,
                        _Float16* as, _Float16* bs) {
 #pragma unroll
@@ -123,7 +124,7 @@ DG_DEV void gemm_issue(const GemmArgs& g, int m0, int n0, int k0, uint32_t off, 
       gemm_dma8(g.Bt8, g.ldb, n0, k0, off8, reinterpret_cast<uint8_t*>(bs), wave + kGemmWaves * i);
   } else {
 #pragma unroll
-    for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma<true>(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
+    for (int i = 0; i < TN / 16 / kGemmWaves; ++i) gemm_dma<BNT>(g.Bt, g.ldb, n0, k0, off, bs, wave + kGemmWaves * i);
   }
 }
 
@@ -219,14 +220,14 @@ DG_DEV void gemm_barrier() {
 // Operand source of the main loop for the K-blocked operands of GemmArgs: issue(s, as, bs) starts
 // the copies of stage s (K offset s * kGemmTK of the workgroup's range) into the given LDS buffers;
 // fix(f, s) adjusts the fragments of stage s after their LDS read (nothing here).
-template <int TN, bool BF8>
+template <int TN, bool BF8, bool BNT = true>
 struct GemmSrc {
   const GemmArgs& g;
   int m0, n0, k_begin;
   uint32_t off, off8;
   int wave;
   DG_DEV void issue(int s, _Float16* as, _Float16* bs) const {
-    gemm_issue<TN, BF8>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, as, bs);
+    gemm_issue<TN, BF8, BNT>(g, m0, n0, k_begin + s * kGemmTK, off, off8, wave, as, bs);
   }
   DG_DEV void fix(GemmFrag<TN>&, int) const {}
 };
@@ -296,22 +297,37 @@ DG_DEV void gemm_main(const Src& src, int nstage, _Float16* As, _Float16* Bs, in
   }
 }
 
-// The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment.
-template <int TN, bool BF8, bool PP>
+// The split-K GEMM; BF8: the right operand is E4M3 (g.Bt8), converted to fp16 fragment by fragment;
+// BNT: the fp16 right operand is loaded non-temporally (launches with one M tile).
+template <int TN, bool BF8, bool PP, bool BNT = true>
 DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int NJ = TN / 128;
   constexpr int kAs = kGemmTM * kGemmTK;                     // halves per A stage
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
   __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
-  // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile
+  // XCD-aware tile order: XCD x owns the contiguous range of linear tiles [x per_xcd, (x + 1) per_xcd)
+  // and its 32 CUs run 32 consecutive ones at a time.  Linear tile t = (split * ntiles + ntile) *
+  // mtiles + mtile: the workgroups of one XCD share their A chunk (single canvas: 16 N tiles of one
+  // split) or their B chunk.  Many M and N tiles without split-K (a batch of canvases, B loaded
+  // normally): t walks blocks of 4 M tiles x 8 N tiles, one block per 32 consecutive tiles, so an
+  // XCD's concurrent workgroups read 4 A and 8 B chunks through its L2 instead of 32 A chunks and
+  // one B chunk.
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
   const int t = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
   if (t >= total) return;
-  const int mt = t % g.mtiles;
-  const int nt = (t / g.mtiles) % g.ntiles;
-  const int split = t / (g.mtiles * g.ntiles);
+  int mt, nt, split;
+  if (!BNT && g.splits == 1 && g.mtiles % 4 == 0 && g.ntiles % 8 == 0 && per_xcd % 32 == 0) {
+    const int blk = t / 32, l = t % 32, nbn = g.ntiles / 8;
+    mt = (blk / nbn) * 4 + l / 8;
+    nt = (blk % nbn) * 8 + l % 8;
+    split = 0;
+  } else {
+    mt = t % g.mtiles;
+    nt = (t / g.mtiles) % g.ntiles;
+    split = t / (g.mtiles * g.ntiles);
+  }
   const int m0 = mt * kGemmTM, n0 = nt * TN;
   const int k_begin = split * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
@@ -322,8 +338,8 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * (TN / 4);
 
   floatx16 acc[4][NJ];
-  gemm_main<TN, BF8, PP, false>(GemmSrc<TN, BF8>{g, m0, n0, k_begin, gemm_lane_offset(),
-                                                  BF8 ? gemm_lane_offset8() : 0u, wave},
+  gemm_main<TN, BF8, PP, false>(GemmSrc<TN, BF8, BNT>{g, m0, n0, k_begin, gemm_lane_offset(),
+                                                       BF8 ? gemm_lane_offset8() : 0u, wave},
                                 nstage, As, Bs, wm, wn, lane, group, acc);
   // accumulator element e of lane l: row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
   float* out = g.part + static_cast<int64_t>(split) * g.M * g.N;
@@ -342,9 +358,9 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
 // ROLE names the instantiation (0: P.E contraction, ping-pong schedule; 1: MLP GEMMs, one barrier per
 // stage), so that profilers also report the dominant P.E launch under its own symbol.  TN is the N tile (256, or 128 when N is not a multiple
 // of 256).
-template <int ROLE, int TN>
+template <int ROLE, int TN, bool BNT = true>
 __global__ __launch_bounds__(kGemmThreads) void gemm_f16_splitk_kernel(GemmArgs g) {
-  gemm_splitk_body<TN, false, ROLE == 0>(g);
+  gemm_splitk_body<TN, false, ROLE == 0, BNT>(g);
 }
 
 

@@ -426,12 +426,21 @@ F32Plan f32_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden) {
 
 unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
 
+// One M tile (a canvas of <= 256 rows): the right operand streams non-temporally; several M tiles
+// (a batch of canvases) re-read each of its chunks, which then stay in L2.
 template <int ROLE>
 void launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-  if (p.tn == 256)
-    gemm_f16_splitk_kernel<ROLE, 256><<<p.grid, kGemmThreads, 0, s>>>(a);
-  else
-    gemm_f16_splitk_kernel<ROLE, 128><<<p.grid, kGemmThreads, 0, s>>>(a);
+  if (p.mtiles == 1) {
+    if (p.tn == 256)
+      gemm_f16_splitk_kernel<ROLE, 256><<<p.grid, kGemmThreads, 0, s>>>(a);
+    else
+      gemm_f16_splitk_kernel<ROLE, 128><<<p.grid, kGemmThreads, 0, s>>>(a);
+  } else {
+    if (p.tn == 256)
+      gemm_f16_splitk_kernel<ROLE, 256, false><<<p.grid, kGemmThreads, 0, s>>>(a);
+    else
+      gemm_f16_splitk_kernel<ROLE, 128, false><<<p.grid, kGemmThreads, 0, s>>>(a);
+  }
 }
 
 // P.E (from the operand w), its reduce, the gated MLP and the embedding: the bf16 path after the
