@@ -306,28 +306,17 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
   __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
-  // XCD-aware tile order: XCD x owns the contiguous range of linear tiles [x per_xcd, (x + 1) per_xcd)
-  // and its 32 CUs run 32 consecutive ones at a time.  Linear tile t = (split * ntiles + ntile) *
-  // mtiles + mtile: the workgroups of one XCD share their A chunk (single canvas: 16 N tiles of one
-  // split) or their B chunk.  Many M and N tiles without split-K (a batch of canvases, B loaded
-  // normally): t walks blocks of 4 M tiles x 8 N tiles, one block per 32 consecutive tiles, so an
-  // XCD's concurrent workgroups read 4 A and 8 B chunks through its L2 instead of 32 A chunks and
-  // one B chunk.
+  // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile; XCD x owns the
+  // contiguous range [x per_xcd, (x + 1) per_xcd) and its 32 CUs run 32 consecutive tiles at a time,
+  // which share their A chunk (one M tile: the N tiles of one split) or their B chunk (several M
+  // tiles: the M tiles of one split and N tile).
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
   const int t = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
   if (t >= total) return;
-  int mt, nt, split;
-  if (!BNT && g.splits == 1 && g.mtiles % 4 == 0 && g.ntiles % 8 == 0 && per_xcd % 32 == 0) {
-    const int blk = t / 32, l = t % 32, nbn = g.ntiles / 8;
-    mt = (blk / nbn) * 4 + l / 8;
-    nt = (blk % nbn) * 8 + l % 8;
-    split = 0;
-  } else {
-    mt = t % g.mtiles;
-    nt = (t / g.mtiles) % g.ntiles;
-    split = t / (g.mtiles * g.ntiles);
-  }
+  const int mt = t % g.mtiles;
+  const int nt = (t / g.mtiles) % g.ntiles;
+  const int split = t / (g.mtiles * g.ntiles);
   const int m0 = mt * kGemmTM, n0 = nt * TN;
   const int k_begin = split * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
@@ -389,9 +378,10 @@ inline GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K, int32_t target_wgs = 
   return {splits, kchunk, mtiles, ntiles, tn, dim3(launched)};
 }
 
-// The same tiling with a given K per split (a multiple of kGemmStages * kGemmTK).
-inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk) {
-  const int32_t tn = (N % 256 == 0) ? 256 : 128;
+// The same tiling with a given K per split (a multiple of kGemmStages * kGemmTK), so that the split
+// of K -- and with it the order of every output's partial sums -- does not depend on M.
+inline GemmPlan plan_gemm_kchunk(int32_t M, int32_t N, int32_t K, int32_t kchunk, bool narrow = false) {
+  const int32_t tn = (N % 256 == 0 && !narrow) ? 256 : 128;
   const int32_t mtiles = (M + kGemmTM - 1) / kGemmTM, ntiles = N / tn;
   const int32_t splits = (K + kchunk - 1) / kchunk;
   const int32_t total = mtiles * ntiles * splits;

@@ -387,13 +387,19 @@ Bf16Plan bf16_plan(int32_t rows, int32_t V, int32_t d, int32_t hidden, bool sc =
   const int64_t rows_p = (static_cast<int64_t>(rows) + kGemmTM - 1) / kGemmTM * kGemmTM;
   p.Mp = rows_p;
   p.Kp = pad128(V);
-  p.pe = sc ? plan_gemm_kchunk(rows, d, static_cast<int32_t>(p.Kp), kScChunk)
-            : plan_gemm(rows, d, static_cast<int32_t>(p.Kp));
-  // the MLP GEMMs are small (M = rows, K = d or hidden): 128-wide N tiles and about 128 workgroups
-  // halve the split-K partials against one 256-wide tile per CU (measured 30 -> 24 us for
-  // 4096 -> 2 x 1024 -> 4096 at 256 rows)
-  p.g1 = plan_gemm(rows, 2 * hidden, d, 128, true);
-  p.g2 = plan_gemm(rows, d, hidden, 128, true);
+  // Every split of K is fixed by K alone (batch invariance: a row's sums run in the same order
+  // whatever the number of rows).  P.E: one split per 16384 vocabulary ids (the operand's runs).
+  // The MLP GEMMs (M = rows, K = d or hidden) use 128-wide N tiles with 8 splits of d and 4 of
+  // hidden, which at 256 rows is about 128 workgroups and halves the split-K partials against one
+  // 256-wide tile per CU (measured 30 -> 24 us for 4096 -> 2 x 1024 -> 4096 at 256 rows).
+  p.pe = plan_gemm_kchunk(rows, d, static_cast<int32_t>(p.Kp), kScChunk);
+  const auto kchunk = [](int32_t K, int32_t parts) {
+    const int32_t r = kGemmStages * kGemmTK;
+    const int32_t c = (K + parts - 1) / parts;
+    return std::max(r, (c + r - 1) / r * r);
+  };
+  p.g1 = plan_gemm_kchunk(rows, 2 * hidden, d, kchunk(d, 8), true);
+  p.g2 = plan_gemm_kchunk(rows, d, hidden, kchunk(hidden, 4), true);
   size_t part = 0;
   part = std::max(part, static_cast<size_t>(p.pe.splits) * rows * d * 4);
   part = std::max(part, static_cast<size_t>(p.g1.splits) * rows * 2 * hidden * 4);

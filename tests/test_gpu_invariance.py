@@ -101,3 +101,91 @@ def test_sampler_alone_equals_in_batch():
         pair = run(logits[2 * C:4 * C], seeds[2:4], steps[2:4], sc)
         for n in names:
             assert torch.equal(pair[n], full[n][2 * C:4 * C]), ("pair", sc, n)
+
+
+def test_lmhead_alone_equals_in_batch():
+    """The fused LM head and P.E from its operand: 16-row requests alone against the same requests in
+    an 18-request launch (288 rows: two row tiles, request 17 in the second), sampler outputs, s, y
+    and x_next bitwise equal."""
+    torch = P.torch_mod()
+    import denoise_step_amd as dg
+    print("lmhead batch invariance", flush=True)
+    V, d, hidden, C = 16464, 256, 128, 16
+    E = synth.normal_bf16(9, "inv.lm.E", (V, d), 1 / 8)
+    wg, wu = (synth.normal_bf16(9, ("inv.lm", t), (d, hidden), 0.5) for t in ("wg", "wu"))
+    wd = synth.normal_bf16(9, "inv.lm.wd", (hidden, d), 0.5)
+    Et = P.dev_bf16(E)
+    lmp = dg.dg_lmhead_prepare(Et)
+    prep = dg.dg_selfcond_prepare(Et, *(P.dev_bf16(a) for a in (wg, wu, wd)))
+    B = 18
+    h_b = synth.lmhead_hidden_bf16(9, "inv.lm.h", E, B * C, 1.5, 0.125)
+    canv = synth.rng_for(9, "inv.lm.canvas").integers(0, V, B * C).astype(np.int32)
+    seeds = np.arange(B, dtype=np.int64) + 100
+    steps = np.arange(B, dtype=np.int32) % 7
+
+    def run(h, seeds, steps, canvas, B):
+        rows = h.shape[0]
+        st, op = dg.dg_lmhead_denoise_sample(P.dev_bf16(h), lmp, V, 4.0, C, P.dev(seeds), P.dev(steps), 0.8)
+        s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+        y_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+        x = dg.dg_selfcond_embed_lm(op, V, st["row_max"], st["row_lnz"], P.dev(np.ones(B, np.uint8)),
+                                    P.dev(canvas.reshape(B, C)), Et, prep, hidden, s_out=s_out, y_out=y_out)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in st.items()}
+        out.update(s=s_out.cpu().numpy(), y=y_out.cpu().numpy(), x=x.view(torch.int16).cpu().numpy())
+        return out
+
+    batch = run(h_b, seeds, steps, canv, B)
+    for r in (0, 3, 17):
+        rows = slice(r * C, (r + 1) * C)
+        alone = run(h_b[rows], seeds[r:r + 1], steps[r:r + 1], canv[rows], 1)
+        for k in alone:
+            assert np.array_equal(alone[k], batch[k][rows]), (r, k)
+
+
+@pytest.mark.parametrize("path", ["logits", "operand"])
+def test_selfcond_alone_equals_in_batch(path):
+    """Self-conditioning (P.E, the MLP and the embedding) of 16-row requests alone against the same
+    requests in an 18-request launch (288 rows, two row tiles): every split of K is fixed by K, so s,
+    y and x_next are bitwise equal.  Both the logits path and the sampler-operand path."""
+    torch = P.torch_mod()
+    import denoise_step_amd as dg
+    print(f"selfcond batch invariance ({path})", flush=True)
+    V, d, hidden, C, B = 20000, 512, 256, 16, 18
+    ld = 20000
+    L = synth.zipf_logits_f32(11, ("inv.sc", path), B * C, ld)
+    bits = synth.f32_to_bf16_bits(L)
+    E = synth.normal_bf16(11, "inv.sc.E", (V, d), 1 / 8)
+    wg, wu = (synth.normal_bf16(11, ("inv.sc", t), (d, hidden), 0.5) for t in ("wg", "wu"))
+    wd = synth.normal_bf16(11, "inv.sc.wd", (hidden, d), 0.5)
+    Et, wgt, wut, wdt = (P.dev_bf16(a) for a in (E, wg, wu, wd))
+    prep = dg.dg_selfcond_prepare(Et, wgt, wut, wdt)
+    canv = synth.rng_for(11, "inv.sc.canvas").integers(0, V, B * C).astype(np.int32)
+    seeds = np.arange(B, dtype=np.int64) + 7
+    steps = np.arange(B, dtype=np.int32) % 5
+
+    def run(rows_sl, nreq):
+        lt = P.dev_bf16(np.ascontiguousarray(bits[rows_sl]))
+        rows = nreq * C
+        s_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+        y_out = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+        cv = P.dev(canv[rows_sl].reshape(nreq, C))
+        on = P.dev(np.ones(nreq, np.uint8))
+        sd, stp = P.dev(seeds[rows_sl.start // C:rows_sl.start // C + nreq]), P.dev(steps[rows_sl.start // C:rows_sl.start // C + nreq])
+        if path == "logits":
+            st = dg.dg_denoise_sample(lt, V, C, sd, stp)
+            x = dg.dg_selfcond_embed(lt, V, st["row_max"], st["row_lnz"], on, cv, Et, wgt, wut, wdt, prep,
+                                     s_out=s_out, y_out=y_out)
+        else:
+            st, op = dg.dg_denoise_sample_sc(lt, V, C, sd, stp)
+            x = dg.dg_selfcond_embed_sc(op, V, st["row_max"], st["row_lnz"], on, cv, Et, prep, hidden, s_out=s_out,
+                                        y_out=y_out)
+        torch.cuda.synchronize()
+        return dict(s=s_out.cpu().numpy(), y=y_out.cpu().numpy(), x=x.view(torch.int16).cpu().numpy())
+
+    batch = run(slice(0, B * C), B)
+    for r in (0, 9, 17):
+        rows = slice(r * C, (r + 1) * C)
+        alone = run(rows, 1)
+        for k in alone:
+            assert np.array_equal(alone[k], batch[k][rows]), (r, k)
