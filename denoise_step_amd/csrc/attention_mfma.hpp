@@ -7,9 +7,14 @@
 //
 // K and V blocks go global -> LDS by direct copies (global_load_lds_dwordx4, one 16-byte chunk per
 // lane, no staging registers; each copy reads whole key rows) into the same XOR-swizzled row-major
-// layout, prefetched one block ahead.  The V operand of the PV product needs several keys at one d
-// per lane: it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each
-// lane of a 16-lane group one column of the 4 rows x 16 columns its lanes address.
+// layout, prefetched one block ahead by waves 0 - 3 (one 16-key page each, a scalar base per page
+// when the page is whole).  The V operand of the PV product needs several keys at one d per lane:
+// it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each lane of a
+// 16-lane group one column of the 4 rows x 16 columns its lanes address.  The swizzle keeps both the
+// K and the V operand reads free of bank conflicts, and every read address is a per-lane base XORed
+// with a constant plus an immediate offset.  The reads run ahead of their MFMAs in hand-pipelined
+// rings (at D = 256: K two steps, V four fragments), since the kernel is bound by LDS latency, not
+// by MFMA or LDS bandwidth.
 //
 // Per 64-key block a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
 // (A = K from LDS, B = Q preloaded in registers): each lane holds 16 scores of
@@ -114,6 +119,8 @@ struct AttArgs {
 
 template <int D, bool E8>
 struct AttSmem;
+// every K / V block buffer starts at a multiple of 1024 bytes of the struct (operand read addressing)
+static_assert(kAttKeys * 128 * 2 % 1024 == 0, "block buffers 1024-aligned");
 template <int D>
 struct AttSmem<D, false> {
   uint16_t K[2][kAttKeys * D];
@@ -129,13 +136,19 @@ struct AttSmem<D, true> {
   uint8_t S[2 * kAttKeys * D];
 };
 
-// K and V in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ (r & 15)).
-// A K operand read has 16 consecutive keys ask for one chunk per 16-lane group, and a transposing
-// V read has 4 consecutive keys ask for 32 bytes each: the XOR puts them in distinct slots of a
-// 256-byte bank row, so the reads are conflict-free.
+// K and V in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ sw(r)),
+// sw(r) = 2 (r mod 8) + (r / 8 mod 2), a permutation of the key's position in its group of 16.  Each
+// key row starts a 256-byte bank row (64 banks x 4 bytes), so only the XOR spreads the accesses over
+// the banks.  A K operand read (16 bytes per lane, 16 lanes per LDS cycle) has 16 consecutive keys
+// ask for one chunk: sw is a permutation, so they hit 16 distinct slots.  A transposing V read (8
+// bytes per lane, 32 lanes per cycle) has the keys 8 h .. 8 h + 7 of a 16-key group (h fixed in the
+// half-wave) ask for two adjacent chunks 2 dt, 2 dt + 1 each: 2 (r mod 8) moves them to distinct
+// chunk pairs and the low bit keeps the pair apart, so both reads are free of bank conflicts (with
+// sw(r) = r mod 16 two keys of a half-wave shared each chunk pair: a 2-way conflict on every V read).
+DG_DEV int att_sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 template <int D>
 DG_DEV int att_kslot(int r, int c) {
-  return r * (D / 8) + (c ^ (r & 15));
+  return r * (D / 8) + (c ^ att_sw(r));
 }
 
 // Keys [x, y) visible to row j of a request (key positions: the cache, then the canvas rows; row j
@@ -284,30 +297,73 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, in
 // probability is 0.
 //
 // Copy q fills slots 64 q .. 64 q + 63, i.e. the 64 / (D / 8) keys q * 64 / (D / 8) ...; lane l
-// fetches chunk (l % (D / 8)) ^ (r & 15) of its key r, so each copy reads whole key rows.
-template <int D, int NT>
+// fetches chunk (l % (D / 8)) ^ sw(r) of its key r, so each copy reads whole key rows.
+// Copies of the bf16 blocks are issued by waves 0 - 3 only: wave w fills keys 16 w .. 16 w + 15 of a
+// block, one whole page of the cache.
+constexpr int kAttCopyWaves = 4;
+
+// One tensor (K or V) of the block at kb into dst, issued by copying wave w (0 - 3).  When its page
+// holds only cached keys below k_end, or only fresh rows inside the launch's rows, the copies take a
+// scalar base and the precomputed per-lane offsets.
+template <int D>
 DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
-                     int k_end, uint16_t* kdst, uint16_t* vdst) {
+                     int k_end, bool is_v, uint16_t* dst) {
   constexpr int kChunks = D / 8;
   constexpr int kKeysPerCopy = kWave / kChunks;
-  constexpr int kPerWave = kChunks / (NT / kWave);  // copies issued by each wave
+  constexpr int kPerWave = kChunks / kAttCopyWaves;  // copies per wave of one tensor and block
+  static_assert(kAttKeys / kAttCopyWaves == 16, "a copying wave fills one 16-key page");
   const int lane = threadIdx.x & (kWave - 1);
+  // copy i of the wave: key lk = i keys-per-copy + lane / chunks of its page, swizzled chunk c; its
+  // lane offset lk D 2 + 16 c bytes from the page's head
+  auto lane_off = [&](int i) {
+    const int lk = i * kKeysPerCopy + lane / kChunks;
+    return static_cast<uint32_t>(lk * D * 2 + 16 * ((lane % kChunks) ^ att_sw(lk)));
+  };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: M0 is scalar
-  // the page ids of the block's four 16-key groups in one 16-byte read (kb - k_begin is a multiple
-  // of 64, so the slot is 4-aligned; slots past the staged range are only picked by keys >= cached)
+  {
+    const int k0 = __builtin_amdgcn_readfirstlane(kb) + 16 * wave;
+    const int cached = __builtin_amdgcn_readfirstlane(sp.cached);
+    const int kend = __builtin_amdgcn_readfirstlane(k_end);
+    const int hks = __builtin_amdgcn_readfirstlane(hk);
+    if (k0 + 15 < min(cached, kend)) {
+      const int64_t pid = __builtin_amdgcn_readfirstlane(pages[k0 / 16 - page_lo]);  // staged, in range
+      const int64_t head = (pid * a.Hkv + hks) * 16 * D * 2;
+      const char* base = reinterpret_cast<const char*>(is_v ? a.v_cache : a.k_cache) + head;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int q = wave * kPerWave + i;
+        lds_copy16<false>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + kWave * 8 * q)), base, lane_off(i));
+      }
+      return;
+    }
+    const int64_t rb = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(sp.row0)) + (k0 - cached);
+    if (k0 >= cached && k0 + 15 < kend && rb >= 0 && rb + 15 < a.rows) {
+      // key lk of the page is row rb + lk: its lk D 2 bytes of the page offset become lk Hkv D 2
+      const int64_t head = (rb * a.Hkv + hks) * D * 2;
+      const char* base = reinterpret_cast<const char*>(is_v ? a.v : a.k) + head;
+      const uint32_t row_extra = static_cast<uint32_t>((lane / kChunks) * (a.Hkv - 1) * D * 2);
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int q = wave * kPerWave + i;
+        const int64_t step = static_cast<int64_t>(i) * kKeysPerCopy * (a.Hkv - 1) * D * 2;
+        lds_copy16<false>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + kWave * 8 * q)), base + step,
+                          lane_off(i) + row_extra);
+      }
+      return;
+    }
+  }
+  // pages straddling the cache end or k_end (or rows outside the launch): per-lane addresses.  The
+  // page ids of the block's four 16-key groups in one 16-byte read (kb - k_begin is a multiple of 64,
+  // so the slot is 4-aligned; slots past the staged range are only picked by keys >= cached)
   const int4 pq = *reinterpret_cast<const int4*>(pages + (kb / 16 - page_lo));
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
     const int q = wave * kPerWave + i;
     const int r = q * kKeysPerCopy + lane / kChunks;
-    const int c = (lane % kChunks) ^ (r & 15);
+    const int c = (lane % kChunks) ^ att_sw(r);
     const int kk = min(kb + r, k_end - 1);
-    const uint16_t* ksrc = att_row<D>(a, sp, pq, kb, hk, kk, false) + 8 * c;
-    const uint16_t* vsrc = att_row<D>(a, sp, pq, kb, hk, kk, true) + 8 * c;
-    const uint32_t klds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kdst + kWave * 8 * q));
-    const uint32_t vlds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(vdst + kWave * 8 * q));
-    lds_copy16(klds, ksrc);
-    lds_copy16(vlds, vsrc);
+    const uint16_t* src = att_row<D>(a, sp, pq, kb, hk, kk, is_v) + 8 * c;
+    lds_copy16(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + kWave * 8 * q)), src);
   }
 }
 
@@ -350,7 +406,7 @@ DG_DEV void att_load8(const AttArgs& a, const dg_split& sp, int hk, int kb, int 
     for (int i = 0; i < kPerWave; ++i) {
       const int q = wave * kPerWave + i;
       const int r = q * kKeysPerCopy + lane / kChunks;
-      const int c = (lane % kChunks) ^ (r & 15);
+      const int c = (lane % kChunks) ^ att_sw(r);
       const int kk = max(min(kb + r, k_end - 1), sp.cached);
       const int64_t row = min(max(sp.row0 + kk - sp.cached, 0), a.rows - 1);
       const int64_t off = (row * a.Hkv + hk) * D + 8 * c;
@@ -447,8 +503,8 @@ DG_DEV void att_append8(const AttArgs& a, const dg_split& sp, int hk, int j0, in
 }
 
 // ---------------------------------------------------------------- the attention kernel
-// Eight waves of 16 packed query rows (two waves per SIMD at ~210 registers each, so one wave's
-// softmax and address arithmetic overlap the other's MFMAs), on v_mfma_f32_16x16x32_bf16; each lane
+// Eight waves of 16 packed query rows (two waves per SIMD at up to 256 registers each, so one
+// wave's softmax and reads overlap the other's MFMAs), on v_mfma_f32_16x16x32_bf16; each lane
 // keeps its row's online-softmax state (max in log2 units, sum) and P stays in registers as the B
 // operand of the PV product.  Operand layouts (lane l, group g = l / 16, t = l % 16):
 //   S^T tile (16 keys x 16 rows) = K Q^T: A = K (key t, d 8 g .. 8 g + 7 of the 32-d step),
@@ -474,17 +530,14 @@ DG_DEV float quad_group_sum(float v) {
   return __int_as_float(r32[0]) + __int_as_float(r32[1]);
 }
 
-// A operand of O^T += V^T P^T for 16-d tile dt and 32-key chunk ch (see the layout above).
-template <int D>
-DG_DEV bf16x8 att_vfrag16(const uint16_t* Vb, int dt, int ch) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int g = lane >> 4, t16 = lane & 15;
-  const int r1 = 32 * ch + 4 * g + (t16 >> 2);
-  const int col = 16 * dt + 4 * (t16 & 3);
-  const uint16_t* p1 = Vb + 8 * att_kslot<D>(r1, col >> 3) + (col & 7);
-  const uint16_t* p2 = Vb + 8 * att_kslot<D>(r1 + 16, col >> 3) + (col & 7);
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p2));
+// A operand of O^T += V^T P^T for a 16-d tile and a 32-key chunk (see the layout above): two
+// transposing LDS reads at the lane's address p (its key row and column within the chunk) and 16 key
+// rows further.
+template <int C8>
+DG_DEV bf16x8 att_vfrag16(const char* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p + 256 * C8));
   const short4v lohi[2] = {lo, hi};
   bf16x8 v;
   __builtin_memcpy(&v, lohi, sizeof(v));
@@ -532,6 +585,8 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
     wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
     wave_lo = max(wave_lo, __shfl_xor(wave_lo, o, kWave));
   }
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);  // equal in every lane: the mask test branches
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
 
   // stage the physical page ids of the split's prefix positions (clamped into range)
   const int page_lo = k_begin / 16;
@@ -557,52 +612,71 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
   for (int dt = 0; dt < kDTiles; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;
 
-  __syncthreads();  // page ids visible
-  if (k_begin < k_end) {
-    if constexpr (E8)
-      att_load8<D, NT>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
-    else
-      att_load<D, NT>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, sm.K[0], sm.V[0]);
-    att_wait();
+  // Per-lane parts of the operand read addresses (att_kslot's swizzle split into a lane part, a part
+  // that is an immediate of each read and a part XORed in per read).  With Kb / Vb the byte offset of
+  // the block buffer from the start of the shared struct (a multiple of 1024, so bits 5 - 9 of the
+  // sums below come from the lane parts alone), the K read of tile tt and step s is at offset
+  // ((Kb + klane) ^ 64 (s & 3)) + 16 kChunks (16 tt) + 256 (s >> 2), and the V read of d tile dt and
+  // chunk ch (rows r and r + 16) at ((Vb + vlane) ^ 32 (dt & 7)) + 512 kChunks ch + 256 (dt >> 3)
+  // (+ 256 kChunks).
+  constexpr int kC8 = D / 8;
+  uint32_t klane, vlane;
+  {
+    const int y = 4 * g + (t16 >> 2), e = (t16 & 3) >> 1;
+    klane = t16 * kC8 * 16 + 64 * ((t16 >> 1) & 3) + 16 * (g ^ (((t16 & 1) << 1) | (t16 >> 3)));
+    vlane = 16 * kC8 * y + 32 * (y & 7) + 16 * (e ^ ((y >> 3) & 1)) + 8 * (t16 & 1);
   }
-  __syncthreads();
-  if constexpr (E8) {
-    if (k_begin < k_end && k_begin < sp.cached) {
-      att_convert8<D, NT>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
-      __syncthreads();
-    }
-  }
-  int buf = 0;
-  for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
-    const bool more = kb + kAttKeys < k_end;
-    if (more) {
-      if constexpr (E8)
-        att_load8<D, NT>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
-      else
-        att_load<D, NT>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, sm.K[buf ^ 1], sm.V[buf ^ 1]);
-    }
-    const uint16_t* Kb = sm.K[buf];
-    const uint16_t* Vb = sm.V[buf];
-    // ---- S^T = K Q^T: four 16-key tiles, K operands of step s + 1 read under the MFMAs of step s
-    floatx4 sc[4];
+
+  // The operand reads are software-pipelined by hand, with scheduling barriers between the steps so
+  // that the reads stay ahead of the MFMAs that use them (left to itself the scheduler issues each
+  // read just before its MFMA, which then waits for the whole LDS latency).
+  //
+  // S^T = K Q^T for the block in Kb: four 16-key tiles; the K fragments of step s + 2 are read while
+  // the MFMAs of step s run (a ring of three steps).
+  constexpr int kKRing = D > 128 ? 2 : 3;
+  const char* smb = reinterpret_cast<const char*>(&sm);
+  auto scores = [&](const uint16_t* Kbuf, floatx4 (&sc)[4]) {
+    const uint32_t kw = static_cast<uint32_t>(reinterpret_cast<const char*>(Kbuf) - smb) + klane;
+    auto kread = [&](int s, int tt) {
+      return *reinterpret_cast<const bf16x8*>(smb + (kw ^ (64 * (s & 3))) + 256 * kC8 * tt + 256 * (s >> 2));
+    };
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) sc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[2][4];
+    bf16x8 kf[kKRing][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      kf[0][tt] = *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(16 * tt + t16, g)]);
+    for (int s = 0; s < kKRing - 1 && s < kDSteps; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) kf[s][tt] = kread(s, tt);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kDSteps; ++s) {
-      if (s + 1 < kDSteps) {
+      if (s + kKRing - 1 < kDSteps) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          kf[(s + 1) & 1][tt] =
-              *reinterpret_cast<const bf16x8*>(&Kb[8 * att_kslot<D>(16 * tt + t16, 4 * (s + 1) + g)]);
+        for (int tt = 0; tt < 4; ++tt) kf[(s + kKRing - 1) % kKRing][tt] = kread(s + kKRing - 1, tt);
       }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][tt], qf[s], sc[tt], 0, 0, 0);
+      for (int tt = 0; tt < 4; ++tt)
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s % kKRing][tt], qf[s], sc[tt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- softmax; element e of tile tt holds key 16 tt + 4 g + e of this lane's row
+  };
+  // Online softmax of the block at kb (element e of tile tt holds key 16 tt + 4 g + e of this lane's
+  // row), then O^T += V^T P^T over its two 32-key chunks with V in Vb: 2 kDTiles steps (chunk, d tile),
+  // the V fragments of step t + kVRing read while the MFMA of step t runs, the first ones before the
+  // softmax.
+  constexpr int kVSteps = 2 * kDTiles;
+  constexpr int kVRing = D > 128 ? 4 : 8;
+  constexpr int kVEarly = D > 128 ? 2 : 4;  // of which read before the softmax
+  auto accumulate = [&](int kb, floatx4 (&sc)[4], const uint16_t* Vbuf) {
+    const uint32_t vw = static_cast<uint32_t>(reinterpret_cast<const char*>(Vbuf) - smb) + vlane;
+    auto vread = [&](int t) {
+      const int c = t / kDTiles, dt = t % kDTiles;
+      return att_vfrag16<kC8>(smb + (vw ^ (32 * (dt & 7))) + 512 * kC8 * c + 256 * (dt >> 3));
+    };
+    bf16x8 vf[kVRing];
+#pragma unroll
+    for (int t = 0; t < kVEarly; ++t) vf[t] = vread(t);
+    __builtin_amdgcn_sched_barrier(0);
     if (kb + kAttKeys > wave_hi || kb < wave_lo) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -642,22 +716,66 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
         pf[tt >> 1][4 * (tt & 1) + e] = static_cast<__bf16>(p);
       }
     l_run += quad_group_sum(psum);
-    // ---- O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int t = kVEarly; t < kVRing; ++t) vf[t] = vread(t);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(att_vfrag16<D>(Vb, dt, c), pf[c], o[dt], 0, 0, 0);
+    for (int t = 0; t < kVSteps; ++t) {
+      const int c = t / kDTiles, dt = t % kDTiles;
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[t % kVRing], pf[c], o[dt], 0, 0, 0);
+      if (t + kVRing < kVSteps) vf[t % kVRing] = vread(t + kVRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) att_wait();
+  };
+
+  __syncthreads();  // page ids visible
+  floatx4 sc[4];
+  if constexpr (!E8) {
+    // Waves 0 - 3 copy the next block (K and V) while every wave works on the current one.
+    const bool lead = __builtin_amdgcn_readfirstlane(wave) < kAttCopyWaves;
+    if (lead && k_begin < k_end) {
+      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, false, sm.K[0]);
+      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, true, sm.V[0]);
+      att_wait();
+    }
     __syncthreads();
-    if constexpr (E8) {
+    int buf = 0;
+    for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
+      const bool more = kb + kAttKeys < k_end;
+      if (lead && more) {
+        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, false, sm.K[buf ^ 1]);
+        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, true, sm.V[buf ^ 1]);
+      }
+      scores(sm.K[buf], sc);
+      accumulate(kb, sc, sm.V[buf]);
+      if (lead && more) att_wait();
+      __syncthreads();
+      buf ^= 1;
+    }
+  } else {
+    if (k_begin < k_end) {
+      att_load8<D, NT>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+      att_wait();
+    }
+    __syncthreads();
+    if (k_begin < k_end && k_begin < sp.cached) {
+      att_convert8<D, NT>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
+      __syncthreads();
+    }
+    int buf = 0;
+    for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
+      const bool more = kb + kAttKeys < k_end;
+      if (more) att_load8<D, NT>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+      scores(sm.K[buf], sc);
+      accumulate(kb, sc, sm.V[buf]);
+      if (more) att_wait();
+      __syncthreads();
       if (more && kb + kAttKeys < sp.cached) {
         att_convert8<D, NT>(a, sp, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
         __syncthreads();
       }
+      buf ^= 1;
     }
-    buf ^= 1;
   }
 
   // append: the split-0 workgroup writes the causal rows whose first packed row is in its tile
@@ -695,7 +813,7 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
 // and share its L2.  Each workgroup first recomputes the launch totals from the descriptors.
 template <int D, bool E8>
 __global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
-  __shared__ __attribute__((aligned(16))) AttSmem<D, E8> sm;
+  __shared__ __attribute__((aligned(1024))) AttSmem<D, E8> sm;
   // requests 0 .. 63: their plans and prefix sums stay in registers (one pass for launches of up to
   // 64 requests; larger launches rescan the descriptors per item)
   const int lane = threadIdx.x & (kWave - 1);
