@@ -17,6 +17,11 @@ The logits stand in for the LM head output of a real backbone.
 samples them in the same kernel (the logits never reach HBM), and dg_selfcond_embed_lm runs P.E
 from its operand; its roofline is the fused LM-head kernel's (2 C V d FLOP per launch, bf16 MFMA).
 
+Before its W warmup steps every workload first runs its own step until the GPU has been busy with
+it for SETTLE_MS (~30 single-canvas steps after the host-side set-up run ~13 % slower while the
+GPU's clocks come up); the JSON line records those steps as `settle_steps`.  The timed region is
+exactly K steps either way.
+
 Prints ONE JSON line (see --help).  The P.E contraction kernel, the step's
 dominant launch, is timed with HIP events recorded around it on the launch
 stream over the whole timed region; its roofline fraction uses the algorithmic
@@ -80,6 +85,23 @@ class HipEvents:
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+SETTLE_MS = 150.0  # GPU time the workload's step runs before the warmup steps
+
+
+def settle(run_one) -> int:
+    """Runs the workload's step (run_one(i), i = 0, 1, ...) until SETTLE_MS of wall time has passed
+    with the GPU busy on it; returns the number of steps run."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        run_one(n)
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1000.0 >= SETTLE_MS:
+                log(f"settled after {n} steps")
+                return n
 
 
 def source_sha(sources=PE_SOURCES) -> str:
@@ -487,9 +509,10 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
     w = [g(tag, sh, 0.02) for tag, sh in (("wg", (d, h)), ("wu", (d, h)), ("wd", (h, d)))]
     prepared = dg.dg_selfcond_prepare(E, *w)
     loop = ServingLoop(cfg, sched, t, selfcond=dict(E=E, prepared=prepared, hidden=h), start=start)
+    n_settle = settle(loop.step)
     log(f"batched: warmup {W} iterations")
     for it in range(W):
-        loop.step(it)
+        loop.step(n_settle + it)
     torch.cuda.synchronize()
     hev = HipEvents()
     pe_ev = [(hev.create(), hev.create()) for _ in range(K)]
@@ -498,7 +521,7 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
     positions = 0
     t0.record()
     for i in range(K):
-        rec = loop.step(W + i, pe_events=pe_ev[i])
+        rec = loop.step(n_settle + W + i, pe_events=pe_ev[i])
         positions += rec["denoise_rows"]
     t1.record()
     torch.cuda.synchronize()
@@ -517,7 +540,7 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
                       {"workload": "batched", "requests": R, "C": C, "V": V, "prefix": [cfg["P_min"], cfg["P_max"]],
                        "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "d_embed": d, "mlp_hidden": h,
                        "max_steps": cfg["max_steps"], "logit_pool": cfg["n_pool"], "self_conditioning": True},
-                      roof, cpu_line, {"positions_per_iteration": positions / K})
+                      roof, cpu_line, {"positions_per_iteration": positions / K, "settle_steps": n_settle})
 
 
 def _cpu_batched(loop, t, E, w, cfg, sched):
@@ -607,6 +630,7 @@ def bench_structured_read(K: int, W: int, cpu: bool) -> dict:
             ev[1].record()
         dg.dg_allowed_probs(slot_logits, V, slot_row, offsets, ids, 1.0, q=qv, answer=ans)
 
+    n_settle = settle(lambda i: one())
     log(f"structured read: warmup {W}")
     for _ in range(W):
         one()
@@ -652,7 +676,7 @@ def bench_structured_read(K: int, W: int, cpu: bool) -> dict:
                       "+ % MFMA roofline", B * C / (ms * 1e-3), "positions/s", K, W, ms,
                       {"workload": "structured_read", "requests": B, "causal_rows": nc, "C": C, "V": V,
                        "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "slots": cfg["slots"]},
-                      roof, cpu_line, {"attention_us": att_ms * 1000.0})
+                      roof, cpu_line, {"attention_us": att_ms * 1000.0, "settle_steps": n_settle})
 
 
 def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
@@ -713,6 +737,7 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
             tgt[b, gmm[b]] = (draft[b, gmm[b]] + 1 + rng.integers(0, V - 1)) % V
             tgt[b, gmm[b] + 1:] = rng.integers(0, V, L16 - 1 - gmm[b])
     target = torch.as_tensor(tgt, device="cuda")
+    n_settle = settle(lambda i: one())
     log(f"block draft: warmup {W}")
     for _ in range(W):
         one()
@@ -765,15 +790,13 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
                        "context": [cfg["L_min"], cfg["L_max"]], "heads_q": Hq, "heads_kv": Hkv, "head_dim": D,
                        "V": V}, roof, cpu_line,
                       {"attention_us_per_pass": att_ms * 1000.0,
-                       "accepted_mean": float(np.minimum(gmm, L16).mean())})
+                       "accepted_mean": float(np.minimum(gmm, L16).mean()), "settle_steps": n_settle})
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # the GPU's clocks are still settling after 5 warmup steps of the single-canvas step (its steady
-    # state, after ~50 steps, is a few per cent faster); the default is the recorded configuration
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=("single_canvas", "single_canvas_lmhead", "batched", "structured_read",
                                            "block_draft"),
                     default="single_canvas",
@@ -825,6 +848,7 @@ def main():
         sys.exit(2)
     w = Workload(dict(CFG, window=args.window, e4m3=args.e4m3, lmhead=lmhead))
     c = w.c
+    n_settle = settle(w.step)
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
         w.step(t)
@@ -861,6 +885,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
