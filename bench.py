@@ -93,6 +93,8 @@ SETTLE_MS = 150.0  # GPU time the workload's step runs before the warmup steps
 def settle(run_one) -> int:
     """Runs the workload's step (run_one(i), i = 0, 1, ...) until SETTLE_MS of wall time has passed
     with the GPU busy on it; returns the number of steps run."""
+    import torch
+
     n, t0 = 0, time.perf_counter()
     while True:
         run_one(n)
