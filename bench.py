@@ -675,7 +675,7 @@ def bench_structured_read(K: int, W: int, cpu: bool) -> dict:
                                 f"+ {C} canvas rows x {Hq} heads (K/V appended), the readout of its {cfg['slots']} "
                                 f"slots; {dt:.1f} s"))
     return _json_line("canvas positions read/sec (structured read: 64 x (2048 causal + 256 canvas), V=262144) "
-                      "+ % MFMA roofline", B * C / (ms * 1e-3), "positions/s", K, W, ms,
+                      "+ % MFMA roofline", B * C * K / (ms * 1e-3), "positions/s", K, W, ms,
                       {"workload": "structured_read", "requests": B, "causal_rows": nc, "C": C, "V": V,
                        "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "slots": cfg["slots"]},
                       roof, cpu_line, {"attention_us": att_ms * 1000.0, "settle_steps": n_settle})
@@ -787,7 +787,7 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
                                 f"16 draft rows x {Hq} heads over their injected context, the argmax of their 64 "
                                 f"logit rows of V={V}, verification; {dt:.1f} s"))
     return _json_line("draft positions/sec (block draft: 128 x 16 positions, 5 layers, V=151936) + % HBM roofline",
-                      B * L16 / (ms * 1e-3), "draft positions/s", K, W, ms,
+                      B * L16 * K / (ms * 1e-3), "draft positions/s", K, W, ms,
                       {"workload": "block_draft", "requests": B, "block": L16, "layers": layers,
                        "context": [cfg["L_min"], cfg["L_max"]], "heads_q": Hq, "heads_kv": Hkv, "head_dim": D,
                        "V": V}, roof, cpu_line,
