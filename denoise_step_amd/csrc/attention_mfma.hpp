@@ -10,9 +10,8 @@
 // layout, prefetched one block ahead by waves 0 - 3 (one 16-key page each, a scalar base per page
 // when the page is whole).  The V operand of the PV product needs several keys at one d per lane:
 // it is read with gfx950's transposing LDS load (ds_read_b64_tr_b16), which gives each lane of a
-// 16-lane group one column of the 4 rows x 16 columns its lanes address.  The swizzle keeps both the
-// K and the V operand reads free of bank conflicts, and every read address is a per-lane base XORed
-// with a constant plus an immediate offset.  The reads run ahead of their MFMAs in hand-pipelined
+// 16-lane group one column of the 4 rows x 16 columns its lanes address.  Every operand read address
+// is a per-lane base XORed with a constant plus an immediate offset.  The reads run ahead of their MFMAs in hand-pipelined
 // rings (at D = 256: K two steps, V four fragments), since the kernel is bound by LDS latency, not
 // by MFMA or LDS bandwidth.
 //
@@ -137,15 +136,12 @@ struct AttSmem<D, true> {
 };
 
 // K and V in LDS: chunk c (8 bf16) of key r of the block sits in 16-byte slot r * (D / 8) + (c ^ sw(r)),
-// sw(r) = 2 (r mod 8) + (r / 8 mod 2), a permutation of the key's position in its group of 16.  Each
-// key row starts a 256-byte bank row (64 banks x 4 bytes), so only the XOR spreads the accesses over
-// the banks.  A K operand read (16 bytes per lane, 16 lanes per LDS cycle) has 16 consecutive keys
-// ask for one chunk: sw is a permutation, so they hit 16 distinct slots.  A transposing V read (8
-// bytes per lane, 32 lanes per cycle) has the keys 8 h .. 8 h + 7 of a 16-key group (h fixed in the
-// half-wave) ask for two adjacent chunks 2 dt, 2 dt + 1 each: 2 (r mod 8) moves them to distinct
-// chunk pairs and the low bit keeps the pair apart, so both reads are free of bank conflicts (with
-// sw(r) = r mod 16 two keys of a half-wave shared each chunk pair: a 2-way conflict on every V read).
-DG_DEV int att_sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// sw(r) = r mod 16.  A K operand read has 16 consecutive keys ask for one chunk per 16-lane group, and
+// a transposing V read has 4 consecutive keys ask for 32 bytes each: the XOR puts them in distinct
+// slots of a 256-byte bank row.  (The bank-conflict counter reads a third of the LDS cycles for this
+// kernel with this swizzle and with two others that spread the reads further; the time does not
+// change with it either.)
+DG_DEV int att_sw(int r) { return r & 15; }
 template <int D>
 DG_DEV int att_kslot(int r, int c) {
   return r * (D / 8) + (c ^ att_sw(r));
@@ -623,8 +619,8 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
   uint32_t klane, vlane;
   {
     const int y = 4 * g + (t16 >> 2), e = (t16 & 3) >> 1;
-    klane = t16 * kC8 * 16 + 64 * ((t16 >> 1) & 3) + 16 * (g ^ (((t16 & 1) << 1) | (t16 >> 3)));
-    vlane = 16 * kC8 * y + 32 * (y & 7) + 16 * (e ^ ((y >> 3) & 1)) + 8 * (t16 & 1);
+    klane = t16 * kC8 * 16 + 64 * (t16 >> 2) + 16 * (g ^ (t16 & 3));
+    vlane = 16 * kC8 * y + 32 * (y >> 1) + 16 * (e ^ (y & 1)) + 8 * (t16 & 1);
   }
 
   // The operand reads are software-pipelined by hand, with scheduling barriers between the steps so
