@@ -172,10 +172,11 @@ void launch_attend_wave(const void* q, const void* k, const void* v, const void*
 // the host does not see; from the launch bounds it sizes the grid (work items) and the split
 // partials so that every set of descriptors within them fits:
 //   a request has at most ns_hi = att_nsplit(1, nb_max) splits (the rule grows with the keys and
-//   shrinks with the rows), and a split request at most kAttTargetItems / (Hkv qt) + 1 splits plus
-//   the ones its key span forces, so over the launch
-//     items      <= n_req kAttTargetItems + Hkv extra (ceil(rows G / 128) + n_req)
-//     split rows <= n_req ceil(128 kAttTargetItems / Hq) + extra rows
+//   shrinks with the rows), and a split request at most T / (Hkv qt) + 1 splits plus the ones its
+//   key span forces (T = att_target_items(tr), tr = att_tile_rows(D) packed rows per tile), so over
+//   the launch
+//     items      <= n_req T + Hkv extra (ceil(rows G / tr) + n_req)
+//     split rows <= n_req ceil(tr T / Hq) + extra rows
 //   with extra = 1 + ceil(nb_max / kAttMaxSplitBlocks); each bound also <= the plain product.
 // The grid holds at most kAttMaxGrid workgroups (a few per CU); each walks its items in turn.
 constexpr int64_t kAttMaxGrid = 4096;
@@ -193,18 +194,19 @@ AttPlan plan_attention(int32_t n_req, int32_t rows, int32_t max_rows, int32_t ma
   p.mfma = dtype == DG_BF16 && (D == 128 || D == 256);
   if (!p.mfma) return p;
   const int64_t G = Hq / Hkv;
-  const int64_t qt_max = cdiv(static_cast<int64_t>(max_rows) * G, kAttRows);
+  const int64_t tr = att_tile_rows(D), target = att_target_items(att_tile_rows(D));
+  const int64_t qt_max = cdiv(static_cast<int64_t>(max_rows) * G, tr);
   const int64_t nb_max = cdiv(max_keys, kAttKeys);
-  const int64_t ns_hi = att_nsplit<int64_t>(1, nb_max, Hkv);
+  const int64_t ns_hi = att_nsplit<int64_t>(1, nb_max, Hkv, target);
   const int64_t extra = 1 + cdiv(nb_max, kAttMaxSplitBlocks);
   p.item_cap = std::min<int64_t>(static_cast<int64_t>(n_req) * ns_hi * Hkv * qt_max,
-                                 static_cast<int64_t>(n_req) * kAttTargetItems +
-                                     Hkv * extra * (cdiv(static_cast<int64_t>(rows) * G, kAttRows) + n_req));
+                                 static_cast<int64_t>(n_req) * target +
+                                     Hkv * extra * (cdiv(static_cast<int64_t>(rows) * G, tr) + n_req));
   p.grid = round_up(static_cast<size_t>(std::min<int64_t>(p.item_cap, kAttMaxGrid)), 8);
   p.fits = p.item_cap < (int64_t{1} << 31);
   p.part_cap = ns_hi < 2 ? 0
                          : std::min<int64_t>(ns_hi * rows, static_cast<int64_t>(n_req) *
-                                                                   cdiv(static_cast<int64_t>(kAttRows) * kAttTargetItems, Hq) +
+                                                                   cdiv(tr * target, Hq) +
                                                                extra * rows);
   if (p.part_cap > 0) {
     const size_t n = static_cast<size_t>(p.part_cap) * Hq;
@@ -235,6 +237,7 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
   a.G = Hq / Hkv;
   a.page_size = page_size;
   a.scale_log2 = scale * kLog2e;
+  a.tile_rows = att_tile_rows(D);
   a.n_req = n_req;
   a.item_cap = plan.item_cap;
   a.part_cap = plan.part_cap;
@@ -244,9 +247,9 @@ dg_status launch_mfma(AttArgs& a, const AttPlan& plan, const void* q, const void
   a.n_part = plan.part_cap > 0 ? reinterpret_cast<int64_t*>(reinterpret_cast<char*>(ws) + plan.off_np) : nullptr;
   const dim3 grid(static_cast<unsigned>(plan.grid));
   if (D == 256)
-    attend_mfma16_kernel<256, E8><<<grid, kAtt16Threads, 0, s>>>(a);
+    attend_mfma16_kernel<256, E8><<<grid, att_threads(256), 0, s>>>(a);
   else
-    attend_mfma16_kernel<128, E8><<<grid, kAtt16Threads, 0, s>>>(a);
+    attend_mfma16_kernel<128, E8><<<grid, att_threads(128), 0, s>>>(a);
   DG_LAUNCHED();
   if (plan.part_cap > 0) {
     const dim3 mgrid(static_cast<unsigned>(std::min<int64_t>(rows, 2048)),

@@ -55,12 +55,17 @@ namespace dg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kAttRows = 128;   // packed query rows per workgroup
+// Packed query rows per workgroup (16 per wave): 128 at head_dim 256; 64 at head_dim 128, where the
+// blocks of a 64-row tile (68 KB of LDS) let two workgroups share a CU and a request with 64 packed
+// rows per KV head (16 rows x 4 query heads of a group) fills its tiles instead of half of them.
+// Fixed by the head size, so a request's tiling depends on its own shape only.
+__host__ __device__ constexpr int att_tile_rows(int D) { return D > 128 ? 128 : 64; }
 constexpr int kAttKeys = 64;    // keys per block
 constexpr int kAttMaxPages = 1024;  // page ids of one split staged in LDS (16K keys)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMergeSplits = 16;     // the most splits of one request
-constexpr int kAttTargetItems = 256;  // work items a request alone is split into at most (one per CU)
+// work items a request alone is split into at most: one per CU for 128-row tiles, two for 64-row tiles
+__host__ __device__ constexpr int att_target_items(int tile_rows) { return 256 * 128 / tile_rows; }
 constexpr int kAttMaxSplitBlocks = kAttMaxPages / 4 - 1;  // a split's pages plus one block fit the staged list
 
 // Keys a request's rows see together: the whole request, or at most its rows plus two windows.
@@ -70,14 +75,12 @@ __host__ __device__ inline int64_t att_span(int64_t cached, int64_t nr, int64_t 
 }
 
 // KV splits of a request with qt row tiles per KV head and nb 64-key blocks (its own shape only):
-// enough splits that the request alone gives about kAttTargetItems work items, at least 4 blocks
-// per split, at most kMergeSplits, and few enough blocks per split for the staged page list.
+// enough splits that the request alone gives about `target` work items, at least 4 blocks per
+// split, at most kMergeSplits, and few enough blocks per split for the staged page list.
 template <typename I>
-__host__ __device__ inline I att_nsplit(I qt, I nb, I Hkv) {
-  // ceil(kAttTargetItems / (Hkv qt)), without forming a product that could overflow
-  const I want = (qt >= kAttTargetItems || Hkv >= kAttTargetItems || Hkv * qt >= kAttTargetItems)
-                     ? I(1)
-                     : (kAttTargetItems + Hkv * qt - 1) / (Hkv * qt);
+__host__ __device__ inline I att_nsplit(I qt, I nb, I Hkv, I target) {
+  // ceil(target / (Hkv qt)), without forming a product that could overflow
+  const I want = (qt >= target || Hkv >= target || Hkv * qt >= target) ? I(1) : (target + Hkv * qt - 1) / (Hkv * qt);
   I n = nb / 4;
   n = n < want ? n : want;
   n = n < kMergeSplits ? n : I(kMergeSplits);
@@ -100,6 +103,7 @@ struct AttArgs {
   int32_t page_table_len;
   const dg_split* splits;
   int32_t n_req, rows, Hq, Hkv, G, page_size;
+  int32_t tile_rows;    // packed query rows per work item: att_tile_rows(D)
   float scale_log2;     // scale * log2(e)
   int64_t item_cap;     // work items the grid holds (the host bound)
   int64_t part_cap;     // split rows the workspace holds
@@ -166,7 +170,7 @@ DG_DEV int2 att_row_keys(const dg_split& sp, int j) {
 
 // ---------------------------------------------------------------- per-request plan and work items
 // A request's plan from its own descriptor: rows nr (clamped to the launch), row tiles qt of
-// kAttRows packed rows per KV head, splits ns and keys per split sk (a multiple of kAttKeys).  A
+// a.tile_rows packed rows per KV head, splits ns and keys per split sk (a multiple of kAttKeys).  A
 // request without rows, or whose key span is beyond what kMergeSplits staged splits hold, has no
 // work (ns = 0): a bad descriptor yields a wrong result, never an out-of-range access.
 struct AttReqPlan {
@@ -178,12 +182,12 @@ DG_DEV AttReqPlan att_req_plan(const AttArgs& a, const dg_split& sp) {
   const int32_t nr = min(static_cast<int32_t>(min(static_cast<int64_t>(max(sp.n_causal, 0)) + max(sp.n_canvas, 0),
                                                   static_cast<int64_t>(a.rows))), a.rows);
   const int64_t nb64 = (att_span(max(sp.cached, 0), nr, sp.window) + kAttKeys - 1) / kAttKeys;
-  const int64_t qt64 = (static_cast<int64_t>(nr) * a.G + kAttRows - 1) / kAttRows;
+  const int64_t qt64 = (static_cast<int64_t>(nr) * a.G + a.tile_rows - 1) / a.tile_rows;
   if (nr == 0 || nb64 > kMergeSplits * kAttMaxSplitBlocks || qt64 > (1 << 24)) return p;
   const int32_t nb = static_cast<int32_t>(nb64);
   p.nr = nr;
   p.qt = static_cast<int32_t>(qt64);
-  const int32_t ns = att_nsplit<int32_t>(p.qt, nb, a.Hkv);
+  const int32_t ns = att_nsplit<int32_t>(p.qt, nb, a.Hkv, att_target_items(a.tile_rows));
   p.sk = (nb + ns - 1) / ns * kAttKeys;
   p.ns = (nb * kAttKeys + p.sk - 1) / p.sk;
   return p;
@@ -511,7 +515,8 @@ DG_DEV void att_append8(const AttArgs& a, const dg_split& sp, int hk, int j0, in
 //     order is two transposing LDS reads (4 keys x 16 d each).
 // A row's 64 scores of a block are spread over the four groups; its max and sum are combined with
 // v_permlane16_swap / v_permlane32_swap (no LDS traffic).
-constexpr int kAtt16Threads = 512;
+// threads of a workgroup at head size D
+__host__ __device__ constexpr int att_threads(int D) { return att_tile_rows(D) / 16 * kWave; }
 
 DG_DEV float quad_group_max(float v) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
@@ -543,7 +548,8 @@ DG_DEV bf16x8 att_vfrag16(const char* p) {
 // One work item: row tile `qtile` of request it.req, KV head it.hk, key split it.split.
 template <int D, bool E8>
 DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it) {
-  constexpr int NT = kAtt16Threads;
+  constexpr int ROWS = att_tile_rows(D);
+  constexpr int NT = att_threads(D);
   constexpr int kDSteps = D / 32;                // MFMA k-steps over D
   constexpr int kDTiles = D / 16;                // 16-wide output tiles over D
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
@@ -555,8 +561,8 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
   const dg_split sp = a.splits[it.req];
   const int nr = it.p.nr;
   const bool split_req = it.p.ns > 1;
-  const int m_tile0 = qtile * kAttRows;
-  const int j_last = min(nr - 1, (m_tile0 + kAttRows - 1) / a.G);
+  const int m_tile0 = qtile * ROWS;
+  const int j_last = min(nr - 1, (m_tile0 + ROWS - 1) / a.G);
   const int tile_lo = att_row_keys(sp, m_tile0 / a.G).x & ~(kAttKeys - 1);
   const int tile_hi = att_row_keys(sp, j_last).y;
   const int k_begin = tile_lo + split * it.p.sk;
@@ -777,7 +783,7 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
   // append: the split-0 workgroup writes the causal rows whose first packed row is in its tile
   if (split == 0) {
     const int j0 = (m_tile0 + a.G - 1) / a.G;
-    const int j1 = min(sp.n_causal, (m_tile0 + kAttRows + a.G - 1) / a.G);
+    const int j1 = min(sp.n_causal, (m_tile0 + ROWS + a.G - 1) / a.G);
     if (j0 < j1) {
       if constexpr (E8)
         att_append8<D, NT>(a, sp, hk, j0, j1);
@@ -808,7 +814,7 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
 // tiles that read the same K/V (same request, split and KV head, consecutive items) run on one XCD
 // and share its L2.  Each workgroup first recomputes the launch totals from the descriptors.
 template <int D, bool E8>
-__global__ __launch_bounds__(kAtt16Threads) void attend_mfma16_kernel(AttArgs a) {
+__global__ __launch_bounds__(att_threads(D), 2) void attend_mfma16_kernel(AttArgs a) {  // two waves per SIMD
   __shared__ __attribute__((aligned(1024))) AttSmem<D, E8> sm;
   // requests 0 .. 63: their plans and prefix sums stay in registers (one pass for launches of up to
   // 64 requests; larger launches rescan the descriptors per item)
