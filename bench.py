@@ -545,46 +545,50 @@ def bench_batched(K: int, W: int, cpu: bool) -> dict:
                       roof, cpu_line, {"positions_per_iteration": positions / K, "settle_steps": n_settle})
 
 
-def _cpu_batched(loop, t, E, w, cfg, sched):
-    """The oracle on one request's denoise iteration (its attention over its own pages, sampler,
-    accept, convergence, P.E + MLP of its 256 rows) of the same loop state and inputs."""
+def _cpu_batched(loop, t, E, w, cfg, sched, n_req=2):
+    """The oracle on n_req requests' denoise iterations (each request's attention over its own pages,
+    sampler, accept, convergence, P.E + MLP of its 256 rows) of the same loop state and inputs."""
     import numpy as np
     import torch
 
     from oracle import accept, attention, converged, sampler, selfcond
     C, V, D, ps = cfg["C"], cfg["V"], cfg["D"], cfg["page_size"]
     f = lambda x: x.float().cpu().numpy().astype(np.float64)
-    r = 0
     sp, _ = loop._splits()
-    i = [k for k in range(sp.shape[0]) if sp[k, 4] == sched["page0"][r]][0]
-    row0, cached, nc, nv = (int(x) for x in sp[i][:4])
-    p0, p1 = int(sched["page0"][r]), int(sched["page0"][r + 1])
-    pt = torch.as_tensor(sched["page_table"][p0:p1].astype(np.int64), device="cuda")
-    sl = slice(row0, row0 + nc + nv)
-    q, k, v = f(t["q"][sl]), f(t["k"][sl]), f(t["v"][sl])
-    kc, vc = f(t["k_cache"][pt]), f(t["v_cache"][pt])
-    logits = f(t["logits"][0][r * C:(r + 1) * C])
+    host = []
+    for r in range(n_req):
+        i = [k for k in range(sp.shape[0]) if sp[k, 4] == sched["page0"][r]][0]
+        row0, cached, nc, nv = (int(x) for x in sp[i][:4])
+        p0, p1 = int(sched["page0"][r]), int(sched["page0"][r + 1])
+        pt = torch.as_tensor(sched["page_table"][p0:p1].astype(np.int64), device="cuda")
+        sl = slice(row0, row0 + nc + nv)
+        host.append(dict(q=f(t["q"][sl]), k=f(t["k"][sl]), v=f(t["v"][sl]), kc=f(t["k_cache"][pt]),
+                         vc=f(t["v_cache"][pt]), logits=f(t["logits"][0][r * C:(r + 1) * C]),
+                         seed=int(sched["seeds"][r]), shape=(cached, nc, nv)))
     Eh = E.float().cpu().numpy()
     wh = [f(x) for x in w]
-    seed = int(sched["seeds"][r])
-    log("cpu baseline: timing the oracle on one request's iteration")
+    log(f"cpu baseline: timing the oracle on {n_req} requests' iterations")
     threads = _blas_threads()
     t0 = time.perf_counter()
-    attention.canvas_attention(q, k, v, kc, vc, np.arange(kc.shape[0], dtype=np.int32), [(0, cached, nc, nv, 0)], ps,
-                               1.0 / math.sqrt(D))
-    so = sampler.denoise_sample(logits, 1.0, [seed], [1], C)
-    st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
-                             unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
-                             step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
-    accept.entropy_accept(so.entropy[None, :], so.sample[None, :], st.canvas, cfg["budget"], [seed], [1], V)
-    converged.converged(so.argmax[None, :], so.entropy[None, :], st, cfg["k"], cfg["tau"], cfg["max_steps"], [seed], V)
-    P = selfcond.probs_from_stats(logits, 1.0, so.row_max, so.row_lnz)
-    selfcond.selfcond_embed(P, st.canvas, st.sc_on, Eh, *wh, C, to_bf16=True)
+    for h in host:
+        cached, nc, nv = h["shape"]
+        attention.canvas_attention(h["q"], h["k"], h["v"], h["kc"], h["vc"], np.arange(h["kc"].shape[0], dtype=np.int32),
+                                   [(0, cached, nc, nv, 0)], ps, 1.0 / math.sqrt(D))
+        so = sampler.denoise_sample(h["logits"], 1.0, [h["seed"]], [1], C)
+        st = converged.LoopState(canvas=np.zeros((1, C), np.int64), prev_argmax=np.zeros((1, C), np.int64),
+                                 unchanged=np.zeros(1, np.int64), step_in_block=np.ones(1, np.int64),
+                                 step_global=np.ones(1, np.int64), sc_on=np.ones(1, np.uint8))
+        accept.entropy_accept(so.entropy[None, :], so.sample[None, :], st.canvas, cfg["budget"], [h["seed"]], [1], V)
+        converged.converged(so.argmax[None, :], so.entropy[None, :], st, cfg["k"], cfg["tau"], cfg["max_steps"],
+                            [h["seed"]], V)
+        P = selfcond.probs_from_stats(h["logits"], 1.0, so.row_max, so.row_lnz)
+        selfcond.selfcond_embed(P, st.canvas, st.sc_on, Eh, *wh, C, to_bf16=True)
     dt = time.perf_counter() - t0
-    return dict(value=C / dt, unit="positions/s", cores=_cores(threads), kind="oracle",
-                sample=(f"one request's iteration of the batched loop on the host in fp64 numpy: attention for its "
-                        f"{nc + nv} rows x {cfg['Hq']} heads over {cached + nc + nv} keys, the sampler over {C} rows "
-                        f"of V={V}, accept + converged, P.E + MLP for {C} rows against the full table; {dt:.1f} s"))
+    keys = ", ".join(f"{nc + nv} rows over {cached + nc + nv} keys" for cached, nc, nv in (h["shape"] for h in host))
+    return dict(value=n_req * C / dt, unit="positions/s", cores=_cores(threads), kind="oracle",
+                sample=(f"{n_req} requests' iterations of the batched loop on the host in fp64 numpy: attention "
+                        f"({keys}, {cfg['Hq']} heads), the sampler over {C} rows of V={V}, accept + converged, "
+                        f"P.E + MLP for {C} rows against the full table, per request; {dt:.1f} s"))
 
 
 def bench_structured_read(K: int, W: int, cpu: bool) -> dict:
@@ -763,7 +767,7 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
     if cpu:
         from oracle import attention, verify
         f = lambda x: x.float().cpu().numpy().astype(np.float64)
-        reqs = (0, 1, 2, 3)
+        reqs = tuple(range(16))
         host = []
         for x, lay in zip(L, lays):
             for r in reqs:
@@ -774,7 +778,7 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
                              f(x["vc"][pages]), s_))
         hl = f(logits[:len(reqs) * L16])
         threads = _blas_threads()
-        log("cpu baseline: timing the oracle on 4 requests")
+        log(f"cpu baseline: timing the oracle on {len(reqs)} requests")
         tc = time.perf_counter()
         for qh, kh, vh, kch, vch, s_ in host:
             attention.canvas_attention(qh, kh, vh, kch, vch, np.arange(kch.shape[0], dtype=np.int32),
@@ -783,9 +787,9 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
         verify.verify_prefix(am, tgt[:len(reqs)])
         dt = time.perf_counter() - tc
         cpu_line = dict(value=len(reqs) * L16 / dt, unit="draft positions/s", cores=_cores(threads), kind="oracle",
-                        sample=(f"4 of the 128 requests on the host in fp64 numpy: 5 layers of attention for their "
-                                f"16 draft rows x {Hq} heads over their injected context, the argmax of their 64 "
-                                f"logit rows of V={V}, verification; {dt:.1f} s"))
+                        sample=(f"{len(reqs)} of the 128 requests on the host in fp64 numpy: 5 layers of attention "
+                                f"for their 16 draft rows x {Hq} heads over their injected context, the argmax of "
+                                f"their {len(reqs) * L16} logit rows of V={V}, verification; {dt:.1f} s"))
     return _json_line("draft positions/sec (block draft: 128 x 16 positions, 5 layers, V=151936) + % HBM roofline",
                       B * L16 * K / (ms * 1e-3), "draft positions/s", K, W, ms,
                       {"workload": "block_draft", "requests": B, "block": L16, "layers": layers,
@@ -936,7 +940,7 @@ def main():
                                            "mfma_frac": lm_tf / MFMA_PEAK_TFLOPS}
         del kernels["denoise_sample"]
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, 1 if lmhead else args.cpu_steps)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
         result["parity"] = w.parity
         result["near_ties"] = w.parity["near_ties"]
     else:
