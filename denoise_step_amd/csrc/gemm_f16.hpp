@@ -306,17 +306,28 @@ DG_DEV void gemm_splitk_body(const GemmArgs& g) {
   constexpr int kBs = BF8 ? TN * kGemmTK / 2 : TN * kGemmTK;  // halves per B stage
   __shared__ __attribute__((aligned(16))) _Float16 As[kGemmStages * kAs];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmStages * kBs];
-  // XCD-aware tile order: linear tile t = (split * ntiles + ntile) * mtiles + mtile; XCD x owns the
-  // contiguous range [x per_xcd, (x + 1) per_xcd) and its 32 CUs run 32 consecutive tiles at a time,
-  // which share their A chunk (one M tile: the N tiles of one split) or their B chunk (several M
-  // tiles: the M tiles of one split and N tile).
+  // XCD-aware tile order: XCD x owns the contiguous range [x per_xcd, (x + 1) per_xcd) of linear
+  // tiles and its 32 CUs run 32 consecutive ones at a time.  One M tile (the single canvas): t =
+  // (split * ntiles + ntile) * mtiles + mtile, so the 32 concurrent tiles are N tiles of one split and
+  // share their A chunk.  Several M tiles (a batch of canvases, B loaded normally): within a split t
+  // walks blocks of 4 M tiles x 8 N tiles, one block per 32 consecutive tiles, so the concurrent
+  // workgroups share 4 A and 8 B chunks through the XCD's L2 instead of reading 32 A chunks.
   const int total = g.mtiles * g.ntiles * g.splits;
   const int per_xcd = (total + kGemmXcds - 1) / kGemmXcds;
   const int t = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
   if (t >= total) return;
-  const int mt = t % g.mtiles;
-  const int nt = (t / g.mtiles) % g.ntiles;
-  const int split = t / (g.mtiles * g.ntiles);
+  int mt, nt, split;
+  if (!BNT && g.mtiles % 4 == 0 && g.ntiles % 8 == 0 && per_xcd % 32 == 0) {
+    const int per_split = g.mtiles * g.ntiles;  // a multiple of 32
+    split = t / per_split;
+    const int loc = t - split * per_split, blk = loc / 32, l = loc % 32, nbn = g.ntiles / 8;
+    mt = (blk / nbn) * 4 + l / 8;
+    nt = (blk % nbn) * 8 + l % 8;
+  } else {
+    mt = t % g.mtiles;
+    nt = (t / g.mtiles) % g.ntiles;
+    split = t / (g.mtiles * g.ntiles);
+  }
   const int m0 = mt * kGemmTM, n0 = nt * TN;
   const int k_begin = split * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
