@@ -238,10 +238,10 @@ DG_DEV bool att_totals(const AttArgs& a, int64_t& n_items, int64_t& np) {
   return ni <= a.item_cap && np <= a.part_cap;
 }
 
-// The request of item t among the 64 requests from r0 (per lane: its request's plan p, items, part
-// and the inclusive scans of items and part), or false when none of them holds it.
-DG_DEV bool att_pick(const AttArgs& a, int64_t t, int r0, const AttReqPlan& p, int64_t items, int64_t part,
-                     int64_t first, int64_t part_first, AttItem& it) {
+// The request of item t among the 64 requests from r0 (per lane: its request's plan p, its items and
+// the exclusive scans of items and parts), or false when none of them holds it.
+DG_DEV bool att_pick(const AttArgs& a, int64_t t, int r0, const AttReqPlan& p, int64_t items, int64_t first,
+                     int64_t part_first, AttItem& it) {
   const uint64_t own = __ballot(items > 0 && t >= first && t < first + items);
   if (!own) return false;
   const int src = __ffsll(static_cast<unsigned long long>(own)) - 1;
@@ -268,7 +268,7 @@ DG_DEV AttItem att_find(const AttArgs& a, int64_t t) {
     int64_t items, part;
     att_req_counts(a, r0 + lane, p, items, part);
     const int64_t inc_i = wave_incl_scan(items), inc_p = wave_incl_scan(part);
-    if (att_pick(a, t, r0, p, items, part, base_i + inc_i - items, base_p + inc_p - part, it)) return it;
+    if (att_pick(a, t, r0, p, items, base_i + inc_i - items, base_p + inc_p - part, it)) return it;
     base_i += __shfl(inc_i, kWave - 1, kWave);
     base_p += __shfl(inc_p, kWave - 1, kWave);
   }
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(att_threads(D), 2) void attend_mfma16_kernel(AttArg
   for (int64_t t = lo + blockIdx.x / 8; t < hi; t += stride) {
     AttItem it{0, 0, 0, 0, AttReqPlan{0, 0, 0, kAttKeys}, 0};
     if (one_pass) {
-      if (!att_pick(a, t, 0, p0, items0, part0, inc_i0 - items0, inc_p0 - part0, it)) break;
+      if (!att_pick(a, t, 0, p0, items0, inc_i0 - items0, inc_p0 - part0, it)) break;
     } else {
       it = att_find(a, t);
       if (it.p.ns == 0) break;  // not reached for t below the total

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kWave) void allowed_probs_kernel(const void* __rest
 
 template <bool BF16>
 __global__ void gather_rows_kernel(const void* __restrict__ table, int32_t n_table, int32_t d,
-                                   const int32_t* __restrict__ idx, int32_t n, void* __restrict__ out) {
-  const int i = blockIdx.x;
+                                   const int32_t* __restrict__ idx, void* __restrict__ out) {
+  const int i = blockIdx.x;  // one workgroup per index: the grid is the index count
   const int64_t src = min(max(idx[i], 0), n_table - 1);
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     if constexpr (BF16)
@@ -197,9 +197,9 @@ extern "C" dg_status dg_gather_rows(const void* table, int32_t n_table, int32_t 
   DG_ARG(table && idx && out && n_table > 0 && d > 0 && n > 0);
   DG_UNSUP(dtype == DG_BF16 || dtype == DG_F32);
   if (dtype == DG_BF16)
-    gather_rows_kernel<true><<<n, 256, 0, as_stream(stream)>>>(table, n_table, d, idx, n, out);
+    gather_rows_kernel<true><<<n, 256, 0, as_stream(stream)>>>(table, n_table, d, idx, out);
   else
-    gather_rows_kernel<false><<<n, 256, 0, as_stream(stream)>>>(table, n_table, d, idx, n, out);
+    gather_rows_kernel<false><<<n, 256, 0, as_stream(stream)>>>(table, n_table, d, idx, out);
   DG_LAUNCHED();
   return DG_OK;
 }

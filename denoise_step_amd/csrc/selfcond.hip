@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void glu_reduce_kernel(const float* __restrict
   for (int c = 0; c < C; ++c) {
     g[c] = make_float4(gelu_tanh(g[c].x * si) * (u[c].x * si), gelu_tanh(g[c].y * si) * (u[c].y * si),
                        gelu_tanh(g[c].z * si) * (u[c].z * si), gelu_tanh(g[c].w * si) * (u[c].w * si));
-    if (4 * (threadIdx.x + 256 * c) < H) amax = fmaxf(amax, f4_amax(g[c]));
+    if (4 * static_cast<int>(threadIdx.x + 256 * c) < H) amax = fmaxf(amax, f4_amax(g[c]));
   }
   const float sc = row_pow2_scale(block_max<256>(amax, red));
 #pragma unroll
