@@ -302,12 +302,13 @@ DG_DEV const uint16_t* att_row(const AttArgs& a, const dg_split& sp, int4 pq, in
 // block, one whole page of the cache.
 constexpr int kAttCopyWaves = 4;
 
-// One tensor (K or V) of the block at kb into dst, issued by copying wave w (0 - 3).  When its page
-// holds only cached keys below k_end, or only fresh rows inside the launch's rows, the copies take a
-// scalar base and the precomputed per-lane offsets.
+// One tensor (K or V) of the block at kb into dst, issued by copying wave w (0 - 3); pq holds the
+// physical ids of the block's four 16-key pages (in range; only used for keys below `cached`).  When
+// its page holds only cached keys below k_end, or only fresh rows inside the launch's rows, the
+// copies take a scalar base and the precomputed per-lane offsets.
 template <int D>
-DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages, int32_t page_lo, int hk, int kb,
-                     int k_end, bool is_v, uint16_t* dst) {
+DG_DEV void att_load(const AttArgs& a, const dg_split& sp, int4 pq, int hk, int kb, int k_end, bool is_v,
+                     uint16_t* dst) {
   constexpr int kChunks = D / 8;
   constexpr int kKeysPerCopy = kWave / kChunks;
   constexpr int kPerWave = kChunks / kAttCopyWaves;  // copies per wave of one tensor and block
@@ -326,7 +327,7 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
     const int kend = __builtin_amdgcn_readfirstlane(k_end);
     const int hks = __builtin_amdgcn_readfirstlane(hk);
     if (k0 + 15 < min(cached, kend)) {
-      const int64_t pid = __builtin_amdgcn_readfirstlane(pages[k0 / 16 - page_lo]);  // staged, in range
+      const int64_t pid = __builtin_amdgcn_readfirstlane(wave == 0 ? pq.x : (wave == 1 ? pq.y : (wave == 2 ? pq.z : pq.w)));
       const int64_t head = (pid * a.Hkv + hks) * 16 * D * 2;
       const char* base = reinterpret_cast<const char*>(is_v ? a.v_cache : a.k_cache) + head;
 #pragma unroll
@@ -352,10 +353,7 @@ DG_DEV void att_load(const AttArgs& a, const dg_split& sp, const int32_t* pages,
       return;
     }
   }
-  // pages straddling the cache end or k_end (or rows outside the launch): per-lane addresses.  The
-  // page ids of the block's four 16-key groups in one 16-byte read (kb - k_begin is a multiple of 64,
-  // so the slot is 4-aligned; slots past the staged range are only picked by keys >= cached)
-  const int4 pq = *reinterpret_cast<const int4*>(pages + (kb / 16 - page_lo));
+  // pages straddling the cache end or k_end (or rows outside the launch): per-lane addresses
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
     const int q = wave * kPerWave + i;
@@ -545,73 +543,160 @@ DG_DEV bf16x8 att_vfrag16(const char* p) {
   return v;
 }
 
-// One work item: row tile `qtile` of request it.req, KV head it.hk, key split it.split.
-template <int D, bool E8>
-DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it) {
+// Uniform description of a work item (row tile it.qtile of request it.req, KV head it.hk, key split
+// it.split): its descriptor, first packed row and key range.  The tile sees keys [lo of its first
+// row, hi of its last row) (both edges grow with the row); the splits cut that range from its first
+// 64-aligned block, the last split also taking the one block the alignment can add beyond ns * sk.
+struct AttRange {
+  dg_split sp;
+  int32_t m_tile0, k_begin, k_end, page_lo;
+};
+
+DG_DEV int32_t att_u(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+DG_DEV int64_t att_u64(int64_t v) {
+  const uint64_t x = static_cast<uint64_t>(v);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(att_u(static_cast<int32_t>(x >> 32)))) << 32) |
+                              static_cast<uint32_t>(att_u(static_cast<int32_t>(x & 0xffffffffu))));
+}
+
+// The item's fields (equal in every lane after a pick) moved into scalar registers, so that the
+// ranges and copy addresses derived from them stay scalar across the walk.
+DG_DEV AttItem att_uniform(const AttItem& it) {
+  AttItem u;
+  u.req = att_u(it.req);
+  u.split = att_u(it.split);
+  u.hk = att_u(it.hk);
+  u.qtile = att_u(it.qtile);
+  u.p = AttReqPlan{att_u(it.p.nr), att_u(it.p.qt), att_u(it.p.ns), att_u(it.p.sk)};
+  u.part_off = att_u64(it.part_off);
+  return u;
+}
+
+template <int D>
+DG_DEV AttRange att_range(const AttArgs& a, const AttItem& it) {
+  constexpr int ROWS = att_tile_rows(D);
+  AttRange r;
+  r.sp = a.splits[it.req];
+  r.m_tile0 = it.qtile * ROWS;
+  const int j_last = min(it.p.nr - 1, (r.m_tile0 + ROWS - 1) / a.G);
+  const int tile_lo = att_row_keys(r.sp, r.m_tile0 / a.G).x & ~(kAttKeys - 1);
+  const int tile_hi = att_row_keys(r.sp, j_last).y;
+  r.k_begin = tile_lo + it.split * it.p.sk;
+  r.k_end = min(tile_hi, r.k_begin + it.p.sk + (it.split == it.p.ns - 1 ? kAttKeys : 0));
+  r.page_lo = r.k_begin / 16;
+  r.sp = dg_split{att_u(r.sp.row0), att_u(r.sp.cached), att_u(r.sp.n_causal), att_u(r.sp.n_canvas),
+                  att_u(r.sp.page0), att_u(r.sp.window)};
+  r.m_tile0 = att_u(r.m_tile0);
+  r.k_begin = att_u(r.k_begin);
+  r.k_end = att_u(r.k_end);
+  r.page_lo = att_u(r.page_lo);
+  return r;
+}
+
+// Physical ids of the four 16-key pages of the block at kb, read from the page table (indexes and ids
+// clamped into range; ids past the request's pages are only used for keys >= cached).
+DG_DEV int4 att_block_pages(const AttArgs& a, const dg_split& sp, int kb) {
+  auto id = [&](int i) {
+    const int ti = min(max(sp.page0 + kb / 16 + i, 0), a.page_table_len - 1);
+    return min(max(a.page_table[ti], 0), a.n_pages - 1);
+  };
+  return make_int4(id(0), id(1), id(2), id(3));
+}
+
+// The workgroup's work items t, t + stride, ... below t_end (pick(t, item) names item t).  While an
+// item runs its last block, the next item's first K/V block is copied into the free buffer, its Q
+// fragments loaded (once the last score MFMAs have read this item's) and its page ids staged, so the
+// next item starts without waiting for its own loads (bf16 cache; the E4M3 path loads each item's
+// first block when it starts).  Every wave waits for all of its loads before an item's block loop:
+// a Q load still in flight there would have the compiler wait on the vector-memory counter inside
+// the loop, where that wait also covers the next block's copies and serialises them with the MFMAs.
+template <int D, bool E8, class Pick>
+DG_DEV void att_walk(const AttArgs& a, AttSmem<D, E8>& sm, int64_t t, int64_t t_end, int64_t stride, Pick pick) {
   constexpr int ROWS = att_tile_rows(D);
   constexpr int NT = att_threads(D);
   constexpr int kDSteps = D / 32;                // MFMA k-steps over D
   constexpr int kDTiles = D / 16;                // 16-wide output tiles over D
   constexpr float kRescaleAbove = 8.f;           // log2 units: move the reference when exceeded by 2^8
-
-  // The tile sees keys [lo of its first row, hi of its last row) (both edges grow with the row); the
-  // splits cut that range from its first 64-aligned block, the last split also taking the one block
-  // the alignment can add beyond ns * sk.
-  const int qtile = it.qtile, hk = it.hk, split = it.split;
-  const dg_split sp = a.splits[it.req];
-  const int nr = it.p.nr;
-  const bool split_req = it.p.ns > 1;
-  const int m_tile0 = qtile * ROWS;
-  const int j_last = min(nr - 1, (m_tile0 + ROWS - 1) / a.G);
-  const int tile_lo = att_row_keys(sp, m_tile0 / a.G).x & ~(kAttKeys - 1);
-  const int tile_hi = att_row_keys(sp, j_last).y;
-  const int k_begin = tile_lo + split * it.p.sk;
-  const int k_end = min(tile_hi, k_begin + it.p.sk + (split == it.p.ns - 1 ? kAttKeys : 0));
+  constexpr int kPageRegs = kAttMaxPages / NT;   // staged page ids per thread
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int g = lane >> 4, t16 = lane & 15;
-  const int m = m_tile0 + wave * 16 + t16;
-  const bool row_ok = m < nr * a.G;
-  const int j = row_ok ? m / a.G : 0;
-  const int h = hk * a.G + (row_ok ? m % a.G : 0);
-  const int row = sp.row0 + j;
-  const bool row_in = row >= 0 && row < a.rows;
-  const int row_c = min(max(row, 0), a.rows - 1);
-  const int2 rk = row_ok ? att_row_keys(sp, j) : make_int2(0, sp.cached + nr);
-  const int lo = rk.x, hi = rk.y;
-  int wave_hi = hi, wave_lo = lo;
+  const bool lead = __builtin_amdgcn_readfirstlane(wave) < kAttCopyWaves;  // the copying waves
+
+  AttItem it{0, 0, 0, 0, AttReqPlan{0, 0, 0, kAttKeys}, 0};
+  if (t >= t_end || !pick(t, it)) return;
+  it = att_uniform(it);
+  AttRange r = att_range<D>(a, it);
+
+  // this lane's packed row of the current item: query row j, head h, keys [lo, hi)
+  bool row_ok = false, row_in = false;
+  int j = 0, h = 0, row = 0, lo = 0, hi = 0, wave_lo = 0, wave_hi = 0;
+  auto set_rows = [&]() {
+    const int m = r.m_tile0 + wave * 16 + t16;
+    row_ok = m < it.p.nr * a.G;
+    j = row_ok ? m / a.G : 0;
+    h = it.hk * a.G + (row_ok ? m % a.G : 0);
+    row = r.sp.row0 + j;
+    row_in = row >= 0 && row < a.rows;
+    const int2 rk = row_ok ? att_row_keys(r.sp, j) : make_int2(0, r.sp.cached + it.p.nr);
+    lo = rk.x;
+    hi = rk.y;
+    int wh = hi, wl = lo;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
-    wave_lo = max(wave_lo, __shfl_xor(wave_lo, o, kWave));
-  }
-  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);  // equal in every lane: the mask test branches
-  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
-
-  // stage the physical page ids of the split's prefix positions (clamped into range)
-  const int page_lo = k_begin / 16;
-  if constexpr (!E8) {
-    const int page_hi = min((min(k_end, sp.cached) + 15) / 16, page_lo + kAttMaxPages);
-    for (int p = page_lo + tid; p < page_hi; p += NT) {
-      const int ti = min(max(sp.page0 + p, 0), a.page_table_len - 1);
-      sm.pages[p - page_lo] = min(max(a.page_table[ti], 0), a.n_pages - 1);
+    for (int o = 32; o > 0; o >>= 1) {
+      wh = min(wh, __shfl_xor(wh, o, kWave));
+      wl = max(wl, __shfl_xor(wl, o, kWave));
     }
-  }
+    wave_hi = __builtin_amdgcn_readfirstlane(wh);  // equal in every lane: the mask test branches
+    wave_lo = __builtin_amdgcn_readfirstlane(wl);
+  };
 
-  // Q^T fragment (B operand): row t16, d 32 s + 8 g .. + 7
+  // Q^T fragment (B operand) of item (qi, qr): row t16, d 32 s + 8 g .. + 7
   bf16x8 qf[kDSteps];
-  {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(row_c) * a.Hq + h) * D;
+  auto load_q = [&](const AttItem& qi, const AttRange& qr) {
+    const int m = qr.m_tile0 + wave * 16 + t16;
+    const bool ok = m < qi.p.nr * a.G;
+    const int jq = ok ? m / a.G : 0;
+    const int hq = qi.hk * a.G + (ok ? m % a.G : 0);
+    const int rc = min(max(qr.sp.row0 + jq, 0), a.rows - 1);
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(rc) * a.Hq + hq) * D;
 #pragma unroll
     for (int s = 0; s < kDSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  }
+  };
+
+  // The physical page ids of a split's prefix positions, staged in LDS for the copies of its blocks
+  // after the first (clamped into range): loaded into registers first and stored after other loads
+  // have been issued.
+  int32_t pv[kPageRegs];
+  auto page_hi = [&](const AttRange& pr) {
+    return min((min(pr.k_end, pr.sp.cached) + 15) / 16, pr.page_lo + kAttMaxPages);
+  };
+  auto load_pages = [&](const AttRange& pr) {
+    const int ph = page_hi(pr);
+#pragma unroll
+    for (int i = 0; i < kPageRegs; ++i) {
+      const int p = pr.page_lo + tid + i * NT;
+      const int ti = min(max(pr.sp.page0 + p, 0), a.page_table_len - 1);
+      pv[i] = p < ph ? min(max(a.page_table[ti], 0), a.n_pages - 1) : 0;
+    }
+  };
+  auto store_pages = [&](auto& smem, const AttRange& pr) {
+    const int ph = page_hi(pr);
+#pragma unroll
+    for (int i = 0; i < kPageRegs; ++i) {
+      const int p = pr.page_lo + tid + i * NT;
+      if (p < ph) smem.pages[p - pr.page_lo] = pv[i];
+    }
+  };
+  // copying waves: K and V of the block at kb of item (ci, cr) into buffer b (pq: its page ids)
+  auto copy_block = [&](const AttItem& ci, const AttRange& cr, int4 pq, int kb, int b) {
+    att_load<D>(a, cr.sp, pq, ci.hk, kb, cr.k_end, false, sm.K[b]);
+    att_load<D>(a, cr.sp, pq, ci.hk, kb, cr.k_end, true, sm.V[b]);
+  };
 
   floatx4 o[kDTiles];
-#pragma unroll
-  for (int dt = 0; dt < kDTiles; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;
 
   // Per-lane parts of the operand read addresses (att_kslot's swizzle split into a lane part, a part
@@ -730,82 +815,139 @@ DG_DEV void att_run_item(const AttArgs& a, AttSmem<D, E8>& sm, const AttItem& it
     }
   };
 
-  __syncthreads();  // page ids visible
+  int buf = 0;
+  bool ready = false;  // the current item's Q, page ids and first block are in place
   floatx4 sc[4];
-  if constexpr (!E8) {
-    // Waves 0 - 3 copy the next block (K and V) while every wave works on the current one.
-    const bool lead = __builtin_amdgcn_readfirstlane(wave) < kAttCopyWaves;
-    if (lead && k_begin < k_end) {
-      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, false, sm.K[0]);
-      att_load<D>(a, sp, sm.pages, page_lo, hk, k_begin, k_end, true, sm.V[0]);
-      att_wait();
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
-      const bool more = kb + kAttKeys < k_end;
-      if (lead && more) {
-        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, false, sm.K[buf ^ 1]);
-        att_load<D>(a, sp, sm.pages, page_lo, hk, kb + kAttKeys, k_end, true, sm.V[buf ^ 1]);
-      }
-      scores(sm.K[buf], sc);
-      accumulate(kb, sc, sm.V[buf]);
-      if (lead && more) att_wait();
-      __syncthreads();
-      buf ^= 1;
-    }
-  } else {
-    if (k_begin < k_end) {
-      att_load8<D, NT>(a, sp, hk, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
-      att_wait();
-    }
-    __syncthreads();
-    if (k_begin < k_end && k_begin < sp.cached) {
-      att_convert8<D, NT>(a, sp, k_begin, k_end, sm.S, sm.K[0], sm.V[0]);
-      __syncthreads();
-    }
-    int buf = 0;
-    for (int kb = k_begin; kb < k_end; kb += kAttKeys) {
-      const bool more = kb + kAttKeys < k_end;
-      if (more) att_load8<D, NT>(a, sp, hk, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
-      scores(sm.K[buf], sc);
-      accumulate(kb, sc, sm.V[buf]);
-      if (more) att_wait();
-      __syncthreads();
-      if (more && kb + kAttKeys < sp.cached) {
-        att_convert8<D, NT>(a, sp, kb + kAttKeys, k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+  for (;;) {
+    set_rows();
+    if (!ready) {
+      if constexpr (!E8) {
+        // page ids, the first block (its page ids from the table) and Q in flight together
+        load_pages(r);
+        if (lead && r.k_begin < r.k_end) copy_block(it, r, att_block_pages(a, r.sp, r.k_begin), r.k_begin, buf);
+        load_q(it, r);
+        store_pages(sm, r);
+        att_wait();
         __syncthreads();
+      } else {
+        load_q(it, r);
+        if (r.k_begin < r.k_end) {
+          att_load8<D, NT>(a, r.sp, it.hk, r.k_begin, r.k_end, sm.S, sm.K[buf], sm.V[buf]);
+          att_wait();
+        }
+        __syncthreads();
+        if (r.k_begin < r.k_end && r.k_begin < r.sp.cached) {
+          att_convert8<D, NT>(a, r.sp, r.k_begin, r.k_end, sm.S, sm.K[buf], sm.V[buf]);
+          __syncthreads();
+        }
       }
-      buf ^= 1;
     }
-  }
-
-  // append: the split-0 workgroup writes the causal rows whose first packed row is in its tile
-  if (split == 0) {
-    const int j0 = (m_tile0 + a.G - 1) / a.G;
-    const int j1 = min(sp.n_causal, (m_tile0 + ROWS + a.G - 1) / a.G);
-    if (j0 < j1) {
-      if constexpr (E8)
-        att_append8<D, NT>(a, sp, hk, j0, j1);
-      else
-        att_append<D, NT>(a, sp, hk, j0, j1);
-    }
-  }
-
-  if (row_ok && row_in) {
-    // O^T tile dt: this lane holds d = 16 dt + 4 g + e (e = 0 .. 3) of its row
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    const int64_t ridx = split_req ? (it.part_off + static_cast<int64_t>(split) * nr + j) * a.Hq + h
-                                   : static_cast<int64_t>(row) * a.Hq + h;
-    uint16_t* orow = (split_req ? a.o_part : a.out) + ridx * D;
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) {
-      uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16(o[dt][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][1] * inv)) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16(o[dt][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+    for (int dt = 0; dt < kDTiles; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m_ref = -INFINITY;
+    l_run = 0.f;
+
+    bool have_next = false;
+    AttItem it_n = it;
+    AttRange r_n = r;
+    auto find_next = [&]() {
+      have_next = t + stride < t_end && pick(t + stride, it_n);
+      if (have_next) {
+        it_n = att_uniform(it_n);
+        r_n = att_range<D>(a, it_n);
+      }
+    };
+    if constexpr (!E8) {
+      // the copying waves fetch the next block while every wave works on the current one
+      int kb = r.k_begin;
+      for (; kb + kAttKeys < r.k_end; kb += kAttKeys) {
+        // (the block's four page ids from the staged list: kb - k_begin is a multiple of 64, so the
+        // slot is 4-aligned; slots past the staged range are only used for keys >= cached)
+        if (lead)
+          copy_block(it, r, *reinterpret_cast<const int4*>(sm.pages + ((kb + kAttKeys) / 16 - r.page_lo)),
+                     kb + kAttKeys, buf ^ 1);
+        scores(sm.K[buf], sc);
+        accumulate(kb, sc, sm.V[buf]);
+        if (lead) att_wait();
+        __syncthreads();
+        buf ^= 1;
+      }
+      if (kb < r.k_end) {
+        // the last block: its copy slot fetches the next item's first block instead
+        if (lead) {
+          find_next();
+          if (have_next && r_n.k_begin < r_n.k_end)
+            copy_block(it_n, r_n, att_block_pages(a, r_n.sp, r_n.k_begin), r_n.k_begin, buf ^ 1);
+        }
+        scores(sm.K[buf], sc);
+        if (!lead) find_next();
+        if (have_next) {
+          load_pages(r_n);
+          load_q(it_n, r_n);
+        }
+        accumulate(kb, sc, sm.V[buf]);
+        if (have_next) store_pages(sm, r_n);
+        att_wait();        // every wave: the next item's Q and page ids (and copies) complete
+        __syncthreads();   // its first block and page list visible
+        buf ^= 1;
+      }
+    } else {
+      for (int kb = r.k_begin; kb < r.k_end; kb += kAttKeys) {
+        const bool more = kb + kAttKeys < r.k_end;
+        if (more) att_load8<D, NT>(a, r.sp, it.hk, kb + kAttKeys, r.k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+        scores(sm.K[buf], sc);
+        accumulate(kb, sc, sm.V[buf]);
+        if (more) att_wait();
+        __syncthreads();
+        if (more && kb + kAttKeys < r.sp.cached) {
+          att_convert8<D, NT>(a, r.sp, kb + kAttKeys, r.k_end, sm.S, sm.K[buf ^ 1], sm.V[buf ^ 1]);
+          __syncthreads();
+        }
+        buf ^= 1;
+      }
     }
-    if (split_req && g == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
+
+    if (row_ok && row_in) {
+      // O^T tile dt: this lane holds d = 16 dt + 4 g + e (e = 0 .. 3) of its row
+      const bool split_req = it.p.ns > 1;
+      const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+      const int64_t ridx = split_req ? (it.part_off + static_cast<int64_t>(it.split) * it.p.nr + j) * a.Hq + h
+                                     : static_cast<int64_t>(row) * a.Hq + h;
+      uint16_t* orow = (split_req ? a.o_part : a.out) + ridx * D;
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(o[dt][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(o[dt][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+      }
+      if (split_req && g == 0) a.ml_part[ridx] = make_float2(m_ref, l_run);
+    }
+
+    // append (after the output, whose registers it reuses): the split-0 workgroup writes the causal
+    // rows whose first packed row is in its tile
+    if (it.split == 0) {
+      const int j0 = (r.m_tile0 + a.G - 1) / a.G;
+      const int j1 = min(r.sp.n_causal, (r.m_tile0 + ROWS + a.G - 1) / a.G);
+      if (j0 < j1) {
+        if constexpr (E8)
+          att_append8<D, NT>(a, r.sp, it.hk, j0, j1);
+        else
+          att_append<D, NT>(a, r.sp, it.hk, j0, j1);
+      }
+    }
+
+    t += stride;
+    if (have_next) {
+      ready = r.k_begin < r.k_end;  // prefetched by this item's last block (an item without blocks has none)
+      it = it_n;
+      r = r_n;
+      continue;
+    }
+    ready = false;
+    if (t >= t_end || !pick(t, it)) break;
+    it = att_uniform(it);
+    r = att_range<D>(a, it);
   }
 }
 
@@ -840,17 +982,19 @@ __global__ __launch_bounds__(att_threads(D), 2) void attend_mfma16_kernel(AttArg
   const int64_t lo = (blockIdx.x % 8) * per_xcd;
   const int64_t hi = min(n_items, lo + per_xcd);
   const int64_t stride = gridDim.x / 8;  // the grid is a multiple of 8
-  for (int64_t t = lo + blockIdx.x / 8; t < hi; t += stride) {
-    AttItem it{0, 0, 0, 0, AttReqPlan{0, 0, 0, kAttKeys}, 0};
+  // (the pick's answer and the walk's bounds are the same in every lane: kept in scalar registers, so
+  // that the walk's control flow, and what it carries from item to item, stays scalar)
+  auto pick = [&](int64_t ti, AttItem& it) -> bool {
+    bool found;
     if (one_pass) {
-      if (!att_pick(a, t, 0, p0, items0, inc_i0 - items0, inc_p0 - part0, it)) break;
+      found = att_pick(a, ti, 0, p0, items0, inc_i0 - items0, inc_p0 - part0, it);
     } else {
-      it = att_find(a, t);
-      if (it.p.ns == 0) break;  // not reached for t below the total
+      it = att_find(a, ti);
+      found = it.p.ns != 0;  // not false for ti below the total
     }
-    att_run_item<D, E8>(a, sm, it);
-    __syncthreads();  // the next item overwrites the LDS blocks and page list
-  }
+    return att_u(found ? 1 : 0) != 0;
+  };
+  att_walk<D, E8>(a, sm, att_u64(lo + blockIdx.x / 8), att_u64(hi), att_u64(stride), pick);
 }
 
 // Combine the KV splits of a split request: out = sum_s c_s Ohat_s / sum_s c_s with
