@@ -798,6 +798,41 @@ def bench_block_draft(K: int, W: int, cpu: bool) -> dict:
                       {"attention_us_per_pass": att_ms * 1000.0,
                        "accepted_mean": float(np.minimum(gmm, L16).mean()), "settle_steps": n_settle})
 
+def pe_probe(passes: int = 3) -> dict:
+    """Self-conditioning passes of the batched configuration (32 x 256 rows, V 262144, d 4096) on
+    synthetic inputs: N(0, 2^2) logits through dg_denoise_sample_sc for the operand, then
+    dg_selfcond_embed_sc `passes` times.  Few kernels run besides the M = 8192 P.E GEMM, so profiler
+    counters (which serialise every kernel) take seconds, where the batched loop's would not."""
+    import torch
+    import denoise_step_amd as dg
+    import synth
+    from synth.configs import BATCHED as c
+    B, C, V, d, hid, s = c["B"], c["C"], c["V"], c["d"], c["hidden"], c["seed"]
+    bf, dev = torch.bfloat16, "cuda"
+    log("pe probe: inputs")
+    logits = synth.normal_torch(s, "pe_probe.logits", (B * C, V), 2.0, bf, dev)
+    E = synth.normal_torch(s, "pe_probe.E", (V, d), 0.02, bf, dev)
+    wg = synth.normal_torch(s, "pe_probe.wg", (d, hid), 0.02, bf, dev)
+    wu = synth.normal_torch(s, "pe_probe.wu", (d, hid), 0.02, bf, dev)
+    wd = synth.normal_torch(s, "pe_probe.wd", (hid, d), 0.02, bf, dev)
+    seed = torch.arange(B, dtype=torch.int64, device=dev) * 7 + 1
+    step = torch.zeros(B, dtype=torch.int32, device=dev)
+    sc_on = torch.ones(B, dtype=torch.uint8, device=dev)
+    canvas = torch.as_tensor(synth.rng_for(s, "pe_probe.canvas").integers(0, V, (B, C)).astype("int32"), device=dev)
+    prepared = dg.dg_selfcond_prepare(E, wg, wu, wd)
+    out, op = dg.dg_denoise_sample_sc(logits, V, C, seed, step)
+    torch.cuda.synchronize()
+    del logits
+    x, ms = None, []
+    for i in range(passes):
+        t0 = time.perf_counter()
+        x = dg.dg_selfcond_embed_sc(op, V, out["row_max"], out["row_lnz"], sc_on, canvas, E, prepared, hid, x_out=x)
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t0) * 1e3)
+        log(f"pe probe: pass {i} {ms[-1]:.2f} ms")
+    return {"pe_probe_rows": B * C, "V": V, "d": d, "passes": passes, "ms_per_pass": [round(m, 3) for m in ms]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -821,6 +856,9 @@ def main():
                     help="run the step as a sliding-window layer of this window (0: full attention)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three plain 1 GiB device copies (reference for HBM counter calibration)")
+    ap.add_argument("--pe-probe", action="store_true",
+                    help="only run three batched self-conditioning passes (P.E over 32 x 256 rows, the MLP) on "
+                         "synthetic inputs: a short run for the counters of the M = 8192 P.E GEMM")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (no sharding, no collectives); "
@@ -840,6 +878,9 @@ def main():
         return
     import denoise_step_amd as dg
     dg.lib()
+    if args.pe_probe:
+        print(json.dumps(pe_probe()), flush=True)
+        return
     if args.serving:
         print(json.dumps(serving_bench()), flush=True)
         return
