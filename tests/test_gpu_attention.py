@@ -63,6 +63,17 @@ def test_attention_single_canvas_full_size():
     run_case([(2048, 0, 256)], 16, 8, 256, "bf16", seed=7)
 
 
+def test_attention_walk_with_empty_items():
+    """More work items than the grid's 4096 workgroups, so workgroups walk several items: 48 requests
+    of 1000 causal + 24 canvas rows, nothing cached, Hq = Hkv = 2, head_dim 128 -> 8 key splits per
+    request and 6144 items, 2304 of them empty (early causal tiles see no key of the later splits).
+    By the launch's item numbering, 1280 walks go from an item that prefetches its successor and 768
+    from an empty item (which cannot), so both ways of starting an item run; every row against the
+    oracle."""
+    print("attention walk with empty items", flush=True)
+    run_case([(0, 1000, 24)] * 48, 2, 2, 128, "bf16", seed=11)
+
+
 def test_attention_tiny_loop_shapes_f32():
     """The tiny loop's launches: 32-row causal prefill, 16-row canvas over 32, 16-row commit pass."""
     for sp in ([(0, 32, 0)], [(32, 0, 16)], [(32, 16, 0)]):
