@@ -958,19 +958,29 @@ DG_DEV void att_walk(const AttArgs& a, AttSmem<D, E8>& sm, int64_t t, int64_t t_
 template <int D, bool E8>
 __global__ __launch_bounds__(att_threads(D), 2) void attend_mfma16_kernel(AttArgs a) {  // two waves per SIMD
   __shared__ __attribute__((aligned(1024))) AttSmem<D, E8> sm;
-  // requests 0 .. 63: their plans and prefix sums stay in registers (one pass for launches of up to
-  // 64 requests; larger launches rescan the descriptors per item)
+  // The plans and prefix sums of the first kGroups x 64 requests stay in registers, one request per
+  // lane and group (launches of up to that many requests pick their items from registers; larger
+  // ones rescan the descriptors per item).  Two groups at head size 128, where the registers allow
+  // them (launches of 128 requests, as a batch of draft blocks, are common there); one at 256.
+  constexpr int kGroups = D > 128 ? 1 : 2;
   const int lane = threadIdx.x & (kWave - 1);
-  AttReqPlan p0;
-  int64_t items0, part0;
+  AttReqPlan p0, p1;
+  int64_t items0, part0, items1 = 0, part1 = 0;
   att_req_counts(a, lane, p0, items0, part0);
   const int64_t inc_i0 = wave_incl_scan(items0), inc_p0 = wave_incl_scan(part0);
-  const bool one_pass = a.n_req <= kWave;
+  const int64_t tot_i0 = __shfl(inc_i0, kWave - 1, kWave), tot_p0 = __shfl(inc_p0, kWave - 1, kWave);
+  int64_t inc_i1 = tot_i0, inc_p1 = tot_p0;
+  if constexpr (kGroups > 1) {
+    att_req_counts(a, kWave + lane, p1, items1, part1);
+    inc_i1 = tot_i0 + wave_incl_scan(items1);
+    inc_p1 = tot_p0 + wave_incl_scan(part1);
+  }
+  const bool one_pass = a.n_req <= kGroups * kWave;
   int64_t n_items, n_part;
   bool ok;
   if (one_pass) {
-    n_items = __shfl(inc_i0, kWave - 1, kWave);
-    n_part = __shfl(inc_p0, kWave - 1, kWave);
+    n_items = __shfl(inc_i1, kWave - 1, kWave);
+    n_part = __shfl(inc_p1, kWave - 1, kWave);
     ok = n_items <= a.item_cap && n_part <= a.part_cap;
   } else {
     ok = att_totals(a, n_items, n_part);
@@ -988,6 +998,8 @@ __global__ __launch_bounds__(att_threads(D), 2) void attend_mfma16_kernel(AttArg
     bool found;
     if (one_pass) {
       found = att_pick(a, ti, 0, p0, items0, inc_i0 - items0, inc_p0 - part0, it);
+      if constexpr (kGroups > 1)
+        found = found || att_pick(a, ti, kWave, p1, items1, inc_i1 - items1, inc_p1 - part1, it);
     } else {
       it = att_find(a, ti);
       found = it.p.ns != 0;  // not false for ti below the total
