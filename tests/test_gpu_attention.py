@@ -74,6 +74,23 @@ def test_attention_walk_with_empty_items():
     run_case([(0, 1000, 24)] * 48, 2, 2, 128, "bf16", seed=11)
 
 
+def _many_requests(n):
+    """n small mixed requests; every ninth one has a long cached prefix, so its keys are split."""
+    return [((1500 + 37 * k) if k % 9 == 4 else (k * 13) % 70, k % 3, 1 + k % 5) for k in range(n)]
+
+
+@pytest.mark.parametrize("n_req,Hq,Hkv,D", [
+    (80, 4, 2, 256),    # beyond the 64 requests whose plans stay in registers at head size 256
+    (100, 8, 2, 128),   # the second register group at head size 128
+    (150, 8, 2, 128),   # beyond both groups: descriptors rescanned per item
+])
+def test_attention_many_requests(n_req, Hq, Hkv, D):
+    """Launches of more requests than one wave's lanes: the kernel's item lookup from the two
+    register groups and from the descriptors themselves; every row against the oracle."""
+    print(f"attention many requests n_req={n_req} D={D}", flush=True)
+    run_case(_many_requests(n_req), Hq, Hkv, D, "bf16", seed=n_req)
+
+
 def test_attention_tiny_loop_shapes_f32():
     """The tiny loop's launches: 32-row causal prefill, 16-row canvas over 32, 16-row commit pass."""
     for sp in ([(0, 32, 0)], [(32, 0, 16)], [(32, 16, 0)]):
