@@ -160,16 +160,23 @@ class Workload:
         Hq, Hkv, D, ps, L = c["Hq"], c["Hkv"], c["D"], c["page_size"], c["L"]
         s = c["seed"]
         log("generating inputs on the GPU")
-        self.q = synth.normal_torch(s, "bench.q", (C, Hq, D), 1.0, bf, dev)
-        self.k = synth.normal_torch(s, "bench.k", (C, Hkv, D), 1.0, bf, dev)
-        self.v = synth.normal_torch(s, "bench.v", (C, Hkv, D), 1.0, bf, dev)
+        # the attention inputs (Q/K/V rows and the paged cache) rotate through a pool of distinct sets,
+        # like the logits, so a step never finds the previous step's KV in the Infinity Cache
         n_pages = L // ps + 2
-        if c["e4m3"]:
-            self.k_cache = synth.e4m3_table_torch(s, "bench.kc8", (n_pages, Hkv, ps, D), 1.0, KV_SCALES[0], dev)
-            self.v_cache = synth.e4m3_table_torch(s, "bench.vc8", (n_pages, Hkv, ps, D), 1.0, KV_SCALES[1], dev)
-        else:
-            self.k_cache = synth.normal_torch(s, "bench.kc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
-            self.v_cache = synth.normal_torch(s, "bench.vc", (n_pages, Hkv, ps, D), 1.0, bf, dev)
+        self.att_pool = []
+        for i in range(c["pool"]):
+            tag = (lambda name: name) if i == 0 else (lambda name, i=i: (name, i))
+            a = dict(q=synth.normal_torch(s, tag("bench.q"), (C, Hq, D), 1.0, bf, dev),
+                     k=synth.normal_torch(s, tag("bench.k"), (C, Hkv, D), 1.0, bf, dev),
+                     v=synth.normal_torch(s, tag("bench.v"), (C, Hkv, D), 1.0, bf, dev))
+            if c["e4m3"]:
+                a["kc"] = synth.e4m3_table_torch(s, tag("bench.kc8"), (n_pages, Hkv, ps, D), 1.0, KV_SCALES[0], dev)
+                a["vc"] = synth.e4m3_table_torch(s, tag("bench.vc8"), (n_pages, Hkv, ps, D), 1.0, KV_SCALES[1], dev)
+            else:
+                a["kc"] = synth.normal_torch(s, tag("bench.kc"), (n_pages, Hkv, ps, D), 1.0, bf, dev)
+                a["vc"] = synth.normal_torch(s, tag("bench.vc"), (n_pages, Hkv, ps, D), 1.0, bf, dev)
+            self.att_pool.append(a)
+        self.q = self.att_pool[0]["q"]
         self.page_table = torch.as_tensor(synth.page_table(s, "bench.pages", n_pages)[: L // ps].copy(), device=dev)
         self.splits = torch.tensor([[0, L, 0, C, 0, c["window"]]], dtype=torch.int32, device=dev)
         # keys the canvas rows see together: the whole request, or the band of a sliding window
@@ -222,12 +229,13 @@ class Workload:
         c, dg, s = self.c, self.dg, self.state
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
+        a = self.att_pool[t % len(self.att_pool)]
         if c["e4m3"]:
-            dg.dg_canvas_attention_e4m3(self.q, self.k, self.v, self.k_cache, self.v_cache, *KV_SCALES,
+            dg.dg_canvas_attention_e4m3(a["q"], a["k"], a["v"], a["kc"], a["vc"], *KV_SCALES,
                                         self.page_table, self.splits, c["C"], self.key_span, self.scale,
                                         out=self.att_out)
         else:
-            dg.dg_canvas_attention(self.q, self.k, self.v, self.k_cache, self.v_cache, self.page_table, self.splits,
+            dg.dg_canvas_attention(a["q"], a["k"], a["v"], a["kc"], a["vc"], self.page_table, self.splits,
                                    c["C"], self.key_span, self.scale, out=self.att_out)
         rec(1)
         if c["lmhead"]:
@@ -301,14 +309,19 @@ def cpu_baseline(w: Workload, steps: int):
     C, V, D = c["C"], c["V"], c["D"]
     log(f"cpu baseline: copying the inputs of {steps} steps to the host")
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-    q = f64(w.q)
-    k_new, v_new = f64(w.k), f64(w.v)
     if c["e4m3"]:
         from oracle import fp8
-        kc, vc = (fp8.decode_table(t.cpu().numpy(), sc) for t, sc in zip((w.k_cache, w.v_cache), KV_SCALES))
+    att = []  # each step's attention inputs (the pool set the GPU step uses)
+    for t in range(steps):
+        a = w.att_pool[t % len(w.att_pool)]
+        if c["e4m3"]:
+            kc, vc = (fp8.decode_table(x.cpu().numpy(), sc) for x, sc in zip((a["kc"], a["vc"]), KV_SCALES))
+        else:
+            kc, vc = f64(a["kc"]), f64(a["vc"])
+        att.append((f64(a["q"]), f64(a["k"]), f64(a["v"]), kc, vc))
+    if c["e4m3"]:
         E = fp8.decode_table(w.E.cpu().numpy(), E4M3_SCALE)
     else:
-        kc, vc = f64(w.k_cache), f64(w.v_cache)
         E = w.E.float().cpu().numpy()
     pt = w.page_table.cpu().numpy()
     if c["lmhead"]:
@@ -323,6 +336,7 @@ def cpu_baseline(w: Workload, steps: int):
     t0 = time.perf_counter()
     for t in range(steps):
         logits = backbone.lm_head(hpool[t], E, LMHEAD["scale"]) if c["lmhead"] else pool[t]
+        q, k_new, v_new, kc, vc = att[t]
         K, Vv = attention.gather_request_kv(kc, vc, k_new, v_new, pt, 0, c["L"], 0, C, 0, c["page_size"])
         group = c["Hq"] // c["Hkv"]
         mask = attention.visibility_mask(c["L"], 0, C, c["window"])
