@@ -201,6 +201,39 @@ class ServingLoop:
                 self.phase[r] = COMMIT
         return rec
 
+    def checkpoint(self) -> dict:
+        """The loop's state between two iterations: the host scheduling state (phases, cached tokens,
+        finished blocks, queue, deficit) and copies of every device buffer a later iteration reads (the
+        per-request state, the paged KV cache, the sampler outputs, and with self-conditioning the
+        probability operand and the next-step embedding).  The library keeps no state of its own and
+        every random draw is keyed by (seed, step, position), so restoring this into a loop over the same
+        schedule and input pools continues it exactly."""
+        dev = {f"state.{k}": v.clone() for k, v in self.state.items()}
+        dev.update({f"so.{k}": v.clone() for k, v in self.so.items()})
+        dev.update(k_cache=self.t["k_cache"].clone(), v_cache=self.t["v_cache"].clone())
+        if self.sc is not None:
+            dev.update(operand=self.operand.clone(), x=self.x.clone())
+        host = dict(phase=self.phase.copy(), cached=self.cached.copy(), blocks_done=self.blocks_done.copy(),
+                    queue=list(self.queue), deficit=self.deficit, steady=self.steady)
+        return dict(host=host, device=dev)
+
+    def restore(self, ck: dict) -> None:
+        """Continue from a checkpoint() of a loop with the same configuration, schedule and input pools
+        (device buffers are copied into this loop's own)."""
+        dev = ck["device"]
+        for k, v in self.state.items():
+            v.copy_(dev[f"state.{k}"])
+        for k, v in self.so.items():
+            v.copy_(dev[f"so.{k}"])
+        self.t["k_cache"].copy_(dev["k_cache"])
+        self.t["v_cache"].copy_(dev["v_cache"])
+        if self.sc is not None:
+            self.operand.copy_(dev["operand"])
+            self.x.copy_(dev["x"])
+        h = ck["host"]
+        self.phase, self.cached, self.blocks_done = h["phase"].copy(), h["cached"].copy(), h["blocks_done"].copy()
+        self.queue, self.deficit, self.steady = list(h["queue"]), h["deficit"], h["steady"]
+
     def run(self, max_iters: int = 100000, record: bool = False, first: int = 0):
         log = []
         for it in range(first, first + max_iters):

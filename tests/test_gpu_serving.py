@@ -207,3 +207,66 @@ def test_batched_loop_lockstep_sampled_requests():
     for i, c in enumerate(pending):
         P.check_bf16_output(c["x"], c["e"] + (y_ref[4 * i:4 * i + 4] if c["on"] else 0.0))
     assert any(not c["on"] for c in pending) and any(c["on"] for c in pending)
+
+
+def test_serving_loop_checkpoint_resume():
+    """Checkpoint / resume: a loop that runs some iterations, is checkpointed and continues, against a
+    fresh loop (its own workspaces, KV cache and state buffers) restored from that checkpoint and run
+    over the same iterations: schedules, attention outputs, canvases, commits, next-step embeddings
+    and the final state and caches must be bitwise equal."""
+    import torch
+
+    import denoise_step_amd as dg
+    from denoise_step_amd.serving import DONE, ServingLoop
+    cfg = dict(SERVING_SMALL, token_budget=72)
+    print("serving loop small: checkpoint after 6 iterations, resume in a fresh loop", flush=True)
+    sched = synth.serving_schedule_inputs(cfg)
+    host = synth.serving_small_tensors(cfg, sched)
+    V, d, h = cfg["V"], cfg["d"], cfg["hidden"]
+    E = P.dev_bf16(synth.normal_bf16(cfg["seed"], "serving.E", (V, d), 1 / 8))
+    w = [P.dev_bf16(synth.normal_bf16(cfg["seed"], t, sh, 0.5))
+         for t, sh in (("serving.wg", (d, h)), ("serving.wu", (d, h)), ("serving.wd", (h, d)))]
+    prepared = dg.dg_selfcond_prepare(E, *w)
+    sc = dict(E=E, prepared=prepared, hidden=h)
+
+    def fresh():
+        return ServingLoop(cfg, sched, {k: P.dev_bf16(v) for k, v in host.items()}, selfcond=sc)
+
+    first = 6
+    a = fresh()
+    for it in range(first):
+        a.step(it)
+    ck = a.checkpoint()
+    b = fresh()
+    b.restore(ck)
+    recs = {}
+    for name, loop in (("continued", a), ("resumed", b)):
+        out = []
+        for it in range(first, first + 40):
+            if np.all(loop.phase == DONE):
+                break
+            r = loop.step(it, record=True)
+            r.pop("gpu_ms")
+            out.append(r)
+        torch.cuda.synchronize()
+        recs[name] = out
+    assert len(recs["continued"]) == len(recs["resumed"]) > 5
+    n_commit = 0
+    for g, o in zip(recs["continued"], recs["resumed"]):
+        t = g["iteration"]
+        assert (g["admitted"], g["tokens"], g["deficit"]) == (o["admitted"], o["tokens"], o["deficit"]), t
+        assert ("splits" in g) == ("splits" in o), t
+        if "splits" in g:
+            assert np.array_equal(g["splits"], o["splits"]), t
+        if "attention" in g:
+            assert np.array_equal(g["attention"], o["attention"]), t
+        assert np.array_equal(g["canvas"], o["canvas"]), t
+        assert sorted(g["committed"]) == sorted(o["committed"]), t
+        assert all(np.array_equal(g["committed"][r], o["committed"][r]) for r in g["committed"]), t
+        n_commit += len(g["committed"])
+        if "x_next" in g:
+            assert np.array_equal(g["x_next"], o["x_next"]), t
+    assert n_commit >= 1
+    for k in a.state:
+        assert torch.equal(a.state[k], b.state[k]), k
+    assert torch.equal(a.t["k_cache"], b.t["k_cache"]) and torch.equal(a.t["v_cache"], b.t["v_cache"])
