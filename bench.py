@@ -875,7 +875,7 @@ def main():
                          "synthetic inputs: a short run for the counters of the M = 8192 P.E GEMM")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (no sharding, no collectives); "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (no sharding, no collectives); "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
