@@ -60,6 +60,11 @@ def test_host_validation_rejects_before_launch(L):
     att = lambda D=128, ps=16, Hq=16, Hkv=8: L.dg_canvas_attention(64, 64, 64, 64, 64, 4, 64, 4, 64, 1, 16, 16, 32,
                                                                      Hq, Hkv, D, ps, 0.1, 1, 64, None, 0, None)
     assert att(D=96) == -2 and att(ps=32) == -2 and att(Hq=12, Hkv=8) == -1
+    # the MFMA path's longest key span: 261120 keys pass validation (then the missing workspace is
+    # reported), one more is unsupported
+    keys = lambda mk: L.dg_canvas_attention(64, 64, 64, 64, 64, 4, 64, 4, 64, 1, 16, 16, mk, 16, 8, 128, 16, 0.1, 1,
+                                            64, None, 0, None)
+    assert keys(261120) == -3 and keys(261121) == -2
     # self-conditioning: bf16 requires d, hidden multiples of 128 and a prepared table
     assert L.dg_selfcond_embed(64, 1024, 1, 1.0, 64, 64, 64, 64, 1, 16, 64, 64, 64, 64, None, 1024, 128, 128, 64,
                                None, None, 64, 1 << 30, None) == -1

@@ -106,6 +106,18 @@ def test_attention_causal_rows_with_key_splits(splits, Hq, Hkv, D):
     run_case(splits, Hq, Hkv, D, "bf16", seed=21)
 
 
+@pytest.mark.parametrize("splits,Hq,Hkv,D", [
+    ([(261120 - 12, 4, 8)], 2, 1, 128),          # the longest supported key span: 16 splits of 255 blocks
+    ([(100000, 3, 5), (40, 2, 2)], 4, 2, 256),    # past one split's 1024 staged pages at head size 256
+])
+def test_attention_longest_prefix(splits, Hq, Hkv, D):
+    """Prefixes so long that a request needs more key splits than its work-item target asks for (each
+    split's page list staged in LDS holds 1024 pages): every row against the oracle, causal rows appended
+    at the end of the long cache."""
+    print(f"attention long prefix {splits[0][0]} keys D={D}", flush=True)
+    run_case(splits, Hq, Hkv, D, "bf16", seed=31)
+
+
 WINDOWED = [
     ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 32, 2, "f32"),      # the W = 2 three-request figure
     ([(0, 6, 0), (6, 0, 4), (6, 4, 0)], 2, 1, 128, 2, "bf16"),
